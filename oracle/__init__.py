@@ -1,0 +1,18 @@
+"""The oracle: a plain CPU reference for the MoE grouped GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__.py
+and the cpu_baseline leg of bench.py may import it.  The HIP library and its
+Python binding never import it, and it shares no code with them.
+
+Parts:
+- accounting.py: the exact integer padding accounting and tile lists, in
+  Python ints and Fractions.
+- oracle.c with gemm.py: fp64 per-expert dot products for the contiguous,
+  masked and K-grouped layouts.  They read the same bf16 / e4m3 bits the GPU
+  receives and decode them with their own decoders.
+
+Every function states the page and section it follows.  Parity pins live in
+tests/test_oracle_*.py and tests/golden/.
+"""
+from . import accounting  # noqa: F401
+from . import gemm  # noqa: F401

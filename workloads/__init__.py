@@ -1,0 +1,282 @@
+"""Seeded synthetic inputs for the MoE grouped GEMM.
+
+This module is shared test and benchmark infrastructure.  It feeds the same
+bits to both sides of every parity check: the HIP library and the CPU oracle.
+It draws per-expert count histograms and operand values, then stores the
+operands in the formats the GEMM consumes:
+
+- bf16, rounded to nearest-even from fp32;
+- OCP e4m3fn codes with fp32 scales, one per 1x128 row group of the
+  activations and one per 128x128 block of the weights.
+
+It holds none of the grouped GEMM's own arithmetic: no tiling, no padding
+accounting, no products or sums over K.
+
+The histograms follow the pages:
+
+- the near-uniform and concentrated eight-expert examples of "MoE GroupGEMM
+  padding under expert skew" (sections "Work a near-uniform routing example"
+  and "Contrast a concentrated histogram");
+- the 32-expert histogram printed in the "Background" of the DeepGEMM issue
+  "Query on performance-modeling of MoE Grouped GEMM".
+
+Where the pages give only a shape, seeded draws with the stated
+distributions stand in for real routing traces (none ship with the pages):
+
+- a Zipf(s=1.2) skew over 64 experts with some experts zeroed;
+- Poisson(24) decode counts capped at the capacity;
+- a Dirichlet(0.3) split of 65536 rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+SCALE_GROUP = 128
+
+# ---------------------------------------------------------------- histograms
+
+
+def hist_near_uniform() -> List[int]:
+    """Eight experts, 132 assignments: the near-uniform worked example."""
+    return [17, 17, 17, 17, 16, 16, 16, 16]
+
+
+def hist_concentrated() -> List[int]:
+    """Eight experts, 132 assignments, two active: the concentrated example."""
+    return [100, 32, 0, 0, 0, 0, 0, 0]
+
+
+def hist_issue_32() -> List[int]:
+    """The 32-expert per-expert M histogram printed in the DeepGEMM issue."""
+    return [4, 1026, 1799, 166, 694, 753, 0, 16, 0, 240, 1119, 19, 6, 0, 46, 659,
+            10, 0, 112, 808, 181, 0, 28, 22, 90, 0, 176, 0, 37, 5, 10, 22]
+
+
+def hist_zipf(seed: int, experts: int = 64, total: int = 32768, s: float = 1.2,
+              p_zero: float = 0.2) -> List[int]:
+    """Zipf-skewed routing over `experts`, with some experts receiving nothing.
+
+    Draw order: a permutation that assigns Zipf ranks to experts, then a
+    Bernoulli(p_zero) mask that zeroes experts, then the multinomial split of
+    `total` rows over the surviving weights r^-s.
+    """
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(experts)
+    w = np.empty(experts, dtype=np.float64)
+    w[perm] = np.arange(1, experts + 1, dtype=np.float64) ** (-s)
+    zero = rng.random(experts) < p_zero
+    if zero.all():
+        zero[perm[0]] = False
+    w[zero] = 0.0
+    return [int(x) for x in rng.multinomial(total, w / w.sum())]
+
+
+def hist_poisson_masked(seed: int, experts: int = 32, cap: int = 256, mean: float = 24.0,
+                        p_zero: float = 0.2) -> List[int]:
+    """Decode-time valid-row counts: Poisson(mean) clipped to [0, cap], some forced to 0."""
+    rng = np.random.default_rng(seed)
+    m = np.clip(rng.poisson(mean, experts), 0, cap)
+    m[rng.random(experts) < p_zero] = 0
+    return [int(x) for x in m]
+
+
+def hist_dirichlet(seed: int, experts: int = 16, total: int = 65536, alpha: float = 0.3) -> List[int]:
+    """Rows per expert for the weight-gradient case: a Dirichlet(alpha) split of `total`."""
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.full(experts, alpha))
+    return [int(x) for x in rng.multinomial(total, p)]
+
+
+# ---------------------------------------------------------------- operand values
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def fp32_uniform(shape, lo: float, hi: float, seed: int, device="cpu") -> torch.Tensor:
+    x = torch.rand(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    return x.mul_(hi - lo).add_(lo)
+
+
+def fp32_normal(shape, std: float, seed: int, device="cpu") -> torch.Tensor:
+    x = torch.randn(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    return x.mul_(std)
+
+
+def to_bf16(x: torch.Tensor) -> torch.Tensor:
+    """Round to bf16, nearest-even (torch's conversion)."""
+    return x.to(torch.bfloat16)
+
+
+def _to_e4m3(x: torch.Tensor) -> torch.Tensor:
+    # torch's cast does not saturate (values past 448 become NaN): clamp first.
+    return x.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+
+
+def quantize_rows_e4m3(x: torch.Tensor):
+    """Activations [..., K] -> (e4m3 codes [..., K], fp32 scales [..., K/128]).
+
+    One scale per 1x128 group along K: s = amax/448 (s = 1 for an all-zero
+    group), code = e4m3(x / s).
+    """
+    *lead, k = x.shape
+    assert k % SCALE_GROUP == 0
+    g = x.float().reshape(*lead, k // SCALE_GROUP, SCALE_GROUP)
+    amax = g.abs().amax(dim=-1, keepdim=True)
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = _to_e4m3(g / s).reshape(*lead, k)
+    return q, s.squeeze(-1).contiguous()
+
+
+def quantize_blocks_e4m3(w: torch.Tensor):
+    """Weights [G, K, N] -> (e4m3 codes [G, K, N], fp32 scales [G, K/128, N/128]).
+
+    One scale per 128x128 block of (K, N): s = amax/448 (1 if all zero).
+    Done one expert at a time to bound temporary memory.
+    """
+    G, K, N = w.shape
+    assert K % SCALE_GROUP == 0 and N % SCALE_GROUP == 0
+    kb, nb = K // SCALE_GROUP, N // SCALE_GROUP
+    q = torch.empty((G, K, N), dtype=torch.float8_e4m3fn, device=w.device)
+    s = torch.empty((G, kb, nb), dtype=torch.float32, device=w.device)
+    for e in range(G):
+        blk = w[e].float().reshape(kb, SCALE_GROUP, nb, SCALE_GROUP)
+        amax = blk.abs().amax(dim=(1, 3), keepdim=True)
+        se = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        q[e] = _to_e4m3(blk / se).reshape(K, N)
+        s[e] = se.reshape(kb, nb)
+    return q, s
+
+
+# ---------------------------------------------------------------- workloads
+
+
+@dataclass
+class Workload:
+    """One grouped-GEMM problem: layout, sizes, histogram and value recipe."""
+    name: str
+    layout: str                 # "contiguous" | "masked" | "k_grouped"
+    dtype: str                  # "bf16" | "fp8"
+    counts: List[int]           # m_sizes / masked_m / t_sizes
+    K: int = 0                  # shared inner width (contiguous / masked)
+    N: int = 0                  # shared output width (contiguous / masked)
+    seg_align: int = 1          # contiguous only
+    cap: int = 0                # masked only
+    Mw: int = 0                 # k_grouped: dW rows
+    Nw: int = 0                 # k_grouped: dW cols
+    values: str = "normal"      # "uniform" | "normal" | "normal_unit"
+    seed: int = 0
+    extra: Dict = field(default_factory=dict)
+
+    @property
+    def G(self) -> int:
+        return len(self.counts)
+
+    @property
+    def rows_total(self) -> int:
+        """Rows of the contiguous A buffer: every segment padded to seg_align."""
+        a = self.seg_align
+        return sum((c + a - 1) // a * a for c in self.counts)
+
+    @property
+    def useful_rows(self) -> int:
+        return sum(self.counts)
+
+    def useful_flops(self) -> int:
+        if self.layout == "k_grouped":
+            return 2 * self.Mw * self.Nw * sum(self.counts)
+        return 2 * sum(self.counts) * self.K * self.N
+
+
+def workload(n: int) -> Workload:
+    """The five benchmark problems, by number 1..5."""
+    if n == 1:
+        return Workload("near-uniform 8 experts bf16 contiguous", "contiguous", "bf16",
+                        hist_near_uniform(), K=512, N=256, values="uniform", seed=1)
+    if n == 2:
+        return Workload("issue histogram 32 experts bf16 contiguous aligned", "contiguous", "bf16",
+                        hist_issue_32(), K=7168, N=4096, seg_align=128, values="normal", seed=2)
+    if n == 3:
+        return Workload("zipf 64 experts fp8 contiguous", "contiguous", "fp8",
+                        hist_zipf(3), K=7168, N=4096, values="normal", seed=3)
+    if n == 4:
+        return Workload("masked decode 32 experts bf16", "masked", "bf16",
+                        hist_poisson_masked(4), K=2048, N=7168, cap=256, values="normal", seed=4)
+    if n == 5:
+        return Workload("k-grouped weight gradient 16 experts bf16", "k_grouped", "bf16",
+                        hist_dirichlet(5), Mw=2048, Nw=7168, values="normal_unit", seed=5)
+    raise ValueError(f"no workload {n}")
+
+
+def _values(shape, wl: Workload, inner: int, seed: int, device) -> torch.Tensor:
+    if wl.values == "uniform":
+        return fp32_uniform(shape, -1.0, 1.0, seed, device)
+    if wl.values == "normal":
+        return fp32_normal(shape, 1.0 / float(np.sqrt(inner)), seed, device)
+    return fp32_normal(shape, 1.0, seed, device)
+
+
+def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw the operands of `wl` on `device`.
+
+    contiguous: A [rows_total, K], B [G, K, N], counts int32 [G]
+    masked:     A [G, cap, K],     B [G, K, N], counts int32 [G]
+    k_grouped:  X [T, Mw], dY [T, Nw],          counts int32 [G]
+    fp8 adds A_scale [..., K/128] and B_scale [G, K/128, N/128].
+    Rows that belong to no expert (segment alignment gaps, capacity rows
+    beyond the valid count) hold NaN when nan_padding is set, so that any
+    leak of padding into a valid output shows.
+    """
+    out: Dict[str, Optional[torch.Tensor]] = {
+        "counts": torch.tensor(wl.counts, dtype=torch.int32, device=device)}
+    s = wl.seed * 1000
+    if wl.layout == "k_grouped":
+        T = sum(wl.counts)
+        out["X"] = to_bf16(_values((T, wl.Mw), wl, T, s + 1, device))
+        out["dY"] = to_bf16(_values((T, wl.Nw), wl, T, s + 2, device))
+        return out
+    if wl.layout == "contiguous":
+        a_shape = (wl.rows_total, wl.K)
+    else:
+        a_shape = (wl.G, wl.cap, wl.K)
+    a = _values(a_shape, wl, wl.K, s + 1, device)
+    if nan_padding:
+        valid = _valid_row_mask(wl, device)
+        a[~valid.reshape(a_shape[:-1])] = float("nan")
+    b = _values((wl.G, wl.K, wl.N), wl, wl.K, s + 2, device)
+    if wl.dtype == "bf16":
+        out["A"], out["A_scale"] = to_bf16(a), None
+        out["B"], out["B_scale"] = to_bf16(b), None
+    else:
+        a_nan = torch.isnan(a)
+        a = a.nan_to_num(0.0)
+        qa, sa = quantize_rows_e4m3(a)
+        # keep padding rows poisoned: e4m3fn NaN code plus a NaN scale
+        qa.view(torch.uint8)[a_nan] = 0x7F
+        sa[a_nan.reshape(*a_nan.shape[:-1], -1, SCALE_GROUP).any(-1)] = float("nan")
+        del a
+        qb, sb = quantize_blocks_e4m3(b)
+        out["A"], out["A_scale"], out["B"], out["B_scale"] = qa, sa, qb, sb
+    return out
+
+
+def _valid_row_mask(wl: Workload, device) -> torch.Tensor:
+    """True for rows that belong to some expert's valid segment."""
+    if wl.layout == "masked":
+        r = torch.arange(wl.cap, device=device)
+        m = torch.tensor(wl.counts, device=device).clamp(0, wl.cap)
+        return (r[None, :] < m[:, None]).reshape(-1)
+    mask = torch.zeros(wl.rows_total, dtype=torch.bool, device=device)
+    off = 0
+    for c in wl.counts:
+        mask[off:off + c] = True
+        off += (c + wl.seg_align - 1) // wl.seg_align * wl.seg_align
+    return mask
