@@ -1,0 +1,216 @@
+"""Benchmark: the MoE grouped GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input
+already resident in HBM:
+    device scheduler (counts -> accounting, tile height, tile list)
+    + the fp8 contiguous grouped GEMM with per-128 fp32 scale promotion.
+
+Default workload: 64 local experts, 32768 routed rows on a seeded Zipf(1.2)
+histogram with some experts empty, K = 7168, N = 4096, e4m3 operands with
+fp32 scales per 1x128 activation group and per 128x128 weight block, bf16
+output, contiguous layout.
+
+Metric: effective TFLOPS = 2 * U * K * N / step time (valid rows only), and its
+fraction of the MI355X dense fp8 MFMA peak.  Physical TFLOPS counts the rows
+the MFMAs actually executed (P_exec).
+
+Prints ONE JSON line on stdout.  `--config n` times another problem (1..5) for
+reporting; the JSON `config.workload` names it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_grouped_gemm_sizes_amd as mg  # noqa: E402
+import workloads as wl  # noqa: E402
+
+PEAK = {"fp8": 5000.0, "bf16": 2500.0}      # dense MFMA TFLOP/s, MI355X
+HBM_PEAK = 8000.0                           # GB/s
+METRIC = "effective TFLOPS (valid rows) + % of MFMA peak, V3-shaped fp8 grouped GEMM"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_step(w: wl.Workload, inp, block_m_hint: int):
+    """Returns (step, gemm_only, outputs) closures for one workload."""
+    dev = "cuda"
+    if w.layout == "contiguous":
+        C = torch.empty((w.rows_total, w.N), dtype=torch.bfloat16, device=dev)
+        ws = mg.workspace(w.G, w.rows_total)
+
+        def sched():
+            mg.schedule(inp["counts"], w.rows_total, ws, seg_align=w.seg_align, block_m=0, N=w.N)
+
+        def gemm():
+            mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"),
+                                                 inp.get("B_scale"), block_m=block_m_hint)
+        return sched, gemm, ws
+    if w.layout == "masked":
+        C = torch.empty((w.G, w.cap, w.N), dtype=torch.bfloat16, device=dev)
+        ws = mg.workspace(w.G, w.G * w.cap)
+
+        def gemm():
+            mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], None, inp.get("A_scale"),
+                                   inp.get("B_scale"))
+        return None, gemm, ws
+    dW = torch.empty((w.G, w.Mw, w.Nw), dtype=torch.float32, device=dev)
+    ws = mg.workspace(w.G, 0)
+
+    def gemm():
+        mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws)
+    return None, gemm, ws
+
+
+def algorithmic_bytes(w: wl.Workload) -> int:
+    """Bytes the method must move once: active experts' weights, valid rows in and out (plus scales)."""
+    active = sum(1 for c in w.counts if c > 0)
+    U = sum(w.counts)
+    if w.layout == "k_grouped":
+        return U * (w.Mw + w.Nw) * 2 + w.G * w.Mw * w.Nw * 4
+    esz = 1 if w.dtype == "fp8" else 2
+    b = active * w.K * w.N * esz + U * w.K * esz + U * w.N * 2
+    if w.dtype == "fp8":
+        b += U * (w.K // 128) * 4 + active * (w.K // 128) * (w.N // 128) * 4
+    return b
+
+
+def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of rows."""
+    from oracle import gemm as og
+    from tests.parity import sample_rows_contiguous
+    og.lib()
+    if w.layout != "contiguous":
+        return None
+    cpu = {k: (v.cpu().contiguous() if v is not None else None) for k, v in inp.items()}
+    rows = sample_rows_contiguous(w.counts, w.seg_align, 256, extra=4096, seed=99)
+    threads = og.threads()
+    probe = rows[:threads]
+    t0 = time.perf_counter()
+    og.contiguous(cpu["A"], cpu["B"], w.counts, probe, seg_align=w.seg_align,
+                  A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
+    dt = time.perf_counter() - t0
+    n = max(threads, min(len(rows), int(target_s / max(dt, 1e-6) * len(probe)) // threads * threads))
+    sample = rows[:n]
+    t0 = time.perf_counter()
+    og.contiguous(cpu["A"], cpu["B"], w.counts, sample, seg_align=w.seg_align,
+                  A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(sample) * w.K * w.N
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} output rows x {w.N} columns of this workload (fp64 oracle, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    mg.lib()
+    w = wl.workload(args.config)
+    log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
+    inp = wl.materialize(w, "cuda")
+    torch.cuda.synchronize()
+
+    # first pass: learn the device's tile-height choice (outside timing)
+    sched, gemm, ws = build_step(w, inp, 0)
+    if sched is not None:
+        sched()
+        torch.cuda.synchronize()
+        st0 = mg.stats_read(ws)
+        sched, gemm, ws = build_step(w, inp, st0.block_m)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        if sched is not None:
+            sched()
+        gemm()
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 2)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        if sched is not None:
+            sched()
+        ev[1 + 2 * i].record(stream)
+        gemm()
+        ev[2 + 2 * i].record(stream)
+    ev[-1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = ev[0].elapsed_time(ev[-1])
+    gemm_ms = [ev[1 + 2 * i].elapsed_time(ev[2 + 2 * i]) for i in range(args.steps)]
+    ms_step = total_ms / args.steps
+    gemm_avg = sum(gemm_ms) / len(gemm_ms)
+
+    st = mg.stats_read(ws) if sched is not None or w.layout != "k_grouped" else None
+    U = sum(w.counts)
+    flops = w.useful_flops()
+    eff = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+    out = {
+        "metric": METRIC if args.config == 3 else f"effective TFLOPS (valid rows), workload {args.config}",
+        "value": round(eff, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if w.dtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
+                   "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed},
+        "pct_mfma_peak": round(100.0 * eff / peak, 2),
+    }
+    if w.layout == "contiguous":
+        phys = 2.0 * st.P_exec * w.K * w.N / (ms_step * 1e-3) / 1e12
+        out.update({"physical_tflops": round(phys, 2), "block_m": st.block_m, "P_exec": st.P_exec,
+                    "padding_fraction_at_block_m": float(st.padding_fraction(st.block_m)),
+                    "effective_experts": round(float(st.effective_experts), 3)})
+    # roofline of the dominant kernel (the GEMM), from HIP events on its own stream
+    achieved_tflops = flops / (gemm_avg * 1e-3) / 1e12
+    bytes_alg = algorithmic_bytes(w)
+    if w.layout == "masked":
+        gbs = bytes_alg / (gemm_avg * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK, 4), "traffic": None}
+    else:
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": peak,
+                           "unit": "TFLOP/s", "frac": round(achieved_tflops / peak, 4), "traffic": None}
+    out["gemm_kernel_ms"] = round(gemm_avg, 4)
+    out["algorithmic_bytes"] = bytes_alg
+    out["wall_s_timed"] = round(wall, 4)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)...")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * moegg.h -- C ABI of the MI355X (gfx950) MoE grouped GEMM library, libmoegg.so.
+ *
+ * The operation: expert e multiplies its m_e routed rows [m_e, K] by its own
+ * weight B_e [K, N].  N and K are shared by all experts.  The counts m_e are
+ * ragged, skewed and often zero.  Grouping tokens by expert changes the
+ * tiling, not the math.  Only M is grouped, because experts share one N and
+ * one K.  (DeepGEMM grouped/masked MoE GEMM record, "Arithmetic intensity".)
+ *
+ * Conventions for every call below:
+ *   - Pointers are device pointers unless the name starts with h_.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *   - Compute calls are asynchronous on `stream`.  They never allocate, never
+ *     synchronize, and never copy to the host, so they can be captured in a
+ *     HIP graph.  Only the *_read calls synchronize.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     keeps no pointer after a call returns.
+ *   - Argument errors are found on the host before anything is enqueued.  The
+ *     call then returns an error code and launches nothing.
+ *   - Bad counts on the device cannot be reported without a host round trip.
+ *     The device clamps them, never reads or writes out of bounds, and sets a
+ *     bit in moegg_stats_t.error_flags.
+ *   - One workspace per stream in flight.  Calls that share a workspace must
+ *     be ordered.
+ */
+#ifndef MOEGG_H
+#define MOEGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOEGG_OK = 0,
+    MOEGG_ERR_INVALID_ARG = 1,   /* null pointer, bad size or count           */
+    MOEGG_ERR_UNSUPPORTED = 2,   /* shape or option this build does not cover */
+    MOEGG_ERR_WORKSPACE = 3,     /* workspace missing or too small            */
+    MOEGG_ERR_HIP = 4            /* a HIP runtime call failed                 */
+} moegg_status_t;
+
+/* Operand storage type.  MOEGG_FP8_E4M3 is OCP e4m3fn (max 448, no inf). */
+typedef enum { MOEGG_BF16 = 0, MOEGG_FP8_E4M3 = 1 } moegg_dtype_t;
+
+/* How each expert's weight B_e is stored.
+ *   MOEGG_B_KN: B[G, K, N], N contiguous.
+ *   MOEGG_B_NK: B[G, N, K], K contiguous.
+ * The fp8 block scales are [G, K/128, N/128] in both cases. */
+typedef enum { MOEGG_B_KN = 0, MOEGG_B_NK = 1 } moegg_b_layout_t;
+
+/* error_flags bits */
+#define MOEGG_FLAG_NEGATIVE_COUNT  0x1u  /* a count < 0 was read as 0                 */
+#define MOEGG_FLAG_ROWS_OVERFLOW   0x2u  /* segments ran past rows_total / T; truncated */
+#define MOEGG_FLAG_COUNT_OVER_CAP  0x4u  /* a masked count > cap was read as cap      */
+
+/* Tile heights the schedule accounts for, in P_at[] order. */
+#define MOEGG_NUM_Q 6                    /* q = 8, 16, 32, 64, 128, 256 */
+
+/*
+ * Padding accounting, written on the device by every scheduled call.  It
+ * follows "MoE GroupGEMM padding under expert skew":
+ *   - section "Calculate padded token columns": U, P(q), P - U;
+ *   - section "Summarize skew without losing the histogram": effective
+ *     experts = U^2 / sum_sq, derived on the host from the exact integers;
+ *   - section "Grouped execution does not require padded experts": capacity
+ *     padding and tail padding are kept apart.
+ */
+typedef struct {
+    int64_t U;               /* useful rows: sum of the (clamped) counts                     */
+    int64_t P_exec;          /* rows the MFMAs executed: each tile's valid rows rounded up to */
+                             /* the kernel's 16-row MFMA block (= tail padding + U)           */
+    int64_t tiles;           /* entries in the tile list (M tiles of height block_m)          */
+    int64_t active;          /* experts with a nonzero count                                  */
+    int64_t sum_sq;          /* sum of squared counts                                         */
+    int64_t capacity_rows;   /* layout rows holding no valid row (alignment gaps, unused cap) */
+    int64_t P_at[MOEGG_NUM_Q]; /* P(q) = sum over active experts of q * ceil(m_e / q)         */
+    int32_t block_m;         /* tile height used                                              */
+    uint32_t error_flags;    /* MOEGG_FLAG_* bits                                             */
+} moegg_stats_t;
+
+/* One entry of the device tile list: expert, tile index within the expert,
+ * first row of the tile in A/C, and valid rows (1..block_m). */
+typedef struct { int32_t expert, tile, row_start, rows_valid; } moegg_tile_t;
+
+/* Library version, (major << 16) | minor. */
+int moegg_version(void);
+
+/* Short text for a status code (static storage). */
+const char* moegg_status_string(moegg_status_t status);
+
+/*
+ * Workspace bytes for a problem with G experts (G = 1..4096) and up to
+ * max_rows rows of A (rows_total for the contiguous layout, G * cap for the
+ * masked one, T for the K-grouped one).  Pure host function.  Returns 0 for
+ * invalid arguments.
+ */
+size_t moegg_workspace_bytes(int G, int64_t max_rows);
+
+/*
+ * Device-side scheduler alone: counts -> tile list + stats in `ws`, with no
+ * host round trip.
+ *
+ * For every expert e with m_e > 0 and every i < ceil(m_e / block_m) it emits
+ *     {e, i, seg_off[e] + i * block_m, min(block_m, m_e - i * block_m)}
+ * in expert-ascending, tile-ascending order, where
+ *     seg_off[e] = sum_{j<e} align_up(m_j, seg_align).
+ * Empty experts emit nothing, so their weights are never loaded.  This is
+ * the variable-M work list of "Grouped execution does not require padded
+ * experts", built from the actual counts.
+ *
+ * block_m must be 64, 128 or 256, or 0 to let the device choose (see
+ * moegg_grouped_gemm_contiguous).  N is the output width of the GEMM the
+ * schedule will feed: the choice rule counts its 256-wide column tiles.
+ * seg_align >= 1.  Segments are truncated at rows_total (flag
+ * MOEGG_FLAG_ROWS_OVERFLOW).
+ */
+moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align,
+                              int block_m, int N, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * M-grouped contiguous layout (DeepGEMM record, "Workarounds": prefill and
+ * training, where token counts are known).
+ *   A        [rows_total, K], row-major.  Expert e's rows start at seg_off[e],
+ *            as in moegg_schedule.  seg_align = 1 packs them back to back.  A
+ *            larger seg_align puts every segment start at a multiple of it.
+ *   A_scale  fp8 only: fp32 [rows_total, K/128], one scale per 1x128 group.
+ *            NULL for bf16.
+ *   B        [G, K, N] or [G, N, K] (b_layout), same dtype as A.
+ *   B_scale  fp8 only: fp32 [G, K/128, N/128], one per 128x128 block.  NULL
+ *            for bf16.
+ *   C        bf16 [rows_total, N], row-major.  Only the rows of valid
+ *            segments are written.  Other rows keep their contents.
+ *   m_sizes  int32 [G] on the device.
+ * Computes, for each valid row R of expert e:
+ *     C[R, n] = bf16_rne( sum_k A[R, k] * B_e[k, n] )
+ * with fp32 accumulation.  For fp8, each 128-wide K group's fp32 partial sum
+ * is multiplied by A_scale[R, k/128] * B_scale[e, k/128, n/128] and added to
+ * the fp32 accumulator.
+ * Constraints: K % 128 == 0 and N % 256 == 0 for fp8.  K % 64 == 0 and
+ * N % 256 == 0 for bf16.  16-byte aligned pointers.  G = 1..4096.
+ * block_m: 64, 128 or 256, or 0 = choose on the device from the histogram.
+ * Every height skips whole 16-row MFMA blocks past a tile's valid rows, so
+ * the executed rows are P(16) for all of them.  What differs is how many
+ * 256x(block_m) tiles there are and how full the last round of tiles is on
+ * 256 CUs.  The device choice minimizes
+ *     cost(q) = ceil(tiles(q) * (N / 256) / 256) * (q + 64)
+ * over q in {64, 128, 256}, with ties going to the larger q (better weight
+ * reuse).  Padding alone does not pick the kernel ("Padding is not the whole
+ * cost model", MoE GroupGEMM padding page).  The grid size is fixed from host
+ * arguments alone, so the call is graph-capturable.
+ */
+moegg_status_t moegg_grouped_gemm_contiguous(
+    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    const int32_t* m_sizes, int G, int64_t rows_total, int K, int N, int seg_align,
+    moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
+    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The contiguous GEMM alone, driven by the tile list that an earlier
+ * moegg_schedule or moegg_grouped_gemm_contiguous call left in `ws`.  One
+ * MoE layer runs several grouped GEMMs over one routing histogram (gate/up,
+ * then down projection); they can share one schedule.  Arguments are those of
+ * moegg_grouped_gemm_contiguous, without m_sizes and seg_align.  The
+ * schedule must come from the same G and rows_total.  block_m = 0 launches
+ * every candidate height, and the scheduled one does the work.  A nonzero
+ * block_m launches only that height; if it differs from the scheduled
+ * height, nothing is written.
+ */
+moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
+    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    int G, int64_t rows_total, int K, int N, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
+    int block_m, const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Masked layout for decode under graph capture (DeepGEMM record,
+ * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
+ * computes only the valid portions, with no CPU sync).
+ *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (fp8) or NULL.
+ *   B        as for the contiguous call.  B_scale as for the contiguous call.
+ *   C        bf16 [G, cap, N].  Only rows r < masked_m[e] are written.
+ *   masked_m int32 [G] on the device, read by the kernel at run time.
+ * The grid depends only on G, cap and N, so a captured graph stays valid when
+ * masked_m changes between replays.  Experts with masked_m[e] = 0 load no
+ * weights.  ws may be NULL (no stats).  Otherwise stats are written as for
+ * the contiguous call, with block_m = the kernel's row tile.
+ * Constraints: as for the contiguous call, plus cap >= 1.
+ */
+moegg_status_t moegg_grouped_gemm_masked(
+    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    const int32_t* masked_m, int G, int cap, int K, int N,
+    moegg_dtype_t dtype, moegg_b_layout_t b_layout,
+    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * K-grouped weight gradient (DeepGEMM record, "Workarounds": MoE weight
+ * backward with M and N fixed and the reduction axis grouped).
+ *   X        bf16 [T, Mw], dY bf16 [T, Nw]: rows grouped by expert in expert
+ *            order, t_sizes[e] rows each (device int32 [G]).
+ *   dW       fp32 [G, Mw, Nw], overwritten:
+ *                dW[e, i, j] = sum over expert e's rows t of X[t, i] * dY[t, j]
+ *            with fp32 accumulation.  t_e = 0 writes zeros.
+ * Experts are started longest first.  Constraints: Mw % 256 == 0,
+ * Nw % 256 == 0, T >= 0.  A workspace is required (expert offsets and
+ * order).
+ */
+moegg_status_t moegg_grouped_gemm_k_grouped(
+    const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G, int64_t T,
+    int Mw, int Nw, void* ws, size_t ws_bytes, void* stream);
+
+/* Copy the stats of the last scheduled call on `ws` to the host.
+ * Synchronizes `stream`. */
+moegg_status_t moegg_stats_read(const void* ws, moegg_stats_t* h_out, void* stream);
+
+/* Copy up to cap_tiles tile-list entries to h_tiles, and the entry count to
+ * *h_n.  Synchronizes `stream`. */
+moegg_status_t moegg_tile_list_read(const void* ws, moegg_tile_t* h_tiles, int64_t cap_tiles,
+                                    int64_t* h_n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEGG_H */

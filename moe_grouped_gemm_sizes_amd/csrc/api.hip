@@ -1,0 +1,209 @@
+// api.hip -- the C ABI declared in include/moegg.h: argument validation,
+// workspace layout and kernel launches.  No call here allocates device
+// memory or synchronizes, except the two *_read calls.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/moegg.h"
+#include "launch.hpp"
+#include "workspace.hpp"
+
+
+using namespace moegg;
+
+namespace {
+
+const int64_t kMaxBufferBytes = 0xFFFFFFF0ll;   // one buffer resource spans < 4 GiB
+
+bool debug_on() {
+    static int on = -1;
+    if (on < 0) {
+        const char* v = getenv("MOEGG_DEBUG");
+        on = (v && v[0] == '1') ? 1 : 0;
+    }
+    return on == 1;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+moegg_status_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MOEGG_OK;
+    if (debug_on()) fprintf(stderr, "moegg: %s failed: %s\n", what, hipGetErrorString(e));
+    return MOEGG_ERR_HIP;
+}
+
+// Shared checks for the contiguous and masked calls.
+moegg_status_t check_common(const void* A, const float* A_scale, const void* B, const float* B_scale,
+                            const void* C, int G, int K, int N, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
+                            int col_tile) {
+    if (!A || !B || !C) return MOEGG_ERR_INVALID_ARG;
+    if (G < 1 || G > kMaxExperts || K < 1 || N < 1) return MOEGG_ERR_INVALID_ARG;
+    if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3) return MOEGG_ERR_INVALID_ARG;
+    if (b_layout != MOEGG_B_KN && b_layout != MOEGG_B_NK) return MOEGG_ERR_INVALID_ARG;
+    const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
+    if (dtype == MOEGG_FP8_E4M3) {
+        if (!A_scale || !B_scale) return MOEGG_ERR_INVALID_ARG;
+        if (!aligned(A_scale, 4) || !aligned(B_scale, 4)) return MOEGG_ERR_INVALID_ARG;
+    }
+    if (K % (128 / esz) != 0 || N % col_tile != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return MOEGG_ERR_INVALID_ARG;
+    if ((int64_t)K * N * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    return MOEGG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moegg_version(void) { return (0 << 16) | 1; }
+
+const char* moegg_status_string(moegg_status_t s) {
+    switch (s) {
+        case MOEGG_OK: return "ok";
+        case MOEGG_ERR_INVALID_ARG: return "invalid argument";
+        case MOEGG_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case MOEGG_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOEGG_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t moegg_workspace_bytes(int G, int64_t max_rows) {
+    if (G < 1 || G > kMaxExperts || max_rows < 0) return 0;
+    return ws_layout(G, max_rows).total;
+}
+
+moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align, int block_m,
+                              int N, void* ws, size_t ws_bytes, void* stream) {
+    if (!m_sizes || G < 1 || G > kMaxExperts || rows_total < 0 || rows_total > INT32_MAX || seg_align < 1)
+        return MOEGG_ERR_INVALID_ARG;
+    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    const WsLayout L = ws_layout(G, rows_total);
+    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+    if (N < 1) return MOEGG_ERR_INVALID_ARG;
+    const int n_col_tiles = N / 256 > 0 ? N / 256 : 1;
+    return hip_status(launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, block_m, n_col_tiles, 0, ws,
+                                   L.max_tiles, (hipStream_t)stream),
+                      "schedule");
+}
+
+moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const float* A_scale, const void* B,
+                                             const float* B_scale, void* C, const int32_t* m_sizes, int G,
+                                             int64_t rows_total, int K, int N, int seg_align,
+                                             moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
+                                             void* ws, size_t ws_bytes, void* stream) {
+    if (!m_sizes || !aligned(m_sizes, 4)) return MOEGG_ERR_INVALID_ARG;
+    moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
+    if (st != MOEGG_OK) return st;
+    if (rows_total < 0 || rows_total > INT32_MAX || seg_align < 1) return MOEGG_ERR_INVALID_ARG;
+    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
+    if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    const WsLayout L = ws_layout(G, rows_total);
+    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, block_m, N / 256, 0, ws, L.max_tiles, s);
+    if (e != hipSuccess) return hip_status(e, "scheduler launch");
+    ContigArgs a{A, A_scale, B, B_scale, C, m_sizes, (const unsigned char*)ws, G, K, N, 0};
+    e = launch_contiguous(a, dtype == MOEGG_FP8_E4M3, b_layout == MOEGG_B_KN, rows_total, block_m, s);
+    if (debug_on())
+        fprintf(stderr, "moegg: contiguous G=%d rows=%lld K=%d N=%d align=%d dtype=%d b_layout=%d block_m=%d\n", G,
+                (long long)rows_total, K, N, seg_align, (int)dtype, (int)b_layout, block_m);
+    return hip_status(e, "contiguous GEMM launch");
+}
+
+moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const float* A_scale, const void* B,
+                                                       const float* B_scale, void* C, int G, int64_t rows_total,
+                                                       int K, int N, moegg_dtype_t dtype,
+                                                       moegg_b_layout_t b_layout, int block_m, const void* ws,
+                                                       size_t ws_bytes, void* stream) {
+    moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
+    if (st != MOEGG_OK) return st;
+    if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
+    if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
+    ContigArgs a{A, A_scale, B, B_scale, C, nullptr, (const unsigned char*)ws, G, K, N, 0};
+    return hip_status(launch_contiguous(a, dtype == MOEGG_FP8_E4M3, b_layout == MOEGG_B_KN, rows_total, block_m,
+                                        (hipStream_t)stream),
+                      "scheduled contiguous GEMM launch");
+}
+
+moegg_status_t moegg_grouped_gemm_masked(const void* A, const float* A_scale, const void* B, const float* B_scale,
+                                         void* C, const int32_t* masked_m, int G, int cap, int K, int N,
+                                         moegg_dtype_t dtype, moegg_b_layout_t b_layout, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    if (!masked_m || !aligned(masked_m, 4)) return MOEGG_ERR_INVALID_ARG;
+    moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, masked_block_n());
+    if (st != MOEGG_OK) return st;
+    if (cap < 1 || (int64_t)G * cap > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
+    if ((int64_t)masked_block_m() * K * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (ws) {
+        if (!aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+        const WsLayout L = ws_layout(G, (int64_t)G * cap);
+        if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+        e = launch_sched(masked_m, G, (int64_t)G * cap, 1, cap, 1, 0, N / masked_block_n(), masked_block_m(), ws,
+                         L.max_tiles, s);
+        if (e != hipSuccess) return hip_status(e, "masked stats launch");
+    }
+    ContigArgs a{A, A_scale, B, B_scale, C, masked_m, (const unsigned char*)ws, G, K, N, cap};
+    e = launch_masked(a, dtype == MOEGG_FP8_E4M3, b_layout == MOEGG_B_KN, s);
+    return hip_status(e, "masked GEMM launch");
+}
+
+moegg_status_t moegg_grouped_gemm_k_grouped(const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G,
+                                            int64_t T, int Mw, int Nw, void* ws, size_t ws_bytes, void* stream) {
+    if (!X || !dY || !dW || !t_sizes) return MOEGG_ERR_INVALID_ARG;
+    if (G < 1 || G > kMaxExperts || T < 0 || Mw < 1 || Nw < 1) return MOEGG_ERR_INVALID_ARG;
+    if (Mw % 256 != 0 || Nw % 256 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(dW, 16) || !aligned(t_sizes, 4))
+        return MOEGG_ERR_INVALID_ARG;
+    if (T * Mw * 2 > kMaxBufferBytes || T * Nw * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    const WsLayout L = ws_layout(G, 0);
+    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_sched_k_grouped(t_sizes, G, T, ws, s);
+    if (e != hipSuccess) return hip_status(e, "K-grouped scheduler launch");
+    KGroupedArgs a{X, dY, dW, (const unsigned char*)ws, G, Mw, Nw};
+    return hip_status(launch_k_grouped(a, s), "K-grouped GEMM launch");
+}
+
+moegg_status_t moegg_stats_read(const void* ws, moegg_stats_t* h_out, void* stream) {
+    if (!ws || !h_out) return MOEGG_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(h_out, ws, sizeof(moegg_stats_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return hip_status(e, "stats read");
+}
+
+moegg_status_t moegg_tile_list_read(const void* ws, moegg_tile_t* h_tiles, int64_t cap_tiles, int64_t* h_n,
+                                    void* stream) {
+    if (!ws || !h_n || cap_tiles < 0 || (cap_tiles > 0 && !h_tiles)) return MOEGG_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    Control ctl;
+    hipError_t e = hipMemcpyAsync(&ctl, (const char*)ws + 128, sizeof(ctl), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "tile count read");
+    *h_n = ctl.n_tiles;
+    int64_t n = ctl.n_tiles < cap_tiles ? ctl.n_tiles : cap_tiles;
+    if (n > 0) {
+        const WsLayout L = ws_layout(ctl.G, 0);
+        e = hipMemcpyAsync(h_tiles, (const char*)ws + L.tiles, sizeof(moegg_tile_t) * (size_t)n,
+                           hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_status(e, "tile list read");
+    }
+    return MOEGG_OK;
+}
+
+}  // extern "C"

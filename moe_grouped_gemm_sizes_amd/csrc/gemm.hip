@@ -1,0 +1,566 @@
+// gemm.hip -- MoE grouped GEMM kernels for gfx950 (CDNA4).
+//
+// Layouts, from the DeepGEMM grouped/masked MoE GEMM record ("Workarounds"):
+//   - M-grouped contiguous: each expert's rows back to back in A; the work
+//     list comes from the device scheduler.
+//   - masked: a capacity buffer [G, cap, K] plus per-expert valid counts,
+//     read at run time, with a fixed grid for graph replay.
+//   - K-grouped weight gradient: the reduction axis is split by expert.
+// "Grouped GEMM changes the tiling, not the math" (same record, "Arithmetic
+// intensity"): every valid output is a plain dot product over K, accumulated
+// in fp32.
+//
+// Kernel structure (one 512-thread workgroup per output tile):
+//   - Stage loads go straight from HBM to LDS (buffer_load_dwordx4 ... lds).
+//     Each buffer resource covers only the tile's valid rows, so padding rows
+//     read as zeros and cost no HBM traffic.
+//   - Every LDS row holds 128 bytes of K: 128 e4m3 values or 64 bf16.  One
+//     such stage feeds one 16x16x128 fp8 MFMA, or two 16x16x32 bf16 MFMAs.
+//   - An operand stored K-contiguous is read with ds_read_b128.  An operand
+//     stored N/M-contiguous ([K, N] weights, K-grouped X and dY) is staged
+//     as-is and transposed on the way out of LDS with ds_read_b64_tr_b8/_b16.
+//   - XOR swizzles on 16-byte chunks keep the DMA writes and the fragment
+//     reads free of bank conflicts.
+//   - The weight tile is the MFMA A operand and the activation tile the B
+//     operand.  So each lane ends with 4 consecutive output columns of one
+//     row: one per-row fp8 scale per lane, and 8-byte (bf16) or 16-byte
+//     (fp32) stores.
+//   - Tail padding: a tile skips every 16-row MFMA block that lies wholly
+//     past its valid rows ("Grouped execution does not require padded
+//     experts" on the MoE GroupGEMM padding page keeps tail padding inside
+//     an MMA tile; here it shrinks to the 16-row MFMA block).
+//   - fp8: each 128-wide K group's fp32 MFMA partial is promoted into the
+//     fp32 accumulator with acc += partial * a_scale[row] * b_scale[block].
+//   - Tile order is XCD-aware.  Block b runs on XCD b % 8, and each XCD
+//     takes runs of 32 consecutive work items: 4 row tiles x 8 column tiles
+//     of one expert, which share A tiles and weight panels in that XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+#include "workspace.hpp"
+
+namespace moegg {
+
+template <int X> struct dependent_false { static constexpr bool value = false; };
+
+// Swizzle of 16-byte chunks in a K-contiguous tile (128-byte rows).
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+
+// Swizzle of 16-byte chunks in an MN-contiguous tile, by element size and
+// row bytes, chosen so the 16 lanes of one transpose read hit distinct banks.
+template <int ESZ, int RB>
+__device__ __forceinline__ int swz_mn(int k) {
+    if constexpr (ESZ == 1 && RB == 256) return (k & 7) | (((k >> 5) & 1) << 3);
+    else if constexpr (ESZ == 1 && RB == 128) return ((k >> 1) & 3) | (((k >> 5) & 1) << 2);
+    else if constexpr (ESZ == 2 && (RB == 512 || RB == 256)) return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+    else if constexpr (ESZ == 2 && RB == 128) return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2);
+    else static_assert(dependent_false<RB>::value, "unsupported MN tile row size");
+    return 0;
+}
+
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct Cfg {
+    static constexpr bool FP8 = FP8_;
+    static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
+    static constexpr int KSTEP = 128 / ESZ;            // K elements per stage
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int STAGES = STAGES_;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
+    static constexpr int MB = WTM / 16, NB = WTN / 16;             // 16x16 blocks per wave
+    static constexpr int A_BYTES = BM * 128;
+    static constexpr int B_BYTES = BN * 128;
+    static constexpr int S_BYTES = FP8 ? BM * 4 : 0;               // per-row A scales
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 16 / THREADS;         // 16-byte DMA per thread per stage
+    static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
+    static constexpr int S_LOADS = FP8 ? 1 : 0;                    // one 4-byte DMA per wave per stage
+    static constexpr int VM_PER_STAGE = A_LOADS + B_LOADS + S_LOADS;
+    static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(!FP8 || WTN <= 128, "one fp8 weight scale block per wave tile");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(VM_PER_STAGE * (STAGES - 1) < 64, "vmcnt range");
+};
+
+// ---------------------------------------------------------------- stage loads
+
+// K-contiguous tile: `rows` rows of 128 bytes from a buffer whose row r
+// starts at r * row_bytes, K-step byte offset kbyte.  Flat 16-byte chunk f
+// (= j * THREADS + tid) lands at LDS byte 16 f.
+template <class C>
+__device__ __forceinline__ void load_tile_k(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t kbyte,
+                                            uint32_t row0, char* lds_tile, int loads) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j >= loads) break;
+        int f = j * C::THREADS + tid;
+        int r = f >> 3, p = f & 7;
+        int c = p ^ swz_k(r);
+        uint32_t off = (row0 + r) * row_bytes + kbyte + c * 16;
+        load16_to_lds(rs, off, lds_tile + (j * C::THREADS + wave * 64) * 16);
+        (void)lane;
+    }
+}
+
+// MN-contiguous tile: KSTEP rows (one per K index) of RB bytes, from a buffer
+// whose K row k starts at k * row_bytes, column byte offset cbyte.
+template <class C, int RB>
+__device__ __forceinline__ void load_tile_mn(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t k0,
+                                             uint32_t cbyte, char* lds_tile, int loads) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    constexpr int CPR = RB / 16;                       // chunks per row
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= loads) break;
+        int f = j * C::THREADS + tid;
+        int r = f / CPR, p = f % CPR;
+        int c = p ^ swz_mn<C::ESZ, RB>(r);
+        uint32_t off = (k0 + r) * row_bytes + cbyte + c * 16;
+        load16_to_lds(rs, off, lds_tile + (j * C::THREADS + wave * 64) * 16);
+    }
+}
+
+// ---------------------------------------------------------------- fragments
+
+// K-contiguous tile, fp8: lane (row r16, group g) gets bytes [32g, 32g+32).
+__device__ __forceinline__ v8i frag_k_fp8(const char* tile, int row) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int s = swz_k(row);
+    v4i lo = lds_read_b128(tile + row * 128 + (((2 * g) ^ s) << 4));
+    v4i hi = lds_read_b128(tile + row * 128 + (((2 * g + 1) ^ s) << 4));
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// K-contiguous tile, bf16, half-step kk: lane gets k = 32kk + 8g + (0..7).
+__device__ __forceinline__ v4i frag_k_bf16(const char* tile, int row, int kk) {
+    const int g = (threadIdx.x & 63) >> 4;
+    return lds_read_b128(tile + row * 128 + (((4 * kk + g) ^ swz_k(row)) << 4));
+}
+
+// MN-contiguous tile, fp8: lane (col n0 + l%16, group g) gets the 32 bytes
+// k = 32g + (0..31) of column n, via four tr8 reads of 8 K rows each.
+template <int RB>
+__device__ __forceinline__ v8i frag_mn_fp8(const char* tile, int n0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, s = lane & 15;
+    const int c = n0 >> 4;               // 16-byte chunk of columns n0..n0+15
+    v2i part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int k = 32 * g + 8 * j + (s >> 1);
+        part[j] = lds_read_tr8(tile + k * RB + ((c ^ swz_mn<1, RB>(k)) << 4) + 8 * (s & 1));
+    }
+    return v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+}
+
+// MN-contiguous tile, bf16, half-step kk: lane gets k = 32kk + 8g + (0..7)
+// of column n0 + l%16, via two tr16 reads of 4 K rows each.
+template <int RB>
+__device__ __forceinline__ v4i frag_mn_bf16(const char* tile, int n0, int kk) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, s = lane & 15;
+    v2i part[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int k = 32 * kk + 8 * g + 4 * j + (s >> 2);
+        int cb = 2 * n0 + 8 * (s & 3);   // column byte
+        int c = cb >> 4;
+        part[j] = lds_read_tr16(tile + k * RB + ((c ^ swz_mn<2, RB>(k)) << 4) + (cb & 15));
+    }
+    return v4i{part[0].x, part[0].y, part[1].x, part[1].y};
+}
+
+// ---------------------------------------------------------------- work items
+
+// Work item -> (row tile, column tile).  Items come in groups of up to 4
+// row tiles; within a group the column tile varies slowest.
+__device__ __forceinline__ void item_to_tiles(int item, int n_rt, int n_ct, int& rt, int& ct) {
+    const int GM = 4;
+    int per_group = GM * n_ct;
+    int g = item / per_group, r = item - g * per_group;
+    int gm = min(GM, n_rt - g * GM);
+    ct = r / gm;
+    rt = g * GM + (r - ct * gm);
+}
+
+// Block -> work item: XCD x (= b % 8) takes items in runs of 32.
+__device__ __forceinline__ int block_to_item(int b) {
+    return (b >> 8) * 256 + (b & 7) * 32 + ((b & 255) >> 3);
+}
+
+// ---------------------------------------------------------------- main loop
+
+// Accumulates one output tile: rows [0, rows_valid) of the activation tile
+// against one weight panel, over nks K steps.
+//   B_KN: weight stored [K, N] (N contiguous), else [N, K].
+template <class C, bool B_KN>
+struct TileGemm {
+    v4f acc[C::NB][C::MB];
+
+    __device__ __forceinline__ void run(char* lds, __amdgpu_buffer_rsrc_t ra, uint32_t a_row_bytes,
+                                        __amdgpu_buffer_rsrc_t rb, uint32_t b_row_bytes, uint32_t b_col_byte,
+                                        __amdgpu_buffer_rsrc_t rsa, uint32_t sa_row_bytes,
+                                        const float* __restrict__ b_scale, int b_scale_stride, int nks,
+                                        int rows_valid) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+        const int r16 = lane & 15;
+        const int mb_active = min(C::MB, max(0, (rows_valid - wm * C::WTM + 15) >> 4));
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i)
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        auto issue = [&](int ks, int slot) {
+            char* base = lds + slot * C::STAGE_BYTES;
+            load_tile_k<C>(ra, a_row_bytes, ks * 128, 0, base, C::A_LOADS);
+            if constexpr (B_KN) {
+                load_tile_mn<C, C::BN * C::ESZ>(rb, b_row_bytes, ks * C::KSTEP, b_col_byte, base + C::A_BYTES,
+                                                C::B_LOADS);
+            } else {
+                load_tile_k<C>(rb, b_row_bytes, ks * 128, 0, base + C::A_BYTES, C::B_LOADS);
+            }
+            if constexpr (C::FP8) {
+                // one 4-byte scale per tile row for K group ks; waves past BM/64 repeat rows
+                int r = (wave % (C::BM / 64)) * 64 + lane;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsa, (MOEGG_LDS void*)(base + C::A_BYTES + C::B_BYTES + (wave % (C::BM / 64)) * 256), 4,
+                    r * sa_row_bytes + ks * 4, 0, 0, 0);
+            }
+        };
+
+#pragma unroll
+        for (int s = 0; s < C::STAGES - 1; ++s)
+            if (s < nks) issue(s, s);
+
+        float bsc = 0.f;
+        if constexpr (C::FP8) bsc = b_scale[0];
+        for (int ks = 0; ks < nks; ++ks) {
+            const int slot = ks % C::STAGES;
+            if (ks + C::STAGES - 1 < nks) {
+                issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
+                wait_vmcnt<C::VM_PER_STAGE * (C::STAGES - 1)>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            float bsc_next = 0.f;
+            if constexpr (C::FP8) bsc_next = (ks + 1 < nks) ? b_scale[(ks + 1) * b_scale_stride] : 0.f;
+            __syncthreads();
+            const char* ta = lds + slot * C::STAGE_BYTES;
+            const char* tb = ta + C::A_BYTES;
+            if constexpr (C::FP8) {
+                const float* ts = (const float*)(tb + C::B_BYTES);
+                v8i ya[C::MB];
+                float sa[C::MB];
+#pragma unroll
+                for (int j = 0; j < C::MB; ++j) {
+                    if (j < mb_active) {
+                        int row = wm * C::WTM + j * 16 + r16;
+                        ya[j] = frag_k_fp8(ta, row);
+                        sa[j] = ts[row] * bsc;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < C::NB; ++i) {
+                    const int n0 = wn * C::WTN + i * 16;
+                    v8i xb;
+                    if constexpr (B_KN) xb = frag_mn_fp8<C::BN>(tb, n0);
+                    else xb = frag_k_fp8(tb, n0 + r16);
+#pragma unroll
+                    for (int j = 0; j < C::MB; ++j) {
+                        if (j < mb_active) {
+                            v4f p = mfma_fp8(xb, ya[j], v4f{0.f, 0.f, 0.f, 0.f});
+                            acc[i][j].x = __builtin_fmaf(p.x, sa[j], acc[i][j].x);
+                            acc[i][j].y = __builtin_fmaf(p.y, sa[j], acc[i][j].y);
+                            acc[i][j].z = __builtin_fmaf(p.z, sa[j], acc[i][j].z);
+                            acc[i][j].w = __builtin_fmaf(p.w, sa[j], acc[i][j].w);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    v4i ya[C::MB];
+#pragma unroll
+                    for (int j = 0; j < C::MB; ++j)
+                        if (j < mb_active) ya[j] = frag_k_bf16(ta, wm * C::WTM + j * 16 + r16, kk);
+#pragma unroll
+                    for (int i = 0; i < C::NB; ++i) {
+                        const int n0 = wn * C::WTN + i * 16;
+                        v4i xb;
+                        if constexpr (B_KN) xb = frag_mn_bf16<C::BN * 2>(tb, n0, kk);
+                        else xb = frag_k_bf16(tb, n0 + r16, kk);
+#pragma unroll
+                        for (int j = 0; j < C::MB; ++j)
+                            if (j < mb_active) acc[i][j] = mfma_bf16(xb, ya[j], acc[i][j]);
+                    }
+                }
+            }
+            if constexpr (C::FP8) bsc = bsc_next;
+            __syncthreads();
+        }
+    }
+
+    // bf16 epilogue: rows < rows_valid of the tile; C rows are row_bytes apart.
+    __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+        const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) {
+            const int row = wm * C::WTM + j * 16 + r16;
+            if (row < rows_valid) {
+#pragma unroll
+                for (int i = 0; i < C::NB; ++i) {
+                    const int col = wn * C::WTN + i * 16 + 4 * g;
+                    v2i d;
+                    d.x = (int)pack_bf16x2(acc[i][j].x, acc[i][j].y);
+                    d.y = (int)pack_bf16x2(acc[i][j].z, acc[i][j].w);
+                    __builtin_amdgcn_raw_buffer_store_b64(d, rc, row * row_bytes + col * 2, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- kernels
+
+
+// M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout.
+template <class C, bool B_KN, bool MASKED>
+__global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    const int n_ct = p.N / C::BN;
+    int e, row_start, rows_valid, ct;
+    if constexpr (MASKED) {
+        const int n_rt = (p.cap + C::BM - 1) / C::BM;
+        const int item = blockIdx.x;
+        const int per_e = n_rt * n_ct;
+        e = item / per_e;
+        if (e >= p.G) return;
+        int r = item - e * per_e;
+        int rt = r / n_ct;
+        ct = r - rt * n_ct;
+        int m = min(max(p.counts[e], 0), p.cap);
+        rows_valid = min(C::BM, m - rt * C::BM);
+        if (rows_valid <= 0) return;             // no weight loads for empty experts
+        row_start = e * p.cap + rt * C::BM;
+    } else {
+        const WsLayout L = ws_layout(p.G, 0);
+        const Control* ctl = (const Control*)(p.ws + L.control);
+        if (ctl->block_m != C::BM) return;       // another candidate height was chosen
+        const int n_rt = ctl->n_tiles;
+        const int item = block_to_item(blockIdx.x);
+        if (item >= n_rt * n_ct) return;
+        int rt;
+        item_to_tiles(item, n_rt, n_ct, rt, ct);
+        const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
+        e = t.expert;
+        row_start = t.row_start;
+        rows_valid = t.rows_valid;
+    }
+    const int n0 = ct * C::BN;
+    const int KB = p.K / 128;
+    const uint32_t a_row_bytes = (uint32_t)p.K * C::ESZ;
+    auto ra = make_rsrc((const char*)p.A + (size_t)row_start * a_row_bytes, (uint32_t)rows_valid * a_row_bytes);
+    const size_t b_expert_bytes = (size_t)p.K * p.N * C::ESZ;
+    const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
+    __amdgpu_buffer_rsrc_t rb;
+    uint32_t b_row_bytes, b_col_byte;
+    if constexpr (B_KN) {
+        rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
+        b_row_bytes = (uint32_t)p.N * C::ESZ;
+        b_col_byte = (uint32_t)n0 * C::ESZ;
+    } else {
+        rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
+        b_row_bytes = (uint32_t)p.K * C::ESZ;
+        b_col_byte = 0;
+    }
+    __amdgpu_buffer_rsrc_t rsa = rb;
+    const float* bs = nullptr;
+    int bs_stride = 0;
+    if constexpr (C::FP8) {
+        rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
+        const int wn = (threadIdx.x >> 6) % C::WAVES_N;
+        bs = p.B_scale + (size_t)e * KB * (p.N / 128) + (n0 + wn * C::WTN) / 128;
+        bs_stride = p.N / 128;
+    }
+    TileGemm<C, B_KN> tg;
+    tg.run(lds, ra, a_row_bytes, rb, b_row_bytes, b_col_byte, rsa, (uint32_t)KB * 4, bs, bs_stride,
+           p.K / C::KSTEP, rows_valid);
+    const uint32_t c_row_bytes = (uint32_t)p.N * 2;
+    auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
+                        (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
+    tg.store_bf16(rc, c_row_bytes, rows_valid);
+}
+
+// ---------------------------------------------------------------- K-grouped
+
+
+// dW[e, i, j] = sum over expert e's rows t of X[t, i] * dY[t, j].
+// Both operands are M/N-contiguous: the dY tile is the MFMA A operand (so each
+// lane holds 4 consecutive j), the X tile the MFMA B operand.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p) {
+    static_assert(!C::FP8, "bf16 only");
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    const WsLayout L = ws_layout(p.G, 0);
+    const int64_t* offs = (const int64_t*)(p.ws + L.offsets);
+    const int32_t* order = (const int32_t*)(p.ws + L.order);
+    const int n_it = p.Mw / C::BM, n_jt = p.Nw / C::BN;
+    const int per_e = n_it * n_jt;
+    const int item = block_to_item(blockIdx.x);
+    if (item >= p.G * per_e) return;
+    const int rank = item / per_e;
+    int it, jt;
+    item_to_tiles(item - rank * per_e, n_it, n_jt, it, jt);
+    const int e = order[rank];
+    const int64_t t0 = offs[e];
+    const int64_t te = max((int64_t)0, min(offs[e + 1], offs[p.G]) - t0);
+    const int i0 = it * C::BM, j0 = jt * C::BN;
+    const uint32_t x_row = (uint32_t)p.Mw * 2, y_row = (uint32_t)p.Nw * 2;
+    auto rx = make_rsrc((const char*)p.X + t0 * x_row, (uint32_t)(te * x_row));
+    auto ry = make_rsrc((const char*)p.dY + t0 * y_row, (uint32_t)(te * y_row));
+    const int nks = (int)((te + C::KSTEP - 1) / C::KSTEP);
+
+    v4f acc[C::NB][C::MB];
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    auto issue = [&](int ks, int slot) {
+        char* base = lds + slot * C::STAGE_BYTES;
+        load_tile_mn<C, C::BM * 2>(rx, x_row, ks * C::KSTEP, i0 * 2, base, C::A_LOADS);
+        load_tile_mn<C, C::BN * 2>(ry, y_row, ks * C::KSTEP, j0 * 2, base + C::A_BYTES, C::B_LOADS);
+    };
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s)
+        if (s < nks) issue(s, s);
+    for (int ks = 0; ks < nks; ++ks) {
+        const int slot = ks % C::STAGES;
+        if (ks + C::STAGES - 1 < nks) {
+            issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
+            wait_vmcnt<C::VM_PER_STAGE * (C::STAGES - 1)>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        const char* tx = lds + slot * C::STAGE_BYTES;
+        const char* ty = tx + C::A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            v4i xa[C::MB];
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j) xa[j] = frag_mn_bf16<C::BM * 2>(tx, wm * C::WTM + j * 16, kk);
+#pragma unroll
+            for (int i = 0; i < C::NB; ++i) {
+                v4i yb = frag_mn_bf16<C::BN * 2>(ty, wn * C::WTN + i * 16, kk);
+#pragma unroll
+                for (int j = 0; j < C::MB; ++j) acc[i][j] = mfma_bf16(yb, xa[j], acc[i][j]);
+            }
+        }
+        __syncthreads();
+    }
+    // fp32 epilogue: lane holds dW[i][j..j+3]
+    const int r16 = lane & 15, g = lane >> 4;
+    float* out = p.dW + (size_t)e * p.Mw * p.Nw;
+#pragma unroll
+    for (int j = 0; j < C::MB; ++j) {
+        const int i = i0 + wm * C::WTM + j * 16 + r16;
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n) {
+            const int col = j0 + wn * C::WTN + n * 16 + 4 * g;
+            *(v4f*)(out + (size_t)i * p.Nw + col) = acc[n][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- configs
+
+// Contiguous: 512 threads, 256 columns per tile, every wave tile 64 rows tall.
+template <bool FP8> using Contig256 = Cfg<FP8, 256, 256, 4, 2, 2>;
+template <bool FP8> using Contig128 = Cfg<FP8, 128, 256, 2, 4, 3>;
+template <bool FP8> using Contig64 = Cfg<FP8, 64, 256, 1, 8, 3>;
+// Masked decode: short row tiles, narrow column tiles, deep pipeline (HBM-bound).
+template <bool FP8> using MaskedCfg = Cfg<FP8, 64, 128, 2, 4, 4>;
+using KGroupedCfg = Cfg<false, 256, 256, 4, 2, 2>;
+
+// Raise a kernel's dynamic LDS limit once per process (it is a function
+// attribute, not a stream operation).
+template <auto Kernel>
+static hipError_t allow_lds(int bytes) {
+    static hipError_t once =
+        hipFuncSetAttribute((const void*)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return once;
+}
+
+template <class C, bool B_KN, bool MASKED>
+static hipError_t launch_one(const ContigArgs& a, int grid, hipStream_t s) {
+    auto k = grouped_gemm_kernel<C, B_KN, MASKED>;
+    hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, MASKED>>(C::LDS_BYTES);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
+
+// Launch the contiguous GEMM for tile height block_m (0 = every candidate;
+// the ones the device did not choose exit at entry).
+template <bool FP8, bool B_KN>
+static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
+    const int64_t n_ct = a.N / 256;
+    hipError_t err = hipSuccess;
+    auto grid_for = [&](int q) { return round256(((rows_total + q - 1) / q + a.G) * n_ct); };
+    if (block_m == 0 || block_m == 256) {
+        err = launch_one<Contig256<FP8>, B_KN, false>(a, grid_for(256), s);
+        if (err != hipSuccess) return err;
+    }
+    if (block_m == 0 || block_m == 128) {
+        err = launch_one<Contig128<FP8>, B_KN, false>(a, grid_for(128), s);
+        if (err != hipSuccess) return err;
+    }
+    if (block_m == 0 || block_m == 64) {
+        err = launch_one<Contig64<FP8>, B_KN, false>(a, grid_for(64), s);
+    }
+    return err;
+}
+
+hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool b_kn, int64_t rows_total, int block_m,
+                             hipStream_t s) {
+    if (fp8) return b_kn ? launch_contig_t<true, true>(a, rows_total, block_m, s)
+                         : launch_contig_t<true, false>(a, rows_total, block_m, s);
+    return b_kn ? launch_contig_t<false, true>(a, rows_total, block_m, s)
+                : launch_contig_t<false, false>(a, rows_total, block_m, s);
+}
+
+int masked_block_m() { return MaskedCfg<false>::BM; }
+int masked_block_n() { return MaskedCfg<false>::BN; }
+
+hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s) {
+    const int n_rt = (a.cap + 63) / 64;
+    const int grid = a.G * n_rt * (a.N / 128);
+    if (fp8) return b_kn ? launch_one<MaskedCfg<true>, true, true>(a, grid, s)
+                         : launch_one<MaskedCfg<true>, false, true>(a, grid, s);
+    return b_kn ? launch_one<MaskedCfg<false>, true, true>(a, grid, s)
+                : launch_one<MaskedCfg<false>, false, true>(a, grid, s);
+}
+
+hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s) {
+    using C = KGroupedCfg;
+    auto k = k_grouped_kernel<C>;
+    hipError_t err = allow_lds<k_grouped_kernel<C>>(C::LDS_BYTES);
+    if (err != hipSuccess) return err;
+    const int64_t items = (int64_t)a.G * (a.Mw / C::BM) * (a.Nw / C::BN);
+    hipLaunchKernelGGL(k, dim3(round256(items)), dim3(C::THREADS), C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moegg

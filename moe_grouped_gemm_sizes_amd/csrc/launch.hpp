@@ -1,0 +1,40 @@
+// launch.hpp -- host-side launcher interface between the C ABI (api.hip) and
+// the kernels (sched.hip, gemm.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moegg {
+
+struct ContigArgs {
+    const void* A;
+    const float* A_scale;
+    const void* B;
+    const float* B_scale;
+    void* C;
+    const int32_t* counts;        // m_sizes, or masked_m for the masked layout
+    const unsigned char* ws;      // scheduler output (contiguous layout)
+    int G, K, N, cap;             // cap: masked layout only
+};
+
+struct KGroupedArgs {
+    const void* X;
+    const void* dY;
+    float* dW;
+    const unsigned char* ws;
+    int G, Mw, Nw;
+};
+
+// mode 0: contiguous (tile list); mode 1: masked (stats only).
+hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int seg_align, int cap, int mode,
+                        int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
+                        hipStream_t stream);
+hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void* ws, hipStream_t stream);
+hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool b_kn, int64_t rows_total, int block_m,
+                             hipStream_t s);
+hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s);
+hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);
+int masked_block_m();
+int masked_block_n();
+
+}  // namespace moegg

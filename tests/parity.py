@@ -1,0 +1,96 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI,
+run the oracle on the same bits, compare.
+
+Bars:
+- integer work (stats, tile lists): bit-exact;
+- bf16 inputs: ||C - C_ref||_F / ||C_ref||_F <= 2e-3;
+- fp8 e4m3 inputs with fp32 group scales: <= 2e-2.
+"""
+from __future__ import annotations
+
+import random
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import moe_grouped_gemm_sizes_amd as mg
+import workloads as wl
+from oracle import accounting as acc
+from oracle import gemm as og
+
+TOL = {"bf16": 2e-3, "fp8": 2e-2}
+SENTINEL_BITS = 0x7BAD          # a finite bf16 pattern the kernels never produce here by chance
+
+
+def cpu(t: Optional[torch.Tensor]):
+    return None if t is None else t.detach().cpu().contiguous()
+
+
+def sentinel_like(shape, device="cuda") -> torch.Tensor:
+    return torch.full(shape, SENTINEL_BITS, dtype=torch.int16, device=device).view(torch.bfloat16)
+
+
+def sample_rows_contiguous(counts: Sequence[int], seg_align: int, block_m: int, extra: int, seed: int) -> List[int]:
+    """First, last and tail-tile rows of every active expert, plus random valid rows."""
+    offs = acc.segment_offsets(counts, seg_align)
+    rows = set()
+    valid = []
+    for e, m in enumerate(counts):
+        if m <= 0:
+            continue
+        s = offs[e]
+        rows.update({s, s + m - 1, s + (m - 1) // block_m * block_m, s + m // 2})
+        valid.append((s, m))
+    rng = random.Random(seed)
+    for _ in range(extra):
+        s, m = rng.choice(valid)
+        rows.add(s + rng.randrange(m))
+    return sorted(rows)
+
+
+def run_contiguous(w: wl.Workload, inp: Dict, block_m: int = 0, b_layout: int = mg.B_KN):
+    A, B = inp["A"], inp["B"]
+    if b_layout == mg.B_NK:
+        B = B.transpose(1, 2).contiguous()
+    C = sentinel_like((w.rows_total, w.N))
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.grouped_gemm_contiguous(A, B, C, inp["counts"], ws, A_scale=inp.get("A_scale"), B_scale=inp.get("B_scale"),
+                               seg_align=w.seg_align, block_m=block_m, b_layout=b_layout)
+    torch.cuda.synchronize()
+    return C, ws
+
+
+def oracle_contiguous_rows(w: wl.Workload, inp_cpu: Dict, rows: Sequence[int]) -> np.ndarray:
+    return og.contiguous(inp_cpu["A"], inp_cpu["B"], w.counts, rows, seg_align=w.seg_align,
+                         A_scale=inp_cpu.get("A_scale"), B_scale=inp_cpu.get("B_scale"))
+
+
+def check_stats(stats: mg.Stats, counts: Sequence[int], block_m: Optional[int] = None):
+    """Device accounting equals the oracle's exact integers."""
+    s = acc.summary(counts)
+    assert stats.U == s["U"]
+    assert stats.active == s["active"]
+    assert stats.sum_sq == s["sum_sq"]
+    assert stats.P_at == s["P"]
+    assert stats.P_exec == s["P"][16]
+    assert stats.error_flags == 0
+    if block_m is not None:
+        assert stats.block_m == block_m
+        assert stats.tiles == acc.tiles_for(counts, block_m)
+
+
+def rows_as_float(C: torch.Tensor, rows: Sequence[int]) -> np.ndarray:
+    return C[torch.tensor(list(rows), device=C.device)].float().cpu().double().numpy()
+
+
+def untouched_rows_ok(C: torch.Tensor, counts: Sequence[int], seg_align: int) -> bool:
+    """Rows that belong to no expert still hold the sentinel."""
+    mask = torch.ones(C.shape[0], dtype=torch.bool)
+    offs = acc.segment_offsets(counts, seg_align)
+    for e, m in enumerate(counts):
+        mask[offs[e]:offs[e] + m] = False
+    idx = mask.nonzero().flatten().to(C.device)
+    if idx.numel() == 0:
+        return True
+    return bool((C[idx].view(torch.int16) == SENTINEL_BITS).all())

@@ -1,0 +1,125 @@
+"""The C ABI on the host (no GPU needed): the library loads and exports every
+symbol include/moegg.h declares, and host-side validation rejects bad
+arguments before anything is enqueued.  No call here reaches a launch."""
+import ctypes
+import re
+
+import pytest
+
+import moe_grouped_gemm_sizes_amd as mg
+
+
+def declared_functions():
+    src = open(mg.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moegg_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.moegg_version() >> 16 == 0
+
+
+def test_status_strings():
+    L = mg.lib()
+    for s in range(5):
+        assert L.moegg_status_string(s)
+    assert L.moegg_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    L = mg.lib()
+    assert L.moegg_workspace_bytes(0, 10) == 0
+    assert L.moegg_workspace_bytes(4097, 10) == 0
+    assert L.moegg_workspace_bytes(8, -1) == 0
+    small = L.moegg_workspace_bytes(8, 132)
+    big = L.moegg_workspace_bytes(8, 1 << 20)
+    assert small > 0 and small % 256 == 0
+    assert big >= small + 16 * ((1 << 20) // 64)          # one 16-byte entry per 64-row tile
+
+
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced: validation fails first
+
+
+def contiguous(**kw):
+    args = dict(A=FAKE, A_scale=None, B=FAKE, B_scale=None, C=FAKE, m=FAKE, G=8, rows=132, K=512, N=256,
+                align=1, dtype=mg.BF16, layout=mg.B_KN, block_m=0, ws=FAKE, ws_bytes=1 << 20)
+    args.update(kw)
+    return mg.lib().moegg_grouped_gemm_contiguous(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), mg.ERR_INVALID_ARG),
+    (dict(m=None), mg.ERR_INVALID_ARG),
+    (dict(G=0), mg.ERR_INVALID_ARG),
+    (dict(G=5000), mg.ERR_INVALID_ARG),
+    (dict(K=100), mg.ERR_UNSUPPORTED),
+    (dict(N=200), mg.ERR_UNSUPPORTED),
+    (dict(dtype=7), mg.ERR_INVALID_ARG),
+    (dict(layout=3), mg.ERR_INVALID_ARG),
+    (dict(dtype=mg.FP8_E4M3), mg.ERR_INVALID_ARG),                 # fp8 without scales
+    (dict(dtype=mg.FP8_E4M3, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
+    (dict(block_m=32), mg.ERR_UNSUPPORTED),
+    (dict(align=0), mg.ERR_INVALID_ARG),
+    (dict(rows=-1), mg.ERR_INVALID_ARG),
+    (dict(ws=None), mg.ERR_WORKSPACE),
+    (dict(ws_bytes=64), mg.ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), mg.ERR_WORKSPACE),        # not 256-byte aligned
+    (dict(A=ctypes.c_void_p(0x100001)), mg.ERR_INVALID_ARG),       # not 16-byte aligned
+])
+def test_contiguous_validation(kw, status):
+    assert contiguous(**kw) == status
+
+
+def test_masked_validation():
+    L = mg.lib()
+    f = L.moegg_grouped_gemm_masked
+    ok = [FAKE, None, FAKE, None, FAKE, FAKE, 32, 256, 2048, 7168, mg.BF16, mg.B_KN, None, 0, None]
+    bad_cap = list(ok)
+    bad_cap[7] = 0
+    assert f(*bad_cap) == mg.ERR_INVALID_ARG
+    bad_n = list(ok)
+    bad_n[9] = 100
+    assert f(*bad_n) == mg.ERR_UNSUPPORTED
+    small_ws = list(ok)
+    small_ws[12], small_ws[13] = FAKE, 16
+    assert f(*small_ws) == mg.ERR_WORKSPACE
+
+
+def test_k_grouped_validation():
+    f = mg.lib().moegg_grouped_gemm_k_grouped
+    assert f(None, FAKE, FAKE, FAKE, 16, 100, 2048, 7168, FAKE, 1 << 20, None) == mg.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 100, 2000, 7168, FAKE, 1 << 20, None) == mg.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 100, 2048, 7168, None, 0, None) == mg.ERR_WORKSPACE
+
+
+def test_schedule_validation():
+    f = mg.lib().moegg_schedule
+    assert f(None, 8, 132, 1, 0, 256, FAKE, 1 << 20, None) == mg.ERR_INVALID_ARG
+    assert f(FAKE, 8, 132, 1, 48, 256, FAKE, 1 << 20, None) == mg.ERR_UNSUPPORTED
+    assert f(FAKE, 8, 132, 1, 0, 256, FAKE, 8, None) == mg.ERR_WORKSPACE
+    assert f(FAKE, 8, 132, 1, 0, 0, FAKE, 1 << 20, None) == mg.ERR_INVALID_ARG
+
+
+def test_scheduled_validation():
+    f = mg.lib().moegg_grouped_gemm_contiguous_scheduled
+    args = [FAKE, None, FAKE, None, FAKE, 8, 132, 512, 256, mg.BF16, mg.B_KN, 0, FAKE, 1 << 20, None]
+    bad = list(args); bad[12] = None
+    assert f(*bad) == mg.ERR_WORKSPACE
+    bad = list(args); bad[11] = 96
+    assert f(*bad) == mg.ERR_UNSUPPORTED
+    bad = list(args); bad[0] = None
+    assert f(*bad) == mg.ERR_INVALID_ARG
+
+
+def test_read_validation():
+    L = mg.lib()
+    assert L.moegg_stats_read(None, None, None) == mg.ERR_INVALID_ARG
+    n = ctypes.c_int64(0)
+    assert L.moegg_tile_list_read(FAKE, None, 5, ctypes.byref(n), None) == mg.ERR_INVALID_ARG

@@ -1,0 +1,357 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name, sizes and seed before touching the GPU, so a
+failing run names its case.
+"""
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_sizes_amd as mg
+import workloads as wl
+from oracle import accounting as acc
+from oracle import gemm as og
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.lib()
+    og.lib()
+
+
+# ----------------------------------------------------------------- scheduler
+
+
+SCHED_HISTS = {
+    "near_uniform": wl.hist_near_uniform(),
+    "concentrated": wl.hist_concentrated(),
+    "issue32": wl.hist_issue_32(),
+    "zipf64": wl.hist_zipf(3),
+    "poisson32": wl.hist_poisson_masked(4),
+    "dirichlet16": wl.hist_dirichlet(5),
+    "all_empty": [0] * 7,
+    "single": [1],
+    "boundaries": [63, 64, 65, 127, 128, 129, 255, 256, 257, 0, 1],
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCHED_HISTS))
+@pytest.mark.parametrize("block_m", [64, 128, 256])
+@pytest.mark.parametrize("seg_align", [1, 128])
+def test_schedule_bit_exact(name, block_m, seg_align):
+    counts = SCHED_HISTS[name]
+    announce("schedule", name, block_m, seg_align)
+    rows_total = sum(acc.ceil_div(c, seg_align) * seg_align for c in counts)
+    m = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    ws = mg.workspace(len(counts), rows_total)
+    mg.schedule(m, rows_total, ws, seg_align=seg_align, block_m=block_m)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, block_m)
+    tiles = mg.tile_list_read(ws, acc.tiles_for(counts, 64) + 5)
+    assert tiles == acc.tile_list(counts, block_m, seg_align)
+    assert st.capacity_rows == rows_total - sum(counts)
+
+
+def test_schedule_random_histograms():
+    rng = random.Random(7)
+    for it in range(200):
+        G = rng.randint(1, 300)
+        counts = [0 if rng.random() < 0.3 else rng.randint(0, 700) for _ in range(G)]
+        align = rng.choice([1, 8, 64, 128])
+        bm = rng.choice([64, 128, 256])
+        rows_total = sum(acc.ceil_div(c, align) * align for c in counts)
+        m = torch.tensor(counts, dtype=torch.int32, device="cuda")
+        ws = mg.workspace(G, rows_total)
+        mg.schedule(m, rows_total, ws, seg_align=align, block_m=bm)
+        st = mg.stats_read(ws)
+        P.check_stats(st, counts, bm)
+        assert mg.tile_list_read(ws, st.tiles) == acc.tile_list(counts, bm, align), (it, counts, align, bm)
+
+
+def test_schedule_clamps_bad_counts():
+    announce("schedule clamps")
+    counts = [5, -3, 200, 7]
+    m = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    ws = mg.workspace(4, 100)
+    mg.schedule(m, 100, ws, seg_align=1, block_m=64)
+    st = mg.stats_read(ws)
+    assert st.error_flags & mg.FLAG_NEGATIVE_COUNT
+    assert st.error_flags & mg.FLAG_ROWS_OVERFLOW
+    # clamped reading: [5, 0, 95, 0] (segment 2 truncated at row 100, segment 3 starts past the end)
+    assert st.U == 100
+    assert mg.tile_list_read(ws, 10) == acc.tile_list([5, 0, 95, 0], 64, 1)
+
+
+def choice_rule(counts, n_col_tiles):
+    """The documented tile-height rule: cost(q) = ceil(tiles(q) * cols / 256) * (q + 64), ties to larger q."""
+    costs = {q: -(-acc.tiles_for(counts, q) * n_col_tiles // 256) * (q + 64) for q in (64, 128, 256)}
+    best = min(costs.values())
+    return max(q for q, c in costs.items() if c == best)
+
+
+@pytest.mark.parametrize("name", sorted(SCHED_HISTS))
+def test_schedule_device_choice_matches_rule(name):
+    """block_m = 0: the device's choice equals the documented rule (one column tile)."""
+    counts = SCHED_HISTS[name]
+    announce("choice", name)
+    rows_total = sum(counts)
+    m = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    ws = mg.workspace(len(counts), rows_total)
+    mg.schedule(m, rows_total, ws, seg_align=1, block_m=0, N=256)
+    st = mg.stats_read(ws)
+    assert st.block_m == choice_rule(counts, 1)
+    assert mg.tile_list_read(ws, st.tiles) == acc.tile_list(counts, st.block_m, 1)
+
+
+# ----------------------------------------------------------------- contiguous, small
+
+
+def small_contig(counts, K, N, dtype, seg_align=1, seed=11, values="normal"):
+    w = wl.Workload("small", "contiguous", dtype, counts, K=K, N=N, seg_align=seg_align, values=values, seed=seed)
+    return w, wl.materialize(w, "cuda")
+
+
+SMALL = [
+    ("ragged_bf16", [300, 0, 17, 513, 64, 1], 512, 512, "bf16", 1),
+    ("aligned_bf16", [100, 0, 250, 3], 256, 256, "bf16", 128),
+    ("ragged_fp8", [300, 0, 17, 513, 64, 1], 512, 512, "fp8", 1),
+    ("aligned_fp8", [129, 0, 0, 256, 40], 1024, 256, "fp8", 64),
+    ("one_expert_bf16", [700], 192, 768, "bf16", 1),
+    ("one_row_fp8", [1], 128, 256, "fp8", 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_contiguous_small_full_compare(case, block_m, b_layout):
+    name, counts, K, N, dtype, align = case
+    announce("contiguous small", name, counts, K, N, dtype, align, block_m, b_layout)
+    w, inp = small_contig(counts, K, N, dtype, align)
+    C, ws = P.run_contiguous(w, inp, block_m=block_m, b_layout=b_layout)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, block_m if block_m else None)
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    rows = [r for r in range(w.rows_total)]
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    valid = ~np.isnan(ref[:, 0])
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got[valid]).all()
+    err = og.rel_frobenius(got[valid], ref[valid])
+    assert err <= P.TOL[dtype], err
+    assert P.untouched_rows_ok(C, counts, align)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_contiguous_integer_exact(dtype):
+    """Inputs in {-1, 0, 1}, K <= 256, unit scales: every result is an integer
+    of magnitude <= 256, exact in bf16, so GPU == oracle bit for bit."""
+    announce("integer exact", dtype)
+    counts, K, N = [37, 0, 200, 5], 256, 512
+    g = torch.Generator().manual_seed(3)
+    A = torch.randint(-1, 2, (sum(counts), K), generator=g).float()
+    Bw = torch.randint(-1, 2, (len(counts), K, N), generator=g).float()
+    if dtype == "bf16":
+        inp = {"A": A.to(torch.bfloat16), "B": Bw.to(torch.bfloat16), "A_scale": None, "B_scale": None}
+    else:
+        inp = {"A": A.to(torch.float8_e4m3fn), "B": Bw.to(torch.float8_e4m3fn),
+               "A_scale": torch.ones(sum(counts), K // 128), "B_scale": torch.ones(len(counts), K // 128, N // 128)}
+    w = wl.Workload("int", "contiguous", dtype, counts, K=K, N=N)
+    inp_gpu = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    inp_gpu["counts"] = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    for bl in (mg.B_KN, mg.B_NK):
+        C, _ = P.run_contiguous(w, inp_gpu, b_layout=bl)
+        ref = og.contiguous(inp["A"], inp["B"], counts, range(w.rows_total), A_scale=inp["A_scale"],
+                            B_scale=inp["B_scale"])
+        got = C.float().cpu().double().numpy()
+        assert np.array_equal(got, ref)
+
+
+def test_contiguous_deterministic_and_empty():
+    announce("determinism + all-empty")
+    w, inp = small_contig([300, 0, 17, 513], 512, 512, "fp8")
+    C1, _ = P.run_contiguous(w, inp)
+    C2, _ = P.run_contiguous(w, inp)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    # every expert empty: nothing written, accounting all zero
+    w0 = wl.Workload("empty", "contiguous", "bf16", [0, 0, 0], K=256, N=256)
+    A = torch.zeros(4, 256, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(3, 256, 256, dtype=torch.bfloat16, device="cuda")
+    C = P.sentinel_like((4, 256))
+    ws = mg.workspace(3, 4)
+    mg.grouped_gemm_contiguous(A, B, C, torch.zeros(3, dtype=torch.int32, device="cuda"), ws)
+    st = mg.stats_read(ws)
+    assert st.U == 0 and st.tiles == 0 and all(v == 0 for v in st.P_at.values())
+    assert bool((C.view(torch.int16) == P.SENTINEL_BITS).all())
+    del w0
+
+
+# ----------------------------------------------------------------- contiguous, full-size configs
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_contiguous_config_full_size(n):
+    w = wl.workload(n)
+    announce("contiguous config", n, w.name, "G", w.G, "K", w.K, "N", w.N, "seed", w.seed)
+    inp = wl.materialize(w, "cuda")
+    C, ws = P.run_contiguous(w, inp, block_m=0)
+    st = mg.stats_read(ws)
+    P.check_stats(st, w.counts)
+    assert st.block_m == choice_rule(w.counts, w.N // 256)
+    if n == 1:
+        assert [st.P_at[q] for q in (8, 16, 32)] == [160, 192, 256]
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, st.block_m, extra=48, seed=n) \
+        if n > 1 else list(range(w.rows_total))
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    del inp
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"config {n}: block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL[w.dtype], err
+    assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+
+
+# ----------------------------------------------------------------- masked
+
+
+def masked_case(counts, cap, K, N, dtype, seed=4):
+    w = wl.Workload("masked", "masked", dtype, counts, K=K, N=N, cap=cap, seed=seed)
+    return w, wl.materialize(w, "cuda")
+
+
+def check_masked(w, inp, C, counts):
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    reqs = [(e, r) for e in range(w.G) for r in range(min(max(counts[e], 0), w.cap))]
+    if not reqs:
+        return
+    ref = og.masked(inp_cpu["A"], inp_cpu["B"], counts, [e for e, _ in reqs], [r for _, r in reqs],
+                    A_scale=inp_cpu.get("A_scale"), B_scale=inp_cpu.get("B_scale"))
+    idx = torch.tensor([e * w.cap + r for e, r in reqs], device="cuda")
+    got = C.reshape(w.G * w.cap, -1)[idx].float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    assert err <= P.TOL[w.dtype], err
+    # rows past masked_m keep the sentinel
+    inval = torch.tensor([e * w.cap + r for e in range(w.G) for r in range(w.cap)
+                          if r >= min(max(counts[e], 0), w.cap)], device="cuda")
+    if inval.numel():
+        assert bool((C.reshape(w.G * w.cap, -1)[inval].view(torch.int16) == P.SENTINEL_BITS).all())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_masked_small(dtype, b_layout):
+    counts = [3, 0, 64, 65, 130, 1]
+    announce("masked small", dtype, b_layout, counts)
+    w, inp = masked_case(counts, 160, 512, 256, dtype)
+    B = inp["B"] if b_layout == mg.B_KN else inp["B"].transpose(1, 2).contiguous()
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, inp.get("A_scale"), inp.get("B_scale"), b_layout)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts)
+    check_masked(w, inp, C, counts)
+
+
+def test_masked_config_full_size():
+    w = wl.workload(4)
+    announce("masked config 4", w.counts)
+    inp = wl.materialize(w, "cuda")
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws)
+    st = mg.stats_read(ws)
+    P.check_stats(st, w.counts)
+    check_masked(w, inp, C, w.counts)
+
+
+def test_masked_graph_replay():
+    """Capture once; rewrite masked_m in place between replays (no host sync
+    in the capture); every replay matches the oracle."""
+    counts0 = [5, 0, 40, 17]
+    announce("masked graph replay")
+    w, inp = masked_case(counts0, 64, 256, 256, "bf16")
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    mm = inp["counts"]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mg.grouped_gemm_masked(inp["A"], inp["B"], C, mm)        # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mg.grouped_gemm_masked(inp["A"], inp["B"], C, mm)
+    for counts in ([5, 0, 40, 17], [0, 0, 0, 0], [64, 64, 64, 64], [1, 63, 0, 2], [5, 0, 40, 17]):
+        # the capture buffer's invalid rows must be NaN for rows that become valid: refill A
+        fresh = wl.materialize(wl.Workload("m", "masked", "bf16", counts, K=256, N=256, cap=64, seed=4), "cuda")
+        inp["A"].copy_(fresh["A"])
+        mm.copy_(torch.tensor(counts, dtype=torch.int32))
+        C.view(torch.int16).fill_(P.SENTINEL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        w.counts = counts
+        check_masked(w, inp, C, counts)
+
+
+# ----------------------------------------------------------------- K-grouped
+
+
+def run_k_grouped(t_sizes, Mw, Nw, seed=5, values="normal_unit"):
+    w = wl.Workload("kg", "k_grouped", "bf16", t_sizes, Mw=Mw, Nw=Nw, values=values, seed=seed)
+    inp = wl.materialize(w, "cuda")
+    dW = torch.full((w.G, Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(w.G, 0)
+    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws)
+    torch.cuda.synchronize()
+    return w, inp, dW, ws
+
+
+def check_k_grouped(w, inp, dW, pairs):
+    X, dY = P.cpu(inp["X"]), P.cpu(inp["dY"])
+    ref = og.k_grouped(X, dY, w.counts, [e for e, _ in pairs], [i for _, i in pairs])
+    got = dW[torch.tensor([e for e, _ in pairs]), torch.tensor([i for _, i in pairs])].cpu().double().numpy()
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    assert err <= 1e-4, err          # fp32 output: no bf16 rounding anywhere, only fp32 accumulation
+    return err
+
+
+def test_k_grouped_small():
+    t = [100, 0, 37, 200, 1]
+    announce("k-grouped small", t)
+    w, inp, dW, ws = run_k_grouped(t, 256, 512)
+    pairs = [(e, i) for e in range(w.G) for i in range(w.Mw)]
+    check_k_grouped(w, inp, dW, pairs)
+    assert not dW[1].any()                        # t_e = 0 -> zeros
+    st = mg.stats_read(ws)
+    assert st.U == sum(t) and st.active == 4 and st.sum_sq == sum(x * x for x in t)
+
+
+def test_k_grouped_config_full_size():
+    w = wl.workload(5)
+    announce("k-grouped config 5", w.counts)
+    w, inp, dW, ws = run_k_grouped(w.counts, w.Mw, w.Nw)
+    rng = random.Random(5)
+    pairs = [(e, i) for e in range(w.G) for i in (0, w.Mw - 1, rng.randrange(w.Mw))]
+    err = check_k_grouped(w, inp, dW, pairs)
+    print(f"config 5: rel_frobenius={err:.3e}", flush=True)
+    for e, t in enumerate(w.counts):
+        if t == 0:
+            assert not dW[e].any()
