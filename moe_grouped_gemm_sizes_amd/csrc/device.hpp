@@ -46,8 +46,12 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)lds_base, 16, voffset, 0, 0, 0);
 }
 
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t voffset) {
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, voffset, 0, 0);
+
+// Same, with a wave-uniform scalar offset added to the address.  The
+// buffer's range check covers voffset, so row masking must live there.
+__device__ __forceinline__ void load16_to_lds_so(__amdgpu_buffer_rsrc_t rs, uint32_t voffset, uint32_t soffset,
+                                                 void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)lds_base, 16, voffset, soffset, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.

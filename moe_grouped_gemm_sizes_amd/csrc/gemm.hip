@@ -36,6 +36,8 @@
 //     of one expert, which share A tiles and weight panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 #include "workspace.hpp"
@@ -43,6 +45,15 @@
 namespace moegg {
 
 template <int X> struct dependent_false { static constexpr bool value = false; };
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // Swizzle of 16-byte chunks in a K-contiguous tile (128-byte rows).
 __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
@@ -60,7 +71,7 @@ __device__ __forceinline__ int swz_mn(int k) {
 }
 
 template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
-struct Cfg {
+struct KCfg {
     static constexpr bool FP8 = FP8_;
     static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
     static constexpr int KSTEP = 128 / ESZ;            // K elements per stage
@@ -89,40 +100,39 @@ struct Cfg {
 
 // ---------------------------------------------------------------- stage loads
 
-// K-contiguous tile: `rows` rows of 128 bytes from a buffer whose row r
-// starts at r * row_bytes, K-step byte offset kbyte.  Flat 16-byte chunk f
-// (= j * THREADS + tid) lands at LDS byte 16 f.
+// One 16-byte-per-lane DMA (the j-th of a stage) of a K-contiguous tile:
+// rows of 128 bytes from a buffer whose row r starts at r * row_bytes, K-step
+// byte offset kbyte.  Flat chunk f = j * THREADS + tid lands at LDS byte 16 f.
 template <class C>
-__device__ __forceinline__ void load_tile_k(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t kbyte,
-                                            uint32_t row0, char* lds_tile, int loads) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j >= loads) break;
-        int f = j * C::THREADS + tid;
-        int r = f >> 3, p = f & 7;
-        int c = p ^ swz_k(r);
-        uint32_t off = (row0 + r) * row_bytes + kbyte + c * 16;
-        load16_to_lds(rs, off, lds_tile + (j * C::THREADS + wave * 64) * 16);
-        (void)lane;
-    }
+__device__ __forceinline__ void load_k_one(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t kbyte,
+                                           char* lds_tile, int j) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int f = j * C::THREADS + tid;
+    const int r = f >> 3, p = f & 7;
+    const int c = p ^ swz_k(r);
+    load16_to_lds(rs, r * row_bytes + kbyte + c * 16, lds_tile + (j * C::THREADS + wave * 64) * 16);
 }
 
-// MN-contiguous tile: KSTEP rows (one per K index) of RB bytes, from a buffer
-// whose K row k starts at k * row_bytes, column byte offset cbyte.
+// One DMA of an MN-contiguous tile: KSTEP rows (one per K index) of RB bytes,
+// from a buffer whose K row k starts at k * row_bytes, column byte cbyte.
+template <class C, int RB>
+__device__ __forceinline__ void load_mn_one(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t k0,
+                                            uint32_t cbyte, char* lds_tile, int j) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    constexpr int CPR = RB / 16;                       // chunks per row
+    const int f = j * C::THREADS + tid;
+    const int r = f / CPR, p = f % CPR;
+    const int c = p ^ swz_mn<C::ESZ, RB>(r);
+    load16_to_lds(rs, (k0 + r) * row_bytes + cbyte + c * 16, lds_tile + (j * C::THREADS + wave * 64) * 16);
+}
+
 template <class C, int RB>
 __device__ __forceinline__ void load_tile_mn(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t k0,
                                              uint32_t cbyte, char* lds_tile, int loads) {
-    const int tid = threadIdx.x, wave = tid >> 6;
-    constexpr int CPR = RB / 16;                       // chunks per row
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j >= loads) break;
-        int f = j * C::THREADS + tid;
-        int r = f / CPR, p = f % CPR;
-        int c = p ^ swz_mn<C::ESZ, RB>(r);
-        uint32_t off = (k0 + r) * row_bytes + cbyte + c * 16;
-        load16_to_lds(rs, off, lds_tile + (j * C::THREADS + wave * 64) * 16);
+        load_mn_one<C, RB>(rs, row_bytes, k0, cbyte, lds_tile, j);
     }
 }
 
@@ -192,127 +202,281 @@ __device__ __forceinline__ int block_to_item(int b) {
     return (b >> 8) * 256 + (b & 7) * 32 + ((b & 255) >> 3);
 }
 
-// ---------------------------------------------------------------- main loop
+// ---------------------------------------------------------------- contiguous / masked
 
-// Accumulates one output tile: rows [0, rows_valid) of the activation tile
-// against one weight panel, over nks K steps.
-//   B_KN: weight stored [K, N] (N contiguous), else [N, K].
+// Tile configuration for the contiguous and masked kernels: 512 threads,
+// WAVES_M x WAVES_N waves, each owning a WTM x WTN block of the BM x BN tile.
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct GCfg {
+    static constexpr bool FP8 = FP8_;
+    static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
+    static constexpr int KSTEP = 128 / ESZ;            // K elements per step (128 bytes)
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int STAGES = STAGES_;             // weight-tile ring depth in LDS
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int MB = WTM / 16, NB = WTN / 16;
+    static constexpr int B_BYTES = BN * 128;           // one K step of the weight tile
+    static constexpr int B_OPS = B_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
+    static constexpr int A_OPS = 2 * MB;               // 16-byte activation loads per lane per step
+    static constexpr int S_OPS = FP8 ? MB : 0;         // per-row scale loads per lane per step
+    static constexpr int SCRATCH_OFF = STAGES * B_BYTES;
+    static constexpr int LDS_BYTES = SCRATCH_OFF + WAVES * 256;
+    static_assert(WAVES == 8, "512-thread tiles");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0 && MB >= 1, "wave tile");
+    static_assert(B_BYTES % (16 * THREADS) == 0, "weight stage split");
+    static_assert(!FP8 || (128 % WTN == 0 || WTN % 128 == 0), "fp8 weight scale blocks");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 3, "ring depth");
+};
+
+// L2 warming distance (K steps) for the activation rows.
+constexpr int PF_DIST = 3;
+
+__device__ __forceinline__ void touch_line(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* scratch) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)scratch, 4, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// One output tile of the contiguous or masked layout.
+//
+// Data flow per K step (128 bytes of K per row):
+//   - activations: each wave loads its own WTM rows straight from L2 into MFMA
+//     B-operand registers, one step ahead, with a 4-byte LDS-DMA "touch" that
+//     pulls the lines PF_DIST steps ahead into L2;
+//   - weights: the BN-column K slice is DMA'd into an LDS ring STAGES deep
+//     (STAGES-1 steps in flight) and read out as MFMA A-operand fragments,
+//     through ds_read_b64_tr_b8/_b16 when the weight is N-contiguous.
+// One workgroup barrier per step publishes the ring slot.
 template <class C, bool B_KN>
 struct TileGemm {
+    // 128-column weight-scale blocks spanned by one wave tile (fp8)
+    static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;
     v4f acc[C::NB][C::MB];
 
-    __device__ __forceinline__ void run(char* lds, __amdgpu_buffer_rsrc_t ra, uint32_t a_row_bytes,
-                                        __amdgpu_buffer_rsrc_t rb, uint32_t b_row_bytes, uint32_t b_col_byte,
-                                        __amdgpu_buffer_rsrc_t rsa, uint32_t sa_row_bytes,
-                                        const float* __restrict__ b_scale, int b_scale_stride, int nks,
-                                        int rows_valid) {
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-        const int r16 = lane & 15;
-        const int mb_active = min(C::MB, max(0, (rows_valid - wm * C::WTM + 15) >> 4));
+    __amdgpu_buffer_rsrc_t ra, rb, rsa;
+    uint32_t a_row_bytes, b_row_bytes, b_col_byte, sa_row_bytes;
+    const float* b_scale;      // this wave's first 128-column scale block, step 0
+    int b_scale_stride;        // scale elements between K steps
+    int wm, wn, r16, g;
+
+    __device__ __forceinline__ int arow(int j) const { return wm * C::WTM + j * 16 + r16; }
+
+    // activation fragments of step ks: fp8 -> bytes [32g, 32g+32) of the row's
+    // 128-byte K slice (two halves); bf16 -> half-step kk bytes [64kk+16g, +16)
+    __device__ __forceinline__ void load_a(int ks, v4i (&ya)[C::MB][2]) const {
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) {
+            const uint32_t v = arow(j) * a_row_bytes;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t kb = C::FP8 ? 32 * g + 16 * h : 64 * h + 16 * g;
+                ya[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, v + kb, ks * 128, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load_s(int ks, float (&sa)[C::MB]) const {
+        if constexpr (C::FP8) {
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j)
+                sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, arow(j) * sa_row_bytes,
+                                                                                         ks * 4, 0));
+        }
+    }
+
+    __device__ __forceinline__ void touch_a(char* lds, int kt) const {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int row = wm * C::WTM + lane % C::WTM;
+        touch_line(ra, row * a_row_bytes + kt * 128, lds + C::SCRATCH_OFF + wave * 256);
+    }
+
+    // weight K slice of step ks into ring slot `slot`
+    __device__ __forceinline__ void load_b(char* lds, int ks, int slot) const {
+        const int tid = threadIdx.x, wave = tid >> 6;
+        char* dst0 = lds + slot * C::B_BYTES + wave * 64 * 16;
+        if constexpr (B_KN) {
+            constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;   // K rows per op
+            const int r0 = tid / CPR, p0 = tid % CPR;
+#pragma unroll
+            for (int j = 0; j < C::B_OPS; ++j) {
+                const int c = p0 ^ swz_mn<C::ESZ, RB>(r0 + j * RPO);
+                load16_to_lds_so(rb, r0 * b_row_bytes + b_col_byte + c * 16,
+                                 (ks * C::KSTEP + j * RPO) * b_row_bytes, dst0 + j * C::THREADS * 16);
+            }
+        } else {
+            const int r0 = tid >> 3;                                   // swz_k(r0 + 64 j) == swz_k(r0)
+            const uint32_t v0 = r0 * b_row_bytes + (((tid & 7) ^ swz_k(r0)) << 4);
+#pragma unroll
+            for (int j = 0; j < C::B_OPS; ++j)
+                load16_to_lds_so(rb, v0, j * 64 * b_row_bytes + ks * 128, dst0 + j * C::THREADS * 16);
+        }
+    }
+
+    __device__ __forceinline__ static void promote(v4f& a, const v4f q, float s) {
+        a.x = __builtin_fmaf(q.x, s, a.x);
+        a.y = __builtin_fmaf(q.y, s, a.y);
+        a.z = __builtin_fmaf(q.z, s, a.z);
+        a.w = __builtin_fmaf(q.w, s, a.w);
+    }
+
+    // MFMA work of one K step for a wave with MBA active 16-row blocks.
+    template <int MBA>
+    __device__ __forceinline__ void compute(const char* tb, const v4i (&ya)[C::MB][2], const float (&sa)[C::MB],
+                                            const float (&bsc)[NSB]) {
+        if constexpr (MBA == 0) {
+            return;
+        } else if constexpr (C::FP8) {
+            float s[NSB][MBA];
+            v8i y[MBA];
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) {
+#pragma unroll
+                for (int b = 0; b < NSB; ++b) s[b][j] = sa[j] * bsc[b];
+                y[j] = v8i{ya[j][0].x, ya[j][0].y, ya[j][0].z, ya[j][0].w,
+                           ya[j][1].x, ya[j][1].y, ya[j][1].z, ya[j][1].w};
+            }
+            auto fragb = [&](int i) -> v8i {
+                const int n0 = wn * C::WTN + i * 16;
+                if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
+                else return frag_k_fp8(tb, n0 + r16);
+            };
+            // per 16-column block i: read block i+1's weight fragment, issue block
+            // i's MFMAs, then promote block i-1's partials (finished meanwhile)
+            v8i xb[2];
+            v4f p[2][MBA];
+            xb[0] = fragb(0);
+            static_for<0, C::NB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) p[i & 1][j] = mfma_fp8(xb[i & 1], y[j], v4f{0.f, 0.f, 0.f, 0.f});
+                if constexpr (i > 0) {
+                    constexpr int sb = NSB > 1 ? (i - 1) * 16 / 128 : 0;
+#pragma unroll
+                    for (int j = 0; j < MBA; ++j) promote(acc[i - 1][j], p[(i - 1) & 1][j], s[sb][j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            constexpr int sb_last = NSB > 1 ? (C::NB - 1) * 16 / 128 : 0;
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) promote(acc[C::NB - 1][j], p[(C::NB - 1) & 1][j], s[sb_last][j]);
+        } else {
+            static_for<0, 2>([&](auto KK) {
+                constexpr int kk = decltype(KK)::value;
+                auto fragb = [&](int i) -> v4i {
+                    const int n0 = wn * C::WTN + i * 16;
+                    if constexpr (B_KN) return frag_mn_bf16<C::BN * 2>(tb, n0, kk);
+                    else return frag_k_bf16(tb, n0 + r16, kk);
+                };
+                v4i xb[2];
+                xb[0] = fragb(0);
+                static_for<0, C::NB>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
+#pragma unroll
+                    for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[i & 1], ya[j][kk], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            });
+        }
+    }
+
+    __device__ __forceinline__ static void barrier() {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    }
+
+    // Issue order per step (vmcnt counts in order): activations and scales
+    // for the next step, one touch, then the weight slice STAGES-1 steps
+    // ahead.  Steps past the end are clamped to the last one so every wave
+    // issues the same number of operations every step.
+    template <int MBA>
+    __device__ __forceinline__ void kloop(char* lds, int nks) {
+        constexpr int S = C::STAGES;
+        v4i ya[C::MB][2], yn[C::MB][2];
+        float sa[C::MB] = {}, sn[C::MB] = {};
+        load_b(lds, 0, 0);
+        compiler_fence();
+        load_a(0, ya);
+        load_s(0, sa);
+        compiler_fence();
+#pragma unroll
+        for (int s = 1; s < S - 1; ++s) load_b(lds, min(s, nks - 1), s);
+#pragma unroll
+        for (int d = 1; d <= PF_DIST; ++d) touch_a(lds, min(d, nks - 1));
+        compiler_fence();
+        wait_vmcnt<(S - 2) * C::B_OPS + PF_DIST>();   // weight slice 0 and step-0 activations landed
+        float bsc[NSB] = {}, bsc_next[NSB] = {};
+        if constexpr (C::FP8) {
+#pragma unroll
+            for (int b = 0; b < NSB; ++b) bsc[b] = b_scale[b];
+        }
+        for (int ks = 0; ks < nks; ++ks) {
+            barrier();        // every wave's slice ks is in LDS; slot (ks-1) % S is free
+            const int kn = min(ks + 1, nks - 1);
+            if constexpr (C::FP8) {
+#pragma unroll
+                for (int b = 0; b < NSB; ++b) bsc_next[b] = b_scale[kn * b_scale_stride + b];
+            }
+            load_a(kn, yn);
+            load_s(kn, sn);
+            compiler_fence();
+            touch_a(lds, min(ks + 1 + PF_DIST, nks - 1));
+            compiler_fence();
+            load_b(lds, min(ks + S - 1, nks - 1), (ks + S - 1) % S);
+            compiler_fence();
+            compute<MBA>(lds + (ks % S) * C::B_BYTES, ya, sa, bsc);
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j) {
+                ya[j][0] = yn[j][0];
+                ya[j][1] = yn[j][1];
+                sa[j] = sn[j];
+            }
+#pragma unroll
+            for (int b = 0; b < NSB; ++b) bsc[b] = bsc_next[b];
+            // next step's weight slice and activations landed (only the touch and
+            // the newest weight slice may still be in flight)
+            wait_vmcnt<1 + C::B_OPS>();
+        }
+        // no LDS DMA may still be in flight when the wave moves on or exits
+        wait_vmcnt<0>();
+    }
+
+    template <int M>
+    __device__ __forceinline__ void dispatch(char* lds, int mba, int nks) {
+        if constexpr (M < 0) {
+            return;
+        } else {
+            if (mba == M) kloop<M>(lds, nks);
+            else dispatch<M - 1>(lds, mba, nks);
+        }
+    }
+
+    __device__ __forceinline__ void run(char* lds, int nks, int rows_valid) {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        wm = wave / C::WAVES_N;
+        wn = wave % C::WAVES_N;
+        r16 = lane & 15;
+        g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < C::NB; ++i)
 #pragma unroll
             for (int j = 0; j < C::MB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        auto issue = [&](int ks, int slot) {
-            char* base = lds + slot * C::STAGE_BYTES;
-            load_tile_k<C>(ra, a_row_bytes, ks * 128, 0, base, C::A_LOADS);
-            if constexpr (B_KN) {
-                load_tile_mn<C, C::BN * C::ESZ>(rb, b_row_bytes, ks * C::KSTEP, b_col_byte, base + C::A_BYTES,
-                                                C::B_LOADS);
-            } else {
-                load_tile_k<C>(rb, b_row_bytes, ks * 128, 0, base + C::A_BYTES, C::B_LOADS);
-            }
-            if constexpr (C::FP8) {
-                // one 4-byte scale per tile row for K group ks; waves past BM/64 repeat rows
-                int r = (wave % (C::BM / 64)) * 64 + lane;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsa, (MOEGG_LDS void*)(base + C::A_BYTES + C::B_BYTES + (wave % (C::BM / 64)) * 256), 4,
-                    r * sa_row_bytes + ks * 4, 0, 0, 0);
-            }
-        };
-
-#pragma unroll
-        for (int s = 0; s < C::STAGES - 1; ++s)
-            if (s < nks) issue(s, s);
-
-        float bsc = 0.f;
-        if constexpr (C::FP8) bsc = b_scale[0];
-        for (int ks = 0; ks < nks; ++ks) {
-            const int slot = ks % C::STAGES;
-            if (ks + C::STAGES - 1 < nks) {
-                issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
-                wait_vmcnt<C::VM_PER_STAGE * (C::STAGES - 1)>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            float bsc_next = 0.f;
-            if constexpr (C::FP8) bsc_next = (ks + 1 < nks) ? b_scale[(ks + 1) * b_scale_stride] : 0.f;
-            __syncthreads();
-            const char* ta = lds + slot * C::STAGE_BYTES;
-            const char* tb = ta + C::A_BYTES;
-            if constexpr (C::FP8) {
-                const float* ts = (const float*)(tb + C::B_BYTES);
-                v8i ya[C::MB];
-                float sa[C::MB];
-#pragma unroll
-                for (int j = 0; j < C::MB; ++j) {
-                    if (j < mb_active) {
-                        int row = wm * C::WTM + j * 16 + r16;
-                        ya[j] = frag_k_fp8(ta, row);
-                        sa[j] = ts[row] * bsc;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < C::NB; ++i) {
-                    const int n0 = wn * C::WTN + i * 16;
-                    v8i xb;
-                    if constexpr (B_KN) xb = frag_mn_fp8<C::BN>(tb, n0);
-                    else xb = frag_k_fp8(tb, n0 + r16);
-#pragma unroll
-                    for (int j = 0; j < C::MB; ++j) {
-                        if (j < mb_active) {
-                            v4f p = mfma_fp8(xb, ya[j], v4f{0.f, 0.f, 0.f, 0.f});
-                            acc[i][j].x = __builtin_fmaf(p.x, sa[j], acc[i][j].x);
-                            acc[i][j].y = __builtin_fmaf(p.y, sa[j], acc[i][j].y);
-                            acc[i][j].z = __builtin_fmaf(p.z, sa[j], acc[i][j].z);
-                            acc[i][j].w = __builtin_fmaf(p.w, sa[j], acc[i][j].w);
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    v4i ya[C::MB];
-#pragma unroll
-                    for (int j = 0; j < C::MB; ++j)
-                        if (j < mb_active) ya[j] = frag_k_bf16(ta, wm * C::WTM + j * 16 + r16, kk);
-#pragma unroll
-                    for (int i = 0; i < C::NB; ++i) {
-                        const int n0 = wn * C::WTN + i * 16;
-                        v4i xb;
-                        if constexpr (B_KN) xb = frag_mn_bf16<C::BN * 2>(tb, n0, kk);
-                        else xb = frag_k_bf16(tb, n0 + r16, kk);
-#pragma unroll
-                        for (int j = 0; j < C::MB; ++j)
-                            if (j < mb_active) acc[i][j] = mfma_bf16(xb, ya[j], acc[i][j]);
-                    }
-                }
-            }
-            if constexpr (C::FP8) bsc = bsc_next;
-            __syncthreads();
-        }
+        // active 16-row blocks of this wave; wave-uniform, so the loop has no divergence
+        const int mba = __builtin_amdgcn_readfirstlane(min(C::MB, max(0, (rows_valid - wm * C::WTM + 15) >> 4)));
+        dispatch<C::MB>(lds, mba, nks);
     }
 
     // bf16 epilogue: rows < rows_valid of the tile; C rows are row_bytes apart.
     __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-        const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int j = 0; j < C::MB; ++j) {
-            const int row = wm * C::WTM + j * 16 + r16;
+            const int row = arow(j);
             if (row < rows_valid) {
 #pragma unroll
                 for (int i = 0; i < C::NB; ++i) {
@@ -326,9 +490,6 @@ struct TileGemm {
         }
     }
 };
-
-// ---------------------------------------------------------------- kernels
-
 
 // M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout.
 template <class C, bool B_KN, bool MASKED>
@@ -365,33 +526,31 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs 
     }
     const int n0 = ct * C::BN;
     const int KB = p.K / 128;
-    const uint32_t a_row_bytes = (uint32_t)p.K * C::ESZ;
-    auto ra = make_rsrc((const char*)p.A + (size_t)row_start * a_row_bytes, (uint32_t)rows_valid * a_row_bytes);
+    TileGemm<C, B_KN> tg;
+    tg.a_row_bytes = (uint32_t)p.K * C::ESZ;
+    tg.ra = make_rsrc((const char*)p.A + (size_t)row_start * tg.a_row_bytes, (uint32_t)rows_valid * tg.a_row_bytes);
     const size_t b_expert_bytes = (size_t)p.K * p.N * C::ESZ;
     const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
-    __amdgpu_buffer_rsrc_t rb;
-    uint32_t b_row_bytes, b_col_byte;
     if constexpr (B_KN) {
-        rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
-        b_row_bytes = (uint32_t)p.N * C::ESZ;
-        b_col_byte = (uint32_t)n0 * C::ESZ;
+        tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
+        tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
+        tg.b_col_byte = (uint32_t)n0 * C::ESZ;
     } else {
-        rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
-        b_row_bytes = (uint32_t)p.K * C::ESZ;
-        b_col_byte = 0;
+        tg.rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
+        tg.b_row_bytes = (uint32_t)p.K * C::ESZ;
+        tg.b_col_byte = 0;
     }
-    __amdgpu_buffer_rsrc_t rsa = rb;
-    const float* bs = nullptr;
-    int bs_stride = 0;
+    tg.rsa = tg.rb;
+    tg.sa_row_bytes = (uint32_t)KB * 4;
+    tg.b_scale = nullptr;
+    tg.b_scale_stride = 0;
     if constexpr (C::FP8) {
-        rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
+        tg.rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
         const int wn = (threadIdx.x >> 6) % C::WAVES_N;
-        bs = p.B_scale + (size_t)e * KB * (p.N / 128) + (n0 + wn * C::WTN) / 128;
-        bs_stride = p.N / 128;
+        tg.b_scale = p.B_scale + (size_t)e * KB * (p.N / 128) + (n0 + wn * C::WTN) / 128;
+        tg.b_scale_stride = p.N / 128;
     }
-    TileGemm<C, B_KN> tg;
-    tg.run(lds, ra, a_row_bytes, rb, b_row_bytes, b_col_byte, rsa, (uint32_t)KB * 4, bs, bs_stride,
-           p.K / C::KSTEP, rows_valid);
+    tg.run(lds, p.K / C::KSTEP, rows_valid);
     const uint32_t c_row_bytes = (uint32_t)p.N * 2;
     auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
                         (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
@@ -484,13 +643,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
 // ---------------------------------------------------------------- configs
 
-// Contiguous: 512 threads, 256 columns per tile, every wave tile 64 rows tall.
-template <bool FP8> using Contig256 = Cfg<FP8, 256, 256, 4, 2, 2>;
-template <bool FP8> using Contig128 = Cfg<FP8, 128, 256, 2, 4, 3>;
-template <bool FP8> using Contig64 = Cfg<FP8, 64, 256, 1, 8, 3>;
-// Masked decode: short row tiles, narrow column tiles, deep pipeline (HBM-bound).
-template <bool FP8> using MaskedCfg = Cfg<FP8, 64, 128, 2, 4, 4>;
-using KGroupedCfg = Cfg<false, 256, 256, 4, 2, 2>;
+// Contiguous: 256-column tiles; 8 waves stacked along M, so every activation
+// row is loaded by exactly one wave; 4-deep weight ring.
+template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 8, 1, 4>;
+template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 8, 1, 4>;
+template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 4, 2, 4>;
+// Masked decode: short row tiles, narrow column tiles, deep weight ring (HBM-bound).
+template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 4, 2, 6>;
+using KGroupedCfg = KCfg<false, 256, 256, 4, 2, 2>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
 // attribute, not a stream operation).
@@ -545,8 +705,8 @@ int masked_block_m() { return MaskedCfg<false>::BM; }
 int masked_block_n() { return MaskedCfg<false>::BN; }
 
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s) {
-    const int n_rt = (a.cap + 63) / 64;
-    const int grid = a.G * n_rt * (a.N / 128);
+    const int n_rt = (a.cap + MaskedCfg<false>::BM - 1) / MaskedCfg<false>::BM;
+    const int grid = a.G * n_rt * (a.N / MaskedCfg<false>::BN);
     if (fp8) return b_kn ? launch_one<MaskedCfg<true>, true, true>(a, grid, s)
                          : launch_one<MaskedCfg<true>, false, true>(a, grid, s);
     return b_kn ? launch_one<MaskedCfg<false>, true, true>(a, grid, s)
