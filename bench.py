@@ -42,8 +42,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_step(w: wl.Workload, inp, block_m_hint: int):
-    """Returns (step, gemm_only, outputs) closures for one workload."""
+def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int):
+    """Returns (scheduler, gemm, workspace) closures for one workload."""
     dev = "cuda"
     if w.layout == "contiguous":
         C = torch.empty((w.rows_total, w.N), dtype=torch.bfloat16, device=dev)
@@ -54,7 +54,7 @@ def build_step(w: wl.Workload, inp, block_m_hint: int):
 
         def gemm():
             mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"),
-                                                 inp.get("B_scale"), block_m=block_m_hint)
+                                                 inp.get("B_scale"), block_m=block_m_hint, b_layout=b_layout)
         return sched, gemm, ws
     if w.layout == "masked":
         C = torch.empty((w.G, w.cap, w.N), dtype=torch.bfloat16, device=dev)
@@ -62,7 +62,7 @@ def build_step(w: wl.Workload, inp, block_m_hint: int):
 
         def gemm():
             mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], None, inp.get("A_scale"),
-                                   inp.get("B_scale"))
+                                   inp.get("B_scale"), b_layout=b_layout)
         return None, gemm, ws
     dW = torch.empty((w.G, w.Mw, w.Nw), dtype=torch.float32, device=dev)
     ws = mg.workspace(w.G, 0)
@@ -85,6 +85,30 @@ def algorithmic_bytes(w: wl.Workload) -> int:
     return b
 
 
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.hpp", "workspace.hpp"):
+        with open(os.path.join(ROOT, "moe_grouped_gemm_sizes_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(w: wl.Workload, b_layout: int):
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on this exact kernel source and workload; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}"
+    e = t.get("entries", {}).get(key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of rows."""
     from oracle import gemm as og
@@ -93,6 +117,8 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
     if w.layout != "contiguous":
         return None
     cpu = {k: (v.cpu().contiguous() if v is not None else None) for k, v in inp.items()}
+    if cpu["B"].shape[1] != w.K:                     # weights were repacked to [G,N,K]
+        cpu["B"] = cpu["B"].transpose(1, 2).contiguous()
     rows = sample_rows_contiguous(w.counts, w.seg_align, 256, extra=4096, seed=99)
     threads = og.threads()
     probe = rows[:threads]
@@ -118,6 +144,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--b-layout", choices=("kn", "nk"), default="nk",
+                    help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE "
+                         "weights are usually kept in); repacking is one-time, outside the timed steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -130,15 +159,18 @@ def main():
     w = wl.workload(args.config)
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
+    b_layout = mg.B_NK if args.b_layout == "nk" else mg.B_KN
+    if b_layout == mg.B_NK and "B" in inp:
+        inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
     torch.cuda.synchronize()
 
     # first pass: learn the device's tile-height choice (outside timing)
-    sched, gemm, ws = build_step(w, inp, 0)
+    sched, gemm, ws = build_step(w, inp, 0, b_layout)
     if sched is not None:
         sched()
         torch.cuda.synchronize()
         st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp, st0.block_m)
+        sched, gemm, ws = build_step(w, inp, st0.block_m, b_layout)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -183,7 +215,8 @@ def main():
         "dtype": "fp8_e4m3" if w.dtype == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
-                   "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed},
+                   "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
+                   "weights": "[G,N,K]" if b_layout == mg.B_NK else "[G,K,N]"},
         "pct_mfma_peak": round(100.0 * eff / peak, 2),
     }
     if w.layout == "contiguous":
@@ -201,6 +234,9 @@ def main():
     else:
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": peak,
                            "unit": "TFLOP/s", "frac": round(achieved_tflops / peak, 4), "traffic": None}
+    tr = traffic_for(w, b_layout)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr
     out["gemm_kernel_ms"] = round(gemm_avg, 4)
     out["algorithmic_bytes"] = bytes_alg
     out["wall_s_timed"] = round(wall, 4)

@@ -204,35 +204,38 @@ __device__ __forceinline__ int block_to_item(int b) {
 
 // ---------------------------------------------------------------- contiguous / masked
 
-// Tile configuration for the contiguous and masked kernels: 512 threads,
+// Tile configuration for the contiguous and masked kernels: 512 threads as
 // WAVES_M x WAVES_N waves, each owning a WTM x WTN block of the BM x BN tile.
-template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// Both operand tiles of a K step (128 bytes of K per row) live in LDS,
+// double-buffered.
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
     static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
-    static constexpr int KSTEP = 128 / ESZ;            // K elements per step (128 bytes)
+    static constexpr int KSTEP = 128 / ESZ;            // K elements per step
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int STAGES = STAGES_;             // weight-tile ring depth in LDS
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int MB = WTM / 16, NB = WTN / 16;
-    static constexpr int B_BYTES = BN * 128;           // one K step of the weight tile
-    static constexpr int B_OPS = B_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
-    static constexpr int A_OPS = 2 * MB;               // 16-byte activation loads per lane per step
-    static constexpr int S_OPS = FP8 ? MB : 0;         // per-row scale loads per lane per step
-    static constexpr int SCRATCH_OFF = STAGES * B_BYTES;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    static constexpr int S_BYTES = FP8 ? BM * 4 : 0;   // per-row activation scales of the step
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int SCRATCH_OFF = 2 * STAGE_BYTES;
     static constexpr int LDS_BYTES = SCRATCH_OFF + WAVES * 256;
+    static constexpr int A_OPS = A_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
+    static constexpr int B_OPS = B_BYTES / 16 / THREADS;
+    static constexpr int OPS = A_OPS + B_OPS + (FP8 ? 1 : 0) + 1;   // + scales + one L2 touch
     static_assert(WAVES == 8, "512-thread tiles");
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0 && MB >= 1, "wave tile");
-    static_assert(B_BYTES % (16 * THREADS) == 0, "weight stage split");
-    static_assert(!FP8 || (128 % WTN == 0 || WTN % 128 == 0), "fp8 weight scale blocks");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
+    static_assert(!FP8 || BM >= 64, "one scale DMA per 64 rows");
+    static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(STAGES >= 3, "ring depth");
 };
 
-// L2 warming distance (K steps) for the activation rows.
+// L2 warming distance (K steps).
 constexpr int PF_DIST = 3;
 
 __device__ __forceinline__ void touch_line(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* scratch) {
@@ -243,77 +246,95 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 
 // One output tile of the contiguous or masked layout.
 //
-// Data flow per K step (128 bytes of K per row):
-//   - activations: each wave loads its own WTM rows straight from L2 into MFMA
-//     B-operand registers, one step ahead, with a 4-byte LDS-DMA "touch" that
-//     pulls the lines PF_DIST steps ahead into L2;
-//   - weights: the BN-column K slice is DMA'd into an LDS ring STAGES deep
-//     (STAGES-1 steps in flight) and read out as MFMA A-operand fragments,
-//     through ds_read_b64_tr_b8/_b16 when the weight is N-contiguous.
-// One workgroup barrier per step publishes the ring slot.
+// Per K step (128 bytes of K per row) every wave, in one instruction stream:
+//   - reads its activation fragments (4 x 16 rows) and, block by block, its
+//     weight fragments (16 columns at a time) from LDS; ds_read_b64_tr_b8/_b16
+//     transpose N-contiguous weights on the way out;
+//   - issues its MFMAs for block i, then promotes block i-1's fp8 partials
+//     (their MFMAs finished meanwhile);
+//   - after each block's MFMAs, issues one or two of its share of the next
+//     step's DMAs (activation tile, weight tile, per-row scales, one L2
+//     touch PF_DIST steps ahead), so address processing runs under the
+//     matrix cores instead of stalling a wave at the top of the step.
+// One vmcnt wait plus one barrier per step publishes the next stage.
 template <class C, bool B_KN>
 struct TileGemm {
-    // 128-column weight-scale blocks spanned by one wave tile (fp8)
-    static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;
+    static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     v4f acc[C::NB][C::MB];
 
     __amdgpu_buffer_rsrc_t ra, rb, rsa;
     uint32_t a_row_bytes, b_row_bytes, b_col_byte, sa_row_bytes;
     const float* b_scale;      // this wave's first 128-column scale block, step 0
     int b_scale_stride;        // scale elements between K steps
-    int wm, wn, r16, g;
+    int wm, wn, r16;
 
-    __device__ __forceinline__ int arow(int j) const { return wm * C::WTM + j * 16 + r16; }
-
-    // activation fragments of step ks: fp8 -> bytes [32g, 32g+32) of the row's
-    // 128-byte K slice (two halves); bf16 -> half-step kk bytes [64kk+16g, +16)
-    __device__ __forceinline__ void load_a(int ks, v4i (&ya)[C::MB][2]) const {
-#pragma unroll
-        for (int j = 0; j < C::MB; ++j) {
-            const uint32_t v = arow(j) * a_row_bytes;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t kb = C::FP8 ? 32 * g + 16 * h : 64 * h + 16 * g;
-                ya[j][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, v + kb, ks * 128, 0);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void load_s(int ks, float (&sa)[C::MB]) const {
-        if constexpr (C::FP8) {
-#pragma unroll
-            for (int j = 0; j < C::MB; ++j)
-                sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, arow(j) * sa_row_bytes,
-                                                                                         ks * 4, 0));
-        }
-    }
-
-    __device__ __forceinline__ void touch_a(char* lds, int kt) const {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        const int row = wm * C::WTM + lane % C::WTM;
-        touch_line(ra, row * a_row_bytes + kt * 128, lds + C::SCRATCH_OFF + wave * 256);
-    }
-
-    // weight K slice of step ks into ring slot `slot`
-    __device__ __forceinline__ void load_b(char* lds, int ks, int slot) const {
-        const int tid = threadIdx.x, wave = tid >> 6;
-        char* dst0 = lds + slot * C::B_BYTES + wave * 64 * 16;
-        if constexpr (B_KN) {
-            constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;   // K rows per op
-            const int r0 = tid / CPR, p0 = tid % CPR;
-#pragma unroll
-            for (int j = 0; j < C::B_OPS; ++j) {
-                const int c = p0 ^ swz_mn<C::ESZ, RB>(r0 + j * RPO);
+    // ---- DMA of one stage, as OPS separately issued operations
+    template <int OP>
+    __device__ __forceinline__ void issue_op(char* lds, int ks, int slot, int nks) const {
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        char* base = lds + slot * C::STAGE_BYTES;
+        if constexpr (OP < C::A_OPS) {
+            // activation rows r0 + 64 OP; swz_k(r0 + 64 j) == swz_k(r0); the row offset stays
+            // in voffset (range-checked: rows past rows_valid read as zero)
+            const int r = (tid >> 3) + OP * (C::THREADS / 8);
+            load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k(r))) << 4), ks * 128,
+                             base + (OP * C::THREADS + wave * 64) * 16);
+        } else if constexpr (OP < C::A_OPS + C::B_OPS) {
+            constexpr int j = OP - C::A_OPS;
+            char* dst = base + C::A_BYTES + (j * C::THREADS + wave * 64) * 16;
+            if constexpr (B_KN) {
+                constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
+                const int r0 = tid / CPR;
+                const int c = (tid % CPR) ^ swz_mn<C::ESZ, RB>(r0 + j * RPO);
                 load16_to_lds_so(rb, r0 * b_row_bytes + b_col_byte + c * 16,
-                                 (ks * C::KSTEP + j * RPO) * b_row_bytes, dst0 + j * C::THREADS * 16);
+                                 (ks * C::KSTEP + j * RPO) * b_row_bytes, dst);
+            } else {
+                const int r0 = tid >> 3;
+                load16_to_lds_so(rb, r0 * b_row_bytes + (((tid & 7) ^ swz_k(r0)) << 4),
+                                 j * (C::THREADS / 8) * b_row_bytes + ks * 128, dst);
             }
+        } else if constexpr (C::FP8 && OP == C::A_OPS + C::B_OPS) {
+            // one 4-byte scale per tile row for K group ks; waves past BM/64 repeat rows
+            const int blk = wave % (C::BM / 64);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsa, (MOEGG_LDS void*)(base + C::A_BYTES + C::B_BYTES + blk * 256), 4,
+                (blk * 64 + lane) * sa_row_bytes, ks * 4, 0, 0);
         } else {
-            const int r0 = tid >> 3;                                   // swz_k(r0 + 64 j) == swz_k(r0)
-            const uint32_t v0 = r0 * b_row_bytes + (((tid & 7) ^ swz_k(r0)) << 4);
-#pragma unroll
-            for (int j = 0; j < C::B_OPS; ++j)
-                load16_to_lds_so(rb, v0, j * 64 * b_row_bytes + ks * 128, dst0 + j * C::THREADS * 16);
+            touch(lds, min(ks + PF_DIST, nks - 1));
         }
+    }
+
+    // L2 touch of step kt: activation rows, then weight lines, 64 per wave
+    __device__ __forceinline__ void touch(char* lds, int kt) const {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        constexpr int LINES = C::BM + C::BN;               // one 128-byte line per tile row / K row pair
+        const int line = (wave * 64 + lane) % LINES;
+        char* scratch = lds + C::SCRATCH_OFF + wave * 256;
+        if (line < C::BM) {
+            touch_line(ra, line * a_row_bytes + kt * 128, scratch);
+        } else {
+            const int l = line - C::BM;
+            if constexpr (B_KN) {
+                constexpr int LPR = C::BN * C::ESZ / 128;
+                touch_line(rb, (kt * C::KSTEP + l / LPR) * b_row_bytes + b_col_byte + (l % LPR) * 128, scratch);
+            } else {
+                touch_line(rb, l * b_row_bytes + kt * 128, scratch);
+            }
+        }
+    }
+
+    template <int LO, int HI>
+    __device__ __forceinline__ void issue_range(char* lds, int ks, int slot, int nks) const {
+        if constexpr (LO < HI) {
+            issue_op<LO>(lds, ks, slot, nks);
+            issue_range<LO + 1, HI>(lds, ks, slot, nks);
+        }
+    }
+
+    // the share of the stage's operations issued after block AT of NBLK
+    template <int AT, int NBLK>
+    __device__ __forceinline__ void issue_share(char* lds, int ks, int slot, int nks) const {
+        issue_range<AT * C::OPS / NBLK, (AT + 1) * C::OPS / NBLK>(lds, ks, slot, nks);
     }
 
     __device__ __forceinline__ static void promote(v4f& a, const v4f q, float s) {
@@ -323,50 +344,64 @@ struct TileGemm {
         a.w = __builtin_fmaf(q.w, s, a.w);
     }
 
-    // MFMA work of one K step for a wave with MBA active 16-row blocks.
+    // One K step for a wave with MBA active 16-row blocks, interleaved with the
+    // DMA of step `next` (already clamped) into the other stage.
     template <int MBA>
-    __device__ __forceinline__ void compute(const char* tb, const v4i (&ya)[C::MB][2], const float (&sa)[C::MB],
-                                            const float (&bsc)[NSB]) {
+    __device__ __forceinline__ void step(char* lds, int ks, int next, int nks, const float (&bsc)[NSB]) {
+        const char* ta = lds + (ks & 1) * C::STAGE_BYTES;
+        const char* tb = ta + C::A_BYTES;
+        const int nslot = (ks + 1) & 1;
         if constexpr (MBA == 0) {
-            return;
+            issue_range<0, C::OPS>(lds, next, nslot, nks);
         } else if constexpr (C::FP8) {
+            const float* ts = (const float*)(tb + C::B_BYTES);
+            v8i ya[MBA];
             float s[NSB][MBA];
-            v8i y[MBA];
 #pragma unroll
             for (int j = 0; j < MBA; ++j) {
+                const int row = wm * C::WTM + j * 16 + r16;
+                ya[j] = frag_k_fp8(ta, row);
+                const float as = ts[row];
 #pragma unroll
-                for (int b = 0; b < NSB; ++b) s[b][j] = sa[j] * bsc[b];
-                y[j] = v8i{ya[j][0].x, ya[j][0].y, ya[j][0].z, ya[j][0].w,
-                           ya[j][1].x, ya[j][1].y, ya[j][1].z, ya[j][1].w};
+                for (int b = 0; b < NSB; ++b) s[b][j] = as * bsc[b];
             }
             auto fragb = [&](int i) -> v8i {
                 const int n0 = wn * C::WTN + i * 16;
                 if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
                 else return frag_k_fp8(tb, n0 + r16);
             };
-            // per 16-column block i: read block i+1's weight fragment, issue block
-            // i's MFMAs, then promote block i-1's partials (finished meanwhile)
+            // The N-contiguous path needs more address registers for its transpose
+            // reads, so it promotes each block right after its MFMAs (one partial
+            // set); the K-contiguous path promotes block i-1 after block i's MFMAs.
+            constexpr int PB = B_KN ? 1 : 2;
             v8i xb[2];
-            v4f p[2][MBA];
+            v4f p[PB][MBA];
             xb[0] = fragb(0);
             static_for<0, C::NB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
                 if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
 #pragma unroll
-                for (int j = 0; j < MBA; ++j) p[i & 1][j] = mfma_fp8(xb[i & 1], y[j], v4f{0.f, 0.f, 0.f, 0.f});
-                if constexpr (i > 0) {
-                    constexpr int sb = NSB > 1 ? (i - 1) * 16 / 128 : 0;
+                for (int j = 0; j < MBA; ++j) p[i % PB][j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
+                issue_share<i, C::NB>(lds, next, nslot, nks);
+                constexpr int ip = PB == 1 ? i : i - 1;      // block promoted now
+                if constexpr (ip >= 0) {
+                    constexpr int sb = NSB > 1 ? ip * 16 / 128 : 0;
 #pragma unroll
-                    for (int j = 0; j < MBA; ++j) promote(acc[i - 1][j], p[(i - 1) & 1][j], s[sb][j]);
+                    for (int j = 0; j < MBA; ++j) promote(acc[ip][j], p[ip % PB][j], s[sb][j]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
-            constexpr int sb_last = NSB > 1 ? (C::NB - 1) * 16 / 128 : 0;
+            if constexpr (PB == 2) {
+                constexpr int sb_last = NSB > 1 ? (C::NB - 1) * 16 / 128 : 0;
 #pragma unroll
-            for (int j = 0; j < MBA; ++j) promote(acc[C::NB - 1][j], p[(C::NB - 1) & 1][j], s[sb_last][j]);
+                for (int j = 0; j < MBA; ++j) promote(acc[C::NB - 1][j], p[(C::NB - 1) % PB][j], s[sb_last][j]);
+            }
         } else {
             static_for<0, 2>([&](auto KK) {
                 constexpr int kk = decltype(KK)::value;
+                v4i ya[MBA];
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) ya[j] = frag_k_bf16(ta, wm * C::WTM + j * 16 + r16, kk);
                 auto fragb = [&](int i) -> v4i {
                     const int n0 = wn * C::WTN + i * 16;
                     if constexpr (B_KN) return frag_mn_bf16<C::BN * 2>(tb, n0, kk);
@@ -378,7 +413,8 @@ struct TileGemm {
                     constexpr int i = decltype(I)::value;
                     if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
 #pragma unroll
-                    for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[i & 1], ya[j][kk], acc[i][j]);
+                    for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[i & 1], ya[j], acc[i][j]);
+                    issue_share<kk * C::NB + i, 2 * C::NB>(lds, next, nslot, nks);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             });
@@ -391,57 +427,33 @@ struct TileGemm {
         compiler_fence();
     }
 
-    // Issue order per step (vmcnt counts in order): activations and scales
-    // for the next step, one touch, then the weight slice STAGES-1 steps
-    // ahead.  Steps past the end are clamped to the last one so every wave
-    // issues the same number of operations every step.
+    // Every step issues exactly OPS operations per wave (the step after the
+    // last is clamped to the last one and lands in the free stage), so one
+    // in-order vmcnt wait -- everything but the newest touch -- publishes the
+    // next stage.
     template <int MBA>
     __device__ __forceinline__ void kloop(char* lds, int nks) {
-        constexpr int S = C::STAGES;
-        v4i ya[C::MB][2], yn[C::MB][2];
-        float sa[C::MB] = {}, sn[C::MB] = {};
-        load_b(lds, 0, 0);
-        compiler_fence();
-        load_a(0, ya);
-        load_s(0, sa);
-        compiler_fence();
+        issue_range<0, C::OPS>(lds, 0, 0, nks);
 #pragma unroll
-        for (int s = 1; s < S - 1; ++s) load_b(lds, min(s, nks - 1), s);
-#pragma unroll
-        for (int d = 1; d <= PF_DIST; ++d) touch_a(lds, min(d, nks - 1));
-        compiler_fence();
-        wait_vmcnt<(S - 2) * C::B_OPS + PF_DIST>();   // weight slice 0 and step-0 activations landed
+        for (int d = 1; d < PF_DIST; ++d) touch(lds, min(d, nks - 1));
+        wait_vmcnt<PF_DIST>();
+        barrier();
         float bsc[NSB] = {}, bsc_next[NSB] = {};
         if constexpr (C::FP8) {
 #pragma unroll
             for (int b = 0; b < NSB; ++b) bsc[b] = b_scale[b];
         }
         for (int ks = 0; ks < nks; ++ks) {
-            barrier();        // every wave's slice ks is in LDS; slot (ks-1) % S is free
-            const int kn = min(ks + 1, nks - 1);
+            const int next = min(ks + 1, nks - 1);
             if constexpr (C::FP8) {
 #pragma unroll
-                for (int b = 0; b < NSB; ++b) bsc_next[b] = b_scale[kn * b_scale_stride + b];
+                for (int b = 0; b < NSB; ++b) bsc_next[b] = b_scale[next * b_scale_stride + b];
             }
-            load_a(kn, yn);
-            load_s(kn, sn);
-            compiler_fence();
-            touch_a(lds, min(ks + 1 + PF_DIST, nks - 1));
-            compiler_fence();
-            load_b(lds, min(ks + S - 1, nks - 1), (ks + S - 1) % S);
-            compiler_fence();
-            compute<MBA>(lds + (ks % S) * C::B_BYTES, ya, sa, bsc);
-#pragma unroll
-            for (int j = 0; j < C::MB; ++j) {
-                ya[j][0] = yn[j][0];
-                ya[j][1] = yn[j][1];
-                sa[j] = sn[j];
-            }
+            step<MBA>(lds, ks, next, nks, bsc);
+            wait_vmcnt<1>();      // the next stage landed; only this step's touch may be in flight
+            barrier();
 #pragma unroll
             for (int b = 0; b < NSB; ++b) bsc[b] = bsc_next[b];
-            // next step's weight slice and activations landed (only the touch and
-            // the newest weight slice may still be in flight)
-            wait_vmcnt<1 + C::B_OPS>();
         }
         // no LDS DMA may still be in flight when the wave moves on or exits
         wait_vmcnt<0>();
@@ -462,7 +474,6 @@ struct TileGemm {
         wm = wave / C::WAVES_N;
         wn = wave % C::WAVES_N;
         r16 = lane & 15;
-        g = lane >> 4;
 #pragma unroll
         for (int i = 0; i < C::NB; ++i)
 #pragma unroll
@@ -474,9 +485,10 @@ struct TileGemm {
 
     // bf16 epilogue: rows < rows_valid of the tile; C rows are row_bytes apart.
     __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
+        const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
         for (int j = 0; j < C::MB; ++j) {
-            const int row = arow(j);
+            const int row = wm * C::WTM + j * 16 + r16;
             if (row < rows_valid) {
 #pragma unroll
                 for (int i = 0; i < C::NB; ++i) {
@@ -643,13 +655,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
 // ---------------------------------------------------------------- configs
 
-// Contiguous: 256-column tiles; 8 waves stacked along M, so every activation
-// row is loaded by exactly one wave; 4-deep weight ring.
-template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 8, 1, 4>;
-template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 8, 1, 4>;
-template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 4, 2, 4>;
-// Masked decode: short row tiles, narrow column tiles, deep weight ring (HBM-bound).
-template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 4, 2, 6>;
+// Contiguous: 256-column tiles, every wave tile 64 rows tall.
+template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 4, 2>;
+template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 2, 4>;
+template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 1, 8>;
+// Masked decode: short row tiles, narrow column tiles (HBM-bound).
+template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4>;
 using KGroupedCfg = KCfg<false, 256, 256, 4, 2, 2>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function

@@ -22,34 +22,57 @@
 
 namespace moegg {
 
-constexpr int kSchedThreads = 1024;
-constexpr int kPerThread = kMaxExperts / kSchedThreads;   // 4 experts per thread
-static_assert(kPerThread * kSchedThreads == kMaxExperts, "sched sizing");
+constexpr int kSchedThreads = 256;                          // 4 waves
+constexpr int kWaves = kSchedThreads / 64;
 
 __device__ __forceinline__ int64_t align_up64(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Block-wide exclusive scan of one int64 value per thread (1024 threads).
-// Returns the exclusive prefix and writes the block total to *total.
-__device__ int64_t block_exclusive_scan(int64_t v, int64_t* buf, int64_t* total) {
-    const int t = threadIdx.x;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-        int64_t add = t >= off ? buf[t - off] : 0;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
+// Block-wide exclusive scan of one int64 per thread: wave shuffles, then the
+// four wave totals through LDS.  Two barriers.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t* wave_buf, int64_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
     }
-    int64_t incl = buf[t];
-    *total = buf[kSchedThreads - 1];
+    if (lane == 63) wave_buf[wave] = incl;
     __syncthreads();
-    return incl - v;
+    int64_t base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int64_t x = wave_buf[w];
+        if (w < wave) base += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
 }
 
-__device__ int64_t block_sum(int64_t v, int64_t* buf) {
-    int64_t tot;
-    block_exclusive_scan(v, buf, &tot);
-    return tot;
+// Block-wide sums of NV int64 values per thread, all at once: two barriers.
+template <int NV>
+__device__ void block_sums(int64_t (&v)[NV], int64_t (*wave_buf)[NV]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v[i] += __shfl_xor(v[i], off, 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) wave_buf[wave][i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int64_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += wave_buf[w][i];
+        v[i] = t;
+    }
+    __syncthreads();
 }
 
 // Tile-height cost over the candidates 64, 128, 256.  A launch holds one
@@ -57,12 +80,12 @@ __device__ int64_t block_sum(int64_t v, int64_t* buf) {
 // height in rows plus a fixed per-tile overhead, so
 //     cost(q) = ceil(tiles(q) * n_col_tiles / 256) * (q + 64).
 // Ties go to the larger q, which reuses weights better.
-__device__ int choose_block_m(const int32_t* cand_tiles, int n_col_tiles) {
+__device__ int choose_block_m(const int64_t* cand_tiles, int n_col_tiles) {
     const int qs[kNumCand] = {64, 128, 256};
     int best = 256;
     int64_t best_cost = -1;
     for (int c = kNumCand - 1; c >= 0; --c) {
-        int64_t items = (int64_t)cand_tiles[c] * n_col_tiles;
+        int64_t items = cand_tiles[c] * n_col_tiles;
         int64_t cost = (items + 255) / 256 * (int64_t)(qs[c] + 64);
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = qs[c]; }
     }
@@ -72,133 +95,133 @@ __device__ int choose_block_m(const int32_t* cand_tiles, int n_col_tiles) {
 // mode 0: contiguous layout (segment starts from aligned counts, tile list).
 // mode 1: masked layout (segment starts e * cap, counts clamped to cap,
 //         stats only: the masked kernel reads masked_m itself).
+// Thread t owns a contiguous run of ceil(G / 256) experts, so block scans run
+// in expert order and, up to 256 experts, every per-expert loop runs once.
+// Those loops stay rolled (values go through LDS) to keep the kernel's code
+// small: it runs cold before every GEMM.
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     const int32_t* __restrict__ counts, int G, int64_t rows_total, int seg_align, int cap,
     int mode, int block_m_req, int n_col_tiles, int exec_block_m, unsigned char* __restrict__ ws,
     int64_t max_tiles) {
-    __shared__ int64_t scan_buf[kSchedThreads];
-    __shared__ int64_t seg_off_s[kMaxExperts];
-    __shared__ int32_t m_s[kMaxExperts];
-    __shared__ int32_t chosen_s;
-    __shared__ uint32_t flags_s;
+    constexpr int NV = 3 + MOEGG_NUM_Q + kNumCand;           // U, active, sum_sq, P(q) x6, tiles(q) x3
+    __shared__ int64_t wave_buf[kWaves];
+    __shared__ int64_t sums_buf[kWaves][NV];
+    __shared__ int32_t m_s[kMaxExperts];                     // clamped (then truncated) counts
+    __shared__ int64_t start_s[kMaxExperts];                 // segment starts
+    __shared__ unsigned int flags_s;
+    __shared__ int32_t toff_s[kMaxExperts + 1];             // first tile of each expert
     const int t = threadIdx.x;
+    const int ept = (G + kSchedThreads - 1) / kSchedThreads;  // experts per thread, contiguous
+    const int e0 = min(G, t * ept), e1 = min(G, e0 + ept);
     WsLayout L = ws_layout(G, 0);
     moegg_stats_t* st = (moegg_stats_t*)(ws + L.stats);
     Control* ctl = (Control*)(ws + L.control);
     int64_t* offsets = (int64_t*)(ws + L.offsets);
     moegg_tile_t* tiles = (moegg_tile_t*)(ws + L.tiles);
-
     if (t == 0) flags_s = 0;
-    __syncthreads();
 
     // 1. count intake, clamped; segment sizes in the layout
-    uint32_t flags = 0;
+    unsigned int flags = 0;
     int64_t seg_local = 0;
-    int32_t m_loc[kPerThread];
-    int64_t seg_loc[kPerThread];
-    for (int j = 0; j < kPerThread; ++j) {
-        int e = t * kPerThread + j;
-        int32_t m = 0;
-        if (e < G) {
-            m = counts[e];
-            if (m < 0) { m = 0; flags |= MOEGG_FLAG_NEGATIVE_COUNT; }
-            if (mode == 1 && m > cap) { m = cap; flags |= MOEGG_FLAG_COUNT_OVER_CAP; }
-        }
-        m_loc[j] = m;
-        seg_loc[j] = e < G ? (mode == 1 ? (int64_t)cap : align_up64(m, seg_align)) : 0;
-        seg_local += seg_loc[j];
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        int32_t m = counts[e];
+        if (m < 0) { m = 0; flags |= MOEGG_FLAG_NEGATIVE_COUNT; }
+        if (mode == 1 && m > cap) { m = cap; flags |= MOEGG_FLAG_COUNT_OVER_CAP; }
+        m_s[e] = m;
+        seg_local += mode == 1 ? cap : (m + seg_align - 1) / seg_align * seg_align;
     }
-    // 2. prefix sums of segment sizes -> segment starts
+    // 2. prefix sums of segment sizes -> segment starts; truncate at rows_total
     int64_t seg_total;
-    int64_t base = block_exclusive_scan(seg_local, scan_buf, &seg_total);
-    for (int j = 0; j < kPerThread; ++j) {
-        int e = t * kPerThread + j;
-        if (e < G) {
-            int64_t start = base;
-            // truncate segments that run past the end of the buffer
-            int64_t room = rows_total - start;
-            if (room < 0) room = 0;
-            if ((int64_t)m_loc[j] > room) { m_loc[j] = (int32_t)room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
-            seg_off_s[e] = start;
-            m_s[e] = m_loc[j];
-            offsets[e] = start;
-        }
-        base += seg_loc[j];
+    int64_t base = block_exclusive_scan(seg_local, wave_buf, &seg_total);
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        const int32_t m = m_s[e];
+        const int64_t seg = mode == 1 ? cap : (m + seg_align - 1) / seg_align * seg_align;
+        int64_t room = rows_total - base;
+        if (room < 0) room = 0;
+        if ((int64_t)m > room) { m_s[e] = (int32_t)room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
+        start_s[e] = base;
+        offsets[e] = base;
+        base += seg;
     }
     if (t == 0) offsets[G] = seg_total;
-    if (flags) atomicOr(&flags_s, flags);
-    __syncthreads();
 
-    // 3. exact accounting
-    const int qs_all[MOEGG_NUM_Q] = {8, 16, 32, 64, 128, 256};
-    int64_t u = 0, act = 0, sq = 0, p_at[MOEGG_NUM_Q] = {0, 0, 0, 0, 0, 0};
-    int64_t cand[kNumCand] = {0, 0, 0};
-    for (int j = 0; j < kPerThread; ++j) {
-        int64_t m = m_loc[j];
-        u += m;
-        act += m > 0;
-        sq += m * m;
-        for (int i = 0; i < MOEGG_NUM_Q; ++i) p_at[i] += m > 0 ? align_up64(m, qs_all[i]) : 0;
-        for (int c = 0; c < kNumCand; ++c) cand[c] += (m + (64 << c) - 1) / (64 << c);
+    // 3. exact accounting, one fused block reduction (tile heights are powers of two)
+    int64_t v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = 0;
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        const int64_t m = m_s[e];
+        v[0] += m;
+        v[1] += m > 0;
+        v[2] += m * m;
+#pragma unroll
+        for (int i = 0; i < MOEGG_NUM_Q; ++i) v[3 + i] += ((m + (8 << i) - 1) >> (3 + i)) << (3 + i);
+#pragma unroll
+        for (int c = 0; c < kNumCand; ++c) v[3 + MOEGG_NUM_Q + c] += (m + (64 << c) - 1) >> (6 + c);
     }
-    int64_t U = block_sum(u, scan_buf);
-    int64_t ACT = block_sum(act, scan_buf);
-    int64_t SQ = block_sum(sq, scan_buf);
-    int64_t P[MOEGG_NUM_Q];
-    for (int i = 0; i < MOEGG_NUM_Q; ++i) P[i] = block_sum(p_at[i], scan_buf);
-    int64_t CT[kNumCand];
-    for (int c = 0; c < kNumCand; ++c) CT[c] = block_sum(cand[c], scan_buf);
+    if (flags) atomicOr(&flags_s, flags);
+    block_sums<NV>(v, sums_buf);       // its barriers also publish m_s, start_s and flags_s
 
     // 4. tile height
-    if (t == 0) {
-        int32_t ct32[kNumCand];
-        for (int c = 0; c < kNumCand; ++c) ct32[c] = (int32_t)CT[c];
-        int bm = block_m_req;
-        if (mode == 1) bm = exec_block_m;
-        else if (bm == 0) bm = choose_block_m(ct32, n_col_tiles);
-        chosen_s = bm;
-    }
-    __syncthreads();
-    const int bm = chosen_s;
+    int bm = block_m_req;
+    if (mode == 1) bm = exec_block_m;
+    else if (bm == 0) bm = choose_block_m(&v[3 + MOEGG_NUM_Q], n_col_tiles);
+    const int lg = 31 - __builtin_clz(bm);                  // bm is a power of two
 
-    // 5. tile list (contiguous mode): expert ascending, tile ascending
+    // 5. tile list (contiguous mode): expert ascending, tile ascending.  Each
+    //    expert's first tile index goes to LDS; then every thread writes tiles
+    //    t, t + 256, ... and finds each tile's expert by binary search.
     int64_t my_tiles = 0;
-    for (int j = 0; j < kPerThread; ++j) my_tiles += (m_loc[j] + bm - 1) / bm;
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) my_tiles += (m_s[e] + bm - 1) >> lg;
     int64_t n_tiles;
-    int64_t tbase = block_exclusive_scan(my_tiles, scan_buf, &n_tiles);
+    int64_t tbase = block_exclusive_scan(my_tiles, wave_buf, &n_tiles);
     if (mode == 0) {
-        for (int j = 0; j < kPerThread; ++j) {
-            int e = t * kPerThread + j;
-            int32_t m = m_loc[j];
-            int nt = (m + bm - 1) / bm;
-            for (int i = 0; i < nt && tbase + i < max_tiles; ++i) {
-                moegg_tile_t tl;
-                tl.expert = e;
-                tl.tile = i;
-                tl.row_start = (int32_t)(seg_off_s[e] + (int64_t)i * bm);
-                tl.rows_valid = min(bm, m - i * bm);
-                tiles[tbase + i] = tl;
+#pragma unroll 1
+        for (int e = e0; e < e1; ++e) {
+            toff_s[e] = (int32_t)tbase;
+            tbase += (m_s[e] + bm - 1) >> lg;
+        }
+        if (t == 0) toff_s[G] = (int32_t)n_tiles;
+        __syncthreads();
+        const int nt_all = (int)(n_tiles < max_tiles ? n_tiles : max_tiles);
+#pragma unroll 1
+        for (int T = t; T < nt_all; T += kSchedThreads) {
+            int lo = 0, hi = G - 1;                          // last e with toff_s[e] <= T
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (toff_s[mid] <= T) lo = mid;
+                else hi = mid - 1;
             }
-            tbase += nt;
+            const int i = T - toff_s[lo];
+            moegg_tile_t tl;
+            tl.expert = lo;
+            tl.tile = i;
+            tl.row_start = (int32_t)(start_s[lo] + ((int64_t)i << lg));
+            tl.rows_valid = min(bm, m_s[lo] - (i << lg));
+            tiles[T] = tl;
         }
     }
 
     // 6. stats and control block
     if (t == 0) {
-        int64_t layout_rows = mode == 1 ? (int64_t)G * cap : rows_total;
-        st->U = U;
-        st->P_exec = P[1];   // tiles skip whole 16-row MFMA blocks past their valid rows
+        const int64_t layout_rows = mode == 1 ? (int64_t)G * cap : rows_total;
+        st->U = v[0];
+        st->P_exec = v[3 + 1];   // tiles skip whole 16-row MFMA blocks past their valid rows
         st->tiles = n_tiles;
-        st->active = ACT;
-        st->sum_sq = SQ;
-        st->capacity_rows = layout_rows - U;
-        for (int i = 0; i < MOEGG_NUM_Q; ++i) st->P_at[i] = P[i];
+        st->active = v[1];
+        st->sum_sq = v[2];
+        st->capacity_rows = layout_rows - v[0];
+        for (int i = 0; i < MOEGG_NUM_Q; ++i) st->P_at[i] = v[3 + i];
         st->block_m = bm;
         st->error_flags = flags_s | (n_tiles > max_tiles ? MOEGG_FLAG_ROWS_OVERFLOW : 0u);
         ctl->n_tiles = (int32_t)(n_tiles < max_tiles ? n_tiles : max_tiles);
         ctl->block_m = bm;
         ctl->G = G;
-        for (int c = 0; c < kNumCand; ++c) ctl->cand_tiles[c] = (int32_t)CT[c];
+        for (int c = 0; c < kNumCand; ++c) ctl->cand_tiles[c] = (int32_t)v[3 + MOEGG_NUM_Q + c];
     }
 }
 
@@ -207,9 +230,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
 // expert index).
 __global__ __launch_bounds__(kSchedThreads) void sched_k_grouped_kernel(
     const int32_t* __restrict__ t_sizes, int G, int64_t T, unsigned char* __restrict__ ws) {
-    __shared__ int64_t scan_buf[kSchedThreads];
+    __shared__ int64_t wave_buf[kWaves];
+    __shared__ int64_t sums_buf[kWaves][3];
     __shared__ int32_t m_s[kMaxExperts];
-    __shared__ uint32_t flags_s;
+    __shared__ unsigned int flags_s;
     const int t = threadIdx.x;
     WsLayout L = ws_layout(G, 0);
     moegg_stats_t* st = (moegg_stats_t*)(ws + L.stats);
@@ -217,59 +241,55 @@ __global__ __launch_bounds__(kSchedThreads) void sched_k_grouped_kernel(
     int64_t* offsets = (int64_t*)(ws + L.offsets);
     int32_t* order = (int32_t*)(ws + L.order);
     if (t == 0) flags_s = 0;
-    __syncthreads();
-    uint32_t flags = 0;
-    int32_t m_loc[kPerThread], m_in[kPerThread];
+    unsigned int flags = 0;
+    const int ept = (G + kSchedThreads - 1) / kSchedThreads;
+    const int e0 = min(G, t * ept), e1 = min(G, e0 + ept);
     int64_t local = 0;
-    for (int j = 0; j < kPerThread; ++j) {
-        int e = t * kPerThread + j;
-        int32_t m = e < G ? t_sizes[e] : 0;
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        int32_t m = t_sizes[e];
         if (m < 0) { m = 0; flags |= MOEGG_FLAG_NEGATIVE_COUNT; }
-        m_loc[j] = m_in[j] = m;
+        m_s[e] = m;
         local += m;
     }
     int64_t tot;
-    int64_t base = block_exclusive_scan(local, scan_buf, &tot);
-    int64_t u = 0, act = 0, sq = 0;
-    for (int j = 0; j < kPerThread; ++j) {
-        int e = t * kPerThread + j;
-        if (e < G) {
-            int64_t room = T - base;
-            if (room < 0) room = 0;
-            if ((int64_t)m_loc[j] > room) { m_loc[j] = (int32_t)room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
-            offsets[e] = base;
-            m_s[e] = m_loc[j];
-            u += m_loc[j];
-            act += m_loc[j] > 0;
-            sq += (int64_t)m_loc[j] * m_loc[j];
-        }
-        base += m_in[j];
+    int64_t base = block_exclusive_scan(local, wave_buf, &tot);
+    int64_t v[3] = {0, 0, 0};
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        const int32_t m_in = m_s[e];
+        int32_t m = m_in;
+        int64_t room = T - base;
+        if (room < 0) room = 0;
+        if ((int64_t)m > room) { m = (int32_t)room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
+        offsets[e] = base;
+        m_s[e] = m;
+        v[0] += m;
+        v[1] += m > 0;
+        v[2] += (int64_t)m * m;
+        base += m_in;
     }
-    if (flags) atomicOr(&flags_s, flags);
-    __syncthreads();
-    // offsets[e] holds starts computed from the unclamped-to-T running sum;
-    // truncated segments end at T, so the end offset is min(sum, T).
+    // offsets[e] are the layout's segment starts; segments truncated at T end there
     if (t == 0) offsets[G] = tot < T ? tot : T;
-    int64_t U = block_sum(u, scan_buf);
-    int64_t ACT = block_sum(act, scan_buf);
-    int64_t SQ = block_sum(sq, scan_buf);
+    if (flags) atomicOr(&flags_s, flags);
+    block_sums<3>(v, sums_buf);        // its barriers also publish m_s and flags_s
     // rank = number of experts that come before e in longest-first order
     for (int e = t; e < G; e += kSchedThreads) {
-        int32_t me = m_s[e];
+        const int32_t me = m_s[e];
         int r = 0;
         for (int j = 0; j < G; ++j) {
-            int32_t mj = m_s[j];
+            const int32_t mj = m_s[j];
             r += (mj > me) || (mj == me && j < e);
         }
         order[r] = e;
     }
     if (t == 0) {
-        st->U = U;
-        st->P_exec = U;
+        st->U = v[0];
+        st->P_exec = v[0];
         st->tiles = 0;
-        st->active = ACT;
-        st->sum_sq = SQ;
-        st->capacity_rows = T - U;
+        st->active = v[1];
+        st->sum_sq = v[2];
+        st->capacity_rows = T - v[0];
         for (int i = 0; i < MOEGG_NUM_Q; ++i) st->P_at[i] = 0;
         st->block_m = 0;
         st->error_flags = flags_s;

@@ -203,11 +203,12 @@ def test_contiguous_deterministic_and_empty():
 
 
 @pytest.mark.parametrize("n", [1, 2, 3])
-def test_contiguous_config_full_size(n):
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_contiguous_config_full_size(n, b_layout):
     w = wl.workload(n)
-    announce("contiguous config", n, w.name, "G", w.G, "K", w.K, "N", w.N, "seed", w.seed)
+    announce("contiguous config", n, w.name, "G", w.G, "K", w.K, "N", w.N, "seed", w.seed, "layout", b_layout)
     inp = wl.materialize(w, "cuda")
-    C, ws = P.run_contiguous(w, inp, block_m=0)
+    C, ws = P.run_contiguous(w, inp, block_m=0, b_layout=b_layout)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
     assert st.block_m == choice_rule(w.counts, w.N // 256)
@@ -268,13 +269,15 @@ def test_masked_small(dtype, b_layout):
     check_masked(w, inp, C, counts)
 
 
-def test_masked_config_full_size():
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_masked_config_full_size(b_layout):
     w = wl.workload(4)
-    announce("masked config 4", w.counts)
+    announce("masked config 4", w.counts, "layout", b_layout)
     inp = wl.materialize(w, "cuda")
     C = P.sentinel_like((w.G, w.cap, w.N))
     ws = mg.workspace(w.G, w.G * w.cap)
-    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws)
+    B = inp["B"] if b_layout == mg.B_KN else inp["B"].transpose(1, 2).contiguous()
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, b_layout=b_layout)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
     check_masked(w, inp, C, w.counts)
