@@ -144,6 +144,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB, so that a "
+                         "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
+                         "a transfer of known size")
     ap.add_argument("--b-layout", choices=("kn", "nk"), default="nk",
                     help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE "
                          "weights are usually kept in); repacking is one-time, outside the timed steps")
@@ -240,6 +244,14 @@ def main():
     out["gemm_kernel_ms"] = round(gemm_avg, 4)
     out["algorithmic_bytes"] = bytes_alg
     out["wall_s_timed"] = round(wall, 4)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 18                         # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)                               # one elementwise kernel: reads n*4, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
         out["cpu_baseline"] = cpu_baseline(w, inp)

@@ -55,8 +55,17 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Swizzle of 16-byte chunks in a K-contiguous tile (128-byte rows).
-__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+// Swizzle of 16-byte chunks in a K-contiguous tile (128-byte rows), by element
+// size.  A fragment read has lane (r = l % 16, g = l / 16) fetch chunk 2g + h
+// (e4m3) or 4kk + g (bf16) of row r.  Measured on gfx950 with 8 waves per CU
+// (SQ_LDS_BANK_CONFLICT against SQ_LDS_IDX_ACTIVE): these two swizzles make
+// their reads take 4 LDS cycles per 1 KB (no bank conflicts); exchanging
+// them, or XOR-ing row & 7, costs 8.
+template <int ESZ>
+__device__ __forceinline__ int swz_k(int row) {
+    if constexpr (ESZ == 1) return ((row & 3) << 1) | ((row >> 2) & 1);
+    else return (row >> 1) & 7;
+}
 
 // Swizzle of 16-byte chunks in an MN-contiguous tile, by element size and
 // row bytes, chosen so the 16 lanes of one transpose read hit distinct banks.
@@ -109,7 +118,7 @@ __device__ __forceinline__ void load_k_one(__amdgpu_buffer_rsrc_t rs, uint32_t r
     const int tid = threadIdx.x, wave = tid >> 6;
     const int f = j * C::THREADS + tid;
     const int r = f >> 3, p = f & 7;
-    const int c = p ^ swz_k(r);
+    const int c = p ^ swz_k<C::ESZ>(r);
     load16_to_lds(rs, r * row_bytes + kbyte + c * 16, lds_tile + (j * C::THREADS + wave * 64) * 16);
 }
 
@@ -141,7 +150,7 @@ __device__ __forceinline__ void load_tile_mn(__amdgpu_buffer_rsrc_t rs, uint32_t
 // K-contiguous tile, fp8: lane (row r16, group g) gets bytes [32g, 32g+32).
 __device__ __forceinline__ v8i frag_k_fp8(const char* tile, int row) {
     const int g = (threadIdx.x & 63) >> 4;
-    const int s = swz_k(row);
+    const int s = swz_k<1>(row);
     v4i lo = lds_read_b128(tile + row * 128 + (((2 * g) ^ s) << 4));
     v4i hi = lds_read_b128(tile + row * 128 + (((2 * g + 1) ^ s) << 4));
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -150,7 +159,7 @@ __device__ __forceinline__ v8i frag_k_fp8(const char* tile, int row) {
 // K-contiguous tile, bf16, half-step kk: lane gets k = 32kk + 8g + (0..7).
 __device__ __forceinline__ v4i frag_k_bf16(const char* tile, int row, int kk) {
     const int g = (threadIdx.x & 63) >> 4;
-    return lds_read_b128(tile + row * 128 + (((4 * kk + g) ^ swz_k(row)) << 4));
+    return lds_read_b128(tile + row * 128 + (((4 * kk + g) ^ swz_k<2>(row)) << 4));
 }
 
 // MN-contiguous tile, fp8: lane (col n0 + l%16, group g) gets the 32 bytes
@@ -204,6 +213,21 @@ __device__ __forceinline__ int block_to_item(int b) {
 
 // ---------------------------------------------------------------- contiguous / masked
 
+// L2 touch per step: 0 none, 1 after the stage DMAs, 2 before them.
+#ifndef MOEGG_TOUCH
+#define MOEGG_TOUCH 0
+#endif
+// L2 warming distance (K steps).
+#ifndef MOEGG_PF_DIST
+#define MOEGG_PF_DIST 3
+#endif
+constexpr int PF_DIST = MOEGG_PF_DIST;
+// The next stage's DMAs are issued after the first ISSUE_SPREAD MFMA blocks of a step.
+#ifndef MOEGG_ISSUE_SPREAD
+#define MOEGG_ISSUE_SPREAD 1
+#endif
+constexpr int ISSUE_SPREAD = MOEGG_ISSUE_SPREAD;
+
 // Tile configuration for the contiguous and masked kernels: 512 threads as
 // WAVES_M x WAVES_N waves, each owning a WTM x WTN block of the BM x BN tile.
 // Both operand tiles of a K step (128 bytes of K per row) live in LDS,
@@ -220,23 +244,26 @@ struct GCfg {
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int MB = WTM / 16, NB = WTN / 16;
     static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-    static constexpr int S_BYTES = FP8 ? BM * 4 : 0;   // per-row activation scales of the step
+    // fp8 scales of the step: one per tile row (activations), then 64 slots for
+    // the weight-block scales of this column tile (BN / 128 of them are used)
+    static constexpr int SA_BYTES = FP8 ? BM * 4 : 0;
+    static constexpr int S_BYTES = FP8 ? SA_BYTES + 256 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int SCRATCH_OFF = 2 * STAGE_BYTES;
     static constexpr int LDS_BYTES = SCRATCH_OFF + WAVES * 256;
     static constexpr int A_OPS = A_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
     static constexpr int B_OPS = B_BYTES / 16 / THREADS;
-    static constexpr int OPS = A_OPS + B_OPS + (FP8 ? 1 : 0) + 1;   // + scales + one L2 touch
+    static constexpr int DMA_OPS = A_OPS + B_OPS + (FP8 ? 1 : 0);   // + scales
+    static constexpr int OPS = DMA_OPS + (MOEGG_TOUCH ? 1 : 0);         // + one L2 touch
     static_assert(WAVES == 8, "512-thread tiles");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
-    static_assert(!FP8 || BM >= 64, "one scale DMA per 64 rows");
+    static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// L2 warming distance (K steps).
-constexpr int PF_DIST = 3;
+
 
 __device__ __forceinline__ void touch_line(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* scratch) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)scratch, 4, off, 0, 0, 0);
@@ -262,22 +289,61 @@ struct TileGemm {
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     v4f acc[C::NB][C::MB];
 
-    __amdgpu_buffer_rsrc_t ra, rb, rsa;
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
     uint32_t a_row_bytes, b_row_bytes, b_col_byte, sa_row_bytes;
-    const float* b_scale;      // this wave's first 128-column scale block, step 0
-    int b_scale_stride;        // scale elements between K steps
+    uint32_t sb_col_byte;      // byte offset of this column tile's first weight-scale block in a K row
+    uint32_t sb_row_bytes;     // weight-scale bytes per K step (N / 128 floats)
     int wm, wn, r16;
+    // Per-wave roles, fixed for the whole tile so that a K step has no branches:
+    //   scale DMA:  rss, voffset ss_voff + ks * ss_step, LDS slot ss_dst in the stage;
+    //   L2 touch:   rst, voffset ts_voff + kt * ts_step.
+    __amdgpu_buffer_rsrc_t rss, rst;
+    uint32_t ss_voff, ss_step, ss_dst, ts_voff, ts_step;
+
+    __device__ __forceinline__ void setup_roles() {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+        if constexpr (C::FP8) {
+            // waves below BM/64: one 4-byte activation scale per tile row; the other
+            // waves: the weight-block scales of this column tile (all write the same
+            // values to the same slots).  The weight-scale K row sits in voffset, so
+            // the range check clamps lanes past the expert's scales.
+            const bool act = wave < C::BM / 64;
+            rss = act ? rsa : rsb;
+            ss_voff = act ? (wave * 64 + lane) * sa_row_bytes : sb_col_byte + lane * 4;
+            ss_step = act ? 4u : sb_row_bytes;
+            ss_dst = C::A_BYTES + C::B_BYTES + (act ? wave * 256 : C::SA_BYTES);
+        }
+        // touch: BM and BN are multiples of 64, so each wave touches lines of one operand
+        constexpr int LINES = C::BM + C::BN;               // one 128-byte line per tile row / K row pair
+        static_assert(LINES % 64 == 0, "whole waves per operand");
+        const int wl = (wave * 64) % LINES;
+        const bool act = wl < C::BM;
+        const int l = wl - C::BM + lane;
+        uint32_t off_b, step_b;
+        if constexpr (B_KN) {
+            constexpr int LPR = C::BN * C::ESZ / 128;
+            off_b = (l / LPR) * b_row_bytes + b_col_byte + (l % LPR) * 128;
+            step_b = C::KSTEP * b_row_bytes;
+        } else {
+            off_b = l * b_row_bytes;
+            step_b = 128;
+        }
+        rst = act ? ra : rb;
+        ts_voff = act ? (wl + lane) * a_row_bytes : off_b;
+        ts_step = act ? 128u : step_b;
+    }
 
     // ---- DMA of one stage, as OPS separately issued operations
-    template <int OP>
+    template <int OP_>
     __device__ __forceinline__ void issue_op(char* lds, int ks, int slot, int nks) const {
-        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int tid = threadIdx.x, wave = tid >> 6;
         char* base = lds + slot * C::STAGE_BYTES;
+        constexpr int OP = MOEGG_TOUCH == 2 ? (OP_ == 0 ? C::DMA_OPS : OP_ - 1) : OP_;
         if constexpr (OP < C::A_OPS) {
             // activation rows r0 + 64 OP; swz_k(r0 + 64 j) == swz_k(r0); the row offset stays
             // in voffset (range-checked: rows past rows_valid read as zero)
             const int r = (tid >> 3) + OP * (C::THREADS / 8);
-            load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k(r))) << 4), ks * 128,
+            load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k<C::ESZ>(r))) << 4), ks * 128,
                              base + (OP * C::THREADS + wave * 64) * 16);
         } else if constexpr (OP < C::A_OPS + C::B_OPS) {
             constexpr int j = OP - C::A_OPS;
@@ -290,37 +356,22 @@ struct TileGemm {
                                  (ks * C::KSTEP + j * RPO) * b_row_bytes, dst);
             } else {
                 const int r0 = tid >> 3;
-                load16_to_lds_so(rb, r0 * b_row_bytes + (((tid & 7) ^ swz_k(r0)) << 4),
+                load16_to_lds_so(rb, r0 * b_row_bytes + (((tid & 7) ^ swz_k<C::ESZ>(r0)) << 4),
                                  j * (C::THREADS / 8) * b_row_bytes + ks * 128, dst);
             }
         } else if constexpr (C::FP8 && OP == C::A_OPS + C::B_OPS) {
-            // one 4-byte scale per tile row for K group ks; waves past BM/64 repeat rows
-            const int blk = wave % (C::BM / 64);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsa, (MOEGG_LDS void*)(base + C::A_BYTES + C::B_BYTES + blk * 256), 4,
-                (blk * 64 + lane) * sa_row_bytes, ks * 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(base + ss_dst), 4,
+                                                     ss_voff + ks * ss_step, 0, 0, 0);
         } else {
             touch(lds, min(ks + PF_DIST, nks - 1));
         }
     }
 
-    // L2 touch of step kt: activation rows, then weight lines, 64 per wave
+    // L2 touch of step kt: 64 lines of 128 bytes per wave (activation rows, then
+    // weight lines), through a 4-byte DMA into this wave's scratch LDS slot.
     __device__ __forceinline__ void touch(char* lds, int kt) const {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        constexpr int LINES = C::BM + C::BN;               // one 128-byte line per tile row / K row pair
-        const int line = (wave * 64 + lane) % LINES;
-        char* scratch = lds + C::SCRATCH_OFF + wave * 256;
-        if (line < C::BM) {
-            touch_line(ra, line * a_row_bytes + kt * 128, scratch);
-        } else {
-            const int l = line - C::BM;
-            if constexpr (B_KN) {
-                constexpr int LPR = C::BN * C::ESZ / 128;
-                touch_line(rb, (kt * C::KSTEP + l / LPR) * b_row_bytes + b_col_byte + (l % LPR) * 128, scratch);
-            } else {
-                touch_line(rb, l * b_row_bytes + kt * 128, scratch);
-            }
-        }
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        touch_line(rst, ts_voff + kt * ts_step, lds + C::SCRATCH_OFF + wave * 256);
     }
 
     template <int LO, int HI>
@@ -334,7 +385,8 @@ struct TileGemm {
     // the share of the stage's operations issued after block AT of NBLK
     template <int AT, int NBLK>
     __device__ __forceinline__ void issue_share(char* lds, int ks, int slot, int nks) const {
-        issue_range<AT * C::OPS / NBLK, (AT + 1) * C::OPS / NBLK>(lds, ks, slot, nks);
+        constexpr int SPREAD = ISSUE_SPREAD < NBLK ? ISSUE_SPREAD : NBLK;
+        if constexpr (AT < SPREAD) issue_range<AT * C::OPS / SPREAD, (AT + 1) * C::OPS / SPREAD>(lds, ks, slot, nks);
     }
 
     __device__ __forceinline__ static void promote(v4f& a, const v4f q, float s) {
@@ -347,7 +399,7 @@ struct TileGemm {
     // One K step for a wave with MBA active 16-row blocks, interleaved with the
     // DMA of step `next` (already clamped) into the other stage.
     template <int MBA>
-    __device__ __forceinline__ void step(char* lds, int ks, int next, int nks, const float (&bsc)[NSB]) {
+    __device__ __forceinline__ void step(char* lds, int ks, int next, int nks) {
         const char* ta = lds + (ks & 1) * C::STAGE_BYTES;
         const char* tb = ta + C::A_BYTES;
         const int nslot = (ks + 1) & 1;
@@ -355,6 +407,10 @@ struct TileGemm {
             issue_range<0, C::OPS>(lds, next, nslot, nks);
         } else if constexpr (C::FP8) {
             const float* ts = (const float*)(tb + C::B_BYTES);
+            const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
+            float bsc[NSB];
+#pragma unroll
+            for (int b = 0; b < NSB; ++b) bsc[b] = tsb[b];
             v8i ya[MBA];
             float s[NSB][MBA];
 #pragma unroll
@@ -373,7 +429,7 @@ struct TileGemm {
             // The N-contiguous path needs more address registers for its transpose
             // reads, so it promotes each block right after its MFMAs (one partial
             // set); the K-contiguous path promotes block i-1 after block i's MFMAs.
-            constexpr int PB = B_KN ? 1 : 2;
+            constexpr int PB = 1;
             v8i xb[2];
             v4f p[PB][MBA];
             xb[0] = fragb(0);
@@ -433,27 +489,18 @@ struct TileGemm {
     // next stage.
     template <int MBA>
     __device__ __forceinline__ void kloop(char* lds, int nks) {
-        issue_range<0, C::OPS>(lds, 0, 0, nks);
+        if constexpr (MOEGG_TOUCH) {
 #pragma unroll
-        for (int d = 1; d < PF_DIST; ++d) touch(lds, min(d, nks - 1));
-        wait_vmcnt<PF_DIST>();
-        barrier();
-        float bsc[NSB] = {}, bsc_next[NSB] = {};
-        if constexpr (C::FP8) {
-#pragma unroll
-            for (int b = 0; b < NSB; ++b) bsc[b] = b_scale[b];
+            for (int d = 1; d < PF_DIST; ++d) touch(lds, min(d, nks - 1));
         }
+        issue_range<0, C::OPS>(lds, 0, 0, nks);
+        wait_vmcnt<MOEGG_TOUCH == 1 ? 1 : 0>();
+        barrier();
         for (int ks = 0; ks < nks; ++ks) {
             const int next = min(ks + 1, nks - 1);
-            if constexpr (C::FP8) {
-#pragma unroll
-                for (int b = 0; b < NSB; ++b) bsc_next[b] = b_scale[next * b_scale_stride + b];
-            }
-            step<MBA>(lds, ks, next, nks, bsc);
-            wait_vmcnt<1>();      // the next stage landed; only this step's touch may be in flight
+            step<MBA>(lds, ks, next, nks);
+            wait_vmcnt<MOEGG_TOUCH == 1 ? 1 : 0>();   // the next stage landed (a trailing touch may still fly)
             barrier();
-#pragma unroll
-            for (int b = 0; b < NSB; ++b) bsc[b] = bsc_next[b];
         }
         // no LDS DMA may still be in flight when the wave moves on or exits
         wait_vmcnt<0>();
@@ -478,6 +525,7 @@ struct TileGemm {
         for (int i = 0; i < C::NB; ++i)
 #pragma unroll
             for (int j = 0; j < C::MB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        setup_roles();
         // active 16-row blocks of this wave; wave-uniform, so the loop has no divergence
         const int mba = __builtin_amdgcn_readfirstlane(min(C::MB, max(0, (rows_valid - wm * C::WTM + 15) >> 4)));
         dispatch<C::MB>(lds, mba, nks);
@@ -553,14 +601,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs 
         tg.b_col_byte = 0;
     }
     tg.rsa = tg.rb;
+    tg.rsb = tg.rb;
     tg.sa_row_bytes = (uint32_t)KB * 4;
-    tg.b_scale = nullptr;
-    tg.b_scale_stride = 0;
+    tg.sb_row_bytes = (uint32_t)(p.N / 128) * 4;
+    tg.sb_col_byte = (uint32_t)(n0 / 128) * 4;
     if constexpr (C::FP8) {
         tg.rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
-        const int wn = (threadIdx.x >> 6) % C::WAVES_N;
-        tg.b_scale = p.B_scale + (size_t)e * KB * (p.N / 128) + (n0 + wn * C::WTN) / 128;
-        tg.b_scale_stride = p.N / 128;
+        // this expert's weight scales [K/128, N/128]; slots past the row read as zero
+        tg.rsb = make_rsrc(p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
     }
     tg.run(lds, p.K / C::KSTEP, rows_valid);
     const uint32_t c_row_bytes = (uint32_t)p.N * 2;
