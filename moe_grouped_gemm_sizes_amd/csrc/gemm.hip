@@ -213,25 +213,10 @@ __device__ __forceinline__ int block_to_item(int b) {
 
 // ---------------------------------------------------------------- contiguous / masked
 
-// L2 touch per step: 0 none, 1 after the stage DMAs, 2 before them.
-#ifndef MOEGG_TOUCH
-#define MOEGG_TOUCH 0
-#endif
-// L2 warming distance (K steps).
-#ifndef MOEGG_PF_DIST
-#define MOEGG_PF_DIST 3
-#endif
-constexpr int PF_DIST = MOEGG_PF_DIST;
-// The next stage's DMAs are issued after the first ISSUE_SPREAD MFMA blocks of a step.
-#ifndef MOEGG_ISSUE_SPREAD
-#define MOEGG_ISSUE_SPREAD 1
-#endif
-constexpr int ISSUE_SPREAD = MOEGG_ISSUE_SPREAD;
-
 // Tile configuration for the contiguous and masked kernels: 512 threads as
 // WAVES_M x WAVES_N waves, each owning a WTM x WTN block of the BM x BN tile.
-// Both operand tiles of a K step (128 bytes of K per row) live in LDS,
-// double-buffered.
+// A stage holds one K step (128 bytes of K per row) of both operand tiles and,
+// for fp8, that step's scales: [activations | weights | scales].  Two stages.
 template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
@@ -249,44 +234,38 @@ struct GCfg {
     static constexpr int SA_BYTES = FP8 ? BM * 4 : 0;
     static constexpr int S_BYTES = FP8 ? SA_BYTES + 256 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int SCRATCH_OFF = 2 * STAGE_BYTES;
-    static constexpr int LDS_BYTES = SCRATCH_OFF + WAVES * 256;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
     static constexpr int A_OPS = A_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
     static constexpr int B_OPS = B_BYTES / 16 / THREADS;
-    static constexpr int DMA_OPS = A_OPS + B_OPS + (FP8 ? 1 : 0);   // + scales
-    static constexpr int OPS = DMA_OPS + (MOEGG_TOUCH ? 1 : 0);         // + one L2 touch
+    static constexpr int S_OPS = FP8 ? 1 : 0;             // one 4-byte scale DMA
+    static constexpr int OPS = A_OPS + B_OPS + S_OPS;
     static_assert(WAVES == 8, "512-thread tiles");
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0 && NB % 2 == 0, "wave tile");
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-
-
-__device__ __forceinline__ void touch_line(__amdgpu_buffer_rsrc_t rs, uint32_t off, char* scratch) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)scratch, 4, off, 0, 0, 0);
-}
-
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // One output tile of the contiguous or masked layout.
 //
-// Per K step (128 bytes of K per row) every wave, in one instruction stream:
-//   - reads its activation fragments (4 x 16 rows) and, block by block, its
-//     weight fragments (16 columns at a time) from LDS; ds_read_b64_tr_b8/_b16
-//     transpose N-contiguous weights on the way out;
-//   - issues its MFMAs for block i, then promotes block i-1's fp8 partials
-//     (their MFMAs finished meanwhile);
-//   - after each block's MFMAs, issues one or two of its share of the next
-//     step's DMAs (activation tile, weight tile, per-row scales, one L2
-//     touch PF_DIST steps ahead), so address processing runs under the
-//     matrix cores instead of stalling a wave at the top of the step.
-// One vmcnt wait plus one barrier per step publishes the next stage.
+// Per K step every wave, in one instruction stream, reads its activation
+// fragments (MB x 16 rows) and the step's scales at the start, then walks its
+// NB weight blocks of 16 columns: each block's fragments are read one block
+// ahead, its MFMAs issued, and (fp8) its partials promoted into the fp32
+// accumulators with acc += p * a_scale[row] * b_scale[block].  Right after the
+// first block's MFMAs the wave issues its share of the next step's DMAs into
+// the other stage.  One vmcnt wait plus one barrier per step publishes it.
+// The wave runs at raised priority (s_setprio) from the barrier to the end of
+// its MFMAs, so a SIMD's two waves drain their MFMA work ahead of the barrier.
 template <class C, bool B_KN>
 struct TileGemm {
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
+    static constexpr int HSEG = C::WTN / 2;                        // weight rows per wave column half
+    static_assert(B_KN || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
+                  "weight DMA row mapping");
     v4f acc[C::NB][C::MB];
 
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
@@ -294,11 +273,10 @@ struct TileGemm {
     uint32_t sb_col_byte;      // byte offset of this column tile's first weight-scale block in a K row
     uint32_t sb_row_bytes;     // weight-scale bytes per K step (N / 128 floats)
     int wm, wn, r16;
-    // Per-wave roles, fixed for the whole tile so that a K step has no branches:
-    //   scale DMA:  rss, voffset ss_voff + ks * ss_step, LDS slot ss_dst in the stage;
-    //   L2 touch:   rst, voffset ts_voff + kt * ts_step.
-    __amdgpu_buffer_rsrc_t rss, rst;
-    uint32_t ss_voff, ss_step, ss_dst, ts_voff, ts_step;
+    // scale DMA of this wave, fixed for the whole tile so that a K step has no
+    // branches: resource rss, voffset ss_voff + ks * ss_step, LDS slot ss_dst
+    __amdgpu_buffer_rsrc_t rss;
+    uint32_t ss_voff, ss_step, ss_dst;
 
     __device__ __forceinline__ void setup_roles() {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -313,80 +291,52 @@ struct TileGemm {
             ss_step = act ? 4u : sb_row_bytes;
             ss_dst = C::A_BYTES + C::B_BYTES + (act ? wave * 256 : C::SA_BYTES);
         }
-        // touch: BM and BN are multiples of 64, so each wave touches lines of one operand
-        constexpr int LINES = C::BM + C::BN;               // one 128-byte line per tile row / K row pair
-        static_assert(LINES % 64 == 0, "whole waves per operand");
-        const int wl = (wave * 64) % LINES;
-        const bool act = wl < C::BM;
-        const int l = wl - C::BM + lane;
-        uint32_t off_b, step_b;
-        if constexpr (B_KN) {
-            constexpr int LPR = C::BN * C::ESZ / 128;
-            off_b = (l / LPR) * b_row_bytes + b_col_byte + (l % LPR) * 128;
-            step_b = C::KSTEP * b_row_bytes;
-        } else {
-            off_b = l * b_row_bytes;
-            step_b = 128;
-        }
-        rst = act ? ra : rb;
-        ts_voff = act ? (wl + lane) * a_row_bytes : off_b;
-        ts_step = act ? 128u : step_b;
     }
 
-    // ---- DMA of one stage, as OPS separately issued operations
-    template <int OP_>
-    __device__ __forceinline__ void issue_op(char* lds, int ks, int slot, int nks) const {
+    // ---- the DMAs of one stage
+    // activation rows r0 + 64 J; swz_k(r0 + 64 j) == swz_k(r0); the row offset stays
+    // in voffset (range-checked: rows past rows_valid read as zero)
+    template <int J>
+    __device__ __forceinline__ void issue_a(char* lds, int ks, int slot) const {
         const int tid = threadIdx.x, wave = tid >> 6;
-        char* base = lds + slot * C::STAGE_BYTES;
-        constexpr int OP = MOEGG_TOUCH == 2 ? (OP_ == 0 ? C::DMA_OPS : OP_ - 1) : OP_;
-        if constexpr (OP < C::A_OPS) {
-            // activation rows r0 + 64 OP; swz_k(r0 + 64 j) == swz_k(r0); the row offset stays
-            // in voffset (range-checked: rows past rows_valid read as zero)
-            const int r = (tid >> 3) + OP * (C::THREADS / 8);
-            load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k<C::ESZ>(r))) << 4), ks * 128,
-                             base + (OP * C::THREADS + wave * 64) * 16);
-        } else if constexpr (OP < C::A_OPS + C::B_OPS) {
-            constexpr int j = OP - C::A_OPS;
-            char* dst = base + C::A_BYTES + (j * C::THREADS + wave * 64) * 16;
-            if constexpr (B_KN) {
-                constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
-                const int r0 = tid / CPR;
-                const int c = (tid % CPR) ^ swz_mn<C::ESZ, RB>(r0 + j * RPO);
-                load16_to_lds_so(rb, r0 * b_row_bytes + b_col_byte + c * 16,
-                                 (ks * C::KSTEP + j * RPO) * b_row_bytes, dst);
-            } else {
-                const int r0 = tid >> 3;
-                load16_to_lds_so(rb, r0 * b_row_bytes + (((tid & 7) ^ swz_k<C::ESZ>(r0)) << 4),
-                                 j * (C::THREADS / 8) * b_row_bytes + ks * 128, dst);
-            }
-        } else if constexpr (C::FP8 && OP == C::A_OPS + C::B_OPS) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(base + ss_dst), 4,
-                                                     ss_voff + ks * ss_step, 0, 0, 0);
+        const int r = (tid >> 3) + J * (C::THREADS / 8);
+        load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k<C::ESZ>(r))) << 4), ks * 128,
+                         lds + slot * C::STAGE_BYTES + (J * C::THREADS + wave * 64) * 16);
+    }
+
+    // weight DMA J of step ks.  K-contiguous weights: DMA J covers column half
+    // h = J % 2 of WAVES_N wave columns ((THREADS / 8) / HSEG of them per DMA);
+    // each wave writes 8 consecutive rows.
+    template <int J>
+    __device__ __forceinline__ void issue_w(char* lds, int ks, int slot) const {
+        const int tid = threadIdx.x, wave = tid >> 6;
+        char* base = lds + slot * C::STAGE_BYTES + C::A_BYTES;
+        if constexpr (B_KN) {
+            constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
+            const int r0 = tid / CPR;
+            const int c = (tid % CPR) ^ swz_mn<C::ESZ, RB>(r0 + J * RPO);
+            load16_to_lds_so(rb, r0 * b_row_bytes + b_col_byte + c * 16, (ks * C::KSTEP + J * RPO) * b_row_bytes,
+                             base + (J * C::THREADS + wave * 64) * 16);
         } else {
-            touch(lds, min(ks + PF_DIST, nks - 1));
+            constexpr int h = J & 1, q = J >> 1, SPO = (C::THREADS / 8) / HSEG;
+            auto row_of = [](int lr) { return (q * SPO + lr / HSEG) * C::WTN + h * HSEG + lr % HSEG; };
+            const int row = row_of(tid >> 3);
+            load16_to_lds_so(rb, row * b_row_bytes + (((tid & 7) ^ swz_k<C::ESZ>(row)) << 4), ks * 128,
+                             base + row_of(wave * 8) * 128);
         }
     }
 
-    // L2 touch of step kt: 64 lines of 128 bytes per wave (activation rows, then
-    // weight lines), through a 4-byte DMA into this wave's scratch LDS slot.
-    __device__ __forceinline__ void touch(char* lds, int kt) const {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        touch_line(rst, ts_voff + kt * ts_step, lds + C::SCRATCH_OFF + wave * 256);
+    __device__ __forceinline__ void issue_s(char* lds, int ks, int slot) const {
+        if constexpr (C::FP8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(lds + slot * C::STAGE_BYTES + ss_dst), 4,
+                                                     ss_voff + ks * ss_step, 0, 0, 0);
     }
 
-    template <int LO, int HI>
-    __device__ __forceinline__ void issue_range(char* lds, int ks, int slot, int nks) const {
-        if constexpr (LO < HI) {
-            issue_op<LO>(lds, ks, slot, nks);
-            issue_range<LO + 1, HI>(lds, ks, slot, nks);
-        }
-    }
-
-    // the share of the stage's operations issued after block AT of NBLK
-    template <int AT, int NBLK>
-    __device__ __forceinline__ void issue_share(char* lds, int ks, int slot, int nks) const {
-        constexpr int SPREAD = ISSUE_SPREAD < NBLK ? ISSUE_SPREAD : NBLK;
-        if constexpr (AT < SPREAD) issue_range<AT * C::OPS / SPREAD, (AT + 1) * C::OPS / SPREAD>(lds, ks, slot, nks);
+    // all DMAs of step ks into stage `slot`
+    __device__ __forceinline__ void issue_all(char* lds, int ks, int slot) const {
+        static_for<0, C::A_OPS>([&](auto J) { issue_a<decltype(J)::value>(lds, ks, slot); });
+        static_for<0, C::B_OPS>([&](auto J) { issue_w<decltype(J)::value>(lds, ks, slot); });
+        issue_s(lds, ks, slot);
     }
 
     __device__ __forceinline__ static void promote(v4f& a, const v4f q, float s) {
@@ -396,110 +346,93 @@ struct TileGemm {
         a.w = __builtin_fmaf(q.w, s, a.w);
     }
 
-    // One K step for a wave with MBA active 16-row blocks, interleaved with the
-    // DMA of step `next` (already clamped) into the other stage.
-    template <int MBA>
-    __device__ __forceinline__ void step(char* lds, int ks, int next, int nks) {
-        const char* ta = lds + (ks & 1) * C::STAGE_BYTES;
-        const char* tb = ta + C::A_BYTES;
-        const int nslot = (ks + 1) & 1;
-        if constexpr (MBA == 0) {
-            issue_range<0, C::OPS>(lds, next, nslot, nks);
-        } else if constexpr (C::FP8) {
-            const float* ts = (const float*)(tb + C::B_BYTES);
-            const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
-            float bsc[NSB];
-#pragma unroll
-            for (int b = 0; b < NSB; ++b) bsc[b] = tsb[b];
-            v8i ya[MBA];
-            float s[NSB][MBA];
-#pragma unroll
-            for (int j = 0; j < MBA; ++j) {
-                const int row = wm * C::WTM + j * 16 + r16;
-                ya[j] = frag_k_fp8(ta, row);
-                const float as = ts[row];
-#pragma unroll
-                for (int b = 0; b < NSB; ++b) s[b][j] = as * bsc[b];
-            }
-            auto fragb = [&](int i) -> v8i {
-                const int n0 = wn * C::WTN + i * 16;
-                if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
-                else return frag_k_fp8(tb, n0 + r16);
-            };
-            // The N-contiguous path needs more address registers for its transpose
-            // reads, so it promotes each block right after its MFMAs (one partial
-            // set); the K-contiguous path promotes block i-1 after block i's MFMAs.
-            constexpr int PB = 1;
-            v8i xb[2];
-            v4f p[PB][MBA];
-            xb[0] = fragb(0);
-            static_for<0, C::NB>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
-#pragma unroll
-                for (int j = 0; j < MBA; ++j) p[i % PB][j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
-                issue_share<i, C::NB>(lds, next, nslot, nks);
-                constexpr int ip = PB == 1 ? i : i - 1;      // block promoted now
-                if constexpr (ip >= 0) {
-                    constexpr int sb = NSB > 1 ? ip * 16 / 128 : 0;
-#pragma unroll
-                    for (int j = 0; j < MBA; ++j) promote(acc[ip][j], p[ip % PB][j], s[sb][j]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            if constexpr (PB == 2) {
-                constexpr int sb_last = NSB > 1 ? (C::NB - 1) * 16 / 128 : 0;
-#pragma unroll
-                for (int j = 0; j < MBA; ++j) promote(acc[C::NB - 1][j], p[(C::NB - 1) % PB][j], s[sb_last][j]);
-            }
-        } else {
-            static_for<0, 2>([&](auto KK) {
-                constexpr int kk = decltype(KK)::value;
-                v4i ya[MBA];
-#pragma unroll
-                for (int j = 0; j < MBA; ++j) ya[j] = frag_k_bf16(ta, wm * C::WTM + j * 16 + r16, kk);
-                auto fragb = [&](int i) -> v4i {
-                    const int n0 = wn * C::WTN + i * 16;
-                    if constexpr (B_KN) return frag_mn_bf16<C::BN * 2>(tb, n0, kk);
-                    else return frag_k_bf16(tb, n0 + r16, kk);
-                };
-                v4i xb[2];
-                xb[0] = fragb(0);
-                static_for<0, C::NB>([&](auto I) {
-                    constexpr int i = decltype(I)::value;
-                    if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
-#pragma unroll
-                    for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[i & 1], ya[j], acc[i][j]);
-                    issue_share<kk * C::NB + i, 2 * C::NB>(lds, next, nslot, nks);
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-            });
-        }
-    }
-
     __device__ __forceinline__ static void barrier() {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         compiler_fence();
     }
 
-    // Every step issues exactly OPS operations per wave (the step after the
-    // last is clamped to the last one and lands in the free stage), so one
-    // in-order vmcnt wait -- everything but the newest touch -- publishes the
-    // next stage.
+    // One K step for a wave with MBA active 16-row blocks.
+    template <int MBA>
+    __device__ __forceinline__ void step(char* lds, int ks, int next) {
+        const char* ta = lds + (ks & 1) * C::STAGE_BYTES;
+        const char* tb = ta + C::A_BYTES;
+        if constexpr (MBA == 0) {
+            issue_all(lds, next, (ks + 1) & 1);
+        } else if constexpr (C::FP8) {
+            const float* ts = (const float*)(tb + C::B_BYTES);
+            const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
+            auto fragb = [&](int i) -> v8i {
+                const int n0 = wn * C::WTN + i * 16;
+                if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
+                else return frag_k_fp8(tb, n0 + r16);
+            };
+            // LDS reads in the order the first MFMAs consume them: weight block 0,
+            // activation blocks, then the scales
+            v8i xb[2];
+            xb[0] = fragb(0);
+            v8i ya[MBA];
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) ya[j] = frag_k_fp8(ta, wm * C::WTM + j * 16 + r16);
+            float bsc[NSB], s[NSB][MBA];
+#pragma unroll
+            for (int b = 0; b < NSB; ++b) bsc[b] = tsb[b];
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) {
+                const float as = ts[wm * C::WTM + j * 16 + r16];
+#pragma unroll
+                for (int b = 0; b < NSB; ++b) s[b][j] = as * bsc[b];
+            }
+            v4f p[MBA];
+            static_for<0, C::NB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) p[j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
+                if constexpr (i == 0) issue_all(lds, next, (ks + 1) & 1);
+                constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) promote(acc[i][j], p[j], s[sb][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else {
+            // both K halves of the step's activation fragments first, then the weight
+            // blocks column half by column half
+            v4i ya[2][MBA];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) ya[kk][j] = frag_k_bf16(ta, wm * C::WTM + j * 16 + r16, kk);
+            auto fragb = [&](int i, int kk) -> v4i {
+                const int n0 = wn * C::WTN + i * 16;
+                if constexpr (B_KN) return frag_mn_bf16<C::BN * 2>(tb, n0, kk);
+                else return frag_k_bf16(tb, n0 + r16, kk);
+            };
+            v4i xb[2];
+            xb[0] = fragb(0, 0);
+            static_for<0, 2 * C::NB>([&](auto U) {
+                constexpr int u = decltype(U)::value, i = u >> 1, kk = u & 1;
+                if constexpr (u + 1 < 2 * C::NB) xb[(u + 1) & 1] = fragb((u + 1) >> 1, (u + 1) & 1);
+#pragma unroll
+                for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[u & 1], ya[kk][j], acc[i][j]);
+                if constexpr (u == 0) issue_all(lds, next, (ks + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    }
+
+    // Every step issues exactly OPS DMAs per wave (the step after the last is
+    // clamped to the last one and lands in the free stage).
     template <int MBA>
     __device__ __forceinline__ void kloop(char* lds, int nks) {
-        if constexpr (MOEGG_TOUCH) {
-#pragma unroll
-            for (int d = 1; d < PF_DIST; ++d) touch(lds, min(d, nks - 1));
-        }
-        issue_range<0, C::OPS>(lds, 0, 0, nks);
-        wait_vmcnt<MOEGG_TOUCH == 1 ? 1 : 0>();
+        issue_all(lds, 0, 0);
+        wait_vmcnt<0>();
         barrier();
         for (int ks = 0; ks < nks; ++ks) {
-            const int next = min(ks + 1, nks - 1);
-            step<MBA>(lds, ks, next, nks);
-            wait_vmcnt<MOEGG_TOUCH == 1 ? 1 : 0>();   // the next stage landed (a trailing touch may still fly)
+            __builtin_amdgcn_s_setprio(1);
+            step<MBA>(lds, ks, min(ks + 1, nks - 1));
+            __builtin_amdgcn_s_setprio(0);
+            wait_vmcnt<0>();      // this wave's DMAs of the next stage landed
             barrier();
         }
         // no LDS DMA may still be in flight when the wave moves on or exits

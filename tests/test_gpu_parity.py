@@ -227,6 +227,33 @@ def test_contiguous_config_full_size(n, b_layout):
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+@pytest.mark.parametrize("block_m", [64, 128, 256])
+def test_contiguous_every_tile_height_long_k(dtype, b_layout, block_m):
+    """Every tile height and weight layout over a long reduction (56 to 112 K
+    steps), where each stage of the load ring is reused many times.  A read that
+    runs ahead of the barrier publishing its part of a stage shows up here as
+    sporadic wrong blocks.  Issue histogram, aligned segments, N = 1024."""
+    w = wl.Workload("long K", "contiguous", dtype, wl.hist_issue_32(), K=7168, N=1024, seg_align=128,
+                    values="normal", seed=2)
+    announce("long K", dtype, "layout", b_layout, "block_m", block_m)
+    inp = wl.materialize(w, "cuda")
+    C, ws = P.run_contiguous(w, inp, block_m=block_m, b_layout=b_layout)
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, block_m, extra=16, seed=1)
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    del inp
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    # no element may be off by more than a few bf16 ulps of the row scale
+    worst = float(np.max(np.abs(got - ref) / (np.abs(ref).max(axis=1, keepdims=True) + 1e-30)))
+    print(f"long K {dtype} layout={b_layout} block_m={block_m}: rel_frobenius={err:.3e} worst={worst:.3e}", flush=True)
+    assert err <= P.TOL[dtype], err
+    assert worst <= 0.05, worst
+
+
 # ----------------------------------------------------------------- masked
 
 
