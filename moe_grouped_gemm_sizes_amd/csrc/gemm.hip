@@ -216,7 +216,9 @@ __device__ __forceinline__ int block_to_item(int b) {
 // Tile configuration for the contiguous and masked kernels: 512 threads as
 // WAVES_M x WAVES_N waves, each owning a WTM x WTN block of the BM x BN tile.
 // A stage holds one K step (128 bytes of K per row) of both operand tiles and,
-// for fp8, that step's scales: [activations | weights | scales].  Two stages.
+// for fp8, that step's scales: [activations | weights | scales].  The ring has
+// as many stages as fit in the 160 KB of LDS, up to four: loads run
+// STAGES - 1 steps ahead of the MFMAs.
 template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
@@ -234,7 +236,8 @@ struct GCfg {
     static constexpr int SA_BYTES = FP8 ? BM * 4 : 0;
     static constexpr int S_BYTES = FP8 ? SA_BYTES + 256 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int STAGES = (160 * 1024) / STAGE_BYTES < 4 ? (160 * 1024) / STAGE_BYTES : 4;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int A_OPS = A_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
     static constexpr int B_OPS = B_BYTES / 16 / THREADS;
     static constexpr int S_OPS = FP8 ? 1 : 0;             // one 4-byte scale DMA
@@ -244,7 +247,7 @@ struct GCfg {
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -256,8 +259,9 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // NB weight blocks of 16 columns: each block's fragments are read one block
 // ahead, its MFMAs issued, and (fp8) its partials promoted into the fp32
 // accumulators with acc += p * a_scale[row] * b_scale[block].  Right after the
-// first block's MFMAs the wave issues its share of the next step's DMAs into
-// the other stage.  One vmcnt wait plus one barrier per step publishes it.
+// first block's MFMAs the wave issues its share of the DMAs of step
+// ks + STAGES - 1 into the stage step ks - 1 used.  One vmcnt wait plus one
+// barrier per step publishes the stage of step ks + 1.
 // The wave runs at raised priority (s_setprio) from the barrier to the end of
 // its MFMAs, so a SIMD's two waves drain their MFMA work ahead of the barrier.
 template <class C, bool B_KN>
@@ -353,12 +357,13 @@ struct TileGemm {
     }
 
     // One K step for a wave with MBA active 16-row blocks.
+    // One K step: reads stage `cur`, issues the DMAs of step `next` into stage `free`.
     template <int MBA>
-    __device__ __forceinline__ void step(char* lds, int ks, int next) {
-        const char* ta = lds + (ks & 1) * C::STAGE_BYTES;
+    __device__ __forceinline__ void step(char* lds, int cur, int next, int free) {
+        const char* ta = lds + cur * C::STAGE_BYTES;
         const char* tb = ta + C::A_BYTES;
         if constexpr (MBA == 0) {
-            issue_all(lds, next, (ks + 1) & 1);
+            issue_all(lds, next, free);
         } else if constexpr (C::FP8) {
             const float* ts = (const float*)(tb + C::B_BYTES);
             const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
@@ -389,7 +394,7 @@ struct TileGemm {
                 if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) p[j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
-                if constexpr (i == 0) issue_all(lds, next, (ks + 1) & 1);
+                if constexpr (i == 0) issue_all(lds, next, free);
                 constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) promote(acc[i][j], p[j], s[sb][j]);
@@ -415,25 +420,32 @@ struct TileGemm {
                 if constexpr (u + 1 < 2 * C::NB) xb[(u + 1) & 1] = fragb((u + 1) >> 1, (u + 1) & 1);
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[u & 1], ya[kk][j], acc[i][j]);
-                if constexpr (u == 0) issue_all(lds, next, (ks + 1) & 1);
+                if constexpr (u == 0) issue_all(lds, next, free);
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
     }
 
-    // Every step issues exactly OPS DMAs per wave (the step after the last is
-    // clamped to the last one and lands in the free stage).
+    // Every step issues exactly OPS DMAs per wave (steps past the last are
+    // clamped to the last one and land in a free stage), so an in-order vmcnt
+    // wait with a fixed allowance -- the STAGES - 2 newest batches -- publishes
+    // the stage of the next step.
     template <int MBA>
     __device__ __forceinline__ void kloop(char* lds, int nks) {
-        issue_all(lds, 0, 0);
-        wait_vmcnt<0>();
+        constexpr int S = C::STAGES;
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s) issue_all(lds, min(s, nks - 1), s);
+        wait_vmcnt<(S - 2) * C::OPS>();
         barrier();
+        int cur = 0, free = S - 1;
         for (int ks = 0; ks < nks; ++ks) {
             __builtin_amdgcn_s_setprio(1);
-            step<MBA>(lds, ks, min(ks + 1, nks - 1));
+            step<MBA>(lds, cur, min(ks + S - 1, nks - 1), free);
             __builtin_amdgcn_s_setprio(0);
-            wait_vmcnt<0>();      // this wave's DMAs of the next stage landed
+            wait_vmcnt<(S - 2) * C::OPS>();   // this wave's DMAs of step ks + 1 landed
             barrier();
+            free = cur;
+            cur = cur + 1 == S ? 0 : cur + 1;
         }
         // no LDS DMA may still be in flight when the wave moves on or exits
         wait_vmcnt<0>();
