@@ -79,11 +79,13 @@ __device__ __forceinline__ int swz_mn(int k) {
     return 0;
 }
 
-template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// Tile configuration of the K-grouped weight gradient (bf16 operands, both
+// M/N-contiguous): 512 threads as WAVES_M x WAVES_N waves over a BM x BN tile
+// of dW; a stage holds KSTEP rows of the reduction axis of both operands.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct KCfg {
-    static constexpr bool FP8 = FP8_;
-    static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
-    static constexpr int KSTEP = 128 / ESZ;            // K elements per stage
+    static constexpr int ESZ = 2;
+    static constexpr int KSTEP = 64;                   // reduction rows per stage (128 bytes of bf16 K)
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
@@ -91,36 +93,20 @@ struct KCfg {
     static constexpr int STAGES = STAGES_;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
     static constexpr int MB = WTM / 16, NB = WTN / 16;             // 16x16 blocks per wave
-    static constexpr int A_BYTES = BM * 128;
-    static constexpr int B_BYTES = BN * 128;
-    static constexpr int S_BYTES = FP8 ? BM * 4 : 0;               // per-row A scales
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int A_BYTES = BM * KSTEP * ESZ;
+    static constexpr int B_BYTES = BN * KSTEP * ESZ;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 16 / THREADS;         // 16-byte DMA per thread per stage
+    static constexpr int A_LOADS = A_BYTES / 16 / THREADS;         // 16-byte DMAs per thread per stage
     static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
-    static constexpr int S_LOADS = FP8 ? 1 : 0;                    // one 4-byte DMA per wave per stage
-    static constexpr int VM_PER_STAGE = A_LOADS + B_LOADS + S_LOADS;
+    static constexpr int OPS = A_LOADS + B_LOADS;
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(!FP8 || WTN <= 128, "one fp8 weight scale block per wave tile");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(VM_PER_STAGE * (STAGES - 1) < 64, "vmcnt range");
+    static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(OPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
 // ---------------------------------------------------------------- stage loads
-
-// One 16-byte-per-lane DMA (the j-th of a stage) of a K-contiguous tile:
-// rows of 128 bytes from a buffer whose row r starts at r * row_bytes, K-step
-// byte offset kbyte.  Flat chunk f = j * THREADS + tid lands at LDS byte 16 f.
-template <class C>
-__device__ __forceinline__ void load_k_one(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t kbyte,
-                                           char* lds_tile, int j) {
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int f = j * C::THREADS + tid;
-    const int r = f >> 3, p = f & 7;
-    const int c = p ^ swz_k<C::ESZ>(r);
-    load16_to_lds(rs, r * row_bytes + kbyte + c * 16, lds_tile + (j * C::THREADS + wave * 64) * 16);
-}
 
 // One DMA of an MN-contiguous tile: KSTEP rows (one per K index) of RB bytes,
 // from a buffer whose K row k starts at k * row_bytes, column byte cbyte.
@@ -301,20 +287,20 @@ struct TileGemm {
     // activation rows r0 + 64 J; swz_k(r0 + 64 j) == swz_k(r0); the row offset stays
     // in voffset (range-checked: rows past rows_valid read as zero)
     template <int J>
-    __device__ __forceinline__ void issue_a(char* lds, int ks, int slot) const {
+    __device__ __forceinline__ void issue_a(char* __restrict__ stage, int ks) const {
         const int tid = threadIdx.x, wave = tid >> 6;
         const int r = (tid >> 3) + J * (C::THREADS / 8);
         load16_to_lds_so(ra, r * a_row_bytes + ((((tid & 7) ^ swz_k<C::ESZ>(r))) << 4), ks * 128,
-                         lds + slot * C::STAGE_BYTES + (J * C::THREADS + wave * 64) * 16);
+                         stage + (J * C::THREADS + wave * 64) * 16);
     }
 
     // weight DMA J of step ks.  K-contiguous weights: DMA J covers column half
     // h = J % 2 of WAVES_N wave columns ((THREADS / 8) / HSEG of them per DMA);
     // each wave writes 8 consecutive rows.
     template <int J>
-    __device__ __forceinline__ void issue_w(char* lds, int ks, int slot) const {
+    __device__ __forceinline__ void issue_w(char* __restrict__ stage, int ks) const {
         const int tid = threadIdx.x, wave = tid >> 6;
-        char* base = lds + slot * C::STAGE_BYTES + C::A_BYTES;
+        char* base = stage + C::A_BYTES;
         if constexpr (B_KN) {
             constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
             const int r0 = tid / CPR;
@@ -330,17 +316,17 @@ struct TileGemm {
         }
     }
 
-    __device__ __forceinline__ void issue_s(char* lds, int ks, int slot) const {
+    __device__ __forceinline__ void issue_s(char* __restrict__ stage, int ks) const {
         if constexpr (C::FP8)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(lds + slot * C::STAGE_BYTES + ss_dst), 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(stage + ss_dst), 4,
                                                      ss_voff + ks * ss_step, 0, 0, 0);
     }
 
-    // all DMAs of step ks into stage `slot`
-    __device__ __forceinline__ void issue_all(char* lds, int ks, int slot) const {
-        static_for<0, C::A_OPS>([&](auto J) { issue_a<decltype(J)::value>(lds, ks, slot); });
-        static_for<0, C::B_OPS>([&](auto J) { issue_w<decltype(J)::value>(lds, ks, slot); });
-        issue_s(lds, ks, slot);
+    // all DMAs of step ks into `stage`
+    __device__ __forceinline__ void issue_all(char* __restrict__ stage, int ks) const {
+        static_for<0, C::A_OPS>([&](auto J) { issue_a<decltype(J)::value>(stage, ks); });
+        static_for<0, C::B_OPS>([&](auto J) { issue_w<decltype(J)::value>(stage, ks); });
+        issue_s(stage, ks);
     }
 
     __device__ __forceinline__ static void promote(v4f& a, const v4f q, float s) {
@@ -357,13 +343,14 @@ struct TileGemm {
     }
 
     // One K step for a wave with MBA active 16-row blocks.
-    // One K step: reads stage `cur`, issues the DMAs of step `next` into stage `free`.
+    // One K step: reads stage `ta`, issues the DMAs of step `next` into stage `wr`.
+    // The two are different stages; saying so (__restrict__) lets the compiler
+    // see that the transpose reads do not depend on the DMAs in flight.
     template <int MBA>
-    __device__ __forceinline__ void step(char* lds, int cur, int next, int free) {
-        const char* ta = lds + cur * C::STAGE_BYTES;
+    __device__ __forceinline__ void step(const char* __restrict__ ta, char* __restrict__ wr, int next) {
         const char* tb = ta + C::A_BYTES;
         if constexpr (MBA == 0) {
-            issue_all(lds, next, free);
+            issue_all(wr, next);
         } else if constexpr (C::FP8) {
             const float* ts = (const float*)(tb + C::B_BYTES);
             const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
@@ -394,7 +381,7 @@ struct TileGemm {
                 if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) p[j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
-                if constexpr (i == 0) issue_all(lds, next, free);
+                if constexpr (i == 0) issue_all(wr, next);
                 constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) promote(acc[i][j], p[j], s[sb][j]);
@@ -420,7 +407,7 @@ struct TileGemm {
                 if constexpr (u + 1 < 2 * C::NB) xb[(u + 1) & 1] = fragb((u + 1) >> 1, (u + 1) & 1);
 #pragma unroll
                 for (int j = 0; j < MBA; ++j) acc[i][j] = mfma_bf16(xb[u & 1], ya[kk][j], acc[i][j]);
-                if constexpr (u == 0) issue_all(lds, next, free);
+                if constexpr (u == 0) issue_all(wr, next);
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
@@ -434,13 +421,13 @@ struct TileGemm {
     __device__ __forceinline__ void kloop(char* lds, int nks) {
         constexpr int S = C::STAGES;
 #pragma unroll
-        for (int s = 0; s < S - 1; ++s) issue_all(lds, min(s, nks - 1), s);
+        for (int s = 0; s < S - 1; ++s) issue_all(lds + s * C::STAGE_BYTES, min(s, nks - 1));
         wait_vmcnt<(S - 2) * C::OPS>();
         barrier();
         int cur = 0, free = S - 1;
         for (int ks = 0; ks < nks; ++ks) {
             __builtin_amdgcn_s_setprio(1);
-            step<MBA>(lds, cur, min(ks + S - 1, nks - 1), free);
+            step<MBA>(lds + cur * C::STAGE_BYTES, lds + free * C::STAGE_BYTES, min(ks + S - 1, nks - 1));
             __builtin_amdgcn_s_setprio(0);
             wait_vmcnt<(S - 2) * C::OPS>();   // this wave's DMAs of step ks + 1 landed
             barrier();
@@ -570,7 +557,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs 
 // lane holds 4 consecutive j), the X tile the MFMA B operand.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p) {
-    static_assert(!C::FP8, "bf16 only");
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const WsLayout L = ws_layout(p.G, 0);
     const int64_t* offs = (const int64_t*)(p.ws + L.offsets);
@@ -599,38 +585,55 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    auto issue = [&](int ks, int slot) {
-        char* base = lds + slot * C::STAGE_BYTES;
+    auto issue = [&](int ks, char* __restrict__ base) {
         load_tile_mn<C, C::BM * 2>(rx, x_row, ks * C::KSTEP, i0 * 2, base, C::A_LOADS);
         load_tile_mn<C, C::BN * 2>(ry, y_row, ks * C::KSTEP, j0 * 2, base + C::A_BYTES, C::B_LOADS);
     };
+    // Same pipeline as the contiguous kernel: loads run STAGES - 1 steps ahead,
+    // the DMAs of a step are issued after the first MFMA block of the step
+    // STAGES - 1 earlier, one vmcnt wait and one barrier per step.  An expert
+    // with no rows runs no steps and writes zeros.
+    if (nks > 0) {
+        constexpr int S = C::STAGES;
 #pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s)
-        if (s < nks) issue(s, s);
-    for (int ks = 0; ks < nks; ++ks) {
-        const int slot = ks % C::STAGES;
-        if (ks + C::STAGES - 1 < nks) {
-            issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
-            wait_vmcnt<C::VM_PER_STAGE * (C::STAGES - 1)>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        for (int s = 0; s < S - 1; ++s) issue(min(s, nks - 1), lds + s * C::STAGE_BYTES);
+        wait_vmcnt<(S - 2) * C::OPS>();
         __syncthreads();
-        const char* tx = lds + slot * C::STAGE_BYTES;
-        const char* ty = tx + C::A_BYTES;
+        int cur = 0, free = S - 1;
+        // the read stage and the DMA stage of a step differ (see TileGemm::step)
+        auto step = [&](const char* __restrict__ tx, char* __restrict__ wr, int next) {
+            const char* ty = tx + C::A_BYTES;
+            // both K halves of this wave's X fragments, then the dY blocks one
+            // ahead of their MFMAs
+            v4i xa[2][C::MB];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            v4i xa[C::MB];
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int j = 0; j < C::MB; ++j) xa[j] = frag_mn_bf16<C::BM * 2>(tx, wm * C::WTM + j * 16, kk);
+                for (int j = 0; j < C::MB; ++j) xa[kk][j] = frag_mn_bf16<C::BM * 2>(tx, wm * C::WTM + j * 16, kk);
+            auto fragy = [&](int i, int kk) { return frag_mn_bf16<C::BN * 2>(ty, wn * C::WTN + i * 16, kk); };
+            v4i yb[2];
+            yb[0] = fragy(0, 0);
+            static_for<0, 2 * C::NB>([&](auto U) {
+                constexpr int u = decltype(U)::value, i = u >> 1, kk = u & 1;
+                if constexpr (u + 1 < 2 * C::NB) yb[(u + 1) & 1] = fragy((u + 1) >> 1, (u + 1) & 1);
 #pragma unroll
-            for (int i = 0; i < C::NB; ++i) {
-                v4i yb = frag_mn_bf16<C::BN * 2>(ty, wn * C::WTN + i * 16, kk);
-#pragma unroll
-                for (int j = 0; j < C::MB; ++j) acc[i][j] = mfma_bf16(yb, xa[j], acc[i][j]);
-            }
+                for (int j = 0; j < C::MB; ++j) acc[i][j] = mfma_bf16(yb[u & 1], xa[kk][j], acc[i][j]);
+                if constexpr (u == 0) issue(next, wr);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int ks = 0; ks < nks; ++ks) {
+            __builtin_amdgcn_s_setprio(1);
+            step(lds + cur * C::STAGE_BYTES, lds + free * C::STAGE_BYTES, min(ks + S - 1, nks - 1));
+            __builtin_amdgcn_s_setprio(0);
+            wait_vmcnt<(S - 2) * C::OPS>();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
+            free = cur;
+            cur = cur + 1 == S ? 0 : cur + 1;
         }
-        __syncthreads();
+        wait_vmcnt<0>();
     }
     // fp32 epilogue: lane holds dW[i][j..j+3]
     const int r16 = lane & 15, g = lane >> 4;
@@ -654,7 +657,7 @@ template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 2, 4>;
 template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 1, 8>;
 // Masked decode: short row tiles, narrow column tiles (HBM-bound).
 template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4>;
-using KGroupedCfg = KCfg<false, 256, 256, 4, 2, 2>;
+using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
 // attribute, not a stream operation).
