@@ -42,7 +42,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int):
+def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_block_m: int = 0):
     """Returns (scheduler, gemm, workspace) closures for one workload."""
     dev = "cuda"
     if w.layout == "contiguous":
@@ -50,7 +50,7 @@ def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int):
         ws = mg.workspace(w.G, w.rows_total)
 
         def sched():
-            mg.schedule(inp["counts"], w.rows_total, ws, seg_align=w.seg_align, block_m=0, N=w.N)
+            mg.schedule(inp["counts"], w.rows_total, ws, seg_align=w.seg_align, block_m=sched_block_m, N=w.N)
 
         def gemm():
             mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"),
@@ -148,6 +148,9 @@ def main():
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
                          "a transfer of known size")
+    ap.add_argument("--block-m", default="auto", choices=("auto", "per-expert", "64", "128", "256"),
+                    help="tile height: auto = one height chosen on the device from the histogram; per-expert = "
+                         "256-row tiles plus a remainder tile per expert sized 64/128/256")
     ap.add_argument("--b-layout", choices=("kn", "nk"), default="nk",
                     help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE "
                          "weights are usually kept in); repacking is one-time, outside the timed steps")
@@ -169,12 +172,14 @@ def main():
     torch.cuda.synchronize()
 
     # first pass: learn the device's tile-height choice (outside timing)
-    sched, gemm, ws = build_step(w, inp, 0, b_layout)
+    bm_req = {"auto": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] if not args.block_m.isdigit() \
+        else int(args.block_m)
+    sched, gemm, ws = build_step(w, inp, 0, b_layout, bm_req)
     if sched is not None:
         sched()
         torch.cuda.synchronize()
         st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp, st0.block_m, b_layout)
+        sched, gemm, ws = build_step(w, inp, st0.block_m, b_layout, bm_req)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -225,8 +230,10 @@ def main():
     }
     if w.layout == "contiguous":
         phys = 2.0 * st.P_exec * w.K * w.N / (ms_step * 1e-3) / 1e12
-        out.update({"physical_tflops": round(phys, 2), "block_m": st.block_m, "P_exec": st.P_exec,
-                    "padding_fraction_at_block_m": float(st.padding_fraction(st.block_m)),
+        bm_q = 256 if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m
+        out.update({"physical_tflops": round(phys, 2),
+                    "block_m": "per-expert" if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m,
+                    "P_exec": st.P_exec, "padding_fraction_at_block_m": float(st.padding_fraction(bm_q)),
                     "effective_experts": round(float(st.effective_experts), 3)})
     # roofline of the dominant kernel (the GEMM), from HIP events on its own stream
     achieved_tflops = flops / (gemm_avg * 1e-3) / 1e12

@@ -55,6 +55,15 @@ typedef enum { MOEGG_B_KN = 0, MOEGG_B_NK = 1 } moegg_b_layout_t;
 #define MOEGG_FLAG_ROWS_OVERFLOW   0x2u  /* segments ran past rows_total / T; truncated */
 #define MOEGG_FLAG_COUNT_OVER_CAP  0x4u  /* a masked count > cap was read as cap      */
 
+/* block_m value for per-expert tile heights: every expert gets 256-row tiles,
+ * and its remainder rows one tile of the smallest height in {64, 128, 256}
+ * that holds them.  The padding page's "Adapt kernels without adding a CPU
+ * stall" section asks for per-histogram kernel choice on the device; this
+ * choice is per expert.  The tile list is the 256-row list, ordered: tiles
+ * with more than 128 valid rows, then tiles with 65..128, then 1..64, each
+ * group in expert order. */
+#define MOEGG_BLOCK_M_PER_EXPERT (-1)
+
 /* Tile heights the schedule accounts for, in P_at[] order. */
 #define MOEGG_NUM_Q 6                    /* q = 8, 16, 32, 64, 128, 256 */
 
@@ -110,8 +119,8 @@ size_t moegg_workspace_bytes(int G, int64_t max_rows);
  * the variable-M work list of "Grouped execution does not require padded
  * experts", built from the actual counts.
  *
- * block_m must be 64, 128 or 256, or 0 to let the device choose (see
- * moegg_grouped_gemm_contiguous).  N is the output width of the GEMM the
+ * block_m must be 64, 128 or 256, 0 to let the device choose one height
+ * (see moegg_grouped_gemm_contiguous), or MOEGG_BLOCK_M_PER_EXPERT.  N is the output width of the GEMM the
  * schedule will feed: the choice rule counts its 256-wide column tiles.
  * seg_align >= 1.  Segments are truncated at rows_total (flag
  * MOEGG_FLAG_ROWS_OVERFLOW).
@@ -140,7 +149,9 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  * the fp32 accumulator.
  * Constraints: K % 128 == 0 and N % 256 == 0 for fp8.  K % 64 == 0 and
  * N % 256 == 0 for bf16.  16-byte aligned pointers.  G = 1..4096.
- * block_m: 64, 128 or 256, or 0 = choose on the device from the histogram.
+ * block_m: 64, 128 or 256; 0 = choose one height on the device from the
+ * histogram; MOEGG_BLOCK_M_PER_EXPERT = per-expert heights (see its
+ * definition), stats block_m then reads MOEGG_BLOCK_M_PER_EXPERT.
  * Every height skips whole 16-row MFMA blocks past a tile's valid rows, so
  * the executed rows are P(16) for all of them.  What differs is how many
  * 256x(block_m) tiles there are and how full the last round of tiles is on
@@ -164,9 +175,9 @@ moegg_status_t moegg_grouped_gemm_contiguous(
  * then down projection); they can share one schedule.  Arguments are those of
  * moegg_grouped_gemm_contiguous, without m_sizes and seg_align.  The
  * schedule must come from the same G and rows_total.  block_m = 0 launches
- * every candidate height, and the scheduled one does the work.  A nonzero
- * block_m launches only that height; if it differs from the scheduled
- * height, nothing is written.
+ * every candidate (the three heights and the per-expert kernel), and the one
+ * matching the schedule does the work.  Any other block_m launches only that
+ * kernel; if it differs from the schedule's, nothing is written.
  */
 moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
     const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,

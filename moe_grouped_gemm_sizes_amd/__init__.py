@@ -26,6 +26,7 @@ BF16, FP8_E4M3 = 0, 1
 B_KN, B_NK = 0, 1
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP = 0x1, 0x2, 0x4
 Q_VALUES = (8, 16, 32, 64, 128, 256)
+BLOCK_M_PER_EXPERT = -1          # per-expert tile heights (include/moegg.h)
 
 
 class MoeggError(RuntimeError):

@@ -75,11 +75,15 @@ size_t moegg_workspace_bytes(int G, int64_t max_rows) {
     return ws_layout(G, max_rows).total;
 }
 
+static bool valid_block_m(int b) {
+    return b == 0 || b == 64 || b == 128 || b == 256 || b == MOEGG_BLOCK_M_PER_EXPERT;
+}
+
 moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align, int block_m,
                               int N, void* ws, size_t ws_bytes, void* stream) {
     if (!m_sizes || G < 1 || G > kMaxExperts || rows_total < 0 || rows_total > INT32_MAX || seg_align < 1)
         return MOEGG_ERR_INVALID_ARG;
-    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     const WsLayout L = ws_layout(G, rows_total);
     if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
@@ -99,7 +103,7 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const float* A_scale
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX || seg_align < 1) return MOEGG_ERR_INVALID_ARG;
-    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
@@ -124,7 +128,7 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const floa
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
-    if (block_m != 0 && block_m != 64 && block_m != 128 && block_m != 256) return MOEGG_ERR_UNSUPPORTED;
+    if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;

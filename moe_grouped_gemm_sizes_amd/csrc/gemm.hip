@@ -36,6 +36,7 @@
 //     of one expert, which share A tiles and weight panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device.hpp"
@@ -235,6 +236,11 @@ struct GCfg {
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Contiguous: 256-column tiles, every wave tile 64 rows tall.
+template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 4, 2>;
+template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 2, 4>;
+template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 1, 8>;
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -483,7 +489,46 @@ struct TileGemm {
     }
 };
 
-// M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout.
+// One output tile: rows [row_start, row_start + rows_valid) of expert e's
+// segment, column tile ct.
+template <class C, bool B_KN>
+__device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows_valid,
+                                            int ct) {
+    const int n0 = ct * C::BN;
+    const int KB = p.K / 128;
+    TileGemm<C, B_KN> tg;
+    tg.a_row_bytes = (uint32_t)p.K * C::ESZ;
+    tg.ra = make_rsrc((const char*)p.A + (size_t)row_start * tg.a_row_bytes, (uint32_t)rows_valid * tg.a_row_bytes);
+    const size_t b_expert_bytes = (size_t)p.K * p.N * C::ESZ;
+    const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
+    if constexpr (B_KN) {
+        tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
+        tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
+        tg.b_col_byte = (uint32_t)n0 * C::ESZ;
+    } else {
+        tg.rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
+        tg.b_row_bytes = (uint32_t)p.K * C::ESZ;
+        tg.b_col_byte = 0;
+    }
+    tg.rsa = tg.rb;
+    tg.rsb = tg.rb;
+    tg.sa_row_bytes = (uint32_t)KB * 4;
+    tg.sb_row_bytes = (uint32_t)(p.N / 128) * 4;
+    tg.sb_col_byte = (uint32_t)(n0 / 128) * 4;
+    if constexpr (C::FP8) {
+        tg.rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
+        // this expert's weight scales [K/128, N/128]; slots past the row read as zero
+        tg.rsb = make_rsrc(p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
+    }
+    tg.run(lds, p.K / C::KSTEP, rows_valid);
+    const uint32_t c_row_bytes = (uint32_t)p.N * 2;
+    auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
+                        (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
+    tg.store_bf16(rc, c_row_bytes, rows_valid);
+}
+
+// M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout, one
+// tile height.
 template <class C, bool B_KN, bool MASKED>
 __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -516,37 +561,32 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs 
         row_start = t.row_start;
         rows_valid = t.rows_valid;
     }
-    const int n0 = ct * C::BN;
-    const int KB = p.K / 128;
-    TileGemm<C, B_KN> tg;
-    tg.a_row_bytes = (uint32_t)p.K * C::ESZ;
-    tg.ra = make_rsrc((const char*)p.A + (size_t)row_start * tg.a_row_bytes, (uint32_t)rows_valid * tg.a_row_bytes);
-    const size_t b_expert_bytes = (size_t)p.K * p.N * C::ESZ;
-    const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
-    if constexpr (B_KN) {
-        tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
-        tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
-        tg.b_col_byte = (uint32_t)n0 * C::ESZ;
-    } else {
-        tg.rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
-        tg.b_row_bytes = (uint32_t)p.K * C::ESZ;
-        tg.b_col_byte = 0;
-    }
-    tg.rsa = tg.rb;
-    tg.rsb = tg.rb;
-    tg.sa_row_bytes = (uint32_t)KB * 4;
-    tg.sb_row_bytes = (uint32_t)(p.N / 128) * 4;
-    tg.sb_col_byte = (uint32_t)(n0 / 128) * 4;
-    if constexpr (C::FP8) {
-        tg.rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
-        // this expert's weight scales [K/128, N/128]; slots past the row read as zero
-        tg.rsb = make_rsrc(p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
-    }
-    tg.run(lds, p.K / C::KSTEP, rows_valid);
-    const uint32_t c_row_bytes = (uint32_t)p.N * 2;
-    auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
-                        (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
-    tg.store_bf16(rc, c_row_bytes, rows_valid);
+    contig_tile<C, B_KN>(p, lds, e, row_start, rows_valid, ct);
+}
+
+// Per-expert tile heights (block_m = MOEGG_BLOCK_M_PER_EXPERT): the tile list
+// is the one of 256-row tiles, ordered tiles of more than 128 valid rows first,
+// then tails of 65..128 rows, then tails of 1..64 rows.  Each tile runs with the
+// smallest configuration that covers its valid rows, so an expert's remainder
+// does not pay for a 256-row tile, and the 128- and 64-row configurations'
+// deeper stage rings keep their loads further ahead.  All three share one
+// launch; the configuration is uniform per workgroup.
+template <bool FP8, bool B_KN>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    const int n_ct = p.N / 256;
+    const WsLayout L = ws_layout(p.G, 0);
+    const Control* ctl = (const Control*)(p.ws + L.control);
+    if (ctl->block_m != MOEGG_BLOCK_M_PER_EXPERT) return;
+    const int n_rt = ctl->n_tiles;
+    const int item = block_to_item(blockIdx.x);
+    if (item >= n_rt * n_ct) return;
+    int rt, ct;
+    item_to_tiles(item, n_rt, n_ct, rt, ct);
+    const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
+    if (t.rows_valid > 128) contig_tile<Contig256<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else if (t.rows_valid > 64) contig_tile<Contig128<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else contig_tile<Contig64<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
 }
 
 // ---------------------------------------------------------------- K-grouped
@@ -651,10 +691,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
 // ---------------------------------------------------------------- configs
 
-// Contiguous: 256-column tiles, every wave tile 64 rows tall.
-template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 4, 2>;
-template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 2, 4>;
-template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 1, 8>;
 // Masked decode: short row tiles, narrow column tiles (HBM-bound).
 template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4>;
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
@@ -686,6 +722,15 @@ static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int b
     const int64_t n_ct = a.N / 256;
     hipError_t err = hipSuccess;
     auto grid_for = [&](int q) { return round256(((rows_total + q - 1) / q + a.G) * n_ct); };
+    // block_m = 0 launches every candidate; the one matching the schedule does the work
+    if (block_m == MOEGG_BLOCK_M_PER_EXPERT || block_m == 0) {
+        constexpr int lds = std::max({Contig256<FP8>::LDS_BYTES, Contig128<FP8>::LDS_BYTES, Contig64<FP8>::LDS_BYTES});
+        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN>>(lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN>), dim3(grid_for(256)), dim3(512), lds, s, a);
+        err = hipGetLastError();
+        if (err != hipSuccess || block_m != 0) return err;
+    }
     if (block_m == 0 || block_m == 256) {
         err = launch_one<Contig256<FP8>, B_KN, false>(a, grid_for(256), s);
         if (err != hipSuccess) return err;

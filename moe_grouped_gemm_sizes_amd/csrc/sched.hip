@@ -165,29 +165,62 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     if (flags) atomicOr(&flags_s, flags);
     block_sums<NV>(v, sums_buf);       // its barriers also publish m_s, start_s and flags_s
 
-    // 4. tile height
+    // 4. tile height (per-expert mode lists 256-row tiles)
     int bm = block_m_req;
     if (mode == 1) bm = exec_block_m;
     else if (bm == 0) bm = choose_block_m(&v[3 + MOEGG_NUM_Q], n_col_tiles);
-    const int lg = 31 - __builtin_clz(bm);                  // bm is a power of two
+    const bool per_expert = bm == MOEGG_BLOCK_M_PER_EXPERT;
+    const int bmt = per_expert ? 256 : bm;
+    const int lg = 31 - __builtin_clz(bmt);                 // a power of two
 
     // 5. tile list (contiguous mode): expert ascending, tile ascending.  Each
     //    expert's first tile index goes to LDS; then every thread writes tiles
     //    t, t + 256, ... and finds each tile's expert by binary search.
-    int64_t my_tiles = 0;
+    //    Per-expert mode: the tiles holding more than 128 valid rows come first
+    //    (expert, tile ascending); then each expert's remainder tile of 65..128
+    //    rows, then of 1..64 rows, in expert order.  Class of expert e's last
+    //    tile: 0 (> 128 rows), 1 (65..128), 2 (1..64).
+    auto tail_class = [&](int m) -> int {
+        if (!per_expert || m <= 0) return 0;
+        const int r = m - (((m + 255) >> 8) - 1) * 256;      // rows of the last tile, 1..256
+        return r > 128 ? 0 : (r > 64 ? 1 : 2);
+    };
+    int64_t my_tiles = 0, my_tails = 0;                      // tails: class-1 count | class-2 count << 32
 #pragma unroll 1
-    for (int e = e0; e < e1; ++e) my_tiles += (m_s[e] + bm - 1) >> lg;
-    int64_t n_tiles;
-    int64_t tbase = block_exclusive_scan(my_tiles, wave_buf, &n_tiles);
+    for (int e = e0; e < e1; ++e) {
+        const int c = tail_class(m_s[e]);
+        my_tiles += ((m_s[e] + bmt - 1) >> lg) - (c ? 1 : 0);
+        my_tails += c == 1 ? 1 : (c == 2 ? (int64_t)1 << 32 : 0);
+    }
+    int64_t n_main, n_tails;
+    int64_t tbase = block_exclusive_scan(my_tiles, wave_buf, &n_main);
+    int64_t tails_base = block_exclusive_scan(my_tails, wave_buf, &n_tails);
+    const int64_t n1 = n_tails & 0xffffffff, n2 = n_tails >> 32;
+    const int64_t n_tiles = n_main + n1 + n2;
     if (mode == 0) {
+        int64_t b1 = n_main + (tails_base & 0xffffffff), b2 = n_main + n1 + (tails_base >> 32);
 #pragma unroll 1
         for (int e = e0; e < e1; ++e) {
+            const int m = m_s[e];
+            const int c = tail_class(m);
             toff_s[e] = (int32_t)tbase;
-            tbase += (m_s[e] + bm - 1) >> lg;
+            tbase += ((m + bmt - 1) >> lg) - (c ? 1 : 0);
+            if (c) {
+                const int i = ((m + 255) >> 8) - 1;
+                const int64_t slot = c == 1 ? b1++ : b2++;
+                if (slot < max_tiles) {
+                    moegg_tile_t tl;
+                    tl.expert = e;
+                    tl.tile = i;
+                    tl.row_start = (int32_t)(start_s[e] + (int64_t)i * 256);
+                    tl.rows_valid = m - i * 256;
+                    tiles[slot] = tl;
+                }
+            }
         }
-        if (t == 0) toff_s[G] = (int32_t)n_tiles;
+        if (t == 0) toff_s[G] = (int32_t)n_main;
         __syncthreads();
-        const int nt_all = (int)(n_tiles < max_tiles ? n_tiles : max_tiles);
+        const int nt_all = (int)(n_main < max_tiles ? n_main : max_tiles);
 #pragma unroll 1
         for (int T = t; T < nt_all; T += kSchedThreads) {
             int lo = 0, hi = G - 1;                          // last e with toff_s[e] <= T
@@ -201,7 +234,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
             tl.expert = lo;
             tl.tile = i;
             tl.row_start = (int32_t)(start_s[lo] + ((int64_t)i << lg));
-            tl.rows_valid = min(bm, m_s[lo] - (i << lg));
+            tl.rows_valid = min(bmt, m_s[lo] - (i << lg));
             tiles[T] = tl;
         }
     }

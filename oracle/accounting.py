@@ -126,6 +126,22 @@ def tile_list(counts: Sequence[int], block_m: int, seg_align: int = 1,
     return out
 
 
+def tile_list_per_expert(counts: Sequence[int], seg_align: int = 1) -> List[Tuple[int, int, int, int]]:
+    """Per-expert tile heights: the 256-row tile list, regrouped by the height of
+    the smallest tile in {64, 128, 256} that holds each tile's valid rows --
+    first the tiles with more than 128 valid rows, then those with 65..128,
+    then 1..64, each group keeping the (expert, tile) order.
+
+    Only an expert's last tile can hold fewer than 129 rows, so every expert
+    keeps its full tiles and gets one remainder tile sized to its remainder (the
+    padding page, "Calculate padded token columns": the padding of an expert is
+    set by its own count and the tile height it runs with).
+    """
+    full = tile_list(counts, 256, seg_align)
+    return ([t for t in full if t[3] > 128] + [t for t in full if 64 < t[3] <= 128]
+            + [t for t in full if t[3] <= 64])
+
+
 def summary(counts: Sequence[int], qs: Sequence[int] = CANDIDATE_Q) -> Dict:
     """Every accounting quantity for one histogram, exactly."""
     return {

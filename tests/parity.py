@@ -77,7 +77,7 @@ def check_stats(stats: mg.Stats, counts: Sequence[int], block_m: Optional[int] =
     assert stats.error_flags == 0
     if block_m is not None:
         assert stats.block_m == block_m
-        assert stats.tiles == acc.tiles_for(counts, block_m)
+        assert stats.tiles == acc.tiles_for(counts, 256 if block_m == mg.BLOCK_M_PER_EXPERT else block_m)
 
 
 def rows_as_float(C: torch.Tensor, rows: Sequence[int]) -> np.ndarray:

@@ -66,6 +66,7 @@ def contiguous(**kw):
     (dict(dtype=mg.FP8_E4M3), mg.ERR_INVALID_ARG),                 # fp8 without scales
     (dict(dtype=mg.FP8_E4M3, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
     (dict(block_m=32), mg.ERR_UNSUPPORTED),
+    (dict(block_m=-2), mg.ERR_UNSUPPORTED),
     (dict(align=0), mg.ERR_INVALID_ARG),
     (dict(rows=-1), mg.ERR_INVALID_ARG),
     (dict(ws=None), mg.ERR_WORKSPACE),

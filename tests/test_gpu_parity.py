@@ -65,6 +65,22 @@ def test_schedule_bit_exact(name, block_m, seg_align):
     assert st.capacity_rows == rows_total - sum(counts)
 
 
+@pytest.mark.parametrize("name", sorted(SCHED_HISTS))
+@pytest.mark.parametrize("seg_align", [1, 128])
+def test_schedule_per_expert_bit_exact(name, seg_align):
+    """Per-expert heights: the device's tile list equals the oracle's regrouped
+    256-row list, entry for entry."""
+    counts = SCHED_HISTS[name]
+    announce("schedule per expert", name, seg_align)
+    rows_total = sum(acc.ceil_div(c, seg_align) * seg_align for c in counts)
+    m = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    ws = mg.workspace(len(counts), rows_total)
+    mg.schedule(m, rows_total, ws, seg_align=seg_align, block_m=mg.BLOCK_M_PER_EXPERT)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, mg.BLOCK_M_PER_EXPERT)
+    assert mg.tile_list_read(ws, st.tiles + 5) == acc.tile_list_per_expert(counts, seg_align)
+
+
 def test_schedule_random_histograms():
     rng = random.Random(7)
     for it in range(200):
@@ -135,7 +151,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-@pytest.mark.parametrize("block_m", [0, 64, 128, 256])
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
 @pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
 def test_contiguous_small_full_compare(case, block_m, b_layout):
     name, counts, K, N, dtype, align = case
@@ -229,7 +245,7 @@ def test_contiguous_config_full_size(n, b_layout):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
-@pytest.mark.parametrize("block_m", [64, 128, 256])
+@pytest.mark.parametrize("block_m", [64, 128, 256, mg.BLOCK_M_PER_EXPERT])
 def test_contiguous_every_tile_height_long_k(dtype, b_layout, block_m):
     """Every tile height and weight layout over a long reduction (56 to 112 K
     steps), where each stage of the load ring is reused many times.  A read that
@@ -240,7 +256,7 @@ def test_contiguous_every_tile_height_long_k(dtype, b_layout, block_m):
     announce("long K", dtype, "layout", b_layout, "block_m", block_m)
     inp = wl.materialize(w, "cuda")
     C, ws = P.run_contiguous(w, inp, block_m=block_m, b_layout=b_layout)
-    rows = P.sample_rows_contiguous(w.counts, w.seg_align, block_m, extra=16, seed=1)
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256 if block_m < 0 else block_m, extra=16, seed=1)
     inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
     del inp
     ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
@@ -252,6 +268,29 @@ def test_contiguous_every_tile_height_long_k(dtype, b_layout, block_m):
     print(f"long K {dtype} layout={b_layout} block_m={block_m}: rel_frobenius={err:.3e} worst={worst:.3e}", flush=True)
     assert err <= P.TOL[dtype], err
     assert worst <= 0.05, worst
+
+
+@pytest.mark.parametrize("n", [2, 3])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_contiguous_per_expert_full_size(n, b_layout):
+    """Per-expert tile heights on the full-size issue-histogram and zipf problems."""
+    w = wl.workload(n)
+    announce("per-expert full size", n, w.name, "layout", b_layout)
+    inp = wl.materialize(w, "cuda")
+    C, ws = P.run_contiguous(w, inp, block_m=mg.BLOCK_M_PER_EXPERT, b_layout=b_layout)
+    st = mg.stats_read(ws)
+    P.check_stats(st, w.counts, mg.BLOCK_M_PER_EXPERT)
+    assert mg.tile_list_read(ws, st.tiles) == acc.tile_list_per_expert(w.counts, w.seg_align)
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 64, extra=48, seed=n)
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    del inp
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"per-expert config {n}: rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL[w.dtype], err
+    assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
 # ----------------------------------------------------------------- masked

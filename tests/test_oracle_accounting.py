@@ -207,3 +207,37 @@ def test_m_occupancy_issue_formula():
 
 def test_average_assignments():
     assert acc.average_assignments(4096, 8, 256) == 128
+
+
+@settings(max_examples=300, deadline=None)
+@given(hist, st.sampled_from((1, 4, 16, 128)))
+def test_per_expert_tile_list(counts, align):
+    """Per-expert heights: every row of every expert in exactly one tile, each
+    tile's height class non-increasing along the list, expert order inside a
+    class, and each expert's tiles all full (256) except its last."""
+    tl = acc.tile_list_per_expert(counts, align)
+    offs = acc.segment_offsets(counts, align)
+    covered = {}
+    for e, i, r0, rv in tl:
+        assert 1 <= rv <= 256 and r0 == offs[e] + 256 * i
+        for r in range(r0, r0 + rv):
+            assert r not in covered
+            covered[r] = e
+        if i < acc.ceil_div(counts[e], 256) - 1:
+            assert rv == 256
+    assert len(covered) == sum(counts)
+    assert sorted(tl) == sorted(acc.tile_list(counts, 256, align))
+    cls = [0 if rv > 128 else (1 if rv > 64 else 2) for _, _, _, rv in tl]
+    assert cls == sorted(cls)
+    for c in (0, 1, 2):
+        keys = [(e, i) for (e, i, _, _), k in zip(tl, cls) if k == c]
+        assert keys == sorted(keys)
+
+
+def test_per_expert_tile_list_example():
+    """Counts [300, 0, 70, 513, 10]: full tiles first, then the 65..128-row
+    remainders (70 of expert 2), then the 1..64-row ones (44, 1, 10)."""
+    tl = acc.tile_list_per_expert([300, 0, 70, 513, 10])
+    assert tl == [(0, 0, 0, 256), (3, 0, 370, 256), (3, 1, 626, 256),
+                  (2, 0, 300, 70),
+                  (0, 1, 256, 44), (3, 2, 882, 1), (4, 0, 883, 10)]
