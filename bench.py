@@ -151,9 +151,10 @@ def main():
     ap.add_argument("--block-m", default="auto", choices=("auto", "per-expert", "64", "128", "256"),
                     help="tile height: auto = one height chosen on the device from the histogram; per-expert = "
                          "256-row tiles plus a remainder tile per expert sized 64/128/256")
-    ap.add_argument("--b-layout", choices=("kn", "nk"), default="nk",
-                    help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE "
-                         "weights are usually kept in); repacking is one-time, outside the timed steps")
+    ap.add_argument("--b-layout", choices=("auto", "kn", "nk"), default="auto",
+                    help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE weights "
+                         "are usually kept in; repacking is one-time, outside the timed steps).  auto: nk for "
+                         "the contiguous workloads, kn (as the masked workload prints it) for the masked one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -166,7 +167,8 @@ def main():
     w = wl.workload(args.config)
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
-    b_layout = mg.B_NK if args.b_layout == "nk" else mg.B_KN
+    layout = args.b_layout if args.b_layout != "auto" else ("kn" if w.layout == "masked" else "nk")
+    b_layout = mg.B_NK if layout == "nk" else mg.B_KN
     if b_layout == mg.B_NK and "B" in inp:
         inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
     torch.cuda.synchronize()

@@ -535,18 +535,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs 
     const int n_ct = p.N / C::BN;
     int e, row_start, rows_valid, ct;
     if constexpr (MASKED) {
-        const int n_rt = (p.cap + C::BM - 1) / C::BM;
-        const int item = blockIdx.x;
-        const int per_e = n_rt * n_ct;
-        e = item / per_e;
+        // one workgroup per (expert, column tile); it walks the expert's row tiles
+        // up to masked_m, so an empty expert loads no weights and the grid depends
+        // only on G and N
+        e = blockIdx.x / n_ct;
+        ct = blockIdx.x - e * n_ct;
         if (e >= p.G) return;
-        int r = item - e * per_e;
-        int rt = r / n_ct;
-        ct = r - rt * n_ct;
-        int m = min(max(p.counts[e], 0), p.cap);
-        rows_valid = min(C::BM, m - rt * C::BM);
-        if (rows_valid <= 0) return;             // no weight loads for empty experts
-        row_start = e * p.cap + rt * C::BM;
+        const int m = min(max(p.counts[e], 0), p.cap);
+#pragma unroll 1
+        for (int rt = 0; rt * C::BM < m; ++rt) {
+            if (rt > 0) __syncthreads();         // the previous tile's LDS is free
+            contig_tile<C, B_KN>(p, lds, e, e * p.cap + rt * C::BM, min(C::BM, m - rt * C::BM), ct);
+        }
+        return;
     } else {
         const WsLayout L = ws_layout(p.G, 0);
         const Control* ctl = (const Control*)(p.ws + L.control);
@@ -757,8 +758,7 @@ int masked_block_m() { return MaskedCfg<false>::BM; }
 int masked_block_n() { return MaskedCfg<false>::BN; }
 
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s) {
-    const int n_rt = (a.cap + MaskedCfg<false>::BM - 1) / MaskedCfg<false>::BM;
-    const int grid = a.G * n_rt * (a.N / MaskedCfg<false>::BN);
+    const int grid = a.G * (a.N / MaskedCfg<false>::BN);
     if (fp8) return b_kn ? launch_one<MaskedCfg<true>, true, true>(a, grid, s)
                          : launch_one<MaskedCfg<true>, false, true>(a, grid, s);
     return b_kn ? launch_one<MaskedCfg<false>, true, true>(a, grid, s)
