@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scratch buffer between steps (more than L2 + MALL), and time each step "
+                         "with its own events; ms_per_step is then the mean of those")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
@@ -190,10 +193,15 @@ def main():
     torch.cuda.synchronize()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 2)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.cold else None
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
+        if args.cold:
+            scratch.fill_(i & 255)                   # evict the inputs from L2 and MALL
+            step_ev[i].record(stream)
         if sched is not None:
             sched()
         ev[1 + 2 * i].record(stream)
@@ -204,7 +212,10 @@ def main():
     wall = time.perf_counter() - t_wall
     total_ms = ev[0].elapsed_time(ev[-1])
     gemm_ms = [ev[1 + 2 * i].elapsed_time(ev[2 + 2 * i]) for i in range(args.steps)]
-    ms_step = total_ms / args.steps
+    if args.cold:
+        ms_step = sum(step_ev[i].elapsed_time(ev[2 + 2 * i]) for i in range(args.steps)) / args.steps
+    else:
+        ms_step = total_ms / args.steps
     gemm_avg = sum(gemm_ms) / len(gemm_ms)
 
     st = mg.stats_read(ws) if sched is not None or w.layout != "k_grouped" else None
@@ -227,7 +238,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
-                   "weights": "[G,N,K]" if b_layout == mg.B_NK else "[G,K,N]"},
+                   "weights": "[G,N,K]" if b_layout == mg.B_NK else "[G,K,N]",
+                   "cache": "cold (512 MiB written between steps)" if args.cold else "warm"},
         "pct_mfma_peak": round(100.0 * eff / peak, 2),
     }
     if w.layout == "contiguous":

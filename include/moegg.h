@@ -214,8 +214,8 @@ moegg_status_t moegg_grouped_gemm_masked(
  *                dW[e, i, j] = sum over expert e's rows t of X[t, i] * dY[t, j]
  *            with fp32 accumulation.  t_e = 0 writes zeros.
  * Experts are started longest first.  Constraints: Mw % 256 == 0,
- * Nw % 256 == 0, T >= 0.  A workspace is required (expert offsets and
- * order).
+ * Nw % 256 == 0, T >= 0; X and dY may be NULL when T = 0.  A workspace is
+ * required (expert offsets and order).
  */
 moegg_status_t moegg_grouped_gemm_k_grouped(
     const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G, int64_t T,

@@ -166,7 +166,8 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const float* A_scale, co
 
 moegg_status_t moegg_grouped_gemm_k_grouped(const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G,
                                             int64_t T, int Mw, int Nw, void* ws, size_t ws_bytes, void* stream) {
-    if (!X || !dY || !dW || !t_sizes) return MOEGG_ERR_INVALID_ARG;
+    // with T = 0 no row is read, so X and dY may be NULL (an empty tensor's pointer)
+    if ((T > 0 && (!X || !dY)) || !dW || !t_sizes) return MOEGG_ERR_INVALID_ARG;
     if (G < 1 || G > kMaxExperts || T < 0 || Mw < 1 || Nw < 1) return MOEGG_ERR_INVALID_ARG;
     if (Mw % 256 != 0 || Nw % 256 != 0) return MOEGG_ERR_UNSUPPORTED;
     if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(dW, 16) || !aligned(t_sizes, 4))

@@ -124,3 +124,10 @@ def test_read_validation():
     assert L.moegg_stats_read(None, None, None) == mg.ERR_INVALID_ARG
     n = ctypes.c_int64(0)
     assert L.moegg_tile_list_read(FAKE, None, 5, ctypes.byref(n), None) == mg.ERR_INVALID_ARG
+
+
+def test_k_grouped_accepts_null_operands_only_without_rows():
+    f = mg.lib().moegg_grouped_gemm_k_grouped
+    # T = 0: X and dY are never read, so NULL passes validation (and fails later only on the workspace)
+    assert f(None, None, FAKE, FAKE, 16, 0, 2048, 7168, None, 0, None) == mg.ERR_WORKSPACE
+    assert f(None, None, FAKE, FAKE, 16, 1, 2048, 7168, None, 0, None) == mg.ERR_INVALID_ARG

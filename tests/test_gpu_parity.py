@@ -424,3 +424,58 @@ def test_k_grouped_config_full_size():
     for e, t in enumerate(w.counts):
         if t == 0:
             assert not dW[e].any()
+
+
+def test_k_grouped_integer_exact_and_ragged():
+    """Inputs in {-1, 0, 1}: every dW entry is an integer of magnitude <= t_e,
+    exact in fp32, so GPU == oracle bit for bit.  Segment lengths straddle the
+    64-row reduction step (1, 63, 64, 65, 127, 0)."""
+    t = [1, 63, 64, 65, 127, 0]
+    T, Mw, Nw = sum(t), 256, 512
+    announce("k-grouped integer exact", t)
+    g = torch.Generator().manual_seed(9)
+    X = torch.randint(-1, 2, (T, Mw), generator=g).to(torch.bfloat16)
+    dY = torch.randint(-1, 2, (T, Nw), generator=g).to(torch.bfloat16)
+    dW = torch.full((len(t), Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(len(t), 0)
+    mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws)
+    torch.cuda.synchronize()
+    pairs = [(e, i) for e in range(len(t)) for i in range(Mw)]
+    ref = og.k_grouped(X, dY, t, [e for e, _ in pairs], [i for _, i in pairs])
+    got = dW.cpu().double().numpy().reshape(len(t) * Mw, Nw)
+    assert np.array_equal(got, ref)
+
+
+def test_k_grouped_empty_truncated_and_deterministic():
+    """All experts empty -> dW all zero; counts past T are truncated (flag set);
+    two runs give identical bits."""
+    announce("k-grouped empty / truncated / deterministic")
+    Mw, Nw = 256, 256
+    X = torch.randn(0, Mw).to(torch.bfloat16).cuda()
+    dY = torch.randn(0, Nw).to(torch.bfloat16).cuda()
+    dW = torch.full((3, Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(3, 0)
+    mg.grouped_gemm_k_grouped(X, dY, dW, torch.zeros(3, dtype=torch.int32, device="cuda"), ws)
+    torch.cuda.synchronize()
+    assert not dW.any()
+    assert mg.stats_read(ws).U == 0
+    # counts summing past T: the last segment is cut at T
+    t, T = [50, 80, 40], 100
+    g = torch.Generator().manual_seed(4)
+    X = torch.randn(T, Mw, generator=g).to(torch.bfloat16)
+    dY = torch.randn(T, Nw, generator=g).to(torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        dW = torch.full((3, Mw, Nw), float("nan"), device="cuda")
+        mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws)
+        torch.cuda.synchronize()
+        outs.append(dW.cpu())
+    st = mg.stats_read(ws)
+    assert st.error_flags & mg.FLAG_ROWS_OVERFLOW and st.U == T
+    assert torch.equal(outs[0], outs[1])
+    clamped = [50, 50, 0]                                   # the reading the device takes
+    pairs = [(e, i) for e in range(2) for i in range(0, Mw, 7)]
+    ref = og.k_grouped(X, dY, clamped, [e for e, _ in pairs], [i for _, i in pairs])
+    got = outs[0][torch.tensor([e for e, _ in pairs]), torch.tensor([i for _, i in pairs])].double().numpy()
+    assert og.rel_frobenius(got, ref) <= 1e-4
+    assert not outs[0][2].any()                             # the segment that starts at T is empty
