@@ -158,9 +158,15 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  * 256 CUs.  The device choice minimizes
  *     cost(q) = ceil(tiles(q) * (N / 256) / 256) * (q + 64)
  * over q in {64, 128, 256}, with ties going to the larger q (better weight
- * reuse).  Padding alone does not pick the kernel ("Padding is not the whole
- * cost model", MoE GroupGEMM padding page).  The grid size is fixed from host
- * arguments alone, so the call is graph-capturable.
+ * reuse), and compares it with per-expert heights, costed class by class:
+ *     cost_pe = sum over c of ceil(n_c * (N / 256) / 256) * (q_c + 64)
+ * where n_c counts the 256-row tiles (q_c = 256), the remainders of 65..128
+ * rows (q_c = 128) and of 1..64 rows (q_c = 64).  Per-expert heights are
+ * chosen only when strictly cheaper; stats block_m then reads
+ * MOEGG_BLOCK_M_PER_EXPERT.  Padding alone does not pick the kernel
+ * ("Padding is not the whole cost model", MoE GroupGEMM padding page).  The
+ * grid size is fixed from host arguments alone, so the call is
+ * graph-capturable.
  */
 moegg_status_t moegg_grouped_gemm_contiguous(
     const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,

@@ -75,21 +75,28 @@ __device__ void block_sums(int64_t (&v)[NV], int64_t (*wave_buf)[NV]) {
     __syncthreads();
 }
 
-// Tile-height cost over the candidates 64, 128, 256.  A launch holds one
-// 512-thread tile per CU (256 CUs).  Each "wave" of 256 tiles costs its tile
-// height in rows plus a fixed per-tile overhead, so
+// Tile-height cost over the candidates 64, 128, 256 and per-expert heights.
+// A launch holds one 512-thread tile per CU (256 CUs).  Each "wave" of 256
+// tiles costs its tile height in rows plus a fixed per-tile overhead, so
 //     cost(q) = ceil(tiles(q) * n_col_tiles / 256) * (q + 64).
-// Ties go to the larger q, which reuses weights better.
-__device__ int choose_block_m(const int64_t* cand_tiles, int n_col_tiles) {
+// Per-expert heights run three classes of tiles (256-row tiles, remainders of
+// 65..128 rows on 128-row tiles, remainders of 1..64 rows on 64-row tiles);
+// each class is costed as its own sequence of waves:
+//     cost_pe = sum over classes c of ceil(n_c * n_col_tiles / 256) * (q_c + 64).
+// Ties go to the larger uniform q, which reuses weights better, and a uniform
+// height wins a tie with per-expert heights.
+__device__ int choose_block_m(const int64_t* cand_tiles, int64_t n_tail128, int64_t n_tail64, int n_col_tiles) {
     const int qs[kNumCand] = {64, 128, 256};
+    auto waves = [&](int64_t tiles, int q) { return (tiles * n_col_tiles + 255) / 256 * (int64_t)(q + 64); };
     int best = 256;
     int64_t best_cost = -1;
     for (int c = kNumCand - 1; c >= 0; --c) {
-        int64_t items = cand_tiles[c] * n_col_tiles;
-        int64_t cost = (items + 255) / 256 * (int64_t)(qs[c] + 64);
+        const int64_t cost = waves(cand_tiles[c], qs[c]);
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = qs[c]; }
     }
-    return best;
+    const int64_t cost_pe =
+        waves(cand_tiles[kNumCand - 1] - n_tail128 - n_tail64, 256) + waves(n_tail128, 128) + waves(n_tail64, 64);
+    return cost_pe < best_cost ? MOEGG_BLOCK_M_PER_EXPERT : best;
 }
 
 // mode 0: contiguous layout (segment starts from aligned counts, tile list).
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     const int32_t* __restrict__ counts, int G, int64_t rows_total, int seg_align, int cap,
     int mode, int block_m_req, int n_col_tiles, int exec_block_m, unsigned char* __restrict__ ws,
     int64_t max_tiles) {
-    constexpr int NV = 3 + MOEGG_NUM_Q + kNumCand;           // U, active, sum_sq, P(q) x6, tiles(q) x3
+    constexpr int NV = 3 + MOEGG_NUM_Q + kNumCand + 2;       // U, active, sum_sq, P(q) x6, tiles(q) x3, tails x2
     __shared__ int64_t wave_buf[kWaves];
     __shared__ int64_t sums_buf[kWaves][NV];
     __shared__ int32_t m_s[kMaxExperts];                     // clamped (then truncated) counts
@@ -161,6 +168,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
         for (int i = 0; i < MOEGG_NUM_Q; ++i) v[3 + i] += ((m + (8 << i) - 1) >> (3 + i)) << (3 + i);
 #pragma unroll
         for (int c = 0; c < kNumCand; ++c) v[3 + MOEGG_NUM_Q + c] += (m + (64 << c) - 1) >> (6 + c);
+        // rows of the last 256-row tile, 1..256: per-expert remainder classes
+        const int64_t r = m - (((m + 255) >> 8) - 1) * 256;
+        v[3 + MOEGG_NUM_Q + kNumCand] += m > 0 && r > 64 && r <= 128;
+        v[3 + MOEGG_NUM_Q + kNumCand + 1] += m > 0 && r <= 64;
     }
     if (flags) atomicOr(&flags_s, flags);
     block_sums<NV>(v, sums_buf);       // its barriers also publish m_s, start_s and flags_s
@@ -168,7 +179,9 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     // 4. tile height (per-expert mode lists 256-row tiles)
     int bm = block_m_req;
     if (mode == 1) bm = exec_block_m;
-    else if (bm == 0) bm = choose_block_m(&v[3 + MOEGG_NUM_Q], n_col_tiles);
+    else if (bm == 0)
+        bm = choose_block_m(&v[3 + MOEGG_NUM_Q], v[3 + MOEGG_NUM_Q + kNumCand], v[3 + MOEGG_NUM_Q + kNumCand + 1],
+                            n_col_tiles);
     const bool per_expert = bm == MOEGG_BLOCK_M_PER_EXPERT;
     const int bmt = per_expert ? 256 : bm;
     const int lg = 31 - __builtin_clz(bmt);                 // a power of two
