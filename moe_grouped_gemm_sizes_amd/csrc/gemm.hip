@@ -206,9 +206,10 @@ __device__ __forceinline__ int block_to_item(int b) {
 // for fp8, that step's scales: [activations | weights | scales].  The ring has
 // as many stages as fit in the 160 KB of LDS, up to four: loads run
 // STAGES - 1 steps ahead of the MFMAs.
-template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_ = 1>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
+    static constexpr int OCC = OCC_;                   // workgroups per CU the LDS ring leaves room for
     static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
     static constexpr int KSTEP = 128 / ESZ;            // K elements per step
     static constexpr int BM = BM_, BN = BN_;
@@ -223,7 +224,8 @@ struct GCfg {
     static constexpr int SA_BYTES = FP8 ? BM * 4 : 0;
     static constexpr int S_BYTES = FP8 ? SA_BYTES + 256 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int STAGES = (160 * 1024) / STAGE_BYTES < 4 ? (160 * 1024) / STAGE_BYTES : 4;
+    static constexpr int STAGES =
+        (160 * 1024 / OCC) / STAGE_BYTES < 4 ? (160 * 1024 / OCC) / STAGE_BYTES : 4;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int A_OPS = A_BYTES / 16 / THREADS;   // 16-byte DMAs per thread per step
     static constexpr int B_OPS = B_BYTES / 16 / THREADS;
@@ -234,7 +236,7 @@ struct GCfg {
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
-    static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 2 && LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
 // Contiguous: 256-column tiles, every wave tile 64 rows tall.
@@ -530,7 +532,7 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
 // M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout, one
 // tile height.
 template <class C, bool B_KN, bool MASKED>
-__global__ __launch_bounds__(C::THREADS, 1) void grouped_gemm_kernel(ContigArgs p) {
+__global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / C::BN;
     int e, row_start, rows_valid, ct;
@@ -693,7 +695,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 // ---------------------------------------------------------------- configs
 
 // Masked decode: short row tiles, narrow column tiles (HBM-bound).
-template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4>;
+// Two workgroups per CU, three stages each: the loads of one overlap the
+// start-up and epilogue of the other, and a CU keeps twice the bytes in flight.
+template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4, 2>;
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
