@@ -94,3 +94,18 @@ def untouched_rows_ok(C: torch.Tensor, counts: Sequence[int], seg_align: int) ->
     if idx.numel() == 0:
         return True
     return bool((C[idx].view(torch.int16) == SENTINEL_BITS).all())
+
+
+def choice_rule(counts, n_col_tiles):
+    """The documented tile-height rule: cost(q) = ceil(tiles(q) * cols / 256) * (q + 64), ties to larger q;
+    per-expert heights (classes of 256-row tiles, 65..128-row and 1..64-row remainders, each class costed as
+    its own waves) only when strictly cheaper."""
+    waves = lambda tiles, q: -(-tiles * n_col_tiles // 256) * (q + 64)
+    costs = {q: waves(acc.tiles_for(counts, q), q) for q in (64, 128, 256)}
+    best = min(costs.values())
+    uniform = max(q for q, c in costs.items() if c == best)
+    rem = [m - (-(-m // 256) - 1) * 256 for m in counts if m > 0]
+    n128 = sum(1 for r in rem if 64 < r <= 128)
+    n64 = sum(1 for r in rem if r <= 64)
+    pe = waves(acc.tiles_for(counts, 256) - n128 - n64, 256) + waves(n128, 128) + waves(n64, 64)
+    return mg.BLOCK_M_PER_EXPERT if pe < best else uniform

@@ -111,21 +111,6 @@ def test_schedule_clamps_bad_counts():
     assert mg.tile_list_read(ws, 10) == acc.tile_list([5, 0, 95, 0], 64, 1)
 
 
-def choice_rule(counts, n_col_tiles):
-    """The documented tile-height rule: cost(q) = ceil(tiles(q) * cols / 256) * (q + 64), ties to larger q;
-    per-expert heights (classes of 256-row tiles, 65..128-row and 1..64-row remainders, each class costed as
-    its own waves) only when strictly cheaper."""
-    waves = lambda tiles, q: -(-tiles * n_col_tiles // 256) * (q + 64)
-    costs = {q: waves(acc.tiles_for(counts, q), q) for q in (64, 128, 256)}
-    best = min(costs.values())
-    uniform = max(q for q, c in costs.items() if c == best)
-    rem = [m - (-(-m // 256) - 1) * 256 for m in counts if m > 0]
-    n128 = sum(1 for r in rem if 64 < r <= 128)
-    n64 = sum(1 for r in rem if r <= 64)
-    pe = waves(acc.tiles_for(counts, 256) - n128 - n64, 256) + waves(n128, 128) + waves(n64, 64)
-    return mg.BLOCK_M_PER_EXPERT if pe < best else uniform
-
-
 def expected_tiles(counts, block_m, seg_align):
     if block_m == mg.BLOCK_M_PER_EXPERT:
         return acc.tile_list_per_expert(counts, seg_align)
@@ -142,7 +127,7 @@ def test_schedule_device_choice_matches_rule(name):
     ws = mg.workspace(len(counts), rows_total)
     mg.schedule(m, rows_total, ws, seg_align=1, block_m=0, N=256)
     st = mg.stats_read(ws)
-    assert st.block_m == choice_rule(counts, 1)
+    assert st.block_m == P.choice_rule(counts, 1)
     assert mg.tile_list_read(ws, st.tiles) == expected_tiles(counts, st.block_m, 1)
 
 
@@ -241,7 +226,7 @@ def test_contiguous_config_full_size(n, b_layout):
     C, ws = P.run_contiguous(w, inp, block_m=0, b_layout=b_layout)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
-    assert st.block_m == choice_rule(w.counts, w.N // 256)
+    assert st.block_m == P.choice_rule(w.counts, w.N // 256)
     if n == 1:
         assert [st.P_at[q] for q in (8, 16, 32)] == [160, 192, 256]
     rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256 if st.block_m < 0 else st.block_m, extra=48, seed=n) \
