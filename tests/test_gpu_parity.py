@@ -378,6 +378,58 @@ def test_masked_graph_replay():
         check_masked(w, inp, C, counts)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_contiguous_graph_replay(dtype):
+    """Scheduler and contiguous GEMM captured together in one graph (block_m = 0:
+    the device picks the height, every candidate kernel is in the graph).  The
+    counts are rewritten in place between replays, with no host round trip
+    inside the capture; each replay matches the oracle on every valid row,
+    leaves the other rows alone, and lists the tiles the oracle lists."""
+    rows_total = 400
+    hists = ([70, 0, 300, 5], [0, 0, 0, 0], [100, 100, 100, 100], [1, 0, 398, 1], [256, 129, 15, 0], [70, 0, 300, 5])
+    announce("contiguous graph replay", dtype)
+    w = wl.Workload("g", "contiguous", dtype, [rows_total, 0, 0, 0], K=256, N=256, values="normal", seed=7)
+    inp = wl.materialize(w, "cuda")
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    m = inp["counts"]
+    C = P.sentinel_like((rows_total, w.N))
+    ws = mg.workspace(w.G, rows_total)
+
+    def step():
+        mg.schedule(m, rows_total, ws, seg_align=1, block_m=0, N=w.N)
+        mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"), inp.get("B_scale"),
+                                             block_m=0)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for counts in hists:
+        m.copy_(torch.tensor(counts, dtype=torch.int32))
+        C.view(torch.int16).fill_(P.SENTINEL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        st = mg.stats_read(ws)
+        P.check_stats(st, counts)
+        assert st.block_m == P.choice_rule(counts, 1)
+        assert mg.tile_list_read(ws, st.tiles) == expected_tiles(counts, st.block_m, 1)
+        wc = wl.Workload("g", "contiguous", dtype, counts, K=256, N=256, values="normal", seed=7)
+        rows = [r for e, s0 in enumerate(acc.segment_offsets(counts, 1)[:-1]) for r in range(s0, s0 + counts[e])]
+        if rows:
+            ref = P.oracle_contiguous_rows(wc, cpu, rows)
+            got = P.rows_as_float(C, rows)
+            assert np.isfinite(got).all()
+            err = og.rel_frobenius(got, ref)
+            assert err <= P.TOL[dtype], (counts, err)
+        assert P.untouched_rows_ok(C, counts, 1), counts
+
+
 # ----------------------------------------------------------------- K-grouped
 
 
