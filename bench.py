@@ -151,6 +151,9 @@ def main():
                             "workloads 2-5, whose operands (0.8-2.2 GB) are streamed once per layer in a model")
     cache.add_argument("--warm", dest="cold", action="store_false",
                        help="back-to-back steps, operands left in L2 and MALL; the default for workload 1")
+    ap.add_argument("--scales", choices=("fp32", "e8m0"), default="fp32",
+                    help="fp8 block scales: fp32 (the workload as stated, promoted on the VALU), or powers of two "
+                         "as E8M0 bytes, applied by the MFMA (contiguous fp8 workloads only)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
@@ -172,6 +175,11 @@ def main():
         sys.exit(2)
     mg.lib()
     w = wl.workload(args.config)
+    if args.scales == "e8m0":
+        if w.dtype != "fp8" or w.layout != "contiguous":
+            print("--scales e8m0 applies to the contiguous fp8 workload only", file=sys.stderr)
+            sys.exit(2)
+        w.scales = "e8m0"
     if args.cold is None:
         args.cold = args.config != 1
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
@@ -185,12 +193,14 @@ def main():
     # first pass: learn the device's tile-height choice (outside timing)
     bm_req = {"auto": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] if not args.block_m.isdigit() \
         else int(args.block_m)
-    sched, gemm, ws = build_step(w, inp, 0, b_layout, bm_req)
+    # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32
+    inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) if w.scales == "e8m0" else inp
+    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req)
     if sched is not None:
         sched()
         torch.cuda.synchronize()
         st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp, st0.block_m, b_layout, bm_req)
+        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -245,6 +255,8 @@ def main():
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
                    "weights": "[G,N,K]" if b_layout == mg.B_NK else "[G,K,N]",
+                   "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else "fp32")
+                   if w.dtype == "fp8" else None,
                    "cache": "cold (512 MiB written between steps)" if args.cold else "warm"},
         "pct_mfma_peak": round(100.0 * eff / peak, 2),
     }

@@ -41,8 +41,16 @@ typedef enum {
     MOEGG_ERR_HIP = 4            /* a HIP runtime call failed                 */
 } moegg_status_t;
 
-/* Operand storage type.  MOEGG_FP8_E4M3 is OCP e4m3fn (max 448, no inf). */
-typedef enum { MOEGG_BF16 = 0, MOEGG_FP8_E4M3 = 1 } moegg_dtype_t;
+/* Operand storage type.  MOEGG_FP8_E4M3 is OCP e4m3fn (max 448, no inf) with
+ * fp32 block scales, promoted into the fp32 accumulator group by group.
+ * MOEGG_FP8_E4M3_E8M0 is the same operands with power-of-two block scales
+ * stored as E8M0 exponent bytes (value 2^(b - 127); 255 is NaN), the packed
+ * UE8M0 scale format the DeepGEMM record names for SM100.  On gfx950 the MFMA
+ * applies them itself (V_MFMA_SCALE_F32_16X16X128_F8F6F4), so nothing is
+ * promoted on the VALU.  Its activation scales are stored transposed:
+ * [K/128, rows] (DeepGEMM's MN-major scale layout), four rows per 32-bit word.
+ * Contiguous layout only. */
+typedef enum { MOEGG_BF16 = 0, MOEGG_FP8_E4M3 = 1, MOEGG_FP8_E4M3_E8M0 = 2 } moegg_dtype_t;
 
 /* How each expert's weight B_e is stored.
  *   MOEGG_B_KN: B[G, K, N], N contiguous.
@@ -134,11 +142,12 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  *   A        [rows_total, K], row-major.  Expert e's rows start at seg_off[e],
  *            as in moegg_schedule.  seg_align = 1 packs them back to back.  A
  *            larger seg_align puts every segment start at a multiple of it.
- *   A_scale  fp8 only: fp32 [rows_total, K/128], one scale per 1x128 group.
- *            NULL for bf16.
+ *   A_scale  MOEGG_FP8_E4M3: fp32 [rows_total, K/128], one scale per 1x128
+ *            group.  MOEGG_FP8_E4M3_E8M0: E8M0 bytes [K/128, rows_total]
+ *            (transposed).  NULL for bf16.
  *   B        [G, K, N] or [G, N, K] (b_layout), same dtype as A.
- *   B_scale  fp8 only: fp32 [G, K/128, N/128], one per 128x128 block.  NULL
- *            for bf16.
+ *   B_scale  MOEGG_FP8_E4M3: fp32 [G, K/128, N/128], one per 128x128 block.
+ *            MOEGG_FP8_E4M3_E8M0: E8M0 bytes, same shape.  NULL for bf16.
  *   C        bf16 [rows_total, N], row-major.  Only the rows of valid
  *            segments are written.  Other rows keep their contents.
  *   m_sizes  int32 [G] on the device.
@@ -146,9 +155,12 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  *     C[R, n] = bf16_rne( sum_k A[R, k] * B_e[k, n] )
  * with fp32 accumulation.  For fp8, each 128-wide K group's fp32 partial sum
  * is multiplied by A_scale[R, k/128] * B_scale[e, k/128, n/128] and added to
- * the fp32 accumulator.
+ * the fp32 accumulator.  With E8M0 scales the MFMA scales its operands by
+ * the two powers of two instead: the same value up to fp32 rounding order.
  * Constraints: K % 128 == 0 and N % 256 == 0 for fp8.  K % 64 == 0 and
- * N % 256 == 0 for bf16.  16-byte aligned pointers.  G = 1..4096.
+ * N % 256 == 0 for bf16.  E8M0 scales also need N % 512 == 0, N <= 32768
+ * and rows_total % 4 == 0 (UNSUPPORTED otherwise).  16-byte aligned
+ * operands, 4-byte aligned scales.  G = 1..4096.
  * block_m: 64, 128 or 256; 0 = choose one height on the device from the
  * histogram; MOEGG_BLOCK_M_PER_EXPERT = per-expert heights (see its
  * definition), stats block_m then reads MOEGG_BLOCK_M_PER_EXPERT.
@@ -169,7 +181,7 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  * graph-capturable.
  */
 moegg_status_t moegg_grouped_gemm_contiguous(
-    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,
     const int32_t* m_sizes, int G, int64_t rows_total, int K, int N, int seg_align,
     moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
     void* ws, size_t ws_bytes, void* stream);
@@ -186,7 +198,7 @@ moegg_status_t moegg_grouped_gemm_contiguous(
  * kernel; if it differs from the schedule's, nothing is written.
  */
 moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
-    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,
     int G, int64_t rows_total, int K, int N, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
     int block_m, const void* ws, size_t ws_bytes, void* stream);
 
@@ -195,6 +207,7 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
  * computes only the valid portions, with no CPU sync).
  *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (fp8) or NULL.
+ *            MOEGG_FP8_E4M3_E8M0 is not supported here (UNSUPPORTED).
  *   B        as for the contiguous call.  B_scale as for the contiguous call.
  *   C        bf16 [G, cap, N].  Only rows r < masked_m[e] are written.
  *   masked_m int32 [G] on the device, read by the kernel at run time.
@@ -206,7 +219,7 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  * Constraints: as for the contiguous call, plus cap >= 1.
  */
 moegg_status_t moegg_grouped_gemm_masked(
-    const void* A, const float* A_scale, const void* B, const float* B_scale, void* C,
+    const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,
     const int32_t* masked_m, int G, int cap, int K, int N,
     moegg_dtype_t dtype, moegg_b_layout_t b_layout,
     void* ws, size_t ws_bytes, void* stream);

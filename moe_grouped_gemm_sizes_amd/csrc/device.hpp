@@ -47,8 +47,10 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_
 }
 
 
-// Same, with a wave-uniform scalar offset added to the address.  The
-// buffer's range check covers voffset, so row masking must live there.
+// Same, with a wave-uniform scalar offset added to the address.  The range
+// check counts soffset as well (measured on gfx950: a load whose step offset
+// sat in soffset past a one-row resource read zeros), so a resource must span
+// every step's bytes; rows past the valid ones are masked through voffset.
 __device__ __forceinline__ void load16_to_lds_so(__amdgpu_buffer_rsrc_t rs, uint32_t voffset, uint32_t soffset,
                                                  void* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MOEGG_LDS void*)lds_base, 16, voffset, soffset, 0, 0);

@@ -206,9 +206,12 @@ __device__ __forceinline__ int block_to_item(int b) {
 // for fp8, that step's scales: [activations | weights | scales].  The ring has
 // as many stages as fit in the 160 KB of LDS, up to four: loads run
 // STAGES - 1 steps ahead of the MFMAs.
-template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_ = 1>
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_ = 1, bool E8M0_ = false>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
+    // fp8 block scales as E8M0 exponent bytes, applied by the MFMA itself
+    // (V_MFMA_SCALE_F32_16X16X128_F8F6F4) instead of promoted on the VALU
+    static constexpr bool E8M0 = E8M0_;
     static constexpr int OCC = OCC_;                   // workgroups per CU the LDS ring leaves room for
     static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
     static constexpr int KSTEP = 128 / ESZ;            // K elements per step
@@ -219,9 +222,12 @@ struct GCfg {
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int MB = WTM / 16, NB = WTN / 16;
     static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-    // fp8 scales of the step: one per tile row (activations), then 64 slots for
-    // the weight-block scales of this column tile (BN / 128 of them are used)
-    static constexpr int SA_BYTES = FP8 ? BM * 4 : 0;
+    // fp8 scales of the step: one per tile row (activations), then 256 bytes of
+    // weight-block scales.  fp32: BM floats, then 64 float slots (BN / 128 of
+    // them used).  E8M0: the tile's rows' bytes from a 4-byte-aligned start
+    // (BM + 3 bytes in two 256-byte halves), then the N / 128 bytes of the
+    // step's weight-scale row.
+    static constexpr int SA_BYTES = FP8 ? (E8M0 ? 512 : BM * 4) : 0;
     static constexpr int S_BYTES = FP8 ? SA_BYTES + 256 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int STAGES =
@@ -235,14 +241,15 @@ struct GCfg {
     static_assert(WTM % 16 == 0 && WTN % 16 == 0 && NB % 2 == 0, "wave tile");
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
+    static_assert(!E8M0 || (FP8 && WAVES >= 3), "E8M0: two waves load activation-scale bytes, the others weight-scale bytes");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(STAGES >= 2 && LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
 // Contiguous: 256-column tiles, every wave tile 64 rows tall.
-template <bool FP8> using Contig256 = GCfg<FP8, 256, 256, 4, 2>;
-template <bool FP8> using Contig128 = GCfg<FP8, 128, 256, 2, 4>;
-template <bool FP8> using Contig64 = GCfg<FP8, 64, 256, 1, 8>;
+template <bool FP8, bool E8 = false> using Contig256 = GCfg<FP8, 256, 256, 4, 2, 1, E8>;
+template <bool FP8, bool E8 = false> using Contig128 = GCfg<FP8, 128, 256, 2, 4, 1, E8>;
+template <bool FP8, bool E8 = false> using Contig64 = GCfg<FP8, 64, 256, 1, 8, 1, E8>;
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -275,10 +282,24 @@ struct TileGemm {
     // branches: resource rss, voffset ss_voff + ks * ss_step, LDS slot ss_dst
     __amdgpu_buffer_rsrc_t rss;
     uint32_t ss_voff, ss_step, ss_dst;
+    // E8M0: byte of tile row 0 inside the activation-scale slot (the slot starts
+    // at the 4-byte boundary at or below the tile's first row), and the first
+    // weight-scale byte of this column tile in the step's scale row
+    int sa_shift, sb_col;
+    uint32_t sa_step_e8;     // bytes per K-block row of the activation scales (rows_total)
 
     __device__ __forceinline__ void setup_roles() {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-        if constexpr (C::FP8) {
+        if constexpr (C::E8M0) {
+            // waves 0-1: the activation-scale bytes (4 per lane, 512 bytes from the
+            // aligned start); the others: the step's weight-scale row, N / 128 bytes
+            // in the first N / 512 lanes (the rest point past the buffer and read zero)
+            const bool act = wave < 2;
+            rss = act ? rsa : rsb;
+            ss_voff = act ? (wave * 64 + lane) * 4u : (lane * 4 < (int)sb_row_bytes ? lane * 4u : 0x80000000u);
+            ss_step = act ? sa_step_e8 : sb_row_bytes;
+            ss_dst = C::A_BYTES + C::B_BYTES + (act ? wave * 256 : C::SA_BYTES);
+        } else if constexpr (C::FP8) {
             // waves below BM/64: one 4-byte activation scale per tile row; the other
             // waves: the weight-block scales of this column tile (all write the same
             // values to the same slots).  The weight-scale K row sits in voffset, so
@@ -325,7 +346,12 @@ struct TileGemm {
     }
 
     __device__ __forceinline__ void issue_s(char* __restrict__ stage, int ks) const {
-        if constexpr (C::FP8)
+        if constexpr (C::E8M0)
+            // the K-block row goes in soffset, the lane's bytes in voffset (lanes with
+            // nothing to load are parked past the buffer and read zero)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(stage + ss_dst), 4, ss_voff,
+                                                     ks * ss_step, 0, 0);
+        else if constexpr (C::FP8)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(stage + ss_dst), 4,
                                                      ss_voff + ks * ss_step, 0, 0, 0);
     }
@@ -359,6 +385,39 @@ struct TileGemm {
         const char* tb = ta + C::A_BYTES;
         if constexpr (MBA == 0) {
             issue_all(wr, next);
+        } else if constexpr (C::E8M0) {
+            // scales go to the MFMA: scale_a (weights, the A operand) is the byte of
+            // the 128-column block, the same in every lane; scale_b (activations)
+            // is each lane's row byte.  The MFMA accumulates straight into acc.
+            const MOEGG_LDS unsigned char* sab = (const MOEGG_LDS unsigned char*)(tb + C::B_BYTES) + sa_shift;
+            const MOEGG_LDS unsigned char* sbb = (const MOEGG_LDS unsigned char*)(tb + C::B_BYTES + C::SA_BYTES) + sb_col;
+            auto fragb = [&](int i) -> v8i {
+                const int n0 = wn * C::WTN + i * 16;
+                if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
+                else return frag_k_fp8(tb, n0 + r16);
+            };
+            v8i xb[2];
+            xb[0] = fragb(0);
+            v8i ya[MBA];
+            int sbj[MBA];
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) ya[j] = frag_k_fp8(ta, wm * C::WTM + j * 16 + r16);
+#pragma unroll
+            for (int j = 0; j < MBA; ++j) sbj[j] = sab[wm * C::WTM + j * 16 + r16];
+            int sai[NSB];
+#pragma unroll
+            for (int b = 0; b < NSB; ++b) sai[b] = sbb[(wn * C::WTN) / 128 + b];
+            static_for<0, C::NB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
+                constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
+#pragma unroll
+                for (int j = 0; j < MBA; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xb[i & 1], ya[j], acc[i][j], 0, 0,
+                                                                                 0, sai[sb], 0, sbj[j]);
+                if constexpr (i == 0) issue_all(wr, next);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else if constexpr (C::FP8) {
             const float* ts = (const float*)(tb + C::B_BYTES);
             const float* tsb = (const float*)(tb + C::B_BYTES + C::SA_BYTES) + wn * C::WTN / 128;
@@ -517,10 +576,24 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
     tg.sa_row_bytes = (uint32_t)KB * 4;
     tg.sb_row_bytes = (uint32_t)(p.N / 128) * 4;
     tg.sb_col_byte = (uint32_t)(n0 / 128) * 4;
-    if constexpr (C::FP8) {
-        tg.rsa = make_rsrc(p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
+    if constexpr (C::E8M0) {
+        // activation-scale bytes [K/128, rows_total]: the step's row of bytes from
+        // the 4-byte boundary at or below the tile's first row (the step's row
+        // offset rides in soffset, which the range check counts too, so the
+        // resource spans every K-block row); rows_total % 4 == 0, so no dword
+        // crosses the end of the array
+        const int a0 = row_start & ~3;
+        tg.sa_shift = row_start - a0;
+        tg.sa_step_e8 = (uint32_t)p.rows_total;
+        tg.rsa = make_rsrc((const unsigned char*)p.A_scale + a0, (uint32_t)((int64_t)KB * p.rows_total - a0));
+        // weight-scale bytes [G, K/128, N/128]: this expert's block, one row per step
+        tg.sb_row_bytes = (uint32_t)(p.N / 128);
+        tg.sb_col = n0 / 128;
+        tg.rsb = make_rsrc((const unsigned char*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * (p.N / 128));
+    } else if constexpr (C::FP8) {
+        tg.rsa = make_rsrc((const float*)p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
         // this expert's weight scales [K/128, N/128]; slots past the row read as zero
-        tg.rsb = make_rsrc(p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
+        tg.rsb = make_rsrc((const float*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
     }
     tg.run(lds, p.K / C::KSTEP, rows_valid);
     const uint32_t c_row_bytes = (uint32_t)p.N * 2;
@@ -574,7 +647,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
 // does not pay for a 256-row tile, and the 128- and 64-row configurations'
 // deeper stage rings keep their loads further ahead.  All three share one
 // launch; the configuration is uniform per workgroup.
-template <bool FP8, bool B_KN>
+template <bool FP8, bool B_KN, bool E8>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / 256;
@@ -587,9 +660,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigA
     int rt, ct;
     item_to_tiles(item, n_rt, n_ct, rt, ct);
     const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
-    if (t.rows_valid > 128) contig_tile<Contig256<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else if (t.rows_valid > 64) contig_tile<Contig128<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else contig_tile<Contig64<FP8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    if (t.rows_valid > 128) contig_tile<Contig256<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else if (t.rows_valid > 64) contig_tile<Contig128<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else contig_tile<Contig64<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
 }
 
 // ---------------------------------------------------------------- K-grouped
@@ -722,40 +795,43 @@ static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
 
 // Launch the contiguous GEMM for tile height block_m (0 = every candidate;
 // the ones the device did not choose exit at entry).
-template <bool FP8, bool B_KN>
+template <bool FP8, bool B_KN, bool E8>
 static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
     const int64_t n_ct = a.N / 256;
     hipError_t err = hipSuccess;
     auto grid_for = [&](int q) { return round256(((rows_total + q - 1) / q + a.G) * n_ct); };
     // block_m = 0 launches every candidate; the one matching the schedule does the work
     if (block_m == MOEGG_BLOCK_M_PER_EXPERT || block_m == 0) {
-        constexpr int lds = std::max({Contig256<FP8>::LDS_BYTES, Contig128<FP8>::LDS_BYTES, Contig64<FP8>::LDS_BYTES});
-        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN>>(lds);
+        constexpr int lds = std::max({Contig256<FP8, E8>::LDS_BYTES, Contig128<FP8, E8>::LDS_BYTES,
+                                      Contig64<FP8, E8>::LDS_BYTES});
+        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8>>(lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN>), dim3(grid_for(256)), dim3(512), lds, s, a);
+        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8>), dim3(grid_for(256)), dim3(512), lds, s, a);
         err = hipGetLastError();
         if (err != hipSuccess || block_m != 0) return err;
     }
     if (block_m == 0 || block_m == 256) {
-        err = launch_one<Contig256<FP8>, B_KN, false>(a, grid_for(256), s);
+        err = launch_one<Contig256<FP8, E8>, B_KN, false>(a, grid_for(256), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 128) {
-        err = launch_one<Contig128<FP8>, B_KN, false>(a, grid_for(128), s);
+        err = launch_one<Contig128<FP8, E8>, B_KN, false>(a, grid_for(128), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 64) {
-        err = launch_one<Contig64<FP8>, B_KN, false>(a, grid_for(64), s);
+        err = launch_one<Contig64<FP8, E8>, B_KN, false>(a, grid_for(64), s);
     }
     return err;
 }
 
-hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool b_kn, int64_t rows_total, int block_m,
+hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool b_kn, int64_t rows_total, int block_m,
                              hipStream_t s) {
-    if (fp8) return b_kn ? launch_contig_t<true, true>(a, rows_total, block_m, s)
-                         : launch_contig_t<true, false>(a, rows_total, block_m, s);
-    return b_kn ? launch_contig_t<false, true>(a, rows_total, block_m, s)
-                : launch_contig_t<false, false>(a, rows_total, block_m, s);
+    if (fp8 && e8m0) return b_kn ? launch_contig_t<true, true, true>(a, rows_total, block_m, s)
+                                 : launch_contig_t<true, false, true>(a, rows_total, block_m, s);
+    if (fp8) return b_kn ? launch_contig_t<true, true, false>(a, rows_total, block_m, s)
+                         : launch_contig_t<true, false, false>(a, rows_total, block_m, s);
+    return b_kn ? launch_contig_t<false, true, false>(a, rows_total, block_m, s)
+                : launch_contig_t<false, false, false>(a, rows_total, block_m, s);
 }
 
 int masked_block_m() { return MaskedCfg<false>::BM; }

@@ -8,13 +8,14 @@ namespace moegg {
 
 struct ContigArgs {
     const void* A;
-    const float* A_scale;
+    const void* A_scale;          // fp32 [rows, K/128], or E8M0 bytes [K/128, rows_total]
     const void* B;
-    const float* B_scale;
+    const void* B_scale;          // fp32 or E8M0 bytes [G, K/128, N/128]
     void* C;
     const int32_t* counts;        // m_sizes, or masked_m for the masked layout
     const unsigned char* ws;      // scheduler output (contiguous layout)
     int G, K, N, cap;             // cap: masked layout only
+    int rows_total;               // contiguous layout: rows of A and C
 };
 
 struct KGroupedArgs {
@@ -30,7 +31,7 @@ hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int se
                         int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
                         hipStream_t stream);
 hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void* ws, hipStream_t stream);
-hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool b_kn, int64_t rows_total, int block_m,
+hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool b_kn, int64_t rows_total, int block_m,
                              hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);

@@ -65,6 +65,10 @@ def contiguous(**kw):
     (dict(layout=3), mg.ERR_INVALID_ARG),
     (dict(dtype=mg.FP8_E4M3), mg.ERR_INVALID_ARG),                 # fp8 without scales
     (dict(dtype=mg.FP8_E4M3, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_E8M0), mg.ERR_INVALID_ARG),            # E8M0 without scales
+    (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=768), mg.ERR_UNSUPPORTED),   # N % 512
+    (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=512, rows=130), mg.ERR_UNSUPPORTED),  # rows % 4
+    (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=ctypes.c_void_p(0x100002), N=512), mg.ERR_INVALID_ARG),
     (dict(block_m=32), mg.ERR_UNSUPPORTED),
     (dict(block_m=-2), mg.ERR_UNSUPPORTED),
     (dict(align=0), mg.ERR_INVALID_ARG),
@@ -91,6 +95,9 @@ def test_masked_validation():
     small_ws = list(ok)
     small_ws[12], small_ws[13] = FAKE, 16
     assert f(*small_ws) == mg.ERR_WORKSPACE
+    e8m0 = list(ok)                         # E8M0 scales: contiguous layout only
+    e8m0[1], e8m0[3], e8m0[9], e8m0[10] = FAKE, FAKE, 7168 - 7168 % 512, mg.FP8_E4M3_E8M0
+    assert f(*e8m0) == mg.ERR_UNSUPPORTED
 
 
 def test_k_grouped_validation():

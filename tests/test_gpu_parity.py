@@ -430,6 +430,63 @@ def test_contiguous_graph_replay(dtype):
         assert P.untouched_rows_ok(C, counts, 1), counts
 
 
+# ----------------------------------------------------------------- fp8 with E8M0 scales
+
+
+def run_contiguous_e8m0(w, inp, block_m, b_layout):
+    B = inp["B"] if b_layout == mg.B_KN else inp["B"].transpose(1, 2).contiguous()
+    C = P.sentinel_like((w.rows_total, w.N))
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.grouped_gemm_contiguous(inp["A"], B, C, inp["counts"], ws, A_scale=inp["A_scale_e8m0"],
+                               B_scale=inp["B_scale_e8m0"], seg_align=w.seg_align, block_m=block_m,
+                               b_layout=b_layout)
+    torch.cuda.synchronize()
+    return C, ws
+
+
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_contiguous_fp8_e8m0(block_m, b_layout):
+    """fp8 with power-of-two block scales given as E8M0 bytes (the MFMA applies
+    them): every valid row against the oracle run on the same scales as fp32."""
+    counts = [70, 0, 300, 6, 129, 3]                     # 508 rows: a multiple of 4, ragged tails
+    announce("contiguous fp8 e8m0", counts, "block_m", block_m, "layout", b_layout)
+    w = wl.Workload("e8", "contiguous", "fp8", counts, K=512, N=512, values="normal", seed=9, scales="e8m0")
+    inp = wl.materialize(w, "cuda")
+    C, ws = run_contiguous_e8m0(w, inp, block_m, b_layout)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts)
+    rows = list(range(w.rows_total))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    ref = P.oracle_contiguous_rows(w, cpu, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"e8m0 block_m={st.block_m} layout={b_layout} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL["fp8"], err
+
+
+def test_contiguous_fp8_e8m0_full_size():
+    """The Zipf fp8 workload with E8M0 scales, K-contiguous weights, device-chosen height."""
+    w = wl.workload(3)
+    w.scales = "e8m0"
+    announce("contiguous fp8 e8m0 full size", w.name)
+    inp = wl.materialize(w, "cuda")
+    C, ws = run_contiguous_e8m0(w, inp, 0, mg.B_NK)
+    st = mg.stats_read(ws)
+    P.check_stats(st, w.counts)
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256, extra=48, seed=13)
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+    del inp
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"e8m0 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL["fp8"], err
+    assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+
+
 # ----------------------------------------------------------------- K-grouped
 
 

@@ -7,7 +7,10 @@ operands in the formats the GEMM consumes:
 
 - bf16, rounded to nearest-even from fp32;
 - OCP e4m3fn codes with fp32 scales, one per 1x128 row group of the
-  activations and one per 128x128 block of the weights.
+  activations and one per 128x128 block of the weights;
+- the same codes with power-of-two scales, handed out twice: as fp32 values
+  and as E8M0 exponent bytes (2^(b - 127)), activation bytes transposed to
+  [K/128, rows].
 
 It holds none of the grouped GEMM's own arithmetic: no tiling, no padding
 accounting, no products or sums over K.
@@ -121,25 +124,42 @@ def _to_e4m3(x: torch.Tensor) -> torch.Tensor:
     return x.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
 
 
-def quantize_rows_e4m3(x: torch.Tensor):
+def _scale_for(amax: torch.Tensor, pow2: bool) -> torch.Tensor:
+    """amax/448, or with pow2 the smallest power of two >= amax/448 (so every
+    scaled value still fits e4m3); 1 for an all-zero group."""
+    s = amax / E4M3_MAX
+    if pow2:
+        s = torch.exp2(torch.ceil(torch.log2(s.clamp_min(2.0 ** -126))))
+    return torch.where(amax > 0, s, torch.ones_like(amax))
+
+
+def e8m0_bytes(s: torch.Tensor) -> torch.Tensor:
+    """Power-of-two fp32 scales -> E8M0 exponent bytes (2^(b - 127)); NaN -> 255."""
+    e = torch.round(torch.log2(s.nan_to_num(1.0))).to(torch.int32) + 127
+    e = torch.where(torch.isnan(s), torch.full_like(e, 255), e)
+    return e.clamp_(0, 255).to(torch.uint8)
+
+
+def quantize_rows_e4m3(x: torch.Tensor, pow2: bool = False):
     """Activations [..., K] -> (e4m3 codes [..., K], fp32 scales [..., K/128]).
 
     One scale per 1x128 group along K: s = amax/448 (s = 1 for an all-zero
-    group), code = e4m3(x / s).
+    group), or the power of two at or above it with pow2; code = e4m3(x / s).
     """
     *lead, k = x.shape
     assert k % SCALE_GROUP == 0
     g = x.float().reshape(*lead, k // SCALE_GROUP, SCALE_GROUP)
     amax = g.abs().amax(dim=-1, keepdim=True)
-    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    s = _scale_for(amax, pow2)
     q = _to_e4m3(g / s).reshape(*lead, k)
     return q, s.squeeze(-1).contiguous()
 
 
-def quantize_blocks_e4m3(w: torch.Tensor):
+def quantize_blocks_e4m3(w: torch.Tensor, pow2: bool = False):
     """Weights [G, K, N] -> (e4m3 codes [G, K, N], fp32 scales [G, K/128, N/128]).
 
-    One scale per 128x128 block of (K, N): s = amax/448 (1 if all zero).
+    One scale per 128x128 block of (K, N): s = amax/448 (1 if all zero), or
+    the power of two at or above it with pow2.
     Done one expert at a time to bound temporary memory.
     """
     G, K, N = w.shape
@@ -150,7 +170,7 @@ def quantize_blocks_e4m3(w: torch.Tensor):
     for e in range(G):
         blk = w[e].float().reshape(kb, SCALE_GROUP, nb, SCALE_GROUP)
         amax = blk.abs().amax(dim=(1, 3), keepdim=True)
-        se = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        se = _scale_for(amax, pow2)
         q[e] = _to_e4m3(blk / se).reshape(K, N)
         s[e] = se.reshape(kb, nb)
     return q, s
@@ -173,6 +193,7 @@ class Workload:
     Mw: int = 0                 # k_grouped: dW rows
     Nw: int = 0                 # k_grouped: dW cols
     values: str = "normal"      # "uniform" | "normal" | "normal_unit"
+    scales: str = "fp32"        # fp8 block scales: "fp32" | "e8m0" (powers of two)
     seed: int = 0
     extra: Dict = field(default_factory=dict)
 
@@ -230,7 +251,10 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
     contiguous: A [rows_total, K], B [G, K, N], counts int32 [G]
     masked:     A [G, cap, K],     B [G, K, N], counts int32 [G]
     k_grouped:  X [T, Mw], dY [T, Nw],          counts int32 [G]
-    fp8 adds A_scale [..., K/128] and B_scale [G, K/128, N/128].
+    fp8 adds A_scale [..., K/128] and B_scale [G, K/128, N/128] (fp32).  With
+    scales == "e8m0" those are powers of two, and A_scale_e8m0 [K/128, rows]
+    (contiguous layout) and B_scale_e8m0 [G, K/128, N/128] hold the same
+    scales as E8M0 bytes.
     Rows that belong to no expert (segment alignment gaps, capacity rows
     beyond the valid count) hold NaN when nan_padding is set, so that any
     leak of padding into a valid output shows.
@@ -258,13 +282,17 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
     else:
         a_nan = torch.isnan(a)
         a = a.nan_to_num(0.0)
-        qa, sa = quantize_rows_e4m3(a)
+        pow2 = wl.scales == "e8m0"
+        qa, sa = quantize_rows_e4m3(a, pow2)
         # keep padding rows poisoned: e4m3fn NaN code plus a NaN scale
         qa.view(torch.uint8)[a_nan] = 0x7F
         sa[a_nan.reshape(*a_nan.shape[:-1], -1, SCALE_GROUP).any(-1)] = float("nan")
         del a
-        qb, sb = quantize_blocks_e4m3(b)
+        qb, sb = quantize_blocks_e4m3(b, pow2)
         out["A"], out["A_scale"], out["B"], out["B_scale"] = qa, sa, qb, sb
+        if pow2:
+            out["A_scale_e8m0"] = e8m0_bytes(sa.reshape(-1, sa.shape[-1]).t().contiguous())
+            out["B_scale_e8m0"] = e8m0_bytes(sb)
     return out
 
 
