@@ -102,7 +102,7 @@ def traffic_for(w: wl.Workload, b_layout: int):
         return None
     with open(path) as f:
         t = json.load(f)
-    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}"
+    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}" + ("|e8m0" if w.scales == "e8m0" else "")
     e = t.get("entries", {}).get(key)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
