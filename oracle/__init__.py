@@ -10,9 +10,12 @@ Parts:
 - oracle.c with gemm.py: fp64 per-expert dot products for the contiguous,
   masked and K-grouped layouts.  They read the same bf16 / e4m3 bits the GPU
   receives and decode them with their own decoders.
+- fp4.py: fp8 activations times packed E2M1 weights with power-of-two block
+  scales (the contiguous layout), with its own E2M1 decoder.
 
 Every function states the page and section it follows.  Parity pins live in
 tests/test_oracle_*.py and tests/golden/.
 """
 from . import accounting  # noqa: F401
 from . import gemm  # noqa: F401
+from . import fp4  # noqa: F401

@@ -1,0 +1,85 @@
+"""fp8 activations times fp4 (E2M1) weights with power-of-two block scales:
+the plain per-expert definition in fp64 (test infrastructure only).
+
+The DeepGEMM record lists low-precision weights (FP8 x FP4) next to the
+SM100 UE8M0 scale format; this is that product written out.  For each valid
+row R of expert e and each column n:
+
+    C[R, n] = sum_k (dec8(A[R, k]) * sa[R, k/128]) * (dec4(W[e, n, k]) * sb[e, k/128, n/128])
+
+with dec8 the oracle's own OCP E4M3FN decoder (gemm.dec_e4m3) and dec4 the
+OCP E2M1 decoder below.  Weights are stored [G, N, K/2], two codes per byte,
+element 2i in the low nibble.  A library matmul serves as the sum over each
+128-wide K group; nothing else is blocked or reordered.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+import torch
+
+from . import accounting as acc
+from . import gemm as og
+
+
+def e2m1_value(code: int) -> float:
+    """OCP E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0
+    is subnormal (0 or 0.5); no infinities or NaN."""
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * 0.5 * m
+    return s * (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+
+
+E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def dec_e2m1_packed(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] -> float64 [..., K]; element 2i is the low nibble of byte i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.float64)
+    out[..., 0::2] = E2M1[p & 0xF]
+    out[..., 1::2] = E2M1[p >> 4]
+    return out
+
+
+def _e4m3_table() -> np.ndarray:
+    return np.array([og.dec_e4m3(c) for c in range(256)], dtype=np.float64)
+
+
+def contiguous_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, W_scale: torch.Tensor,
+                       counts: Sequence[int], rows: Sequence[int], seg_align: int = 1) -> np.ndarray:
+    """Rows `rows` of C for the contiguous layout (segment starts as in the tile
+    list of the accounting module).  A: e4m3 codes [rows_total, K]; A_scale fp32
+    [rows_total, K/128]; W: packed E2M1 [G, N, K/2]; W_scale fp32 [G, K/128, N/128]."""
+    dec8 = _e4m3_table()
+    a_codes = A.contiguous().view(torch.uint8).numpy()
+    sa = A_scale.double().numpy()
+    w = W.contiguous().numpy()
+    sb = W_scale.double().numpy()
+    K = a_codes.shape[1]
+    N = w.shape[1]
+    offs = acc.segment_offsets(counts, seg_align)
+    out = np.zeros((len(rows), N), dtype=np.float64)
+    expert_of = {}
+    for e, c in enumerate(counts):
+        for r in range(offs[e], offs[e] + c):
+            expert_of[r] = e
+    by_e = {}
+    for i, r in enumerate(rows):
+        by_e.setdefault(expert_of[r], []).append(i)
+    for e, idx in by_e.items():
+        rr = [rows[i] for i in idx]
+        a = dec8[a_codes[rr]]                                  # [m, K]
+        we = dec_e2m1_packed(w[e])                             # [N, K]
+        res = np.zeros((len(rr), N), dtype=np.float64)
+        for kb in range(K // 128):
+            ks = slice(kb * 128, (kb + 1) * 128)
+            part = a[:, ks] @ we[:, ks].T                      # [m, N], the group's sum
+            colscale = np.repeat(sb[e, kb], 128)[:N]           # weight block scale per column
+            res += part * sa[rr, kb][:, None] * colscale[None, :]
+        out[idx] = res
+    return out

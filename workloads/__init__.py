@@ -10,7 +10,9 @@ operands in the formats the GEMM consumes:
   activations and one per 128x128 block of the weights;
 - the same codes with power-of-two scales, handed out twice: as fp32 values
   and as E8M0 exponent bytes (2^(b - 127)), activation bytes transposed to
-  [K/128, rows].
+  [K/128, rows];
+- OCP E2M1 (fp4) weight codes with power-of-two 128x128 block scales, packed
+  two per byte along K ([G, N, K/2], element 2i in the low nibble).
 
 It holds none of the grouped GEMM's own arithmetic: no tiling, no padding
 accounting, no products or sums over K.
@@ -39,6 +41,9 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+E2M1_MAX = 6.0
+# E2M1 magnitude -> code (sign in bit 3)
+_E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
 SCALE_GROUP = 128
 
 # ---------------------------------------------------------------- histograms
@@ -140,6 +145,42 @@ def e8m0_bytes(s: torch.Tensor) -> torch.Tensor:
     return e.clamp_(0, 255).to(torch.uint8)
 
 
+def to_e2m1_codes(x: torch.Tensor) -> torch.Tensor:
+    """Round (already scaled) values to the nearest E2M1 value, ties to the even
+    code, clamped to +-6; returns codes 0..15 (uint8, sign in bit 3).  The grid
+    spacing is 0.5 below 2, 1 on [2, 4) and 2 on [4, 6]; torch.round rounds half
+    to even, and an even multiple of the spacing is an even code."""
+    a = x.abs().clamp(max=E2M1_MAX)
+    q = torch.where(a < 2, torch.round(a * 2) / 2, torch.where(a < 4, torch.round(a), torch.round(a / 2) * 2))
+    mag = torch.zeros_like(q, dtype=torch.uint8)
+    for v, c in _E2M1_CODE.items():
+        mag[q == v] = c
+    return mag | ((x < 0).to(torch.uint8) << 3)
+
+
+def quantize_blocks_e2m1(w: torch.Tensor):
+    """Weights [G, K, N] -> (packed E2M1 codes [G, N, K/2], fp32 scales [G, K/128, N/128]).
+
+    One power-of-two scale per 128x128 block of (K, N): the smallest 2^j with
+    amax / 2^j <= 6 (1 for an all-zero block).  Codes are stored K-contiguous,
+    two per byte, element 2i in the low nibble."""
+    G, K, N = w.shape
+    assert K % SCALE_GROUP == 0 and N % SCALE_GROUP == 0
+    kb, nb = K // SCALE_GROUP, N // SCALE_GROUP
+    packed = torch.empty((G, N, K // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((G, kb, nb), dtype=torch.float32, device=w.device)
+    for e in range(G):
+        blk = w[e].float().reshape(kb, SCALE_GROUP, nb, SCALE_GROUP)
+        amax = blk.abs().amax(dim=(1, 3), keepdim=True)
+        se = amax / E2M1_MAX
+        se = torch.exp2(torch.ceil(torch.log2(se.clamp_min(2.0 ** -126))))
+        se = torch.where(amax > 0, se, torch.ones_like(amax))
+        codes = to_e2m1_codes(blk / se).reshape(K, N).t().contiguous()      # [N, K]
+        packed[e] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        s[e] = se.reshape(kb, nb)
+    return packed, s
+
+
 def quantize_rows_e4m3(x: torch.Tensor, pow2: bool = False):
     """Activations [..., K] -> (e4m3 codes [..., K], fp32 scales [..., K/128]).
 
@@ -194,6 +235,7 @@ class Workload:
     Nw: int = 0                 # k_grouped: dW cols
     values: str = "normal"      # "uniform" | "normal" | "normal_unit"
     scales: str = "fp32"        # fp8 block scales: "fp32" | "e8m0" (powers of two)
+    weights: str = "e4m3"       # fp8 workloads' weight codes: "e4m3" | "e2m1" (fp4, needs e8m0 scales)
     seed: int = 0
     extra: Dict = field(default_factory=dict)
 
@@ -288,7 +330,11 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
         qa.view(torch.uint8)[a_nan] = 0x7F
         sa[a_nan.reshape(*a_nan.shape[:-1], -1, SCALE_GROUP).any(-1)] = float("nan")
         del a
-        qb, sb = quantize_blocks_e4m3(b, pow2)
+        if wl.weights == "e2m1":
+            assert pow2, "fp4 weights come with power-of-two (E8M0) scales"
+            qb, sb = quantize_blocks_e2m1(b)
+        else:
+            qb, sb = quantize_blocks_e4m3(b, pow2)
         out["A"], out["A_scale"], out["B"], out["B_scale"] = qa, sa, qb, sb
         if pow2:
             out["A_scale_e8m0"] = e8m0_bytes(sa.reshape(-1, sa.shape[-1]).t().contiguous())
