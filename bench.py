@@ -79,9 +79,11 @@ def algorithmic_bytes(w: wl.Workload) -> int:
     if w.layout == "k_grouped":
         return U * (w.Mw + w.Nw) * 2 + w.G * w.Mw * w.Nw * 4
     esz = 1 if w.dtype == "fp8" else 2
-    b = active * w.K * w.N * esz + U * w.K * esz + U * w.N * 2
+    w_bytes = w.K * w.N // 2 if w.weights == "e2m1" else w.K * w.N * esz
+    b = active * w_bytes + U * w.K * esz + U * w.N * 2
     if w.dtype == "fp8":
-        b += U * (w.K // 128) * 4 + active * (w.K // 128) * (w.N // 128) * 4
+        ssz = 1 if w.scales == "e8m0" else 4
+        b += U * (w.K // 128) * ssz + active * (w.K // 128) * (w.N // 128) * ssz
     return b
 
 
@@ -102,7 +104,8 @@ def traffic_for(w: wl.Workload, b_layout: int):
         return None
     with open(path) as f:
         t = json.load(f)
-    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}" + ("|e8m0" if w.scales == "e8m0" else "")
+    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}" + ("|e8m0" if w.scales == "e8m0" else "") + \
+        ("|e2m1" if w.weights == "e2m1" else "")
     e = t.get("entries", {}).get(key)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
@@ -117,20 +120,31 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
     if w.layout != "contiguous":
         return None
     cpu = {k: (v.cpu().contiguous() if v is not None else None) for k, v in inp.items()}
-    if cpu["B"].shape[1] != w.K:                     # weights were repacked to [G,N,K]
-        cpu["B"] = cpu["B"].transpose(1, 2).contiguous()
+    if w.weights == "e2m1":
+        from oracle import fp4
+
+        def run(rows):
+            fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], w.counts, rows,
+                                   seg_align=w.seg_align)
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    else:
+        if cpu["B"].shape[1] != w.K:                     # weights were repacked to [G,N,K]
+            cpu["B"] = cpu["B"].transpose(1, 2).contiguous()
+
+        def run(rows):
+            og.contiguous(cpu["A"], cpu["B"], w.counts, rows, seg_align=w.seg_align,
+                          A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
+        threads = og.threads()
     rows = sample_rows_contiguous(w.counts, w.seg_align, 256, extra=4096, seed=99)
-    threads = og.threads()
     probe = rows[:threads]
     t0 = time.perf_counter()
-    og.contiguous(cpu["A"], cpu["B"], w.counts, probe, seg_align=w.seg_align,
-                  A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
+    run(probe)
     dt = time.perf_counter() - t0
     n = max(threads, min(len(rows), int(target_s / max(dt, 1e-6) * len(probe)) // threads * threads))
     sample = rows[:n]
     t0 = time.perf_counter()
-    og.contiguous(cpu["A"], cpu["B"], w.counts, sample, seg_align=w.seg_align,
-                  A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
+    run(sample)
     dt = time.perf_counter() - t0
     flops = 2.0 * len(sample) * w.K * w.N
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
@@ -154,6 +168,9 @@ def main():
     ap.add_argument("--scales", choices=("fp32", "e8m0"), default="fp32",
                     help="fp8 block scales: fp32 (the workload as stated, promoted on the VALU), or powers of two "
                          "as E8M0 bytes, applied by the MFMA (contiguous fp8 workloads only)")
+    ap.add_argument("--weights", choices=("e4m3", "e2m1"), default="e4m3",
+                    help="fp8 workload weights: e4m3 (as stated), or packed fp4 E2M1 [G,N,K/2] with E8M0 scales "
+                         "(implies --scales e8m0; contiguous fp8 workloads only)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
@@ -175,6 +192,9 @@ def main():
         sys.exit(2)
     mg.lib()
     w = wl.workload(args.config)
+    if args.weights == "e2m1":
+        args.scales = "e8m0"
+        w.weights = "e2m1"
     if args.scales == "e8m0":
         if w.dtype != "fp8" or w.layout != "contiguous":
             print("--scales e8m0 applies to the contiguous fp8 workload only", file=sys.stderr)
@@ -185,8 +205,11 @@ def main():
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
     layout = args.b_layout if args.b_layout != "auto" else ("kn" if w.layout == "masked" else "nk")
+    if w.weights == "e2m1" and layout != "nk":
+        print("fp4 weights are stored [G,N,K/2] only", file=sys.stderr)
+        sys.exit(2)
     b_layout = mg.B_NK if layout == "nk" else mg.B_KN
-    if b_layout == mg.B_NK and "B" in inp:
+    if b_layout == mg.B_NK and "B" in inp and w.weights != "e2m1":
         inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
     torch.cuda.synchronize()
 
@@ -250,11 +273,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if w.dtype == "fp8" else "bf16",
+        "dtype": ("fp8_e4m3 x fp4_e2m1" if w.weights == "e2m1" else "fp8_e4m3") if w.dtype == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
-                   "weights": "[G,N,K]" if b_layout == mg.B_NK else "[G,K,N]",
+                   "weights": ("[G,N,K/2] packed e2m1" if w.weights == "e2m1" else "[G,N,K]")
+                   if b_layout == mg.B_NK else "[G,K,N]",
                    "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else "fp32")
                    if w.dtype == "fp8" else None,
                    "cache": "cold (512 MiB written between steps)" if args.cold else "warm"},

@@ -49,8 +49,20 @@ typedef enum {
  * applies them itself (V_MFMA_SCALE_F32_16X16X128_F8F6F4), so nothing is
  * promoted on the VALU.  Its activation scales are stored transposed:
  * [K/128, rows] (DeepGEMM's MN-major scale layout), four rows per 32-bit word.
- * Contiguous layout only. */
-typedef enum { MOEGG_BF16 = 0, MOEGG_FP8_E4M3 = 1, MOEGG_FP8_E4M3_E8M0 = 2 } moegg_dtype_t;
+ * Contiguous layout only.
+ * MOEGG_FP8_E4M3_FP4_E2M1 is the low-precision-weight case the DeepGEMM
+ * record lists for SM100 (FP8 x FP4): activations as for
+ * MOEGG_FP8_E4M3_E8M0, weights as OCP E2M1 (fp4: sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two per
+ * byte, element 2i in the low nibble, stored [G, N, K/2] (b_layout must be
+ * MOEGG_B_NK), with E8M0 weight-block scales [G, K/128, N/128].  The same
+ * gfx950 MFMA takes the fp4 operand directly.  Contiguous layout only. */
+typedef enum {
+    MOEGG_BF16 = 0,
+    MOEGG_FP8_E4M3 = 1,
+    MOEGG_FP8_E4M3_E8M0 = 2,
+    MOEGG_FP8_E4M3_FP4_E2M1 = 3
+} moegg_dtype_t;
 
 /* How each expert's weight B_e is stored.
  *   MOEGG_B_KN: B[G, K, N], N contiguous.
@@ -146,8 +158,10 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  *            group.  MOEGG_FP8_E4M3_E8M0: E8M0 bytes [K/128, rows_total]
  *            (transposed).  NULL for bf16.
  *   B        [G, K, N] or [G, N, K] (b_layout), same dtype as A.
+ *            MOEGG_FP8_E4M3_FP4_E2M1: packed E2M1 bytes [G, N, K/2].
  *   B_scale  MOEGG_FP8_E4M3: fp32 [G, K/128, N/128], one per 128x128 block.
- *            MOEGG_FP8_E4M3_E8M0: E8M0 bytes, same shape.  NULL for bf16.
+ *            MOEGG_FP8_E4M3_E8M0 and MOEGG_FP8_E4M3_FP4_E2M1: E8M0 bytes,
+ *            same shape.  NULL for bf16.
  *   C        bf16 [rows_total, N], row-major.  Only the rows of valid
  *            segments are written.  Other rows keep their contents.
  *   m_sizes  int32 [G] on the device.
@@ -159,7 +173,8 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
  * the two powers of two instead: the same value up to fp32 rounding order.
  * Constraints: K % 128 == 0 and N % 256 == 0 for fp8.  K % 64 == 0 and
  * N % 256 == 0 for bf16.  E8M0 scales also need N % 512 == 0, N <= 32768
- * and rows_total % 4 == 0 (UNSUPPORTED otherwise).  16-byte aligned
+ * and rows_total % 4 == 0 (UNSUPPORTED otherwise); fp4 weights also need
+ * b_layout = MOEGG_B_NK (UNSUPPORTED otherwise).  16-byte aligned
  * operands, 4-byte aligned scales.  G = 1..4096.
  * block_m: 64, 128 or 256; 0 = choose one height on the device from the
  * histogram; MOEGG_BLOCK_M_PER_EXPERT = per-expert heights (see its
@@ -207,7 +222,8 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
  * computes only the valid portions, with no CPU sync).
  *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (fp8) or NULL.
- *            MOEGG_FP8_E4M3_E8M0 is not supported here (UNSUPPORTED).
+ *            MOEGG_FP8_E4M3_E8M0 and MOEGG_FP8_E4M3_FP4_E2M1 are not
+ *            supported here (UNSUPPORTED).
  *   B        as for the contiguous call.  B_scale as for the contiguous call.
  *   C        bf16 [G, cap, N].  Only rows r < masked_m[e] are written.
  *   masked_m int32 [G] on the device, read by the kernel at run time.

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libmoegg.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moegg.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-BF16, FP8_E4M3, FP8_E4M3_E8M0 = 0, 1, 2
+BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1 = 0, 1, 2, 3
 B_KN, B_NK = 0, 1
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP = 0x1, 0x2, 0x4
 Q_VALUES = (8, 16, 32, 64, 128, 256)
@@ -122,11 +122,14 @@ def _check(status: int, what: str):
         raise MoeggError(status, what)
 
 
-def _dtype(t: torch.Tensor, scale: Optional[torch.Tensor] = None) -> int:
-    """Operand type code; fp8 with uint8 (E8M0) scales is MOEGG_FP8_E4M3_E8M0."""
+def _dtype(t: torch.Tensor, scale: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None) -> int:
+    """Operand type code: fp8 with uint8 (E8M0) scales is MOEGG_FP8_E4M3_E8M0,
+    and with uint8 weights (packed E2M1 [G, N, K/2]) MOEGG_FP8_E4M3_FP4_E2M1."""
     if t.dtype == torch.bfloat16:
         return BF16
     if t.dtype == torch.float8_e4m3fn:
+        if w is not None and w.dtype == torch.uint8:
+            return FP8_E4M3_FP4_E2M1
         return FP8_E4M3_E8M0 if scale is not None and scale.dtype == torch.uint8 else FP8_E4M3
     raise TypeError(f"bf16 or float8_e4m3fn operands expected, got {t.dtype}")
 
@@ -154,7 +157,7 @@ def grouped_gemm_contiguous_scheduled(A, B, C, G: int, ws, A_scale=None, B_scale
     K = A.shape[1]
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_contiguous_scheduled(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, A.shape[0], K, N, _dtype(A, A_scale), b_layout, block_m,
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, A.shape[0], K, N, _dtype(A, A_scale, B), b_layout, block_m,
         _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_contiguous_scheduled")
 
 
@@ -165,7 +168,7 @@ def grouped_gemm_contiguous(A, B, C, m_sizes, ws, A_scale=None, B_scale=None, se
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_contiguous(
         _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), m_sizes.numel(), A.shape[0], K, N,
-        seg_align, _dtype(A, A_scale), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
+        seg_align, _dtype(A, A_scale, B), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
         "moegg_grouped_gemm_contiguous")
 
 
@@ -175,7 +178,7 @@ def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, 
     G, cap, K = A.shape
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_masked(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, _dtype(A, A_scale), b_layout,
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, _dtype(A, A_scale, B), b_layout,
         _p(ws), 0 if ws is None else ws.numel(), _stream(stream)), "moegg_grouped_gemm_masked")
 
 

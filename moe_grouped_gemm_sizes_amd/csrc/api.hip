@@ -34,24 +34,31 @@ moegg_status_t hip_status(hipError_t e, const char* what) {
     return MOEGG_ERR_HIP;
 }
 
+// Block scales stored as E8M0 exponent bytes.
+bool e8m0_scales(moegg_dtype_t d) { return d == MOEGG_FP8_E4M3_E8M0 || d == MOEGG_FP8_E4M3_FP4_E2M1; }
+
 // Shared checks for the contiguous and masked calls.
 moegg_status_t check_common(const void* A, const void* A_scale, const void* B, const void* B_scale,
                             const void* C, int G, int K, int N, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
                             int col_tile) {
     if (!A || !B || !C) return MOEGG_ERR_INVALID_ARG;
     if (G < 1 || G > kMaxExperts || K < 1 || N < 1) return MOEGG_ERR_INVALID_ARG;
-    if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3 && dtype != MOEGG_FP8_E4M3_E8M0) return MOEGG_ERR_INVALID_ARG;
+    if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3 && dtype != MOEGG_FP8_E4M3_E8M0 &&
+        dtype != MOEGG_FP8_E4M3_FP4_E2M1)
+        return MOEGG_ERR_INVALID_ARG;
     if (b_layout != MOEGG_B_KN && b_layout != MOEGG_B_NK) return MOEGG_ERR_INVALID_ARG;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
+    const bool w4 = dtype == MOEGG_FP8_E4M3_FP4_E2M1;
     if (dtype != MOEGG_BF16) {
         if (!A_scale || !B_scale) return MOEGG_ERR_INVALID_ARG;
         if (!aligned(A_scale, 4) || !aligned(B_scale, 4)) return MOEGG_ERR_INVALID_ARG;
     }
+    if (w4 && b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;      // packed E2M1 is K-contiguous
     // E8M0 scale rows are read four bytes at a time: N / 128 bytes per weight-scale row
-    if (dtype == MOEGG_FP8_E4M3_E8M0 && (N % 512 != 0 || N / 128 > 256)) return MOEGG_ERR_UNSUPPORTED;
+    if (e8m0_scales(dtype) && (N % 512 != 0 || N / 128 > 256)) return MOEGG_ERR_UNSUPPORTED;
     if (K % (128 / esz) != 0 || N % col_tile != 0) return MOEGG_ERR_UNSUPPORTED;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return MOEGG_ERR_INVALID_ARG;
-    if ((int64_t)K * N * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if ((w4 ? (int64_t)K * N / 2 : (int64_t)K * N * esz) > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     return MOEGG_OK;
 }
 
@@ -105,7 +112,7 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX || seg_align < 1) return MOEGG_ERR_INVALID_ARG;
-    if (dtype == MOEGG_FP8_E4M3_E8M0 && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (e8m0_scales(dtype) && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
@@ -116,8 +123,8 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
     hipError_t e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, block_m, N / 256, 0, ws, L.max_tiles, s);
     if (e != hipSuccess) return hip_status(e, "scheduler launch");
     ContigArgs a{A, A_scale, B, B_scale, C, m_sizes, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
-    e = launch_contiguous(a, dtype != MOEGG_BF16, dtype == MOEGG_FP8_E4M3_E8M0, b_layout == MOEGG_B_KN, rows_total,
-                          block_m, s);
+    e = launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
+                          b_layout == MOEGG_B_KN, rows_total, block_m, s);
     if (debug_on())
         fprintf(stderr, "moegg: contiguous G=%d rows=%lld K=%d N=%d align=%d dtype=%d b_layout=%d block_m=%d\n", G,
                 (long long)rows_total, K, N, seg_align, (int)dtype, (int)b_layout, block_m);
@@ -132,15 +139,15 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
-    if (dtype == MOEGG_FP8_E4M3_E8M0 && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (e8m0_scales(dtype) && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
     ContigArgs a{A, A_scale, B, B_scale, C, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
-    return hip_status(launch_contiguous(a, dtype != MOEGG_BF16, dtype == MOEGG_FP8_E4M3_E8M0, b_layout == MOEGG_B_KN,
-                                        rows_total, block_m, (hipStream_t)stream),
+    return hip_status(launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
+                                        b_layout == MOEGG_B_KN, rows_total, block_m, (hipStream_t)stream),
                       "scheduled contiguous GEMM launch");
 }
 
@@ -151,7 +158,7 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     if (!masked_m || !aligned(masked_m, 4)) return MOEGG_ERR_INVALID_ARG;
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, masked_block_n());
     if (st != MOEGG_OK) return st;
-    if (dtype == MOEGG_FP8_E4M3_E8M0) return MOEGG_ERR_UNSUPPORTED;     // contiguous layout only
+    if (e8m0_scales(dtype)) return MOEGG_ERR_UNSUPPORTED;     // contiguous layout only
     if (cap < 1 || (int64_t)G * cap > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
     if ((int64_t)masked_block_m() * K * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;

@@ -143,10 +143,43 @@ __device__ __forceinline__ v8i frag_k_fp8(const char* tile, int row) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// K-contiguous tile, fp8, in the MFMA's own K order: lane (row r16, group g)
+// gets bytes [16g, 16g+16) and [64+16g, 64+16g+16).  Measured on gfx950 with
+// one-hot operands: the 16x16x128 MFMA takes an e4m3 operand's 32 bytes per
+// lane as k = 16g + (0..15), then 64 + 16g + (0..15), but an E2M1 operand's
+// 16 bytes as k = 32g + (0..31).  Two e4m3 operands read alike (frag_k_fp8)
+// pair up whatever the order; against fp4 weights the activations are read
+// this way.
+__device__ __forceinline__ v8i frag_k_fp8_mfma_order(const char* tile, int row) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int s = swz_k<1>(row);
+    v4i lo = lds_read_b128(tile + row * 128 + ((g ^ s) << 4));
+    v4i hi = lds_read_b128(tile + row * 128 + (((g + 4) ^ s) << 4));
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
 // K-contiguous tile, bf16, half-step kk: lane gets k = 32kk + 8g + (0..7).
 __device__ __forceinline__ v4i frag_k_bf16(const char* tile, int row, int kk) {
     const int g = (threadIdx.x & 63) >> 4;
     return lds_read_b128(tile + row * 128 + (((4 * kk + g) ^ swz_k<2>(row)) << 4));
+}
+
+// Swizzle of 16-byte chunks in a K-contiguous fp4 weight tile (64-byte rows:
+// 128 E2M1 values, two per byte).  A fragment read has lane (r = l % 16,
+// g = l / 16) fetch chunk g of row r; XOR-ing it with bits 1..2 of the row,
+// flipped by bit 3, puts the 16 rows a chunk index is read from on 16
+// distinct 16-byte slots of 256 bytes, and any 8 consecutive rows on 8
+// distinct slots of 128 bytes.
+__device__ __forceinline__ int swz_w4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// K-contiguous fp4 tile: lane (row r16, group g) gets the 16 bytes holding
+// k = 32g + (0..31), element 2i in the low nibble of byte i -- the E2M1
+// operand layout of the 16x16x128 MFMA (8 values per register, lowest
+// nibble first).  The upper half of the operand is unused for fp4.
+__device__ __forceinline__ v8i frag_k_fp4(const char* tile, int row) {
+    const int g = (threadIdx.x & 63) >> 4;
+    v4i v = lds_read_b128(tile + row * 64 + ((g ^ swz_w4(row)) << 4));
+    return v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
 }
 
 // MN-contiguous tile, fp8: lane (col n0 + l%16, group g) gets the 32 bytes
@@ -206,12 +239,17 @@ __device__ __forceinline__ int block_to_item(int b) {
 // for fp8, that step's scales: [activations | weights | scales].  The ring has
 // as many stages as fit in the 160 KB of LDS, up to four: loads run
 // STAGES - 1 steps ahead of the MFMAs.
-template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_ = 1, bool E8M0_ = false>
+template <bool FP8_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int OCC_ = 1, bool E8M0_ = false,
+          bool W4_ = false>
 struct GCfg {
     static constexpr bool FP8 = FP8_;
     // fp8 block scales as E8M0 exponent bytes, applied by the MFMA itself
     // (V_MFMA_SCALE_F32_16X16X128_F8F6F4) instead of promoted on the VALU
     static constexpr bool E8M0 = E8M0_;
+    // weights as packed E2M1 (fp4), K-contiguous: a K step's weight row is
+    // 64 bytes; the MFMA takes them as its fp4 operand
+    static constexpr bool W4 = W4_;
+    static constexpr int WROW = W4 ? 64 : 128;         // weight bytes per row per K step
     static constexpr int OCC = OCC_;                   // workgroups per CU the LDS ring leaves room for
     static constexpr int ESZ = FP8 ? 1 : 2;            // bytes per element
     static constexpr int KSTEP = 128 / ESZ;            // K elements per step
@@ -221,7 +259,7 @@ struct GCfg {
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int MB = WTM / 16, NB = WTN / 16;
-    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * WROW;
     // fp8 scales of the step: one per tile row (activations), then 256 bytes of
     // weight-block scales.  fp32: BM floats, then 64 float slots (BN / 128 of
     // them used).  E8M0: the tile's rows' bytes from a 4-byte-aligned start
@@ -242,14 +280,15 @@ struct GCfg {
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(!FP8 || (BM >= 64 && BM / 64 < WAVES), "one activation-scale DMA per 64 rows, one wave left for weight scales");
     static_assert(!E8M0 || (FP8 && WAVES >= 3), "E8M0: two waves load activation-scale bytes, the others weight-scale bytes");
+    static_assert(!W4 || E8M0, "fp4 weights come with E8M0 scales");
     static_assert(!FP8 || 128 % WTN == 0 || WTN % 128 == 0, "fp8 weight scale blocks");
     static_assert(STAGES >= 2 && LDS_BYTES * OCC <= 160 * 1024, "LDS budget");
 };
 
 // Contiguous: 256-column tiles, every wave tile 64 rows tall.
-template <bool FP8, bool E8 = false> using Contig256 = GCfg<FP8, 256, 256, 4, 2, 1, E8>;
-template <bool FP8, bool E8 = false> using Contig128 = GCfg<FP8, 128, 256, 2, 4, 1, E8>;
-template <bool FP8, bool E8 = false> using Contig64 = GCfg<FP8, 64, 256, 1, 8, 1, E8>;
+template <bool FP8, bool E8 = false, bool W4 = false> using Contig256 = GCfg<FP8, 256, 256, 4, 2, 1, E8, W4>;
+template <bool FP8, bool E8 = false, bool W4 = false> using Contig128 = GCfg<FP8, 128, 256, 2, 4, 1, E8, W4>;
+template <bool FP8, bool E8 = false, bool W4 = false> using Contig64 = GCfg<FP8, 64, 256, 1, 8, 1, E8, W4>;
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -330,7 +369,15 @@ struct TileGemm {
     __device__ __forceinline__ void issue_w(char* __restrict__ stage, int ks) const {
         const int tid = threadIdx.x, wave = tid >> 6;
         char* base = stage + C::A_BYTES;
-        if constexpr (B_KN) {
+        if constexpr (C::W4) {
+            // 64-byte rows, four lanes per row: DMA J fills rows 16 (J * WAVES + wave)
+            // and the 15 after it; the K step rides in soffset
+            static_assert(!B_KN, "fp4 weights are K-contiguous");
+            const int f = J * C::THREADS + tid;
+            const int row = f >> 2;
+            load16_to_lds_so(rb, row * b_row_bytes + (((f & 3) ^ swz_w4(row)) << 4), ks * C::WROW,
+                             base + (J * C::THREADS + wave * 64) * 16);
+        } else if constexpr (B_KN) {
             constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
             const int r0 = tid / CPR;
             const int c = (tid % CPR) ^ swz_mn<C::ESZ, RB>(r0 + J * RPO);
@@ -393,15 +440,21 @@ struct TileGemm {
             const MOEGG_LDS unsigned char* sbb = (const MOEGG_LDS unsigned char*)(tb + C::B_BYTES + C::SA_BYTES) + sb_col;
             auto fragb = [&](int i) -> v8i {
                 const int n0 = wn * C::WTN + i * 16;
-                if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
+                if constexpr (C::W4) return frag_k_fp4(tb, n0 + r16);
+                else if constexpr (B_KN) return frag_mn_fp8<C::BN>(tb, n0);
                 else return frag_k_fp8(tb, n0 + r16);
             };
+            // operand formats: 4 = E2M1 (fp4) weights, 0 = e4m3
+            constexpr int FMT_W = C::W4 ? 4 : 0;
             v8i xb[2];
             xb[0] = fragb(0);
             v8i ya[MBA];
             int sbj[MBA];
 #pragma unroll
-            for (int j = 0; j < MBA; ++j) ya[j] = frag_k_fp8(ta, wm * C::WTM + j * 16 + r16);
+            for (int j = 0; j < MBA; ++j) {
+                if constexpr (C::W4) ya[j] = frag_k_fp8_mfma_order(ta, wm * C::WTM + j * 16 + r16);
+                else ya[j] = frag_k_fp8(ta, wm * C::WTM + j * 16 + r16);
+            }
 #pragma unroll
             for (int j = 0; j < MBA; ++j) sbj[j] = sab[wm * C::WTM + j * 16 + r16];
             int sai[NSB];
@@ -413,8 +466,8 @@ struct TileGemm {
                 constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
 #pragma unroll
                 for (int j = 0; j < MBA; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xb[i & 1], ya[j], acc[i][j], 0, 0,
-                                                                                 0, sai[sb], 0, sbj[j]);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xb[i & 1], ya[j], acc[i][j], FMT_W,
+                                                                                 0, 0, sai[sb], 0, sbj[j]);
                 if constexpr (i == 0) issue_all(wr, next);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -560,9 +613,14 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
     TileGemm<C, B_KN> tg;
     tg.a_row_bytes = (uint32_t)p.K * C::ESZ;
     tg.ra = make_rsrc((const char*)p.A + (size_t)row_start * tg.a_row_bytes, (uint32_t)rows_valid * tg.a_row_bytes);
-    const size_t b_expert_bytes = (size_t)p.K * p.N * C::ESZ;
+    const size_t b_expert_bytes = C::W4 ? (size_t)p.K * p.N / 2 : (size_t)p.K * p.N * C::ESZ;
     const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
-    if constexpr (B_KN) {
+    if constexpr (C::W4) {
+        // packed E2M1 [G, N, K/2]: this column tile's BN rows of K/2 bytes
+        tg.b_row_bytes = (uint32_t)p.K / 2;
+        tg.rb = make_rsrc(b_base + (size_t)n0 * tg.b_row_bytes, (uint32_t)C::BN * tg.b_row_bytes);
+        tg.b_col_byte = 0;
+    } else if constexpr (B_KN) {
         tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
         tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
         tg.b_col_byte = (uint32_t)n0 * C::ESZ;
@@ -647,7 +705,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
 // does not pay for a 256-row tile, and the 128- and 64-row configurations'
 // deeper stage rings keep their loads further ahead.  All three share one
 // launch; the configuration is uniform per workgroup.
-template <bool FP8, bool B_KN, bool E8>
+template <bool FP8, bool B_KN, bool E8, bool W4>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / 256;
@@ -660,9 +718,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigA
     int rt, ct;
     item_to_tiles(item, n_rt, n_ct, rt, ct);
     const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
-    if (t.rows_valid > 128) contig_tile<Contig256<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else if (t.rows_valid > 64) contig_tile<Contig128<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else contig_tile<Contig64<FP8, E8>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    if (t.rows_valid > 128)
+        contig_tile<Contig256<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else if (t.rows_valid > 64)
+        contig_tile<Contig128<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    else
+        contig_tile<Contig64<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
 }
 
 // ---------------------------------------------------------------- K-grouped
@@ -795,37 +856,39 @@ static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
 
 // Launch the contiguous GEMM for tile height block_m (0 = every candidate;
 // the ones the device did not choose exit at entry).
-template <bool FP8, bool B_KN, bool E8>
+template <bool FP8, bool B_KN, bool E8, bool W4 = false>
 static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
     const int64_t n_ct = a.N / 256;
     hipError_t err = hipSuccess;
     auto grid_for = [&](int q) { return round256(((rows_total + q - 1) / q + a.G) * n_ct); };
     // block_m = 0 launches every candidate; the one matching the schedule does the work
     if (block_m == MOEGG_BLOCK_M_PER_EXPERT || block_m == 0) {
-        constexpr int lds = std::max({Contig256<FP8, E8>::LDS_BYTES, Contig128<FP8, E8>::LDS_BYTES,
-                                      Contig64<FP8, E8>::LDS_BYTES});
-        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8>>(lds);
+        constexpr int lds = std::max({Contig256<FP8, E8, W4>::LDS_BYTES, Contig128<FP8, E8, W4>::LDS_BYTES,
+                                      Contig64<FP8, E8, W4>::LDS_BYTES});
+        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4>>(lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8>), dim3(grid_for(256)), dim3(512), lds, s, a);
+        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4>), dim3(grid_for(256)), dim3(512), lds,
+                           s, a);
         err = hipGetLastError();
         if (err != hipSuccess || block_m != 0) return err;
     }
     if (block_m == 0 || block_m == 256) {
-        err = launch_one<Contig256<FP8, E8>, B_KN, false>(a, grid_for(256), s);
+        err = launch_one<Contig256<FP8, E8, W4>, B_KN, false>(a, grid_for(256), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 128) {
-        err = launch_one<Contig128<FP8, E8>, B_KN, false>(a, grid_for(128), s);
+        err = launch_one<Contig128<FP8, E8, W4>, B_KN, false>(a, grid_for(128), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 64) {
-        err = launch_one<Contig64<FP8, E8>, B_KN, false>(a, grid_for(64), s);
+        err = launch_one<Contig64<FP8, E8, W4>, B_KN, false>(a, grid_for(64), s);
     }
     return err;
 }
 
-hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool b_kn, int64_t rows_total, int block_m,
-                             hipStream_t s) {
+hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,
+                             int block_m, hipStream_t s) {
+    if (w4) return b_kn ? hipErrorInvalidValue : launch_contig_t<true, false, true, true>(a, rows_total, block_m, s);
     if (fp8 && e8m0) return b_kn ? launch_contig_t<true, true, true>(a, rows_total, block_m, s)
                                  : launch_contig_t<true, false, true>(a, rows_total, block_m, s);
     if (fp8) return b_kn ? launch_contig_t<true, true, false>(a, rows_total, block_m, s)

@@ -69,6 +69,13 @@ def contiguous(**kw):
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=768), mg.ERR_UNSUPPORTED),   # N % 512
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=512, rows=130), mg.ERR_UNSUPPORTED),  # rows % 4
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=ctypes.c_void_p(0x100002), N=512), mg.ERR_INVALID_ARG),
+    (dict(dtype=mg.FP8_E4M3_FP4_E2M1), mg.ERR_INVALID_ARG),        # fp4 weights without scales
+    (dict(dtype=mg.FP8_E4M3_FP4_E2M1, A_scale=FAKE, B_scale=FAKE, N=512), mg.ERR_UNSUPPORTED),   # [G,K,N] fp4
+    (dict(dtype=mg.FP8_E4M3_FP4_E2M1, A_scale=FAKE, B_scale=FAKE, N=768, layout=mg.B_NK), mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_FP4_E2M1, A_scale=FAKE, B_scale=FAKE, N=512, layout=mg.B_NK, rows=130),
+     mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_FP4_E2M1, A_scale=FAKE, B_scale=FAKE, N=512, layout=mg.B_NK, K=192),
+     mg.ERR_UNSUPPORTED),
     (dict(block_m=32), mg.ERR_UNSUPPORTED),
     (dict(block_m=-2), mg.ERR_UNSUPPORTED),
     (dict(align=0), mg.ERR_INVALID_ARG),
@@ -98,6 +105,9 @@ def test_masked_validation():
     e8m0 = list(ok)                         # E8M0 scales: contiguous layout only
     e8m0[1], e8m0[3], e8m0[9], e8m0[10] = FAKE, FAKE, 7168 - 7168 % 512, mg.FP8_E4M3_E8M0
     assert f(*e8m0) == mg.ERR_UNSUPPORTED
+    w4 = list(e8m0)                         # fp4 weights: contiguous layout only
+    w4[10], w4[11] = mg.FP8_E4M3_FP4_E2M1, mg.B_NK
+    assert f(*w4) == mg.ERR_UNSUPPORTED
 
 
 def test_k_grouped_validation():

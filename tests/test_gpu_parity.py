@@ -13,6 +13,7 @@ import torch
 import moe_grouped_gemm_sizes_amd as mg
 import workloads as wl
 from oracle import accounting as acc
+from oracle import fp4
 from oracle import gemm as og
 from tests import parity as P
 
@@ -483,6 +484,90 @@ def test_contiguous_fp8_e8m0_full_size():
     assert np.isfinite(got).all()
     err = og.rel_frobenius(got, ref)
     print(f"e8m0 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL["fp8"], err
+    assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+
+
+# ----------------------------------------------------------------- fp8 x fp4 (E2M1 weights)
+
+
+def run_contiguous_fp4(w, inp, block_m):
+    C = P.sentinel_like((w.rows_total, w.N))
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.grouped_gemm_contiguous(inp["A"], inp["B"], C, inp["counts"], ws, A_scale=inp["A_scale_e8m0"],
+                               B_scale=inp["B_scale_e8m0"], seg_align=w.seg_align, block_m=block_m,
+                               b_layout=mg.B_NK)
+    torch.cuda.synchronize()
+    return C, ws
+
+
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+def test_contiguous_fp8_fp4(block_m):
+    """fp8 activations x packed E2M1 weights, both with E8M0 block scales:
+    every valid row against the fp8 x fp4 oracle."""
+    counts = [70, 0, 300, 6, 129, 3]                     # 508 rows: a multiple of 4, ragged tails
+    announce("contiguous fp8 x fp4", counts, "block_m", block_m)
+    w = wl.Workload("f4", "contiguous", "fp8", counts, K=512, N=512, values="normal", seed=9, scales="e8m0",
+                    weights="e2m1")
+    inp = wl.materialize(w, "cuda")
+    assert mg._dtype(inp["A"], inp["A_scale_e8m0"], inp["B"]) == mg.FP8_E4M3_FP4_E2M1
+    C, ws = run_contiguous_fp4(w, inp, block_m)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts)
+    rows = list(range(w.rows_total))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"fp4 block_m={st.block_m} rel_frobenius={err:.3e}", flush=True)
+    assert err <= P.TOL["fp8"], err
+    assert P.untouched_rows_ok(C, counts, 1)
+
+
+@pytest.mark.parametrize("block_m", [64, 256, mg.BLOCK_M_PER_EXPERT])
+def test_contiguous_fp8_fp4_integer_exact(block_m):
+    """Activations in {-1, 0, 1}, weights in {0, +-0.5, +-1}, unit scales,
+    K = 128: every result is a multiple of 0.5 of magnitude <= 128, exact in
+    bf16, so GPU == oracle bit for bit.  Pins the fp4 operand's nibble order
+    and K slots against the fp8 operand's."""
+    announce("fp8 x fp4 integer exact", block_m)
+    counts, K, N = [37, 0, 200, 7], 128, 512
+    G, rows_total = len(counts), sum(counts)
+    g = torch.Generator().manual_seed(7)
+    A = torch.randint(-1, 2, (rows_total, K), generator=g).float().to(torch.float8_e4m3fn)
+    codes = torch.tensor([0, 1, 2, 9, 10], dtype=torch.uint8)[torch.randint(0, 5, (G, N, K), generator=g)]
+    B = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    A_s8 = torch.full((K // 128, rows_total), 127, dtype=torch.uint8)
+    B_s8 = torch.full((G, K // 128, N // 128), 127, dtype=torch.uint8)
+    w = wl.Workload("int4", "contiguous", "fp8", counts, K=K, N=N, scales="e8m0", weights="e2m1")
+    inp = {"A": A.cuda(), "B": B.contiguous().cuda(), "A_scale_e8m0": A_s8.cuda(), "B_scale_e8m0": B_s8.cuda(),
+           "counts": torch.tensor(counts, dtype=torch.int32, device="cuda")}
+    C, _ = run_contiguous_fp4(w, inp, block_m)
+    ref = fp4.contiguous_fp8_fp4(A, torch.ones(rows_total, K // 128), B.contiguous(), torch.ones(G, K // 128, N // 128),
+                                 counts, range(rows_total))
+    got = C.float().cpu().double().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_contiguous_fp8_fp4_full_size():
+    """The Zipf workload (64 experts, 32768 rows, K = 7168, N = 4096) with fp4
+    weights, device-chosen height, on sampled rows."""
+    w = wl.workload(3)
+    w.scales, w.weights = "e8m0", "e2m1"
+    announce("contiguous fp8 x fp4 full size", w.name)
+    inp = wl.materialize(w, "cuda")
+    C, ws = run_contiguous_fp4(w, inp, 0)
+    st = mg.stats_read(ws)
+    P.check_stats(st, w.counts)
+    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256, extra=48, seed=13)
+    cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+    del inp
+    ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], w.counts, rows)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    err = og.rel_frobenius(got, ref)
+    print(f"fp4 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
     assert err <= P.TOL["fp8"], err
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
