@@ -74,6 +74,7 @@ typedef enum { MOEGG_B_KN = 0, MOEGG_B_NK = 1 } moegg_b_layout_t;
 #define MOEGG_FLAG_NEGATIVE_COUNT  0x1u  /* a count < 0 was read as 0                 */
 #define MOEGG_FLAG_ROWS_OVERFLOW   0x2u  /* segments ran past rows_total / T; truncated */
 #define MOEGG_FLAG_COUNT_OVER_CAP  0x4u  /* a masked count > cap was read as cap      */
+#define MOEGG_FLAG_BAD_EXEMPLAR    0x8u  /* an exemplar named an invalid block_m      */
 
 /* block_m value for per-expert tile heights: every expert gets 256-row tiles,
  * and its remainder rows one tile of the smallest height in {64, 128, 256}
@@ -147,6 +148,69 @@ size_t moegg_workspace_bytes(int G, int64_t max_rows);
  */
 moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align,
                               int block_m, int N, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Distribution-aware tile-height selection ("MoE GroupGEMM padding under
+ * expert skew", section "Adapt kernels without adding a CPU stall": sort and
+ * normalize the per-expert counts, match them against exemplars tuned
+ * offline, and keep neighbouring histograms from flipping the kernel).
+ *
+ * An exemplar describes one histogram by
+ *   size_class  4 * floor(log2 U) + the two bits of U below its leading one
+ *               (quarter-octave steps of the row count U; 0 when U = 0);
+ *   lorenz[i]   floor(65536 * S(k_i) / U), i = 0..7, where S(k) is the sum of
+ *               the k largest counts and k_i = ceil(G * (i + 1) / 8): the share
+ *               of the rows held by the top eighth, quarter, ... of experts
+ *               (all 0 when U = 0);
+ * and names the configuration measured fastest for it (block_m: 64, 128,
+ * 256 or MOEGG_BLOCK_M_PER_EXPERT).
+ */
+typedef struct {
+    int32_t size_class;
+    int32_t lorenz[8];
+    int32_t block_m;
+} moegg_exemplar_t;
+
+#define MOEGG_MAX_EXEMPLARS 256
+#define MOEGG_EXEMPLAR_SIZE_WEIGHT 8192   /* distance per quarter-octave of U */
+
+/*
+ * moegg_schedule with the tile height chosen by exemplar matching on the
+ * device.  The histogram's descriptor (as above, from the clamped counts)
+ * is compared with each exemplar by
+ *     D = sum_i |lorenz[i] - ex.lorenz[i]|
+ *         + MOEGG_EXEMPLAR_SIZE_WEIGHT * |size_class - ex.size_class|,
+ * and the nearest exemplar wins (ties: lowest index).  Hysteresis: `ws`
+ * remembers the exemplar the previous call on it chose; that one is kept
+ * while its distance is at most the nearest one's plus `hysteresis`.  A
+ * workspace that no call of this kind has used carries no choice (a 64-bit
+ * tag marks a valid one).  The chosen exemplar's block_m then drives the tile
+ * list exactly as in moegg_schedule; stats block_m reports it.  If it is not
+ * a valid block_m, the cost rule of moegg_grouped_gemm_contiguous decides
+ * (for output width N) and error_flags gets MOEGG_FLAG_BAD_EXEMPLAR.
+ * Arguments other than the three below are those of moegg_schedule.
+ *   exemplars  device array of n_exemplars entries (1..MOEGG_MAX_EXEMPLARS),
+ *              read during the call; caller-owned.
+ *   hysteresis >= 0, in distance units.
+ * Graph-capturable: nothing leaves the device.  Calls that share a
+ * workspace must be ordered (the remembered choice is part of it).
+ */
+moegg_status_t moegg_schedule_exemplar(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align, int N,
+                                       const moegg_exemplar_t* exemplars, int n_exemplars, int hysteresis,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/* What the last moegg_schedule_exemplar call on a workspace saw and chose. */
+typedef struct {
+    int32_t exemplar;        /* index of the chosen exemplar                    */
+    int32_t size_class;      /* the histogram's descriptor, as defined above    */
+    int32_t lorenz[8];
+    int64_t distance;        /* distance from the histogram to the chosen exemplar */
+} moegg_selection_t;
+
+/* Copy the selection of the last moegg_schedule_exemplar call on `ws` to
+ * the host.  Synchronizes `stream`.  MOEGG_ERR_INVALID_ARG if no such call
+ * has used `ws`. */
+moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, void* stream);
 
 /*
  * M-grouped contiguous layout (DeepGEMM record, "Workarounds": prefill and

@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moegg.h")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1 = 0, 1, 2, 3
 B_KN, B_NK = 0, 1
-FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP = 0x1, 0x2, 0x4
+FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP, FLAG_BAD_EXEMPLAR = 0x1, 0x2, 0x4, 0x8
 Q_VALUES = (8, 16, 32, 64, 128, 256)
 BLOCK_M_PER_EXPERT = -1          # per-expert tile heights (include/moegg.h)
 
@@ -76,6 +76,8 @@ EXPORTS = {
     "moegg_status_string": (ctypes.c_char_p, [_I32]),
     "moegg_workspace_bytes": (_SZ, [_I32, _I64]),
     "moegg_schedule": (_I32, [_VP, _I32, _I64, _I32, _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_schedule_exemplar": (_I32, [_VP, _I32, _I64, _I32, _I32, _VP, _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_selection_read": (_I32, [_VP, _VP, _VP]),
     "moegg_grouped_gemm_contiguous_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                                        _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_contiguous": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
@@ -149,6 +151,50 @@ def schedule(m_sizes: torch.Tensor, rows_total: int, ws: torch.Tensor, seg_align
              N: int = 256, stream=None):
     _check(lib().moegg_schedule(_p(m_sizes), m_sizes.numel(), rows_total, seg_align, block_m, N, _p(ws),
                                 ws.numel(), _stream(stream)), "moegg_schedule")
+
+
+EXEMPLAR_FIELDS = 10            # moegg_exemplar_t: size_class, lorenz[8], block_m (int32 each)
+EXEMPLAR_TABLE_PATH = os.path.join(_HERE, "exemplars_mi355x.json")
+
+
+def exemplar_table(device="cuda", path: Optional[str] = None) -> torch.Tensor:
+    """The exemplar table as an int32 [n, 10] device tensor (moegg_exemplar_t rows).
+    Default: the table measured on MI355X that ships with the package."""
+    import json
+    with open(path or EXEMPLAR_TABLE_PATH) as f:
+        rows = json.load(f)["exemplars"]
+    t = torch.tensor([[r["size_class"], *r["lorenz"], r["block_m"]] for r in rows], dtype=torch.int32)
+    return t.to(device)
+
+
+def schedule_exemplar(m_sizes: torch.Tensor, rows_total: int, ws: torch.Tensor, exemplars: torch.Tensor,
+                      hysteresis: int = 0, seg_align: int = 1, N: int = 256, stream=None):
+    """moegg_schedule with the tile height matched to an exemplar on the device (see moegg.h)."""
+    if exemplars.dtype != torch.int32 or exemplars.dim() != 2 or exemplars.shape[1] != EXEMPLAR_FIELDS:
+        raise ValueError("exemplars: int32 [n, 10] expected")
+    _check(lib().moegg_schedule_exemplar(_p(m_sizes), m_sizes.numel(), rows_total, seg_align, N, _p(exemplars),
+                                         exemplars.shape[0], hysteresis, _p(ws), ws.numel(), _stream(stream)),
+           "moegg_schedule_exemplar")
+
+
+class _Selection(ctypes.Structure):
+    _fields_ = [("exemplar", ctypes.c_int32), ("size_class", ctypes.c_int32), ("lorenz", ctypes.c_int32 * 8),
+                ("distance", ctypes.c_int64)]
+
+
+@dataclass
+class Selection:
+    exemplar: int
+    size_class: int
+    lorenz: Tuple[int, ...]
+    distance: int
+
+
+def selection_read(ws: torch.Tensor, stream=None) -> Selection:
+    s = _Selection()
+    _check(lib().moegg_selection_read(_p(ws), ctypes.c_void_p(ctypes.addressof(s)), _stream(stream)),
+           "moegg_selection_read")
+    return Selection(s.exemplar, s.size_class, tuple(s.lorenz), s.distance)
 
 
 def grouped_gemm_contiguous_scheduled(A, B, C, G: int, ws, A_scale=None, B_scale=None, block_m: int = 0,

@@ -103,6 +103,39 @@ moegg_status_t moegg_schedule(const int32_t* m_sizes, int G, int64_t rows_total,
                       "schedule");
 }
 
+moegg_status_t moegg_schedule_exemplar(const int32_t* m_sizes, int G, int64_t rows_total, int seg_align, int N,
+                                       const moegg_exemplar_t* exemplars, int n_exemplars, int hysteresis,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    if (!m_sizes || !aligned(m_sizes, 4) || G < 1 || G > kMaxExperts || rows_total < 0 || rows_total > INT32_MAX ||
+        seg_align < 1 || N < 1)
+        return MOEGG_ERR_INVALID_ARG;
+    if (!exemplars || !aligned(exemplars, 4) || n_exemplars < 1 || hysteresis < 0) return MOEGG_ERR_INVALID_ARG;
+    if (n_exemplars > MOEGG_MAX_EXEMPLARS) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    const WsLayout L = ws_layout(G, rows_total);
+    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+    // the cost rule (used if an exemplar names no valid height) counts 256-wide column tiles
+    const int n_col_tiles = N / 256 > 0 ? N / 256 : 1;
+    return hip_status(launch_sched_exemplar(m_sizes, G, rows_total, seg_align, n_col_tiles, exemplars, n_exemplars,
+                                            hysteresis, ws, L.max_tiles, (hipStream_t)stream),
+                      "exemplar schedule");
+}
+
+moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, void* stream) {
+    if (!ws || !h_out) return MOEGG_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    Control ctl;
+    hipError_t e = hipMemcpyAsync(&ctl, (const char*)ws + 128, sizeof(ctl), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "selection read");
+    if (ctl.sel_tag != kSelectorTag) return MOEGG_ERR_INVALID_ARG;
+    h_out->exemplar = ctl.sel_prev;
+    h_out->size_class = ctl.sel_size_class;
+    for (int q = 0; q < 8; ++q) h_out->lorenz[q] = ctl.sel_lorenz[q];
+    h_out->distance = ctl.sel_distance;
+    return MOEGG_OK;
+}
+
 moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale, const void* B,
                                              const void* B_scale, void* C, const int32_t* m_sizes, int G,
                                              int64_t rows_total, int K, int N, int seg_align,

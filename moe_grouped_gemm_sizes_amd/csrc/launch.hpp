@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moegg.h"
+
 namespace moegg {
 
 struct ContigArgs {
@@ -30,6 +32,11 @@ struct KGroupedArgs {
 hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int seg_align, int cap, int mode,
                         int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
                         hipStream_t stream);
+// exemplar-matching tile height (moegg_schedule_exemplar); exemplars: device
+// array of n_ex entries
+hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_total, int seg_align, int n_col_tiles,
+                                 const moegg_exemplar_t* exemplars, int n_ex, int hysteresis, void* ws,
+                                 int64_t max_tiles, hipStream_t stream);
 hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void* ws, hipStream_t stream);
 // w4: packed E2M1 weights [G, N, K/2] (needs fp8 activations, E8M0 scales, !b_kn)
 hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,

@@ -99,6 +99,94 @@ __device__ int choose_block_m(const int64_t* cand_tiles, int64_t n_tail128, int6
     return cost_pe < best_cost ? MOEGG_BLOCK_M_PER_EXPERT : best;
 }
 
+// Quarter-octave size class of U: 4 * floor(log2 U) plus the two bits below
+// U's leading one; 0 for U = 0.
+__device__ __forceinline__ int32_t size_class(int64_t U) {
+    if (U <= 0) return 0;
+    const int e = 63 - __builtin_clzll((unsigned long long)U);
+    const int64_t frac = e >= 2 ? (U >> (e - 2)) & 3 : (U << (2 - e)) & 3;
+    return 4 * e + (int32_t)frac;
+}
+
+__device__ __forceinline__ bool valid_block_m_dev(int b) {
+    return b == 64 || b == 128 || b == 256 || b == MOEGG_BLOCK_M_PER_EXPERT;
+}
+
+// Distribution-aware choice ("Adapt kernels without adding a CPU stall" on the
+// MoE GroupGEMM padding page): sort the counts, normalize their top-k sums by
+// U into an eight-point concentration curve, and take the nearest exemplar,
+// keeping the workspace's previous exemplar while it is within `hysteresis`
+// of the nearest.  Called by all threads after the accounting; the counts
+// are in m_s.  Returns the exemplar's block_m (or -2 when it names no valid
+// one).  Thread 0 records the selection in the control block.
+__device__ int select_exemplar(const int32_t* m_s, int32_t* srt_s, int64_t (*lor_buf)[8], int G, int64_t U,
+                               const moegg_exemplar_t* __restrict__ ex, int n_ex, int hysteresis, Control* ctl,
+                               int* bm_s) {
+    const int t = threadIdx.x;
+    // 1. bitonic sort, descending, over the next power of two (padded with zeros)
+    int P = 1;
+    while (P < G) P <<= 1;
+    for (int i = t; i < P; i += kSchedThreads) srt_s[i] = i < G ? m_s[i] : 0;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < P; i += kSchedThreads) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const int32_t a = srt_s[i], b = srt_s[l];
+                    const bool down = (i & k) == 0;
+                    if (down ? a < b : a > b) { srt_s[i] = b; srt_s[l] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // 2. sums of the k_q = ceil(G (q + 1) / 8) largest counts
+    int64_t top[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) top[q] = 0;
+    for (int i = t; i < G; i += kSchedThreads) {
+        const int64_t m = srt_s[i];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) top[q] += i < (G * (q + 1) + 7) / 8 ? m : 0;
+    }
+    block_sums<8>(top, lor_buf);
+    // 3. descriptor, distances, hysteresis (one thread; at most 256 exemplars)
+    if (t == 0) {
+        int32_t lor[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lor[q] = U > 0 ? (int32_t)((top[q] << 16) / U) : 0;
+        const int32_t sc = size_class(U);
+        auto dist = [&](int x) -> int64_t {
+            int64_t d = (int64_t)MOEGG_EXEMPLAR_SIZE_WEIGHT * llabs((int64_t)sc - ex[x].size_class);
+            for (int q = 0; q < 8; ++q) d += llabs((int64_t)lor[q] - ex[x].lorenz[q]);
+            return d;
+        };
+        int best = 0;
+        int64_t best_d = dist(0);
+        for (int x = 1; x < n_ex; ++x) {
+            const int64_t d = dist(x);
+            if (d < best_d) { best_d = d; best = x; }
+        }
+        int chosen = best;
+        int64_t chosen_d = best_d;
+        if (ctl->sel_tag == kSelectorTag && ctl->sel_prev >= 0 && ctl->sel_prev < n_ex) {
+            const int64_t dp = dist(ctl->sel_prev);
+            if (dp <= best_d + hysteresis) { chosen = ctl->sel_prev; chosen_d = dp; }
+        }
+        const int bm = ex[chosen].block_m;
+        *bm_s = valid_block_m_dev(bm) ? bm : -2;
+        ctl->sel_tag = kSelectorTag;
+        ctl->sel_prev = chosen;
+        ctl->sel_size_class = sc;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ctl->sel_lorenz[q] = lor[q];
+        ctl->sel_distance = chosen_d;
+    }
+    __syncthreads();
+    return *bm_s;
+}
+
 // mode 0: contiguous layout (segment starts from aligned counts, tile list).
 // mode 1: masked layout (segment starts e * cap, counts clamped to cap,
 //         stats only: the masked kernel reads masked_m itself).
@@ -109,7 +197,7 @@ __device__ int choose_block_m(const int64_t* cand_tiles, int64_t n_tail128, int6
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     const int32_t* __restrict__ counts, int G, int64_t rows_total, int seg_align, int cap,
     int mode, int block_m_req, int n_col_tiles, int exec_block_m, unsigned char* __restrict__ ws,
-    int64_t max_tiles) {
+    int64_t max_tiles, const moegg_exemplar_t* __restrict__ exemplars, int n_ex, int hysteresis) {
     constexpr int NV = 3 + MOEGG_NUM_Q + kNumCand + 2;       // U, active, sum_sq, P(q) x6, tiles(q) x3, tails x2
     __shared__ int64_t wave_buf[kWaves];
     __shared__ int64_t sums_buf[kWaves][NV];
@@ -117,6 +205,9 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     __shared__ int64_t start_s[kMaxExperts];                 // segment starts
     __shared__ unsigned int flags_s;
     __shared__ int32_t toff_s[kMaxExperts + 1];             // first tile of each expert
+    __shared__ int32_t srt_s[kMaxExperts];                   // exemplar mode: sorted counts
+    __shared__ int64_t lor_buf[kWaves][8];
+    __shared__ int bm_s;
     const int t = threadIdx.x;
     const int ept = (G + kSchedThreads - 1) / kSchedThreads;  // experts per thread, contiguous
     const int e0 = min(G, t * ept), e1 = min(G, e0 + ept);
@@ -176,10 +267,19 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     if (flags) atomicOr(&flags_s, flags);
     block_sums<NV>(v, sums_buf);       // its barriers also publish m_s, start_s and flags_s
 
-    // 4. tile height (per-expert mode lists 256-row tiles)
+    // 4. tile height (per-expert mode lists 256-row tiles): requested, matched
+    //    to an exemplar, or from the cost rule
     int bm = block_m_req;
-    if (mode == 1) bm = exec_block_m;
-    else if (bm == 0)
+    if (mode == 1) {
+        bm = exec_block_m;
+    } else if (n_ex > 0) {
+        bm = select_exemplar(m_s, srt_s, lor_buf, G, v[0], exemplars, n_ex, hysteresis, ctl, &bm_s);
+        if (bm == -2) {
+            bm = 0;
+            if (t == 0) flags_s |= MOEGG_FLAG_BAD_EXEMPLAR;
+        }
+    }
+    if (mode == 0 && bm == 0)
         bm = choose_block_m(&v[3 + MOEGG_NUM_Q], v[3 + MOEGG_NUM_Q + kNumCand], v[3 + MOEGG_NUM_Q + kNumCand + 1],
                             n_col_tiles);
     const bool per_expert = bm == MOEGG_BLOCK_M_PER_EXPERT;
@@ -355,7 +455,16 @@ hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int se
                         int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
                         hipStream_t stream) {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, counts, G, rows_total, seg_align,
-                       cap, mode, block_m_req, n_col_tiles, exec_block_m, (unsigned char*)ws, max_tiles);
+                       cap, mode, block_m_req, n_col_tiles, exec_block_m, (unsigned char*)ws, max_tiles,
+                       (const moegg_exemplar_t*)nullptr, 0, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_total, int seg_align, int n_col_tiles,
+                                 const moegg_exemplar_t* exemplars, int n_ex, int hysteresis, void* ws,
+                                 int64_t max_tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, counts, G, rows_total, seg_align, 0,
+                       0, 0, n_col_tiles, 0, (unsigned char*)ws, max_tiles, exemplars, n_ex, hysteresis);
     return hipGetLastError();
 }
 

@@ -19,12 +19,23 @@ constexpr int kMinBlockM = 64;     // smallest schedulable tile height
 constexpr int kExecRows = 16;      // MFMA row block: rows are executed in 16s
 constexpr int kNumCand = 3;        // candidate tile heights 64, 128, 256
 
+// Tag of a valid exemplar-selector state in the control block.
+constexpr uint64_t kSelectorTag = 0x4D4F454753454C31ull;
+
 struct Control {
     int32_t n_tiles;               // entries in the tile list
     int32_t block_m;               // tile height used
     int32_t cand_tiles[kNumCand];  // tiles(q) for q = 64, 128, 256
     int32_t G;                     // expert count of the last scheduled call
-    int32_t pad[26];
+    // exemplar selector: the exemplar the last moegg_schedule_exemplar call on
+    // this workspace chose (valid when sel_tag == kSelectorTag), and the
+    // descriptor and distance of that call's histogram
+    uint64_t sel_tag;
+    int32_t sel_prev;
+    int32_t sel_size_class;
+    int32_t sel_lorenz[8];
+    int64_t sel_distance;
+    int32_t pad[12];
 };
 static_assert(sizeof(moegg_stats_t) <= 128, "stats block");
 static_assert(sizeof(Control) == 128, "control block");

@@ -1,0 +1,102 @@
+"""Measure the exemplar table of the distribution-aware tile-height selector
+(moegg_schedule_exemplar) on this GPU and write it as JSON.
+
+The padding page ("MoE GroupGEMM padding under expert skew") asks for kernel
+choice from the routing histogram on the device, matched against exemplars
+tuned offline ("Adapt kernels without adding a CPU stall"), and for the
+candidates to be benchmarked on the deployed GPU rather than chosen from the
+padding formula ("Padding is not the whole cost model").  This tool does the
+benchmarking:
+
+  - exemplar histograms: 64 experts, U in {256, 1024, 4096, 16384, 32768}
+    routed rows, Zipf exponents 0 (uniform), 0.8, 1.2 and 2.0 over the
+    experts, a fifth of the experts empty (the seeded generator of the
+    workloads module);
+  - for each, the contiguous fp8 GEMM (K = 7168, N = 4096, e4m3 with fp32
+    block scales, [G, N, K] weights, 512 MiB written between calls so the
+    operands come from HBM) at every tile configuration: 64, 128 and 256 rows
+    and per-expert heights; the median of 8 timed calls;
+  - each entry keeps the histogram, its descriptor as the device computes it
+    (moegg_selection_read), the times, and the fastest configuration.
+
+Usage, on the GPU:  python -m moe_grouped_gemm_sizes_amd.tune_exemplars [--out PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+
+import moe_grouped_gemm_sizes_amd as mg  # noqa: E402
+import workloads as wl  # noqa: E402
+
+SIZES = (256, 1024, 4096, 16384, 32768)
+SKEWS = (0.0, 0.8, 1.2, 2.0)
+CONFIGS = (64, 128, 256, mg.BLOCK_M_PER_EXPERT)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=mg.EXEMPLAR_TABLE_PATH)
+    ap.add_argument("--iters", type=int, default=8)
+    args = ap.parse_args()
+    w = wl.workload(3)                        # shapes of the fp8 Zipf workload: 64 experts, K 7168, N 4096
+    inp = wl.materialize(w, "cuda", nan_padding=False)
+    A, As, Bs = inp["A"], inp["A_scale"], inp["B_scale"]
+    B = inp["B"].transpose(1, 2).contiguous()
+    del inp
+    G, R, N = w.G, w.rows_total, w.N
+    C = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    ws = mg.workspace(G, R)
+    ws_d = torch.zeros_like(ws)
+    probe = torch.zeros((1, mg.EXEMPLAR_FIELDS), dtype=torch.int32, device="cuda")
+    probe[0, -1] = 256
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    entries = []
+    for U in SIZES:
+        for s in SKEWS:
+            counts = wl.hist_zipf(seed=1000 + U + int(10 * s), experts=G, total=U, s=s)
+            ct = torch.tensor(counts, dtype=torch.int32, device="cuda")
+            ws_d.zero_()
+            mg.schedule_exemplar(ct, R, ws_d, probe, N=N)
+            d = mg.selection_read(ws_d)
+            times = {}
+            for bm in CONFIGS:
+                mg.schedule(ct, R, ws, block_m=bm, N=N)
+
+                def gemm():
+                    mg.grouped_gemm_contiguous_scheduled(A, B, C, G, ws, As, Bs, block_m=bm, b_layout=mg.B_NK)
+                gemm()
+                gemm()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.iters)]
+                for i, (e0, e1) in enumerate(ev):
+                    scratch.fill_(i & 255)
+                    e0.record()
+                    gemm()
+                    e1.record()
+                torch.cuda.synchronize()
+                t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+                times[str(bm)] = round(t[len(t) // 2], 4)
+            best = int(min(times, key=times.get))
+            entries.append({"name": f"zipf{s}_U{U}", "U": U, "counts": counts, "size_class": d.size_class,
+                            "lorenz": list(d.lorenz), "block_m": best, "times_ms": times})
+            print(f"U={U:6d} s={s:3.1f} size_class={d.size_class} block_m={best:4d} {times}", flush=True)
+    out = {"device": torch.cuda.get_device_name(0),
+           "workload": "64 experts, K 7168, N 4096, fp8 e4m3 with fp32 block scales, [G,N,K] weights, contiguous, "
+                       "cold caches; median of %d calls per configuration" % args.iters,
+           "command": "python -m moe_grouped_gemm_sizes_amd.tune_exemplars",
+           "exemplars": entries}
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {len(entries)} exemplars to {args.out}", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,6 +12,8 @@ Parts:
   receives and decode them with their own decoders.
 - fp4.py: fp8 activations times packed E2M1 weights with power-of-two block
   scales (the contiguous layout), with its own E2M1 decoder.
+- select.py: the distribution-aware tile-height choice (sorted, normalized
+  histogram matched against an exemplar table, with hysteresis).
 
 Every function states the page and section it follows.  Parity pins live in
 tests/test_oracle_*.py and tests/golden/.
@@ -19,3 +21,4 @@ tests/test_oracle_*.py and tests/golden/.
 from . import accounting  # noqa: F401
 from . import gemm  # noqa: F401
 from . import fp4  # noqa: F401
+from . import select  # noqa: F401

@@ -136,6 +136,33 @@ def test_scheduled_validation():
     assert f(*bad) == mg.ERR_INVALID_ARG
 
 
+def test_schedule_exemplar_validation():
+    f = mg.lib().moegg_schedule_exemplar
+    ok = [FAKE, 8, 132, 1, 256, FAKE, 4, 0, FAKE, 1 << 20, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == mg.ERR_INVALID_ARG          # counts
+    assert call(a1=0) == mg.ERR_INVALID_ARG             # G
+    assert call(a4=0) == mg.ERR_INVALID_ARG             # N
+    assert call(a5=None) == mg.ERR_INVALID_ARG          # table
+    assert call(a6=0) == mg.ERR_INVALID_ARG             # empty table
+    assert call(a6=257) == mg.ERR_UNSUPPORTED           # more than MOEGG_MAX_EXEMPLARS
+    assert call(a7=-1) == mg.ERR_INVALID_ARG            # negative hysteresis
+    assert call(a8=None) == mg.ERR_WORKSPACE
+    assert call(a9=16) == mg.ERR_WORKSPACE
+    assert mg.lib().moegg_selection_read(None, None, None) == mg.ERR_INVALID_ARG
+
+
+def test_exemplar_struct_matches_the_header():
+    src = open(mg.HEADER_PATH).read()
+    assert "int32_t lorenz[8];" in src and mg.EXEMPLAR_FIELDS == 10
+    assert ctypes.sizeof(mg._Selection) == 48
+
+
 def test_read_validation():
     L = mg.lib()
     assert L.moegg_stats_read(None, None, None) == mg.ERR_INVALID_ARG

@@ -15,6 +15,7 @@ import workloads as wl
 from oracle import accounting as acc
 from oracle import fp4
 from oracle import gemm as og
+from oracle import select as oselect
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -570,6 +571,136 @@ def test_contiguous_fp8_fp4_full_size():
     print(f"fp4 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
     assert err <= P.TOL["fp8"], err
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+
+
+# ----------------------------------------------------------------- exemplar selection
+
+
+SELECT_HISTS = dict(SCHED_HISTS, **{
+    f"zipf{s_}_{u}": wl.hist_zipf(seed=77 + u, experts=64, total=u, s=s_)
+    for u in (300, 3000, 30000) for s_ in (0.0, 1.0, 1.6)})
+
+
+def run_selection(counts, table, ws, hysteresis=0, N=4096):
+    ct = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    rows = max(1, sum(counts))
+    mg.schedule_exemplar(ct, rows, ws, table, hysteresis=hysteresis, N=N)
+    return mg.selection_read(ws), mg.stats_read(ws)
+
+
+def check_selection(counts, table_rows, got, st, expect_idx, expect_d):
+    assert got.exemplar == expect_idx
+    assert got.distance == expect_d
+    assert (got.size_class, list(got.lorenz)) == oselect.descriptor(counts)
+    bm = table_rows[expect_idx][-1]
+    assert st.block_m == bm
+    P.check_stats(st, counts)
+
+
+@pytest.mark.parametrize("name", sorted(SELECT_HISTS))
+def test_exemplar_selection_matches_oracle(name):
+    """Descriptor, nearest exemplar, distance and the resulting tile list,
+    bit-exact against the oracle, with the shipped MI355X table."""
+    counts = SELECT_HISTS[name]
+    announce("exemplar selection", name, len(counts))
+    table = mg.exemplar_table()
+    rows = table.cpu().tolist()
+    rows_total = max(1, sum(counts))
+    ws = torch.zeros(mg.workspace_bytes(len(counts), rows_total), dtype=torch.uint8, device="cuda")
+    got, st = run_selection(counts, table, ws)
+    idx, d = oselect.select(counts, rows)
+    check_selection(counts, rows, got, st, idx, d)
+    bm = rows[idx][-1]
+    if bm == mg.BLOCK_M_PER_EXPERT:
+        expect = acc.tile_list_per_expert(counts, 1)
+    else:
+        expect = acc.tile_list(counts, bm, 1)
+    assert mg.tile_list_read(ws, len(expect) + 4) == expect
+
+
+def test_exemplar_hysteresis_sequence():
+    """One workspace through a drifting sequence of histograms: the device
+    keeps or switches exemplars exactly as the oracle's state machine does."""
+    table_rows = [[sel_sc, *oselect.lorenz(h), bm] for sel_sc, h, bm in (
+        (oselect.size_class(4096), [64] * 64, 64),
+        (oselect.size_class(4096), [1024, 1024] + [32] * 62, 256),
+        (oselect.size_class(4096), [3000] + [17] * 63, mg.BLOCK_M_PER_EXPERT))]
+    table = torch.tensor(table_rows, dtype=torch.int32, device="cuda")
+    rng = random.Random(9)
+    ws = torch.zeros(mg.workspace_bytes(64, 8192), dtype=torch.uint8, device="cuda")
+    prev = None
+    H = 20000
+    switches = 0
+    for step in range(40):
+        hot = rng.choice([0, 300, 600, 900, 1200, 2000, 3000])
+        counts = [hot] + [max(0, (4096 - hot) // 63 + rng.randint(-3, 3)) for _ in range(63)]
+        announce("hysteresis step", step, hot)
+        got, st = run_selection(counts, table, ws, hysteresis=H)
+        idx, d = oselect.select(counts, table_rows, hysteresis=H, prev=prev)
+        check_selection(counts, table_rows, got, st, idx, d)
+        switches += prev is not None and idx != prev
+        prev = idx
+    assert switches > 0
+
+
+def test_exemplar_invalid_block_m_falls_back_to_the_cost_rule():
+    counts = wl.hist_issue_32()
+    table = torch.tensor([[0] * 9 + [96]], dtype=torch.int32, device="cuda")
+    ws = torch.zeros(mg.workspace_bytes(32, sum(counts)), dtype=torch.uint8, device="cuda")
+    announce("exemplar fallback")
+    ct = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    mg.schedule_exemplar(ct, sum(counts), ws, table, N=4096)
+    st = mg.stats_read(ws)
+    assert st.error_flags == mg.FLAG_BAD_EXEMPLAR
+    assert st.block_m == P.choice_rule(counts, 4096 // 256)
+
+
+def test_exemplar_selection_in_a_graph():
+    """Selection and GEMM captured once, replayed with new counts written in
+    place: each replay's choice, tile list and output rows match the oracle,
+    and the remembered choice carries from replay to replay."""
+    G, K, N, R = 16, 256, 512, 2048
+    w = wl.Workload("sel-graph", "contiguous", "bf16", [128] * G, K=K, N=N, values="normal", seed=31)
+    inp = wl.materialize(w, "cuda", nan_padding=False)
+    table_rows = [[oselect.size_class(R), *oselect.lorenz([128] * G), 64],
+                  [oselect.size_class(R), *oselect.lorenz([1800] + [16] * (G - 1)), 256]]
+    table = torch.tensor(table_rows, dtype=torch.int32, device="cuda")
+    counts_t = torch.tensor([128] * G, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(mg.workspace_bytes(G, R), dtype=torch.uint8, device="cuda")
+    C = torch.zeros((R, N), dtype=torch.bfloat16, device="cuda")
+    announce("exemplar graph capture")
+
+    def step():
+        mg.schedule_exemplar(counts_t, R, ws, table, hysteresis=1000, N=N)
+        mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, G, ws, block_m=0)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ws.zero_()                                          # no remembered choice before the first replay
+    torch.cuda.synchronize()
+    prev = None
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    for counts in ([128] * G, [1800] + [16] * (G - 1), [1700] + [20] * (G - 2) + [48], [100] * G):
+        announce("graph replay", counts[:3])
+        counts_t.copy_(torch.tensor(counts, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got, st = mg.selection_read(ws), mg.stats_read(ws)
+        idx, d = oselect.select(counts, table_rows, hysteresis=1000, prev=prev)
+        check_selection(counts, table_rows, got, st, idx, d)
+        prev = idx
+        rows = P.sample_rows_contiguous(counts, 1, 64, extra=16, seed=5)
+        ref = og.contiguous(cpu["A"], cpu["B"], counts, rows)
+        err = og.rel_frobenius(P.rows_as_float(C, rows), ref)
+        assert err <= P.TOL["bf16"], err
 
 
 # ----------------------------------------------------------------- K-grouped
