@@ -42,15 +42,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_block_m: int = 0):
-    """Returns (scheduler, gemm, workspace) closures for one workload."""
+def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_block_m: int = 0, exemplars=None,
+               hysteresis: int = 0):
+    """Returns (scheduler, gemm, workspace) closures for one workload.  With an
+    exemplar table the scheduler picks the tile height by exemplar matching."""
     dev = "cuda"
     if w.layout == "contiguous":
         C = torch.empty((w.rows_total, w.N), dtype=torch.bfloat16, device=dev)
         ws = mg.workspace(w.G, w.rows_total)
 
         def sched():
-            mg.schedule(inp["counts"], w.rows_total, ws, seg_align=w.seg_align, block_m=sched_block_m, N=w.N)
+            if exemplars is not None:
+                mg.schedule_exemplar(inp["counts"], w.rows_total, ws, exemplars, hysteresis=hysteresis,
+                                     seg_align=w.seg_align, N=w.N)
+            else:
+                mg.schedule(inp["counts"], w.rows_total, ws, seg_align=w.seg_align, block_m=sched_block_m, N=w.N)
 
         def gemm():
             mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"),
@@ -175,9 +181,10 @@ def main():
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
                          "a transfer of known size")
-    ap.add_argument("--block-m", default="auto", choices=("auto", "per-expert", "64", "128", "256"),
-                    help="tile height: auto = one height chosen on the device from the histogram; per-expert = "
-                         "256-row tiles plus a remainder tile per expert sized 64/128/256")
+    ap.add_argument("--block-m", default="auto", choices=("auto", "exemplar", "per-expert", "64", "128", "256"),
+                    help="tile height: auto = chosen on the device by the cost rule; exemplar = chosen on the "
+                         "device by matching the histogram to the MI355X exemplar table (hysteresis 4096); "
+                         "per-expert = 256-row tiles plus a remainder tile per expert sized 64/128/256")
     ap.add_argument("--b-layout", choices=("auto", "kn", "nk"), default="auto",
                     help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE weights "
                          "are usually kept in; repacking is one-time, outside the timed steps).  auto: nk for "
@@ -214,16 +221,17 @@ def main():
     torch.cuda.synchronize()
 
     # first pass: learn the device's tile-height choice (outside timing)
-    bm_req = {"auto": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] if not args.block_m.isdigit() \
-        else int(args.block_m)
+    bm_req = {"auto": 0, "exemplar": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] \
+        if not args.block_m.isdigit() else int(args.block_m)
+    exemplars = mg.exemplar_table() if args.block_m == "exemplar" and w.layout == "contiguous" else None
     # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32
     inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) if w.scales == "e8m0" else inp
-    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req)
+    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req, exemplars, 4096)
     if sched is not None:
         sched()
         torch.cuda.synchronize()
         st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req)
+        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req, exemplars, 4096)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -281,7 +289,9 @@ def main():
                    if b_layout == mg.B_NK else "[G,K,N]",
                    "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else "fp32")
                    if w.dtype == "fp8" else None,
-                   "cache": "cold (512 MiB written between steps)" if args.cold else "warm"},
+                   "cache": "cold (512 MiB written between steps)" if args.cold else "warm",
+                   "tile_choice": "exemplar table (MI355X)" if exemplars is not None else
+                   ("cost rule" if args.block_m == "auto" else "fixed")},
         "pct_mfma_peak": round(100.0 * eff / peak, 2),
     }
     if w.layout == "contiguous":
