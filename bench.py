@@ -157,6 +157,77 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
             "sample": f"{len(sample)} output rows x {w.N} columns of this workload (fp64 oracle, {dt:.1f} s)"}
 
 
+def run_mlp(args):
+    """Expert MLP on the Zipf histogram (64 experts, 32768 rows), DeepSeek-V3 expert shape: K 7168, I 2048,
+    N2 7168.  One step: scheduler, L1 (fp8 e4m3, fp32 scales) with the fused SwiGLU epilogue writing H bf16,
+    L2 (bf16) on H from the same schedule.  Cold caches between steps."""
+    counts = wl.workload(3).counts
+    K, I, N2 = 7168, 2048, 7168
+    G, R = len(counts), sum(counts)
+    log(f"expert MLP: G={G}, U={R}, K={K}, I={I}, N2={N2}")
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda")
+    for k in ("W_gate", "W_up"):
+        inp.pop(k)
+    torch.cuda.empty_cache()
+    ws = mg.workspace(G, R)
+    H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((R, N2), dtype=torch.bfloat16, device="cuda")
+    mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
+    torch.cuda.synchronize()
+    bm = mg.stats_read(ws).block_m
+    stream = torch.cuda.current_stream()
+
+    def sched():
+        mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
+
+    def l1():
+        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"], block_m=bm)
+
+    def l2():
+        mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, block_m=bm, b_layout=mg.B_NK)
+    for _ in range(args.warmup):
+        sched(); l1(); l2()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        scratch.fill_(i & 255)
+        ev[i][0].record(stream)
+        sched()
+        ev[i][1].record(stream)
+        l1()
+        ev[i][2].record(stream)
+        l2()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    l1_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    l2_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    f1, f2 = 2.0 * R * K * 2 * I, 2.0 * R * I * N2
+    st = mg.stats_read(ws)
+    out = {
+        "metric": "effective TFLOPS (valid rows), expert MLP L1 -> SwiGLU -> L2",
+        "value": round((f1 + f2) / (ms * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 (L1) + bf16 (L2)", "data": "synthetic",
+        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8 + SwiGLU, L2 bf16)", "experts": G,
+                   "routed_rows": R, "K": K, "I": I, "N2": N2, "layout": "contiguous", "seed": 3,
+                   "weights": "W1 [G,2I,K] gate/up interleaved, W2 [G,N2,I]",
+                   "cache": "cold (512 MiB written between steps)"},
+        "block_m": "per-expert" if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m,
+        "l1_swiglu_ms": round(l1_ms, 4), "l2_ms": round(l2_ms, 4),
+        "l1_tflops": round(f1 / (l1_ms * 1e-3) / 1e12, 2), "l2_tflops": round(f2 / (l2_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(f1 / (l1_ms * 1e-3) / 1e12, 2), "peak": PEAK["fp8"],
+                     "unit": "TFLOP/s", "frac": round(f1 / (l1_ms * 1e-3) / 1e12 / PEAK["fp8"], 4),
+                     "traffic": None, "kernel": "L1 with the SwiGLU epilogue"},
+        "l2_roofline_frac": round(f2 / (l2_ms * 1e-3) / 1e12 / PEAK["bf16"], 4),
+        "wall_s_timed": round(wall, 4), "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +248,9 @@ def main():
     ap.add_argument("--weights", choices=("e4m3", "e2m1"), default="e4m3",
                     help="fp8 workload weights: e4m3 (as stated), or packed fp4 E2M1 [G,N,K/2] with E8M0 scales "
                          "(implies --scales e8m0; contiguous fp8 workloads only)")
+    ap.add_argument("--mlp", action="store_true",
+                    help="time the expert MLP (scheduler, L1 fp8 with the fused SwiGLU epilogue, L2 bf16) on the "
+                         "Zipf histogram at the DeepSeek-V3 expert shape instead of one grouped GEMM")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "
@@ -198,6 +272,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     mg.lib()
+    if args.mlp:
+        run_mlp(args)
+        return
     w = wl.workload(args.config)
     if args.weights == "e2m1":
         args.scales = "e8m0"

@@ -282,6 +282,32 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
     int block_m, const void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * First expert projection with SwiGLU fused into its epilogue, for the
+ * compute half of a fused MoE layer on one GPU (the DeepGEMM record's Mega
+ * MoE fuses the expert GEMMs and SwiGLU so activations stay on chip; here
+ * the gate and up products never reach HBM: only H does, once, in bf16).
+ * Driven by the tile list an earlier moegg_schedule or
+ * moegg_grouped_gemm_contiguous call left in `ws` (same G, rows_total).
+ *   A        [rows_total, K] as for the contiguous call (bf16 or e4m3 with
+ *            fp32 1x128 scales; E8M0 and fp4 are not supported here).
+ *   W1       [G, 2I, K] (K-contiguous; b_layout must be MOEGG_B_NK): for
+ *            q = 0 .. I/16 - 1 and w = 0 .. 15, row 32q + w is gate column
+ *            16q + w and row 32q + 16 + w is up column 16q + w.  W1_scale
+ *            (fp8): fp32 [G, K/128, 2I/128] over those interleaved rows.
+ *   H        bf16 [rows_total, I].  For each valid row R of expert e:
+ *                g = sum_k A[R,k] Wgate_e[k,c],  u = sum_k A[R,k] Wup_e[k,c],
+ *                H[R, c] = bf16_rne( silu(g) * u ),  silu(g) = g / (1 + e^-g)
+ *            with fp32 accumulation and fp32 SwiGLU.  Other rows untouched.
+ * The down projection is then moegg_grouped_gemm_contiguous_scheduled on H
+ * (K = I) from the same schedule.  Constraints: those of the contiguous call
+ * with N = 2I, so I % 128 == 0.  block_m as in the scheduled call.
+ */
+moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
+    const void* A, const void* A_scale, const void* W1, const void* W1_scale, void* H,
+    int G, int64_t rows_total, int K, int I, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
+    int block_m, const void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Masked layout for decode under graph capture (DeepGEMM record,
  * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
  * computes only the valid portions, with no CPU sync).

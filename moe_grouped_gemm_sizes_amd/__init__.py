@@ -82,6 +82,8 @@ EXPORTS = {
                                                        _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_contiguous": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                              _I32, _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_grouped_gemm_swiglu_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
+                                                   _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_masked": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _VP, _SZ, _VP]),
     "moegg_grouped_gemm_k_grouped": (_I32, [_VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _VP, _SZ, _VP]),
@@ -216,6 +218,27 @@ def grouped_gemm_contiguous(A, B, C, m_sizes, ws, A_scale=None, B_scale=None, se
         _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), m_sizes.numel(), A.shape[0], K, N,
         seg_align, _dtype(A, A_scale, B), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
         "moegg_grouped_gemm_contiguous")
+
+
+def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """Gate and up weights [G, I, K] (K-contiguous) -> W1 [G, 2I, K] in the row
+    order moegg_grouped_gemm_swiglu_scheduled takes: 16 gate rows, then the 16
+    up rows of the same outputs.  A one-time weight transform."""
+    G, I, K = w_gate.shape
+    if w_up.shape != w_gate.shape or I % 16:
+        raise ValueError("gate and up weights [G, I, K] with I % 16 == 0 expected")
+    return torch.stack([w_gate.reshape(G, I // 16, 16, K), w_up.reshape(G, I // 16, 16, K)], dim=2) \
+        .reshape(G, 2 * I, K).contiguous()
+
+
+def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=None, block_m: int = 0,
+                                  stream=None):
+    """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h)."""
+    K = A.shape[1]
+    I = W1.shape[1] // 2
+    _check(lib().moegg_grouped_gemm_swiglu_scheduled(
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), G, A.shape[0], K, I, _dtype(A, A_scale), B_NK, block_m,
+        _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 
 def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, b_layout: int = B_KN,

@@ -184,6 +184,27 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
                       "scheduled contiguous GEMM launch");
 }
 
+moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_scale, const void* W1,
+                                                   const void* W1_scale, void* H, int G, int64_t rows_total, int K,
+                                                   int I, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
+                                                   int block_m, const void* ws, size_t ws_bytes, void* stream) {
+    if (I < 1 || (int64_t)I * 2 > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    const int N = 2 * I;
+    moegg_status_t st = check_common(A, A_scale, W1, W1_scale, H, G, K, N, dtype, b_layout, 256);
+    if (st != MOEGG_OK) return st;
+    if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3) return MOEGG_ERR_UNSUPPORTED;
+    if (b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;
+    if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
+    const int esz = dtype == MOEGG_BF16 ? 2 : 1;
+    if (256ll * K * esz > kMaxBufferBytes || 256ll * N > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
+    ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
+    return hip_status(launch_contiguous_swiglu(a, dtype == MOEGG_FP8_E4M3, rows_total, block_m, (hipStream_t)stream),
+                      "SwiGLU GEMM launch");
+}
+
 moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, const void* B, const void* B_scale,
                                          void* C, const int32_t* masked_m, int G, int cap, int K, int N,
                                          moegg_dtype_t dtype, moegg_b_layout_t b_layout, void* ws,

@@ -292,6 +292,10 @@ template <bool FP8, bool E8 = false, bool W4 = false> using Contig64 = GCfg<FP8,
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// SiLU in fp32: x * sigmoid(x) = x / (1 + e^-x); e^-x overflowing to inf for
+// very negative x gives -0, the limit.
+__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+
 // One output tile of the contiguous or masked layout.
 //
 // Per K step every wave, in one instruction stream, reads its activation
@@ -601,11 +605,36 @@ struct TileGemm {
             }
         }
     }
+
+    // SwiGLU epilogue: the tile's columns come in groups of 32, gate columns
+    // then the matching up columns, so blocks 2i and 2i + 1 of a wave hold the
+    // gate and up values of the same 16 outputs in the same lanes.  Writes
+    // silu(gate) * up as bf16: 4 consecutive outputs per lane, rows <
+    // rows_valid, output row_bytes apart, BN / 2 outputs per tile.
+    __device__ __forceinline__ void store_swiglu(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
+        static_assert(C::NB % 2 == 0, "gate/up block pairs");
+        const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) {
+            const int row = wm * C::WTM + j * 16 + r16;
+            if (row < rows_valid) {
+#pragma unroll
+                for (int ip = 0; ip < C::NB / 2; ++ip) {
+                    const v4f gt = acc[2 * ip][j], up = acc[2 * ip + 1][j];
+                    const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
+                    v2i d;
+                    d.x = (int)pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y);
+                    d.y = (int)pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w);
+                    __builtin_amdgcn_raw_buffer_store_b64(d, rc, row * row_bytes + col * 2, 0, 0);
+                }
+            }
+        }
+    }
 };
 
 // One output tile: rows [row_start, row_start + rows_valid) of expert e's
 // segment, column tile ct.
-template <class C, bool B_KN>
+template <class C, bool B_KN, bool SWIGLU = false>
 __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows_valid,
                                             int ct) {
     const int n0 = ct * C::BN;
@@ -654,15 +683,23 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         tg.rsb = make_rsrc((const float*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
     }
     tg.run(lds, p.K / C::KSTEP, rows_valid);
-    const uint32_t c_row_bytes = (uint32_t)p.N * 2;
-    auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
-                        (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
-    tg.store_bf16(rc, c_row_bytes, rows_valid);
+    if constexpr (SWIGLU) {
+        // output H [rows_total, N / 2]: the tile's BN interleaved columns give BN / 2 outputs
+        const uint32_t h_row_bytes = (uint32_t)p.N;              // N / 2 bf16
+        auto rh = make_rsrc((char*)p.C + (size_t)row_start * h_row_bytes + (size_t)n0,
+                            (uint32_t)(rows_valid - 1) * h_row_bytes + C::BN);
+        tg.store_swiglu(rh, h_row_bytes, rows_valid);
+    } else {
+        const uint32_t c_row_bytes = (uint32_t)p.N * 2;
+        auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
+                            (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
+        tg.store_bf16(rc, c_row_bytes, rows_valid);
+    }
 }
 
 // M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout, one
 // tile height.
-template <class C, bool B_KN, bool MASKED>
+template <class C, bool B_KN, bool MASKED, bool SWIGLU = false>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / C::BN;
@@ -695,7 +732,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
         row_start = t.row_start;
         rows_valid = t.rows_valid;
     }
-    contig_tile<C, B_KN>(p, lds, e, row_start, rows_valid, ct);
+    contig_tile<C, B_KN, SWIGLU>(p, lds, e, row_start, rows_valid, ct);
 }
 
 // Per-expert tile heights (block_m = MOEGG_BLOCK_M_PER_EXPERT): the tile list
@@ -705,7 +742,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
 // does not pay for a 256-row tile, and the 128- and 64-row configurations'
 // deeper stage rings keep their loads further ahead.  All three share one
 // launch; the configuration is uniform per workgroup.
-template <bool FP8, bool B_KN, bool E8, bool W4>
+template <bool FP8, bool B_KN, bool E8, bool W4, bool SWIGLU = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / 256;
@@ -719,11 +756,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigA
     item_to_tiles(item, n_rt, n_ct, rt, ct);
     const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
     if (t.rows_valid > 128)
-        contig_tile<Contig256<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
     else if (t.rows_valid > 64)
-        contig_tile<Contig128<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
     else
-        contig_tile<Contig64<FP8, E8, W4>, B_KN>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
 }
 
 // ---------------------------------------------------------------- K-grouped
@@ -843,10 +880,10 @@ static hipError_t allow_lds(int bytes) {
     return once;
 }
 
-template <class C, bool B_KN, bool MASKED>
+template <class C, bool B_KN, bool MASKED, bool SWIGLU = false>
 static hipError_t launch_one(const ContigArgs& a, int grid, hipStream_t s) {
-    auto k = grouped_gemm_kernel<C, B_KN, MASKED>;
-    hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, MASKED>>(C::LDS_BYTES);
+    auto k = grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>;
+    hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>>(C::LDS_BYTES);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, a);
     return hipGetLastError();
@@ -856,7 +893,7 @@ static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
 
 // Launch the contiguous GEMM for tile height block_m (0 = every candidate;
 // the ones the device did not choose exit at entry).
-template <bool FP8, bool B_KN, bool E8, bool W4 = false>
+template <bool FP8, bool B_KN, bool E8, bool W4 = false, bool SW = false>
 static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
     const int64_t n_ct = a.N / 256;
     hipError_t err = hipSuccess;
@@ -865,23 +902,23 @@ static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int b
     if (block_m == MOEGG_BLOCK_M_PER_EXPERT || block_m == 0) {
         constexpr int lds = std::max({Contig256<FP8, E8, W4>::LDS_BYTES, Contig128<FP8, E8, W4>::LDS_BYTES,
                                       Contig64<FP8, E8, W4>::LDS_BYTES});
-        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4>>(lds);
+        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4, SW>>(lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4>), dim3(grid_for(256)), dim3(512), lds,
-                           s, a);
+        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4, SW>), dim3(grid_for(256)), dim3(512),
+                           lds, s, a);
         err = hipGetLastError();
         if (err != hipSuccess || block_m != 0) return err;
     }
     if (block_m == 0 || block_m == 256) {
-        err = launch_one<Contig256<FP8, E8, W4>, B_KN, false>(a, grid_for(256), s);
+        err = launch_one<Contig256<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(256), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 128) {
-        err = launch_one<Contig128<FP8, E8, W4>, B_KN, false>(a, grid_for(128), s);
+        err = launch_one<Contig128<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(128), s);
         if (err != hipSuccess) return err;
     }
     if (block_m == 0 || block_m == 64) {
-        err = launch_one<Contig64<FP8, E8, W4>, B_KN, false>(a, grid_for(64), s);
+        err = launch_one<Contig64<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(64), s);
     }
     return err;
 }
@@ -895,6 +932,11 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
                          : launch_contig_t<true, false, false>(a, rows_total, block_m, s);
     return b_kn ? launch_contig_t<false, true, false>(a, rows_total, block_m, s)
                 : launch_contig_t<false, false, false>(a, rows_total, block_m, s);
+}
+
+hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s) {
+    return fp8 ? launch_contig_t<true, false, false, false, true>(a, rows_total, block_m, s)
+               : launch_contig_t<false, false, false, false, true>(a, rows_total, block_m, s);
 }
 
 int masked_block_m() { return MaskedCfg<false>::BM; }

@@ -41,6 +41,9 @@ hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void
 // w4: packed E2M1 weights [G, N, K/2] (needs fp8 activations, E8M0 scales, !b_kn)
 hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,
                              int block_m, hipStream_t s);
+// L1 GEMM with the SwiGLU epilogue: [G, N, K] weights whose N columns interleave
+// gate and up in groups of 16; C receives [rows_total, N / 2] bf16
+hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);
 int masked_block_m();

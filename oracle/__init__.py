@@ -14,6 +14,7 @@ Parts:
   scales (the contiguous layout), with its own E2M1 decoder.
 - select.py: the distribution-aware tile-height choice (sorted, normalized
   histogram matched against an exemplar table, with hysteresis).
+- mlp.py: the expert MLP, L1 projection -> SwiGLU -> L2 projection, in fp64.
 
 Every function states the page and section it follows.  Parity pins live in
 tests/test_oracle_*.py and tests/golden/.
@@ -22,3 +23,4 @@ from . import accounting  # noqa: F401
 from . import gemm  # noqa: F401
 from . import fp4  # noqa: F401
 from . import select  # noqa: F401
+from . import mlp  # noqa: F401

@@ -1,0 +1,67 @@
+"""Expert MLP of a MoE layer on one GPU: L1 projection -> SwiGLU -> L2
+projection, written out in fp64 (test infrastructure only).
+
+The DeepGEMM record's Mega MoE fuses an expert's two GEMMs and the SwiGLU
+between them.  For each valid row R of expert e (contiguous layout):
+
+    g[R, c] = sum_k A[R, k] * Wgate_e[k, c]
+    u[R, c] = sum_k A[R, k] * Wup_e[k, c]
+    h[R, c] = silu(g) * u,   silu(x) = x / (1 + e^-x)
+    y[R, n] = sum_c h[R, c] * W2_e[c, n]
+
+The library takes the gate and up weights as one matrix W1 [G, 2I, K] whose
+row 32q + w is gate column 16q + w and row 32q + 16 + w is up column 16q + w
+(w < 16); `split_gate_up` undoes that order by its definition.  The two L1
+sums come from the C oracle (gemm.contiguous, fp64 on the decoded bf16/e4m3
+bits and fp32 scales); silu, the product and the L2 sum are plain numpy fp64.
+"""
+from __future__ import annotations
+
+from typing import Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import accounting as acc
+from . import gemm as og
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):             # e^-x = inf for very negative x: the limit -0
+        return x / (1.0 + np.exp(-x))
+
+
+def split_gate_up(c: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Columns of an interleaved [.., 2I] result -> (gate [.., I], up [.., I])."""
+    n2 = c.shape[-1]
+    I = n2 // 2
+    cols = np.arange(I)
+    gate_idx = 32 * (cols // 16) + cols % 16
+    return c[..., gate_idx], c[..., gate_idx + 16]
+
+
+def swiglu_rows(A: torch.Tensor, W1: torch.Tensor, counts: Sequence[int], rows: Sequence[int],
+                A_scale=None, W1_scale=None, seg_align: int = 1) -> np.ndarray:
+    """h for the given rows, fp64 [len(rows), I].  A [rows_total, K] and W1
+    [G, 2I, K] hold the bits the GPU receives (bf16, or e4m3 with fp32
+    1x128 / 128x128 scales over W1's interleaved rows)."""
+    B = W1.transpose(1, 2).contiguous()                   # [G, K, 2I]: the oracle's B layout
+    c = og.contiguous(A, B, counts, rows, seg_align=seg_align, A_scale=A_scale, B_scale=W1_scale)
+    g, u = split_gate_up(c)
+    return silu(g) * u
+
+
+def down_rows(h: np.ndarray, W2: torch.Tensor, counts: Sequence[int], rows: Sequence[int],
+              seg_align: int = 1) -> np.ndarray:
+    """y = h @ W2_e for the given rows (h fp64, as swiglu_rows returns it);
+    W2 [G, N2, I] bf16 (K-contiguous).  fp64 [len(rows), N2]."""
+    offs = acc.segment_offsets(counts, seg_align)
+    out = np.empty((len(rows), W2.shape[1]), dtype=np.float64)
+    by_e = {}
+    for i, r in enumerate(rows):
+        e = next(e for e in range(len(counts)) if offs[e] <= r < offs[e] + counts[e])
+        by_e.setdefault(e, []).append(i)
+    for e, idx in by_e.items():
+        w2 = W2[e].double().numpy()                  # [N2, I]
+        out[idx] = h[idx] @ w2.T
+    return out

@@ -15,6 +15,7 @@ import workloads as wl
 from oracle import accounting as acc
 from oracle import fp4
 from oracle import gemm as og
+from oracle import mlp as omlp
 from oracle import select as oselect
 from tests import parity as P
 
@@ -701,6 +702,95 @@ def test_exemplar_selection_in_a_graph():
         ref = og.contiguous(cpu["A"], cpu["B"], counts, rows)
         err = og.rel_frobenius(P.rows_as_float(C, rows), ref)
         assert err <= P.TOL["bf16"], err
+
+
+# ----------------------------------------------------------------- expert MLP: L1 -> SwiGLU -> L2
+
+# y goes through two bf16 roundings in sequence (h, then y), each about 1.7e-3 of
+# rel. Frobenius error on this data; in quadrature about 2.4e-3
+TOL_MLP_BF16 = 3e-3
+
+
+def run_mlp(counts, inp, block_m, N2):
+    G, R = len(counts), sum(counts)
+    I = inp["W1"].shape[1] // 2
+    ws = mg.workspace(G, R)
+    H = P.sentinel_like((R, I))
+    Y = P.sentinel_like((R, N2))
+    mg.schedule(inp["counts"], R, ws, block_m=block_m, N=2 * I)
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"],
+                                     block_m=block_m)
+    mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, block_m=block_m, b_layout=mg.B_NK)
+    torch.cuda.synchronize()
+    return H, Y, ws
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+def test_swiglu_and_down_projection(dtype, block_m):
+    """L1 with the fused SwiGLU epilogue, then L2 on H from the same schedule:
+    H and y on every valid row against the fp64 chain."""
+    counts = [70, 0, 300, 6, 129, 3]
+    K, I, N2 = 256, 256, 512
+    announce("expert MLP", dtype, counts, "block_m", block_m)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype=dtype, seed=12, device="cuda")
+    H, Y, ws = run_mlp(counts, inp, block_m, N2)
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = list(range(sum(counts)))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
+    y = omlp.down_rows(h, cpu["W2"], counts, rows)
+    got_h, got_y = P.rows_as_float(H, rows), P.rows_as_float(Y, rows)
+    assert np.isfinite(got_h).all() and np.isfinite(got_y).all()
+    eh, ey = og.rel_frobenius(got_h, h), og.rel_frobenius(got_y, y)
+    print(f"mlp {dtype} block_m={block_m} h {eh:.3e} y {ey:.3e}", flush=True)
+    assert eh <= P.TOL[dtype], eh
+    assert ey <= (TOL_MLP_BF16 if dtype == "bf16" else P.TOL["fp8"]), ey
+
+
+def test_swiglu_leaves_other_rows_alone_and_handles_empty():
+    counts = [0, 37, 0, 0]
+    K, I, N2 = 128, 128, 256
+    announce("expert MLP gaps", counts)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="bf16", seed=13, device="cuda")
+    R = 64                                                   # rows past the segment stay untouched
+    A = torch.zeros((R, K), dtype=torch.bfloat16, device="cuda")
+    A[:37] = inp["A"]
+    H = P.sentinel_like((R, I))
+    ws = mg.workspace(4, R)
+    mg.schedule(inp["counts"], R, ws, block_m=64, N=2 * I)
+    mg.grouped_gemm_swiglu_scheduled(A, inp["W1"], H, 4, ws, block_m=64)
+    torch.cuda.synchronize()
+    assert bool((H[37:].view(torch.int16) == P.SENTINEL_BITS).all())
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, list(range(37)))
+    assert og.rel_frobenius(P.rows_as_float(H, range(37)), h) <= P.TOL["bf16"]
+    ws0 = mg.workspace(4, R)
+    mg.schedule(torch.zeros(4, dtype=torch.int32, device="cuda"), R, ws0, block_m=0, N=2 * I)
+    H0 = P.sentinel_like((R, I))
+    mg.grouped_gemm_swiglu_scheduled(A, inp["W1"], H0, 4, ws0, block_m=0)
+    torch.cuda.synchronize()
+    assert bool((H0.view(torch.int16) == P.SENTINEL_BITS).all())
+
+
+def test_expert_mlp_full_size():
+    """DeepSeek-V3-shaped experts on the Zipf histogram (64 experts, 32768 rows):
+    K = 7168, I = 2048, N2 = 7168; fp8 L1 with fp32 scales, bf16 L2; sampled rows."""
+    counts = wl.workload(3).counts
+    K, I, N2 = 7168, 2048, 7168
+    announce("expert MLP full size", K, I, N2)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda")
+    H, Y, ws = run_mlp(counts, inp, 0, N2)
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = P.sample_rows_contiguous(counts, 1, 256, extra=32, seed=15)
+    got_h, got_y = P.rows_as_float(H, rows), P.rows_as_float(Y, rows)
+    cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("W_gate", "W_up")}
+    del inp
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
+    y = omlp.down_rows(h, cpu["W2"], counts, rows)
+    eh, ey = og.rel_frobenius(got_h, h), og.rel_frobenius(got_y, y)
+    print(f"mlp full size rows={len(rows)} h {eh:.3e} y {ey:.3e}", flush=True)
+    assert eh <= P.TOL["fp8"] and ey <= P.TOL["fp8"], (eh, ey)
 
 
 # ----------------------------------------------------------------- K-grouped
