@@ -552,6 +552,24 @@ def test_contiguous_fp8_fp4_integer_exact(block_m):
     assert np.array_equal(got, ref)
 
 
+def test_contiguous_fp8_fp4_aligned_segments():
+    """fp4 weights with segments aligned to 64 rows (gaps between experts stay untouched)."""
+    counts = [70, 0, 300, 6, 129, 3]
+    announce("contiguous fp8 x fp4 aligned", counts)
+    w = wl.Workload("f4a", "contiguous", "fp8", counts, K=256, N=512, seg_align=64, values="normal", seed=19,
+                    scales="e8m0", weights="e2m1")
+    inp = wl.materialize(w, "cuda")
+    C, ws = run_contiguous_fp4(w, inp, 0)
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = [r for e, s0 in enumerate(acc.segment_offsets(counts, 64)[:-1]) for r in range(s0, s0 + counts[e])]
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, rows, seg_align=64)
+    got = P.rows_as_float(C, rows)
+    assert np.isfinite(got).all()
+    assert og.rel_frobenius(got, ref) <= P.TOL["fp8"]
+    assert P.untouched_rows_ok(C, counts, 64)
+
+
 def test_contiguous_fp8_fp4_full_size():
     """The Zipf workload (64 experts, 32768 rows, K = 7168, N = 4096) with fp4
     weights, device-chosen height, on sampled rows."""
@@ -617,6 +635,21 @@ def test_exemplar_selection_matches_oracle(name):
     else:
         expect = acc.tile_list(counts, bm, 1)
     assert mg.tile_list_read(ws, len(expect) + 4) == expect
+
+
+@pytest.mark.parametrize("G", [255, 1000, 4096])
+def test_exemplar_descriptor_large_expert_counts(G):
+    """The device sort covers up to 4096 experts (padded to a power of two):
+    descriptor and choice against the oracle on random skewed histograms."""
+    rng = random.Random(G)
+    counts = [0 if rng.random() < 0.3 else int(rng.paretovariate(1.1) * 3) for _ in range(G)]
+    announce("exemplar large G", G, sum(counts))
+    table = mg.exemplar_table()
+    rows = table.cpu().tolist()
+    ws = torch.zeros(mg.workspace_bytes(G, max(1, sum(counts))), dtype=torch.uint8, device="cuda")
+    got, st = run_selection(counts, table, ws)
+    idx, d = oselect.select(counts, rows)
+    check_selection(counts, rows, got, st, idx, d)
 
 
 def test_exemplar_hysteresis_sequence():
