@@ -159,18 +159,22 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
 
 def run_mlp(args):
     """Expert MLP on the Zipf histogram (64 experts, 32768 rows), DeepSeek-V3 expert shape: K 7168, I 2048,
-    N2 7168.  One step: scheduler, L1 (fp8 e4m3, fp32 scales) with the fused SwiGLU epilogue writing H bf16,
-    L2 (bf16) on H from the same schedule.  Cold caches between steps."""
+    N2 7168.  One step: scheduler, L1 (fp8 e4m3, fp32 scales) with the fused SwiGLU epilogue writing H, L2 on H
+    from the same schedule.  --mlp-h fp8 (default): H e4m3 with 1x128 scales quantized in the epilogue and an
+    fp8 L2; bf16: H bf16 and a bf16 L2.  Cold caches between steps."""
     counts = wl.workload(3).counts
     K, I, N2 = 7168, 2048, 7168
     G, R = len(counts), sum(counts)
-    log(f"expert MLP: G={G}, U={R}, K={K}, I={I}, N2={N2}")
-    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda")
+    fp8_h = args.mlp_h == "fp8"
+    log(f"expert MLP: G={G}, U={R}, K={K}, I={I}, N2={N2}, H {args.mlp_h}")
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda",
+                             l2="fp8" if fp8_h else "bf16")
     for k in ("W_gate", "W_up"):
         inp.pop(k)
     torch.cuda.empty_cache()
     ws = mg.workspace(G, R)
-    H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((R, I), dtype=torch.float8_e4m3fn if fp8_h else torch.bfloat16, device="cuda")
+    Hs = torch.empty((R, I // 128), device="cuda") if fp8_h else None
     Y = torch.empty((R, N2), dtype=torch.bfloat16, device="cuda")
     mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
     torch.cuda.synchronize()
@@ -181,10 +185,12 @@ def run_mlp(args):
         mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
 
     def l1():
-        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"], block_m=bm)
+        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"], block_m=bm,
+                                         H_scale=Hs)
 
     def l2():
-        mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, block_m=bm, b_layout=mg.B_NK)
+        mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=bm,
+                                             b_layout=mg.B_NK)
     for _ in range(args.warmup):
         sched(); l1(); l2()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -211,8 +217,9 @@ def run_mlp(args):
         "metric": "effective TFLOPS (valid rows), expert MLP L1 -> SwiGLU -> L2",
         "value": round((f1 + f2) / (ms * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3 (L1) + bf16 (L2)", "data": "synthetic",
-        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8 + SwiGLU, L2 bf16)", "experts": G,
+        "vs_baseline": None, "dtype": "fp8_e4m3" if fp8_h else "fp8_e4m3 (L1) + bf16 (L2)", "data": "synthetic",
+        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8 + SwiGLU, L2 %s)" % ("fp8" if fp8_h else "bf16"),
+                   "experts": G,
                    "routed_rows": R, "K": K, "I": I, "N2": N2, "layout": "contiguous", "seed": 3,
                    "weights": "W1 [G,2I,K] gate/up interleaved, W2 [G,N2,I]",
                    "cache": "cold (512 MiB written between steps)"},
@@ -222,7 +229,7 @@ def run_mlp(args):
         "roofline": {"bound": "mfma", "achieved": round(f1 / (l1_ms * 1e-3) / 1e12, 2), "peak": PEAK["fp8"],
                      "unit": "TFLOP/s", "frac": round(f1 / (l1_ms * 1e-3) / 1e12 / PEAK["fp8"], 4),
                      "traffic": None, "kernel": "L1 with the SwiGLU epilogue"},
-        "l2_roofline_frac": round(f2 / (l2_ms * 1e-3) / 1e12 / PEAK["bf16"], 4),
+        "l2_roofline_frac": round(f2 / (l2_ms * 1e-3) / 1e12 / PEAK["fp8" if fp8_h else "bf16"], 4),
         "wall_s_timed": round(wall, 4), "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -251,6 +258,8 @@ def main():
     ap.add_argument("--mlp", action="store_true",
                     help="time the expert MLP (scheduler, L1 fp8 with the fused SwiGLU epilogue, L2 bf16) on the "
                          "Zipf histogram at the DeepSeek-V3 expert shape instead of one grouped GEMM")
+    ap.add_argument("--mlp-h", choices=("fp8", "bf16"), default="fp8",
+                    help="with --mlp: H quantized to e4m3 in L1's epilogue and an fp8 L2 (default), or bf16 H and L2")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB, so that a "
                          "counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by "

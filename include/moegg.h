@@ -294,16 +294,23 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  *            q = 0 .. I/16 - 1 and w = 0 .. 15, row 32q + w is gate column
  *            16q + w and row 32q + 16 + w is up column 16q + w.  W1_scale
  *            (fp8): fp32 [G, K/128, 2I/128] over those interleaved rows.
- *   H        bf16 [rows_total, I].  For each valid row R of expert e:
+ *   H        [rows_total, I].  For each valid row R of expert e:
  *                g = sum_k A[R,k] Wgate_e[k,c],  u = sum_k A[R,k] Wup_e[k,c],
- *                H[R, c] = bf16_rne( silu(g) * u ),  silu(g) = g / (1 + e^-g)
- *            with fp32 accumulation and fp32 SwiGLU.  Other rows untouched.
+ *                h[R, c] = silu(g) * u,  silu(g) = g / (1 + e^-g)
+ *            with fp32 accumulation and fp32 SwiGLU.  H_scale NULL: H is bf16,
+ *            H[R, c] = bf16_rne(h).  H_scale set: H holds e4m3 codes and
+ *            H_scale fp32 [rows_total, I/128] one scale per 1x128 group, the
+ *            input format of the fp8 contiguous call:
+ *                s = amax over the group of |h| / 448 (1 if the amax is 0),
+ *                H[R, c] = e4m3_rne(clamp(h / s, -448, 448)).
+ *            Other rows untouched.
  * The down projection is then moegg_grouped_gemm_contiguous_scheduled on H
- * (K = I) from the same schedule.  Constraints: those of the contiguous call
- * with N = 2I, so I % 128 == 0.  block_m as in the scheduled call.
+ * (K = I, with H_scale as its A_scale in the e4m3 case) from the same
+ * schedule.  Constraints: those of the contiguous call with N = 2I, so
+ * I % 128 == 0; H_scale 4-byte aligned.  block_m as in the scheduled call.
  */
 moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
-    const void* A, const void* A_scale, const void* W1, const void* W1_scale, void* H,
+    const void* A, const void* A_scale, const void* W1, const void* W1_scale, void* H, void* H_scale,
     int G, int64_t rows_total, int K, int I, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
     int block_m, const void* ws, size_t ws_bytes, void* stream);
 

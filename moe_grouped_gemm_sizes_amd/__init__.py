@@ -82,8 +82,8 @@ EXPORTS = {
                                                        _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_contiguous": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                              _I32, _I32, _I32, _VP, _SZ, _VP]),
-    "moegg_grouped_gemm_swiglu_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32, _I32,
-                                                   _I32, _VP, _SZ, _VP]),
+    "moegg_grouped_gemm_swiglu_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
+                                                   _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_masked": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _VP, _SZ, _VP]),
     "moegg_grouped_gemm_k_grouped": (_I32, [_VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _VP, _SZ, _VP]),
@@ -232,13 +232,16 @@ def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor
 
 
 def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=None, block_m: int = 0,
-                                  stream=None):
-    """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h)."""
+                                  H_scale=None, stream=None):
+    """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h).
+    H bf16 [rows, I]; or, with H_scale (fp32 [rows, I/128]), H float8_e4m3fn codes."""
     K = A.shape[1]
     I = W1.shape[1] // 2
+    if (H_scale is None) != (H.dtype == torch.bfloat16):
+        raise ValueError("H: bf16 without H_scale, float8_e4m3fn with it")
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
-        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), G, A.shape[0], K, I, _dtype(A, A_scale), B_NK, block_m,
-        _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I, _dtype(A, A_scale),
+        B_NK, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 
 def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, b_layout: int = B_KN,

@@ -185,10 +185,12 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
 }
 
 moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_scale, const void* W1,
-                                                   const void* W1_scale, void* H, int G, int64_t rows_total, int K,
-                                                   int I, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
-                                                   int block_m, const void* ws, size_t ws_bytes, void* stream) {
+                                                   const void* W1_scale, void* H, void* H_scale, int G,
+                                                   int64_t rows_total, int K, int I, moegg_dtype_t dtype,
+                                                   moegg_b_layout_t b_layout, int block_m, const void* ws,
+                                                   size_t ws_bytes, void* stream) {
     if (I < 1 || (int64_t)I * 2 > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    if (H_scale && !aligned(H_scale, 4)) return MOEGG_ERR_INVALID_ARG;
     const int N = 2 * I;
     moegg_status_t st = check_common(A, A_scale, W1, W1_scale, H, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
@@ -200,7 +202,8 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
-    ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
+    ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total,
+                 H_scale};
     return hip_status(launch_contiguous_swiglu(a, dtype == MOEGG_FP8_E4M3, rows_total, block_m, (hipStream_t)stream),
                       "SwiGLU GEMM launch");
 }

@@ -296,6 +296,20 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // very negative x gives -0, the limit.
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
 
+// OCP e4m3 (bias 7) code of x, |x| <= 448, round to nearest even, subnormals
+// included.  Below 2^-6 the e4m3 values are multiples of 2^-9: the code is
+// rint(|x| * 512) (exact scaling, rint rounds half to even; 8 is the smallest
+// normal, code 0x08).  Above, the fp32 mantissa is rounded to 3 bits, nearest
+// even, a carry moving into the exponent; 448 = 1.75 * 2^8 is code 0x7E.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.f);
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    return sign | ((((b >> 23) - 120u) << 3) | ((b >> 20) & 7u));
+}
+
 // One output tile of the contiguous or masked layout.
 //
 // Per K step every wave, in one instruction stream, reads its activation
@@ -630,11 +644,73 @@ struct TileGemm {
             }
         }
     }
+
+    // SwiGLU epilogue with H quantized for an e4m3 down projection: the tile's
+    // BN / 2 = 128 outputs of a row form one 1x128 group.  Its amax is reduced
+    // over the lane's 4 x NB / 2 values, the four lane groups holding the row
+    // (lane shuffles) and the WAVES_N wave columns (through LDS, which no stage
+    // uses any more); scale = amax / 448 (1 when amax = 0); code = e4m3(h /
+    // scale), clamped to +-448, round to nearest even (e4m3_code).  Codes go to rh (4 per
+    // lane and 16-column block), the scale to rs[row, group].
+    __device__ __forceinline__ void store_swiglu_e4m3(__amdgpu_buffer_rsrc_t rh, uint32_t row_bytes,
+                                                      __amdgpu_buffer_rsrc_t rs, uint32_t s_row_bytes, int group,
+                                                      char* lds, int rows_valid) {
+        static_assert(C::NB % 2 == 0 && C::BN == 256, "one 128-wide group per tile row");
+        const int lane = threadIdx.x & 63, g = lane >> 4;
+        float h[C::MB][C::NB / 2][4];
+        float amax[C::MB];
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) {
+            amax[j] = 0.f;
+#pragma unroll
+            for (int ip = 0; ip < C::NB / 2; ++ip) {
+                const v4f gt = acc[2 * ip][j], up = acc[2 * ip + 1][j];
+                h[j][ip][0] = silu(gt.x) * up.x;
+                h[j][ip][1] = silu(gt.y) * up.y;
+                h[j][ip][2] = silu(gt.z) * up.z;
+                h[j][ip][3] = silu(gt.w) * up.w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) amax[j] = fmaxf(amax[j], fabsf(h[j][ip][t]));
+            }
+            amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16, 64));
+            amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32, 64));
+        }
+        // every wave's DMAs have landed once all waves pass this barrier
+        __syncthreads();
+        float* red = (float*)lds;                             // [WAVES_N][BM]
+        if (g == 0) {
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j) red[wn * C::BM + wm * C::WTM + j * 16 + r16] = amax[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < C::MB; ++j) {
+            const int row = wm * C::WTM + j * 16 + r16;
+            float m = 0.f;
+#pragma unroll
+            for (int w = 0; w < C::WAVES_N; ++w) m = fmaxf(m, red[w * C::BM + row]);
+            const float scale = m > 0.f ? m / 448.f : 1.f;
+            if (row < rows_valid) {
+#pragma unroll
+                for (int ip = 0; ip < C::NB / 2; ++ip) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        v |= e4m3_code(fminf(fmaxf(h[j][ip][t] / scale, -448.f), 448.f)) << (8 * t);
+                    const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
+                    __builtin_amdgcn_raw_buffer_store_b32((int)v, rh, row * row_bytes + col, 0, 0);
+                }
+                if (wn == 0 && g == 0)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, scale), rs,
+                                                          row * s_row_bytes + group * 4, 0, 0);
+            }
+        }
+    }
 };
 
 // One output tile: rows [row_start, row_start + rows_valid) of expert e's
 // segment, column tile ct.
-template <class C, bool B_KN, bool SWIGLU = false>
+template <class C, bool B_KN, int SWIGLU = 0>
 __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows_valid,
                                             int ct) {
     const int n0 = ct * C::BN;
@@ -683,7 +759,16 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         tg.rsb = make_rsrc((const float*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
     }
     tg.run(lds, p.K / C::KSTEP, rows_valid);
-    if constexpr (SWIGLU) {
+    if constexpr (SWIGLU == 2) {
+        // output H e4m3 [rows_total, N / 2] and its scales [rows_total, N / 256]: the tile's
+        // BN / 2 = 128 outputs per row are one scale group (group ct)
+        const uint32_t h_row_bytes = (uint32_t)p.N / 2;
+        const uint32_t s_row_bytes = (uint32_t)(p.N / 256) * 4;
+        auto rh = make_rsrc((char*)p.C + (size_t)row_start * h_row_bytes + (size_t)ct * (C::BN / 2),
+                            (uint32_t)(rows_valid - 1) * h_row_bytes + C::BN / 2);
+        auto rs = make_rsrc((char*)p.C_scale + (size_t)row_start * s_row_bytes, (uint32_t)rows_valid * s_row_bytes);
+        tg.store_swiglu_e4m3(rh, h_row_bytes, rs, s_row_bytes, ct, lds, rows_valid);
+    } else if constexpr (SWIGLU == 1) {
         // output H [rows_total, N / 2]: the tile's BN interleaved columns give BN / 2 outputs
         const uint32_t h_row_bytes = (uint32_t)p.N;              // N / 2 bf16
         auto rh = make_rsrc((char*)p.C + (size_t)row_start * h_row_bytes + (size_t)n0,
@@ -699,7 +784,7 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
 
 // M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout, one
 // tile height.
-template <class C, bool B_KN, bool MASKED, bool SWIGLU = false>
+template <class C, bool B_KN, bool MASKED, int SWIGLU = 0>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / C::BN;
@@ -742,7 +827,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
 // does not pay for a 256-row tile, and the 128- and 64-row configurations'
 // deeper stage rings keep their loads further ahead.  All three share one
 // launch; the configuration is uniform per workgroup.
-template <bool FP8, bool B_KN, bool E8, bool W4, bool SWIGLU = false>
+template <bool FP8, bool B_KN, bool E8, bool W4, int SWIGLU = 0>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / 256;
@@ -880,7 +965,7 @@ static hipError_t allow_lds(int bytes) {
     return once;
 }
 
-template <class C, bool B_KN, bool MASKED, bool SWIGLU = false>
+template <class C, bool B_KN, bool MASKED, int SWIGLU = 0>
 static hipError_t launch_one(const ContigArgs& a, int grid, hipStream_t s) {
     auto k = grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>;
     hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>>(C::LDS_BYTES);
@@ -893,7 +978,7 @@ static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
 
 // Launch the contiguous GEMM for tile height block_m (0 = every candidate;
 // the ones the device did not choose exit at entry).
-template <bool FP8, bool B_KN, bool E8, bool W4 = false, bool SW = false>
+template <bool FP8, bool B_KN, bool E8, bool W4 = false, int SW = 0>
 static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
     const int64_t n_ct = a.N / 256;
     hipError_t err = hipSuccess;
@@ -935,8 +1020,11 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
 }
 
 hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s) {
-    return fp8 ? launch_contig_t<true, false, false, false, true>(a, rows_total, block_m, s)
-               : launch_contig_t<false, false, false, false, true>(a, rows_total, block_m, s);
+    const bool q = a.C_scale != nullptr;      // e4m3 H with fp32 scales
+    if (fp8) return q ? launch_contig_t<true, false, false, false, 2>(a, rows_total, block_m, s)
+                      : launch_contig_t<true, false, false, false, 1>(a, rows_total, block_m, s);
+    return q ? launch_contig_t<false, false, false, false, 2>(a, rows_total, block_m, s)
+             : launch_contig_t<false, false, false, false, 1>(a, rows_total, block_m, s);
 }
 
 int masked_block_m() { return MaskedCfg<false>::BM; }

@@ -51,6 +51,41 @@ def swiglu_rows(A: torch.Tensor, W1: torch.Tensor, counts: Sequence[int], rows: 
     return silu(g) * u
 
 
+def _e4m3_positive() -> np.ndarray:
+    """Values of the non-negative finite e4m3 codes 0x00 .. 0x7E, ascending with the code."""
+    return np.array([og.dec_e4m3(c) for c in range(0x7F)], dtype=np.float64)
+
+
+_E4M3_POS = None
+
+
+def e4m3_rne(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 value to each |x| <= 448, ties to the even code (the code's
+    last mantissa bit 0), sign kept."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = _e4m3_positive()
+    v = _E4M3_POS
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(v, a), 1, len(v) - 1)
+    lo = hi - 1
+    dlo, dhi = a - v[lo], v[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return np.sign(x) * v[pick]
+
+
+def quantize_groups(h: np.ndarray, group: int = 128) -> Tuple[np.ndarray, np.ndarray]:
+    """h [rows, I] -> (e4m3 values [rows, I], scales [rows, I / group]): per
+    1 x group slice s = amax / 448 (1 if the amax is 0), value = e4m3_rne of
+    h / s clamped to +-448."""
+    r, n = h.shape
+    g = h.reshape(r, n // group, group)
+    amax = np.abs(g).max(axis=2)
+    s = np.where(amax > 0, amax / 448.0, 1.0)
+    q = e4m3_rne(np.clip(g / s[:, :, None], -448.0, 448.0))
+    return np.ascontiguousarray(q.reshape(r, n)), np.ascontiguousarray(s)
+
+
 def down_rows(h: np.ndarray, W2: torch.Tensor, counts: Sequence[int], rows: Sequence[int],
               seg_align: int = 1) -> np.ndarray:
     """y = h @ W2_e for the given rows (h fp64, as swiglu_rows returns it);

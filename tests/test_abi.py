@@ -165,19 +165,20 @@ def test_exemplar_struct_matches_the_header():
 
 def test_swiglu_validation():
     f = mg.lib().moegg_grouped_gemm_swiglu_scheduled
-    ok = [FAKE, None, FAKE, None, FAKE, 8, 132, 512, 128, mg.BF16, mg.B_NK, 0, FAKE, 1 << 20, None]
+    ok = [FAKE, None, FAKE, None, FAKE, None, 8, 132, 512, 128, mg.BF16, mg.B_NK, 0, FAKE, 1 << 20, None]
 
     def call(i, v):
         a = list(ok)
         a[i] = v
         return f(*a)
     assert call(0, None) == mg.ERR_INVALID_ARG              # A
-    assert call(8, 0) == mg.ERR_INVALID_ARG                 # I
-    assert call(8, 64) == mg.ERR_UNSUPPORTED                # 2I % 256
-    assert call(10, mg.B_KN) == mg.ERR_UNSUPPORTED          # W1 must be K-contiguous
-    assert call(9, mg.FP8_E4M3_E8M0) == mg.ERR_INVALID_ARG  # no scales given
-    assert call(12, None) == mg.ERR_WORKSPACE
-    assert call(11, 48) == mg.ERR_UNSUPPORTED               # block_m
+    assert call(9, 0) == mg.ERR_INVALID_ARG                 # I
+    assert call(9, 64) == mg.ERR_UNSUPPORTED                # 2I % 256
+    assert call(11, mg.B_KN) == mg.ERR_UNSUPPORTED          # W1 must be K-contiguous
+    assert call(10, mg.FP8_E4M3_E8M0) == mg.ERR_INVALID_ARG  # no scales given
+    assert call(13, None) == mg.ERR_WORKSPACE
+    assert call(12, 48) == mg.ERR_UNSUPPORTED               # block_m
+    assert call(5, ctypes.c_void_p(0x100002)) == mg.ERR_INVALID_ARG   # H_scale alignment
 
 
 def test_read_validation():

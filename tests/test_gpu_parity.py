@@ -781,6 +781,106 @@ def test_swiglu_and_down_projection(dtype, block_m):
     assert ey <= (TOL_MLP_BF16 if dtype == "bf16" else P.TOL["fp8"]), ey
 
 
+def dequant_h(H, Hs):
+    return (H.float().double() * Hs.double().repeat_interleave(128, dim=1)).cpu().numpy()
+
+
+def e4m3_ordinal(v: np.ndarray) -> np.ndarray:
+    """Signed position of each e4m3 value on the code line (adjacent values differ by 1)."""
+    c = torch.from_numpy(v).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def check_fp8_h(H, Hs, h_ref, rows):
+    """GPU e4m3 H against the oracle's quantization of its fp64 h: dequantized
+    values within the fp8 bar; codes equal except where the GPU's fp32 h and the
+    fp64 h fall on opposite sides of a rounding boundary (measured about 0.15 %
+    of codes)."""
+    q, s = omlp.quantize_groups(h_ref)
+    idx = torch.tensor(list(rows), device=H.device)
+    got = dequant_h(H[idx], Hs[idx])
+    err = og.rel_frobenius(got, q * np.repeat(s, 128, axis=1))
+    gq = H[idx].float().cpu().double().numpy()
+    step = np.abs(e4m3_ordinal(gq) - e4m3_ordinal(q))
+    # the GPU's h carries an absolute error of about 1e-5 of the group's amax (measured:
+    # two-step differences at |h / s| ~ 0.05); once |h / s| >= 4 that is under half a
+    # step (code spacing >= 1/16 relative), so there a code can only move to its neighbour
+    big = np.abs(q) >= 4.0
+    assert err <= P.TOL["fp8"], err
+    assert not ((step > 1) & big).any(), (gq[(step > 1) & big][:8], q[(step > 1) & big][:8])
+    assert float(np.mean(step > 0)) <= 1e-2, float(np.mean(step > 0))
+    return q, s
+
+
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+def test_swiglu_e4m3_h_and_fp8_down_projection(block_m):
+    """Both expert GEMMs in fp8: L1's epilogue quantizes H to e4m3 with 1x128
+    scales, L2 runs on those codes and scales.  H and y on every valid row."""
+    counts = [70, 0, 300, 6, 129, 3]
+    K, I, N2 = 256, 256, 512
+    G, R = len(counts), sum(counts)
+    announce("expert MLP fp8 H", counts, "block_m", block_m)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=16, device="cuda", l2="fp8")
+    ws = mg.workspace(G, R)
+    mg.schedule(inp["counts"], R, ws, block_m=block_m, N=2 * I)
+    H = torch.empty((R, I), dtype=torch.float8_e4m3fn, device="cuda")
+    Hs = torch.full((R, I // 128), float("nan"), device="cuda")
+    Y = P.sentinel_like((R, N2))
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"],
+                                     block_m=block_m, H_scale=Hs)
+    mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=block_m,
+                                         b_layout=mg.B_NK)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = list(range(R))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
+    assert bool(torch.isfinite(Hs).all())
+    q, s = check_fp8_h(H, Hs, h, rows)
+    qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
+    y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
+                      A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
+    ey = og.rel_frobenius(P.rows_as_float(Y, rows), y)
+    assert ey <= P.TOL["fp8"], ey
+
+
+def test_expert_mlp_fp8_full_size():
+    """Both GEMMs fp8 at the DeepSeek-V3 expert shape on the Zipf histogram; sampled rows."""
+    counts = wl.workload(3).counts
+    K, I, N2 = 7168, 2048, 7168
+    G, R = len(counts), sum(counts)
+    announce("expert MLP fp8 full size")
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=17, device="cuda", l2="fp8")
+    for k in ("W_gate", "W_up"):
+        inp.pop(k)
+    ws = mg.workspace(G, R)
+    mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
+    H = torch.empty((R, I), dtype=torch.float8_e4m3fn, device="cuda")
+    Hs = torch.empty((R, I // 128), device="cuda")
+    Y = torch.empty((R, N2), dtype=torch.bfloat16, device="cuda")
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"], H_scale=Hs)
+    mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], b_layout=mg.B_NK)
+    torch.cuda.synchronize()
+    rows = P.sample_rows_contiguous(counts, 1, 256, extra=32, seed=18)
+    got_y = P.rows_as_float(Y, rows)
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    del inp
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
+    q, s = check_fp8_h(H, Hs, h, rows)
+    # L2 on the oracle's own codes for the sampled rows: a compact [rows, I] operand, one expert per row
+    offs = acc.segment_offsets(counts, 1)
+    ex = [next(e for e in range(G) if offs[e] <= r < offs[e] + counts[e]) for r in rows]
+    w2 = cpu["W2"]
+    y = np.empty((len(rows), N2))
+    for e in sorted(set(ex)):
+        idx = [i for i, x in enumerate(ex) if x == e]
+        w2e = w2[e].float().double().numpy() * np.repeat(np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0),
+                                                          128, 1).T
+        y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
+    ey = og.rel_frobenius(got_y, y)
+    assert ey <= P.TOL["fp8"], ey
+
+
 def test_swiglu_leaves_other_rows_alone_and_handles_empty():
     counts = [0, 37, 0, 0]
     K, I, N2 = 128, 128, 256

@@ -89,3 +89,28 @@ def test_fp8_chain_uses_the_dequantized_interleaved_weights():
         c = w[e] @ a[r]
         g, u = mlp.split_gate_up(c)
         assert np.allclose(h[i], g / (1 + np.exp(-g)) * u, rtol=1e-12, atol=1e-14)
+
+
+def test_e4m3_rne_matches_the_library_cast():
+    """The oracle's own e4m3 rounding against torch's float8_e4m3fn cast
+    (round to nearest even) on values spread over the whole range, ties included."""
+    g = torch.Generator().manual_seed(5)
+    x = torch.cat([(torch.rand(20000, generator=g) * 2 - 1) * 448,
+                   torch.randn(20000, generator=g) * 0.01,
+                   torch.tensor([0.0, 1.0625, 1.1875, -1.0625, 0.0078125 * 1.5, 240.0, 232.0, 448.0, -448.0])])
+    x = x.double()
+    ours = mlp.e4m3_rne(x.numpy())
+    ref = x.float().to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_quantize_groups_definition():
+    h = np.zeros((2, 256))
+    h[0, :128] = np.linspace(-3.0, 5.0, 128)          # amax 5 -> s = 5/448
+    h[1, 128] = -0.25                                  # one nonzero value in the second group
+    q, s = mlp.quantize_groups(h)
+    assert s.shape == (2, 2)
+    assert s[0, 0] == 5.0 / 448.0 and s[0, 1] == 1.0 and s[1, 0] == 1.0 and s[1, 1] == 0.25 / 448.0
+    assert q[0, 127] == 448.0 and q[1, 128] == -448.0  # the group's amax maps to the largest code
+    assert np.all(np.abs(q[0, :128] * s[0, 0] - h[0, :128]) <= np.abs(h[0, :128]) / 16 + 1e-12)
+    assert not q[0, 128:].any()

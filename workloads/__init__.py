@@ -357,14 +357,15 @@ def _valid_row_mask(wl: Workload, device) -> torch.Tensor:
 
 
 def materialize_mlp(counts: Sequence[int], K: int, I: int, N2: int, dtype: str = "bf16", seed: int = 6,
-                    device="cpu") -> Dict[str, Optional[torch.Tensor]]:
+                    device="cpu", l2: str = "bf16") -> Dict[str, Optional[torch.Tensor]]:
     """Operands of an expert MLP (L1 -> SwiGLU -> L2), contiguous layout, packed segments.
 
     A [rows, K] ~ N(0, 1); gate and up weights [G, I, K] ~ N(0, 1)/sqrt(K),
     stored together as W1 [G, 2I, K] with row 32q + w = gate row 16q + w and
     row 32q + 16 + w = up row 16q + w (w < 16); W2 [G, N2, I] ~ N(0, 1)/sqrt(I).
     dtype "bf16": A, W1 bf16.  "fp8": A e4m3 with fp32 1x128 scales, W1 e4m3
-    with fp32 scales per 128x128 block of the interleaved rows.  W2 is bf16.
+    with fp32 scales per 128x128 block of the interleaved rows.  W2 is bf16,
+    or with l2 = "fp8" e4m3 with fp32 scales W2_scale [G, I/128, N2/128].
     Also returns the plain gate / up weights (W_gate, W_up, as W1's dtype
     before quantization: bf16 or fp32) for checks of the interleave."""
     G, R = len(counts), sum(counts)
@@ -373,8 +374,14 @@ def materialize_mlp(counts: Sequence[int], K: int, I: int, N2: int, dtype: str =
     wg = fp32_normal((G, I, K), 1.0 / float(np.sqrt(K)), s + 2, device)
     wu = fp32_normal((G, I, K), 1.0 / float(np.sqrt(K)), s + 3, device)
     w1 = torch.stack([wg.reshape(G, I // 16, 16, K), wu.reshape(G, I // 16, 16, K)], dim=2).reshape(G, 2 * I, K)
-    out = {"counts": torch.tensor(list(counts), dtype=torch.int32, device=device),
-           "W2": to_bf16(fp32_normal((G, N2, I), 1.0 / float(np.sqrt(I)), s + 4, device))}
+    w2 = fp32_normal((G, N2, I), 1.0 / float(np.sqrt(I)), s + 4, device)
+    out = {"counts": torch.tensor(list(counts), dtype=torch.int32, device=device), "W2_scale": None}
+    if l2 == "fp8":
+        q2, s2 = quantize_blocks_e4m3(w2.transpose(1, 2).contiguous())
+        out["W2"], out["W2_scale"] = q2.transpose(1, 2).contiguous(), s2
+    else:
+        out["W2"] = to_bf16(w2)
+    del w2
     if dtype == "bf16":
         out.update({"A": to_bf16(a), "A_scale": None, "W1": to_bf16(w1), "W1_scale": None,
                     "W_gate": to_bf16(wg), "W_up": to_bf16(wu)})
