@@ -1,0 +1,71 @@
+/* Host-side driver for the sanitizer test (tests/test_host_sanitizers.py):
+ * calls every entry point of include/moegg.h down its argument-validation
+ * paths and the pure host helpers.  No call reaches a kernel launch, so no GPU
+ * is needed.  Prints "ok" and exits 0 when every status is the expected one. */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../include/moegg.h"
+
+static int fails = 0;
+#define EXPECT(call, want)                                                              \
+    do {                                                                                \
+        int got_ = (int)(call);                                                         \
+        if (got_ != (int)(want)) {                                                      \
+            fprintf(stderr, "line %d: %s -> %d, want %d\n", __LINE__, #call, got_, (int)(want)); \
+            ++fails;                                                                    \
+        }                                                                               \
+    } while (0)
+
+int main(void) {
+    void* fake = (void*)(uintptr_t)0x100000;       /* aligned, never dereferenced */
+    void* odd = (void*)(uintptr_t)0x100002;
+    size_t ws = moegg_workspace_bytes(64, 32768);
+    if (ws == 0 || ws % 256) ++fails;
+    EXPECT(moegg_workspace_bytes(0, 1), 0);
+    EXPECT(moegg_workspace_bytes(4097, 1), 0);
+    for (int s = 0; s < 6; ++s)
+        if (!moegg_status_string((moegg_status_t)s)) ++fails;
+    if (moegg_version() < 1) ++fails;
+
+    EXPECT(moegg_schedule(NULL, 8, 132, 1, 0, 256, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_schedule(fake, 8, 132, 1, 48, 256, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_schedule(fake, 8, 132, 1, 0, 256, fake, 8, NULL), MOEGG_ERR_WORKSPACE);
+    EXPECT(moegg_schedule_exemplar(fake, 8, 132, 1, 256, NULL, 4, 0, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_schedule_exemplar(fake, 8, 132, 1, 256, fake, 300, 0, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_schedule_exemplar(fake, 8, 132, 1, 256, fake, 4, -1, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+
+    EXPECT(moegg_grouped_gemm_contiguous(NULL, NULL, fake, NULL, fake, fake, 8, 132, 512, 256, 1, MOEGG_BF16,
+                                         MOEGG_B_KN, 0, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_contiguous(fake, NULL, fake, NULL, fake, fake, 8, 132, 100, 256, 1, MOEGG_BF16,
+                                         MOEGG_B_KN, 0, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_contiguous(fake, fake, fake, fake, fake, fake, 8, 132, 512, 512, 1,
+                                         MOEGG_FP8_E4M3_FP4_E2M1, MOEGG_B_KN, 0, fake, ws, NULL),
+           MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_contiguous(fake, fake, fake, odd, fake, fake, 8, 132, 512, 512, 1,
+                                         MOEGG_FP8_E4M3_E8M0, MOEGG_B_NK, 0, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_contiguous(fake, NULL, fake, NULL, fake, fake, 8, 132, 512, 256, 1, MOEGG_BF16,
+                                         MOEGG_B_KN, 0, NULL, 0, NULL), MOEGG_ERR_WORKSPACE);
+    EXPECT(moegg_grouped_gemm_contiguous_scheduled(fake, NULL, fake, NULL, fake, 8, 132, 512, 256, MOEGG_BF16,
+                                                   MOEGG_B_KN, 96, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_swiglu_scheduled(fake, NULL, fake, NULL, fake, NULL, 8, 132, 512, 64, MOEGG_BF16,
+                                               MOEGG_B_NK, 0, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_swiglu_scheduled(fake, NULL, fake, NULL, fake, odd, 8, 132, 512, 128, MOEGG_BF16,
+                                               MOEGG_B_NK, 0, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_masked(fake, NULL, fake, NULL, fake, fake, 32, 0, 2048, 7168, MOEGG_BF16, MOEGG_B_KN,
+                                     NULL, 0, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_masked(fake, fake, fake, fake, fake, fake, 32, 256, 2048, 7168, MOEGG_FP8_E4M3_E8M0,
+                                     MOEGG_B_KN, NULL, 0, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_k_grouped(fake, fake, fake, fake, 16, 100, 2000, 7168, fake, ws, NULL),
+           MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_k_grouped(NULL, NULL, fake, fake, 16, 1, 2048, 7168, fake, ws, NULL),
+           MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_stats_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_selection_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
+    int64_t n = 0;
+    EXPECT(moegg_tile_list_read(fake, NULL, 5, &n, NULL), MOEGG_ERR_INVALID_ARG);
+    if (fails) return 1;
+    printf("ok\n");
+    return 0;
+}
