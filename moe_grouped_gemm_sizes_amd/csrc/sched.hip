@@ -117,11 +117,13 @@ __device__ __forceinline__ bool valid_block_m_dev(int b) {
 // U into an eight-point concentration curve, and take the nearest exemplar,
 // keeping the workspace's previous exemplar while it is within `hysteresis`
 // of the nearest.  Called by all threads after the accounting; the counts
-// are in m_s.  Returns the exemplar's block_m (or -2 when it names no valid
-// one).  Thread 0 records the selection in the control block.
-__device__ int select_exemplar(const int32_t* m_s, int32_t* srt_s, int64_t (*lor_buf)[8], int G, int64_t U,
-                               const moegg_exemplar_t* __restrict__ ex, int n_ex, int hysteresis, Control* ctl,
-                               int* bm_s) {
+// are in m_s.  Each thread scores its own exemplars (at most 256, so one
+// each), so the table is read once, in parallel.  Returns the exemplar's
+// block_m (or -2 when it names no valid one).  Thread 0 records the
+// selection in the control block.
+__device__ int select_exemplar(const int32_t* m_s, int32_t* srt_s, int64_t (*lor_buf)[8], int64_t* dist_s, int G,
+                               int64_t U, const moegg_exemplar_t* __restrict__ ex, int n_ex, int hysteresis,
+                               Control* ctl, int* bm_s) {
     const int t = threadIdx.x;
     // 1. bitonic sort, descending, over the next power of two (padded with zeros)
     int P = 1;
@@ -150,38 +152,48 @@ __device__ int select_exemplar(const int32_t* m_s, int32_t* srt_s, int64_t (*lor
 #pragma unroll
         for (int q = 0; q < 8; ++q) top[q] += i < (G * (q + 1) + 7) / 8 ? m : 0;
     }
-    block_sums<8>(top, lor_buf);
-    // 3. descriptor, distances, hysteresis (one thread; at most 256 exemplars)
-    if (t == 0) {
-        int32_t lor[8];
+    block_sums<8>(top, lor_buf);               // every thread now holds the eight sums
+    // 3. descriptor (every thread), one exemplar's distance per thread into LDS
+    int32_t lor[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) lor[q] = U > 0 ? (int32_t)((top[q] << 16) / U) : 0;
-        const int32_t sc = size_class(U);
-        auto dist = [&](int x) -> int64_t {
-            int64_t d = (int64_t)MOEGG_EXEMPLAR_SIZE_WEIGHT * llabs((int64_t)sc - ex[x].size_class);
-            for (int q = 0; q < 8; ++q) d += llabs((int64_t)lor[q] - ex[x].lorenz[q]);
-            return d;
-        };
-        int best = 0;
-        int64_t best_d = dist(0);
-        for (int x = 1; x < n_ex; ++x) {
-            const int64_t d = dist(x);
-            if (d < best_d) { best_d = d; best = x; }
-        }
-        int chosen = best;
-        int64_t chosen_d = best_d;
-        if (ctl->sel_tag == kSelectorTag && ctl->sel_prev >= 0 && ctl->sel_prev < n_ex) {
-            const int64_t dp = dist(ctl->sel_prev);
-            if (dp <= best_d + hysteresis) { chosen = ctl->sel_prev; chosen_d = dp; }
-        }
-        const int bm = ex[chosen].block_m;
-        *bm_s = valid_block_m_dev(bm) ? bm : -2;
-        ctl->sel_tag = kSelectorTag;
-        ctl->sel_prev = chosen;
-        ctl->sel_size_class = sc;
+    for (int q = 0; q < 8; ++q) lor[q] = U > 0 ? (int32_t)((top[q] << 16) / U) : 0;
+    const int32_t sc = size_class(U);
+    for (int x = t; x < n_ex; x += kSchedThreads) {
+        int64_t d = (int64_t)MOEGG_EXEMPLAR_SIZE_WEIGHT * llabs((int64_t)sc - ex[x].size_class);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ctl->sel_lorenz[q] = lor[q];
-        ctl->sel_distance = chosen_d;
+        for (int q = 0; q < 8; ++q) d += llabs((int64_t)lor[q] - ex[x].lorenz[q]);
+        dist_s[x] = d;
+    }
+    __syncthreads();
+    // 4. nearest exemplar, ties to the lower index: wave 0 scans, then a shuffle
+    //    reduction over (distance, index); thread 0 applies the hysteresis
+    if (t < 64) {
+        int64_t best_d = INT64_MAX;
+        int best = n_ex;
+        for (int x = t; x < n_ex; x += 64)
+            if (dist_s[x] < best_d) { best_d = dist_s[x]; best = x; }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const int64_t od = __shfl_xor(best_d, off, 64);
+            const int ob = __shfl_xor(best, off, 64);
+            if (od < best_d || (od == best_d && ob < best)) { best_d = od; best = ob; }
+        }
+        if (t == 0) {
+            int chosen = best;
+            int64_t chosen_d = best_d;
+            if (ctl->sel_tag == kSelectorTag && ctl->sel_prev >= 0 && ctl->sel_prev < n_ex) {
+                const int64_t dp = dist_s[ctl->sel_prev];
+                if (dp <= best_d + hysteresis) { chosen = ctl->sel_prev; chosen_d = dp; }
+            }
+            const int bm = ex[chosen].block_m;
+            *bm_s = valid_block_m_dev(bm) ? bm : -2;
+            ctl->sel_tag = kSelectorTag;
+            ctl->sel_prev = chosen;
+            ctl->sel_size_class = sc;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ctl->sel_lorenz[q] = lor[q];
+            ctl->sel_distance = chosen_d;
+        }
     }
     __syncthreads();
     return *bm_s;
@@ -207,6 +219,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     __shared__ int32_t toff_s[kMaxExperts + 1];             // first tile of each expert
     __shared__ int32_t srt_s[kMaxExperts];                   // exemplar mode: sorted counts
     __shared__ int64_t lor_buf[kWaves][8];
+    __shared__ int64_t dist_s[MOEGG_MAX_EXEMPLARS];           // exemplar mode: distances
     __shared__ int bm_s;
     const int t = threadIdx.x;
     const int ept = (G + kSchedThreads - 1) / kSchedThreads;  // experts per thread, contiguous
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     if (mode == 1) {
         bm = exec_block_m;
     } else if (n_ex > 0) {
-        bm = select_exemplar(m_s, srt_s, lor_buf, G, v[0], exemplars, n_ex, hysteresis, ctl, &bm_s);
+        bm = select_exemplar(m_s, srt_s, lor_buf, dist_s, G, v[0], exemplars, n_ex, hysteresis, ctl, &bm_s);
         if (bm == -2) {
             bm = 0;
             if (t == 0) flags_s |= MOEGG_FLAG_BAD_EXEMPLAR;
