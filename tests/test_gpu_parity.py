@@ -198,6 +198,37 @@ def test_contiguous_integer_exact(dtype):
         assert np.array_equal(got, ref)
 
 
+def test_contiguous_maximum_expert_count():
+    """G = 4096 (the library's maximum) with tiny ragged counts, a third empty:
+    accounting, tile list and every valid row."""
+    rng = random.Random(41)
+    counts = [0 if rng.random() < 0.33 else rng.randint(1, 5) for _ in range(4096)]
+    announce("contiguous G=4096", sum(counts))
+    w, inp = small_contig(counts, 128, 256, "bf16")
+    C, ws = P.run_contiguous(w, inp, block_m=64)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, 64)
+    assert mg.tile_list_read(ws, st.tiles + 4) == acc.tile_list(counts, 64, 1)
+    rows = list(range(w.rows_total))
+    ref = P.oracle_contiguous_rows(w, {k: P.cpu(v) for k, v in inp.items()}, rows)
+    assert og.rel_frobenius(P.rows_as_float(C, rows), ref) <= P.TOL["bf16"]
+
+
+def test_contiguous_e8m0_widest_output():
+    """E8M0 scales at their widest supported output, N = 32768 (N / 128 = 256
+    scale bytes per row), on a small ragged histogram; sampled rows."""
+    counts = [40, 0, 200, 4]                              # 244 rows: a multiple of 4
+    announce("contiguous e8m0 N=32768", counts)
+    w = wl.Workload("e8w", "contiguous", "fp8", counts, K=256, N=32768, values="normal", seed=23, scales="e8m0")
+    inp = wl.materialize(w, "cuda")
+    C, ws = run_contiguous_e8m0(w, inp, 0, mg.B_NK)
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = P.sample_rows_contiguous(counts, 1, 64, extra=16, seed=3)
+    cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+    ref = P.oracle_contiguous_rows(w, cpu, rows)
+    assert og.rel_frobenius(P.rows_as_float(C, rows), ref) <= P.TOL["fp8"]
+
+
 def test_contiguous_deterministic_and_empty():
     announce("determinism + all-empty")
     w, inp = small_contig([300, 0, 17, 513], 512, 512, "fp8")
