@@ -289,15 +289,20 @@ def main():
         args.scales = "e8m0"
         w.weights = "e2m1"
     if args.scales == "e8m0":
-        if w.dtype != "fp8" or w.layout != "contiguous":
-            print("--scales e8m0 applies to the contiguous fp8 workload only", file=sys.stderr)
+        if w.layout == "masked" and w.dtype == "bf16":
+            # the decode workload with fp8 activations (power-of-two 1x128 scales) in place of bf16
+            w.dtype, w.name = "fp8", w.name.replace("bf16", "fp8")
+        if w.dtype != "fp8" or w.layout == "k_grouped":
+            print("--scales e8m0 / --weights e2m1 apply to the fp8 contiguous and the masked workloads",
+                  file=sys.stderr)
             sys.exit(2)
         w.scales = "e8m0"
     if args.cold is None:
         args.cold = args.config != 1
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
-    layout = args.b_layout if args.b_layout != "auto" else ("kn" if w.layout == "masked" else "nk")
+    layout = args.b_layout if args.b_layout != "auto" else \
+        ("kn" if w.layout == "masked" and w.weights != "e2m1" else "nk")
     if w.weights == "e2m1" and layout != "nk":
         print("fp4 weights are stored [G,N,K/2] only", file=sys.stderr)
         sys.exit(2)

@@ -49,14 +49,14 @@ typedef enum {
  * applies them itself (V_MFMA_SCALE_F32_16X16X128_F8F6F4), so nothing is
  * promoted on the VALU.  Its activation scales are stored transposed:
  * [K/128, rows] (DeepGEMM's MN-major scale layout), four rows per 32-bit word.
- * Contiguous layout only.
+ * Contiguous and masked layouts.
  * MOEGG_FP8_E4M3_FP4_E2M1 is the low-precision-weight case the DeepGEMM
  * record lists for SM100 (FP8 x FP4): activations as for
  * MOEGG_FP8_E4M3_E8M0, weights as OCP E2M1 (fp4: sign, 2 exponent bits with
  * bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two per
  * byte, element 2i in the low nibble, stored [G, N, K/2] (b_layout must be
  * MOEGG_B_NK), with E8M0 weight-block scales [G, K/128, N/128].  The same
- * gfx950 MFMA takes the fp4 operand directly.  Contiguous layout only. */
+ * gfx950 MFMA takes the fp4 operand directly.  Contiguous and masked layouts. */
 typedef enum {
     MOEGG_BF16 = 0,
     MOEGG_FP8_E4M3 = 1,
@@ -318,9 +318,9 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
  * Masked layout for decode under graph capture (DeepGEMM record,
  * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
  * computes only the valid portions, with no CPU sync).
- *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (fp8) or NULL.
- *            MOEGG_FP8_E4M3_E8M0 and MOEGG_FP8_E4M3_FP4_E2M1 are not
- *            supported here (UNSUPPORTED).
+ *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (MOEGG_FP8_E4M3), E8M0
+ *            bytes [K/128, G * cap] (MOEGG_FP8_E4M3_E8M0 and
+ *            MOEGG_FP8_E4M3_FP4_E2M1; G * cap % 4 == 0), or NULL (bf16).
  *   B        as for the contiguous call.  B_scale as for the contiguous call.
  *   C        bf16 [G, cap, N].  Only rows r < masked_m[e] are written.
  *   masked_m int32 [G] on the device, read by the kernel at run time.

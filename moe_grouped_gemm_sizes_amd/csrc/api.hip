@@ -215,9 +215,10 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     if (!masked_m || !aligned(masked_m, 4)) return MOEGG_ERR_INVALID_ARG;
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, masked_block_n());
     if (st != MOEGG_OK) return st;
-    if (e8m0_scales(dtype)) return MOEGG_ERR_UNSUPPORTED;     // contiguous layout only
     if (cap < 1 || (int64_t)G * cap > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
-    const int esz = dtype == MOEGG_FP8_E4M3 ? 1 : 2;
+    // E8M0 activation scales [K/128, G * cap] are read four bytes at a time
+    if (e8m0_scales(dtype) && ((int64_t)G * cap) % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if ((int64_t)masked_block_m() * K * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -229,8 +230,9 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
                          L.max_tiles, s);
         if (e != hipSuccess) return hip_status(e, "masked stats launch");
     }
-    ContigArgs a{A, A_scale, B, B_scale, C, masked_m, (const unsigned char*)ws, G, K, N, cap, 0};
-    e = launch_masked(a, dtype == MOEGG_FP8_E4M3, b_layout == MOEGG_B_KN, s);
+    ContigArgs a{A, A_scale, B, B_scale, C, masked_m, (const unsigned char*)ws, G, K, N, cap, G * cap};
+    e = launch_masked(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
+                      b_layout == MOEGG_B_KN, s);
     return hip_status(e, "masked GEMM launch");
 }
 

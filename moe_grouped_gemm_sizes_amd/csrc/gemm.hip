@@ -326,7 +326,7 @@ template <class C, bool B_KN>
 struct TileGemm {
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     static constexpr int HSEG = C::WTN / 2;                        // weight rows per wave column half
-    static_assert(B_KN || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
+    static_assert(B_KN || C::W4 || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
                   "weight DMA row mapping");
     v4f acc[C::NB][C::MB];
 
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 // Masked decode: short row tiles, narrow column tiles (HBM-bound).
 // Two workgroups per CU, three stages each: the loads of one overlap the
 // start-up and epilogue of the other, and a CU keeps twice the bytes in flight.
-template <bool FP8> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4, 2>;
+template <bool FP8, bool E8 = false, bool W4 = false> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4, 2, E8, W4>;
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
@@ -1030,8 +1030,11 @@ hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_
 int masked_block_m() { return MaskedCfg<false>::BM; }
 int masked_block_n() { return MaskedCfg<false>::BN; }
 
-hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s) {
+hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s) {
     const int grid = a.G * (a.N / MaskedCfg<false>::BN);
+    if (w4) return b_kn ? hipErrorInvalidValue : launch_one<MaskedCfg<true, true, true>, false, true>(a, grid, s);
+    if (e8m0) return b_kn ? launch_one<MaskedCfg<true, true>, true, true>(a, grid, s)
+                          : launch_one<MaskedCfg<true, true>, false, true>(a, grid, s);
     if (fp8) return b_kn ? launch_one<MaskedCfg<true>, true, true>(a, grid, s)
                          : launch_one<MaskedCfg<true>, false, true>(a, grid, s);
     return b_kn ? launch_one<MaskedCfg<false>, true, true>(a, grid, s)

@@ -17,7 +17,7 @@ struct ContigArgs {
     const int32_t* counts;        // m_sizes, or masked_m for the masked layout
     const unsigned char* ws;      // scheduler output (contiguous layout)
     int G, K, N, cap;             // cap: masked layout only
-    int rows_total;               // contiguous layout: rows of A and C
+    int rows_total;               // rows of A and C (masked layout: G * cap)
     void* C_scale;                // SwiGLU with e4m3 output: fp32 [rows_total, N / 256] scales, else NULL
 };
 
@@ -46,7 +46,7 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
 // gate and up in groups of 16; C receives [rows_total, N / 2] bf16, or e4m3 codes
 // with fp32 1x128 scales in C_scale when that is set
 hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s);
-hipError_t launch_masked(const ContigArgs& a, bool fp8, bool b_kn, hipStream_t s);
+hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);
 int masked_block_m();
 int masked_block_n();

@@ -83,3 +83,35 @@ def contiguous_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, 
             res += part * sa[rr, kb][:, None] * colscale[None, :]
         out[idx] = res
     return out
+
+
+def masked_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, W_scale: torch.Tensor,
+                   masked_m: Sequence[int], pairs: Sequence[tuple]) -> np.ndarray:
+    """Masked layout: C[e, r, n] for each (e, r) in `pairs` (r < masked_m[e]).
+    A: e4m3 codes [G, cap, K]; A_scale fp32 [G, cap, K/128]; W packed E2M1
+    [G, N, K/2]; W_scale fp32 [G, K/128, N/128].  Same sum as
+    contiguous_fp8_fp4, with row r of expert e at A[e, r]."""
+    dec8 = _e4m3_table()
+    a_codes = A.contiguous().view(torch.uint8).numpy()
+    sa = A_scale.double().numpy()
+    w = W.contiguous().numpy()
+    sb = W_scale.double().numpy()
+    K = a_codes.shape[2]
+    N = w.shape[1]
+    out = np.zeros((len(pairs), N), dtype=np.float64)
+    by_e = {}
+    for i, (e, r) in enumerate(pairs):
+        assert 0 <= r < masked_m[e]
+        by_e.setdefault(e, []).append(i)
+    for e, idx in by_e.items():
+        rr = [pairs[i][1] for i in idx]
+        a = dec8[a_codes[e, rr]]                               # [m, K]
+        we = dec_e2m1_packed(w[e])                             # [N, K]
+        res = np.zeros((len(rr), N), dtype=np.float64)
+        for kb in range(K // 128):
+            ks = slice(kb * 128, (kb + 1) * 128)
+            part = a[:, ks] @ we[:, ks].T
+            colscale = np.repeat(sb[e, kb], 128)[:N]
+            res += part * sa[e, rr, kb][:, None] * colscale[None, :]
+        out[idx] = res
+    return out

@@ -55,7 +55,7 @@ int main(void) {
                                                MOEGG_B_NK, 0, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
     EXPECT(moegg_grouped_gemm_masked(fake, NULL, fake, NULL, fake, fake, 32, 0, 2048, 7168, MOEGG_BF16, MOEGG_B_KN,
                                      NULL, 0, NULL), MOEGG_ERR_INVALID_ARG);
-    EXPECT(moegg_grouped_gemm_masked(fake, fake, fake, fake, fake, fake, 32, 256, 2048, 7168, MOEGG_FP8_E4M3_E8M0,
+    EXPECT(moegg_grouped_gemm_masked(fake, fake, fake, fake, fake, fake, 31, 255, 2048, 7168, MOEGG_FP8_E4M3_E8M0,
                                      MOEGG_B_KN, NULL, 0, NULL), MOEGG_ERR_UNSUPPORTED);
     EXPECT(moegg_grouped_gemm_k_grouped(fake, fake, fake, fake, 16, 100, 2000, 7168, fake, ws, NULL),
            MOEGG_ERR_UNSUPPORTED);

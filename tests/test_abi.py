@@ -102,12 +102,17 @@ def test_masked_validation():
     small_ws = list(ok)
     small_ws[12], small_ws[13] = FAKE, 16
     assert f(*small_ws) == mg.ERR_WORKSPACE
-    e8m0 = list(ok)                         # E8M0 scales: contiguous layout only
-    e8m0[1], e8m0[3], e8m0[9], e8m0[10] = FAKE, FAKE, 7168 - 7168 % 512, mg.FP8_E4M3_E8M0
+    e8m0 = list(ok)                         # E8M0 scale bytes [K/128, G * cap] need G * cap % 4 == 0
+    e8m0[1], e8m0[3], e8m0[6], e8m0[7], e8m0[10] = FAKE, FAKE, 31, 255, mg.FP8_E4M3_E8M0
     assert f(*e8m0) == mg.ERR_UNSUPPORTED
-    w4 = list(e8m0)                         # fp4 weights: contiguous layout only
-    w4[10], w4[11] = mg.FP8_E4M3_FP4_E2M1, mg.B_NK
+    w4 = list(e8m0)                         # fp4 weights: K-contiguous only, then the same row rule
+    w4[10] = mg.FP8_E4M3_FP4_E2M1
     assert f(*w4) == mg.ERR_UNSUPPORTED
+    w4[11] = mg.B_NK
+    assert f(*w4) == mg.ERR_UNSUPPORTED
+    e8n = list(e8m0)                        # E8M0 also needs N % 512 == 0
+    e8n[6], e8n[7], e8n[9] = 32, 256, 7168 + 256
+    assert f(*e8n) == mg.ERR_UNSUPPORTED
 
 
 def test_k_grouped_validation():

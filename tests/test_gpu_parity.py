@@ -368,6 +368,60 @@ def test_masked_small(dtype, b_layout):
     check_masked(w, inp, C, counts)
 
 
+def run_masked_low_precision(counts, cap, K, N, weights, b_layout, seed):
+    """Masked layout with fp8 activations and E8M0 scales, e4m3 or packed E2M1 weights."""
+    w = wl.Workload("masked-lp", "masked", "fp8", counts, K=K, N=N, cap=cap, seed=seed, scales="e8m0",
+                    weights=weights)
+    inp = wl.materialize(w, "cuda")
+    B = inp["B"] if (b_layout == mg.B_KN or weights == "e2m1") else inp["B"].transpose(1, 2).contiguous()
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, inp["A_scale_e8m0"], inp["B_scale_e8m0"], b_layout)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), counts)
+    return w, inp, C
+
+
+def check_masked_fp4(w, inp, C, counts, pairs=None):
+    cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+    pairs = pairs or [(e, r) for e in range(w.G) for r in range(min(counts[e], w.cap))]
+    ref = fp4.masked_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, pairs)
+    idx = torch.tensor([e * w.cap + r for e, r in pairs], device="cuda")
+    got = C.reshape(w.G * w.cap, -1)[idx].float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    assert og.rel_frobenius(got, ref) <= P.TOL["fp8"]
+
+
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
+def test_masked_fp8_e8m0(b_layout):
+    counts = [3, 0, 64, 65, 130, 1]
+    announce("masked fp8 e8m0", b_layout, counts)
+    w, inp, C = run_masked_low_precision(counts, 160, 512, 512, "e4m3", b_layout, seed=24)
+    w.scales = "e8m0"
+    check_masked(w, {k: v for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}, C, counts)
+
+
+def test_masked_fp8_fp4():
+    counts = [3, 0, 64, 65, 130, 1]
+    announce("masked fp8 x fp4", counts)
+    w, inp, C = run_masked_low_precision(counts, 160, 512, 512, "e2m1", mg.B_NK, seed=25)
+    check_masked_fp4(w, inp, C, counts)
+    inval = torch.tensor([e * w.cap + r for e in range(w.G) for r in range(w.cap) if r >= counts[e]], device="cuda")
+    assert bool((C.reshape(w.G * w.cap, -1)[inval].view(torch.int16) == P.SENTINEL_BITS).all())
+
+
+def test_masked_fp8_fp4_full_size():
+    """The masked decode workload (32 experts, cap 256, K 2048, N 7168) with fp8
+    activations and fp4 weights; sampled rows."""
+    w0 = wl.workload(4)
+    announce("masked fp8 x fp4 full size", w0.name)
+    w, inp, C = run_masked_low_precision(w0.counts, w0.cap, w0.K, w0.N, "e2m1", mg.B_NK, seed=w0.seed)
+    rng = random.Random(7)
+    pairs = sorted({(e, r) for e in range(w.G) for r in range(w0.counts[e]) if r in (0, w0.counts[e] - 1)
+                    or rng.random() < 0.1})
+    check_masked_fp4(w, inp, C, w0.counts, pairs)
+
+
 @pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
 def test_masked_config_full_size(b_layout):
     w = wl.workload(4)

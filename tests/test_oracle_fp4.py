@@ -78,3 +78,19 @@ def test_e2m1_weights_fit_and_scales_are_powers_of_two():
     sb = inp["B_scale"]
     assert bool((torch.log2(sb) == torch.round(torch.log2(sb))).all())
     assert torch.equal(inp["B_scale_e8m0"].int() - 127, torch.log2(sb).round().int())
+
+
+def test_masked_oracle_matches_the_contiguous_one():
+    """The masked fp8 x fp4 sum equals the contiguous one on the same rows laid out back to back."""
+    masked, cap = [5, 0, 8], 8
+    w = wl.Workload("m4", "masked", "fp8", masked, K=256, N=256, cap=cap, values="normal", seed=3, scales="e8m0",
+                    weights="e2m1")
+    inp = wl.materialize(w, "cpu", nan_padding=False)
+    pairs = [(e, r) for e in range(3) for r in range(masked[e])]
+    got = fp4.masked_fp8_fp4(inp["A"], inp["A_scale"], inp["B"],
+                                                                   inp["B_scale"], masked, pairs)
+    rows = [e * cap + r for e, r in pairs]
+    A = inp["A"].reshape(3 * cap, -1)[rows].contiguous()
+    As = inp["A_scale"].reshape(3 * cap, -1)[rows].contiguous()
+    ref = fp4.contiguous_fp8_fp4(A, As, inp["B"], inp["B_scale"], masked, list(range(len(rows))))
+    assert np.array_equal(got, ref)
