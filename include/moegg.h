@@ -36,7 +36,7 @@ extern "C" {
 typedef enum {
     MOEGG_OK = 0,
     MOEGG_ERR_INVALID_ARG = 1,   /* null pointer, bad size or count           */
-    MOEGG_ERR_UNSUPPORTED = 2,   /* shape or option this build does not cover */
+    MOEGG_ERR_UNSUPPORTED = 2,   /* shape or option the library does not cover */
     MOEGG_ERR_WORKSPACE = 3,     /* workspace missing or too small            */
     MOEGG_ERR_HIP = 4            /* a HIP runtime call failed                 */
 } moegg_status_t;
