@@ -166,9 +166,11 @@ def run_mlp(args):
     K, I, N2 = 7168, 2048, 7168
     G, R = len(counts), sum(counts)
     fp8_h = args.mlp_h == "fp8"
-    log(f"expert MLP: G={G}, U={R}, K={K}, I={I}, N2={N2}, H {args.mlp_h}")
+    w4 = args.weights == "e2m1"               # fp4 gate/up weights, E8M0 scales (L1)
+    log(f"expert MLP: G={G}, U={R}, K={K}, I={I}, N2={N2}, H {args.mlp_h}, L1 weights {args.weights}")
     inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda",
-                             l2="fp8" if fp8_h else "bf16")
+                             l2="fp8" if fp8_h else "bf16", w1_format="e2m1" if w4 else "e4m3")
+    a_s, w1_s = (inp["A_scale_e8m0"], inp["W1_scale_e8m0"]) if w4 else (inp["A_scale"], inp["W1_scale"])
     for k in ("W_gate", "W_up"):
         inp.pop(k)
     torch.cuda.empty_cache()
@@ -185,8 +187,7 @@ def run_mlp(args):
         mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
 
     def l1():
-        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale"], inp["W1_scale"], block_m=bm,
-                                         H_scale=Hs)
+        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, a_s, w1_s, block_m=bm, H_scale=Hs)
 
     def l2():
         mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=bm,
@@ -218,7 +219,8 @@ def run_mlp(args):
         "value": round((f1 + f2) / (ms * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3" if fp8_h else "fp8_e4m3 (L1) + bf16 (L2)", "data": "synthetic",
-        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8 + SwiGLU, L2 %s)" % ("fp8" if fp8_h else "bf16"),
+        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8%s + SwiGLU, L2 %s)" % (
+                       " x fp4" if w4 else "", "fp8" if fp8_h else "bf16"),
                    "experts": G,
                    "routed_rows": R, "K": K, "I": I, "N2": N2, "layout": "contiguous", "seed": 3,
                    "weights": "W1 [G,2I,K] gate/up interleaved, W2 [G,N2,I]",

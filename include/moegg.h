@@ -288,12 +288,16 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  * the gate and up products never reach HBM: only H does, once, in bf16).
  * Driven by the tile list an earlier moegg_schedule or
  * moegg_grouped_gemm_contiguous call left in `ws` (same G, rows_total).
- *   A        [rows_total, K] as for the contiguous call (bf16 or e4m3 with
- *            fp32 1x128 scales; E8M0 and fp4 are not supported here).
+ *   A        [rows_total, K] as for the contiguous call: bf16, e4m3 with
+ *            fp32 1x128 scales, or (MOEGG_FP8_E4M3_FP4_E2M1) e4m3 with E8M0
+ *            scale bytes [K/128, rows_total].  MOEGG_FP8_E4M3_E8M0 is not
+ *            supported here.
  *   W1       [G, 2I, K] (K-contiguous; b_layout must be MOEGG_B_NK): for
  *            q = 0 .. I/16 - 1 and w = 0 .. 15, row 32q + w is gate column
  *            16q + w and row 32q + 16 + w is up column 16q + w.  W1_scale
  *            (fp8): fp32 [G, K/128, 2I/128] over those interleaved rows.
+ *            MOEGG_FP8_E4M3_FP4_E2M1: packed E2M1 [G, 2I, K/2], same row
+ *            order, E8M0 W1_scale bytes [G, K/128, 2I/128].
  *   H        [rows_total, I].  For each valid row R of expert e:
  *                g = sum_k A[R,k] Wgate_e[k,c],  u = sum_k A[R,k] Wup_e[k,c],
  *                h[R, c] = silu(g) * u,  silu(g) = g / (1 + e^-g)

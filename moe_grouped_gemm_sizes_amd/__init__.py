@@ -240,7 +240,7 @@ def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=N
     if (H_scale is None) != (H.dtype == torch.bfloat16):
         raise ValueError("H: bf16 without H_scale, float8_e4m3fn with it")
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
-        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I, _dtype(A, A_scale),
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I, _dtype(A, A_scale, W1),
         B_NK, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 

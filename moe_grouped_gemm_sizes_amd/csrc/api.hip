@@ -194,7 +194,8 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     const int N = 2 * I;
     moegg_status_t st = check_common(A, A_scale, W1, W1_scale, H, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
-    if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3) return MOEGG_ERR_UNSUPPORTED;
+    if (dtype == MOEGG_FP8_E4M3_E8M0) return MOEGG_ERR_UNSUPPORTED;
+    if (dtype == MOEGG_FP8_E4M3_FP4_E2M1 && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
     if (b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
@@ -204,7 +205,8 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
     ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total,
                  H_scale};
-    return hip_status(launch_contiguous_swiglu(a, dtype == MOEGG_FP8_E4M3, rows_total, block_m, (hipStream_t)stream),
+    return hip_status(launch_contiguous_swiglu(a, dtype != MOEGG_BF16, dtype == MOEGG_FP8_E4M3_FP4_E2M1, rows_total,
+                                               block_m, (hipStream_t)stream),
                       "SwiGLU GEMM launch");
 }
 

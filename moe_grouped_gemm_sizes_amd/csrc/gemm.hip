@@ -1019,8 +1019,11 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
                 : launch_contig_t<false, false, false>(a, rows_total, block_m, s);
 }
 
-hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s) {
+hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int64_t rows_total, int block_m,
+                                    hipStream_t s) {
     const bool q = a.C_scale != nullptr;      // e4m3 H with fp32 scales
+    if (w4) return q ? launch_contig_t<true, false, true, true, 2>(a, rows_total, block_m, s)
+                     : launch_contig_t<true, false, true, true, 1>(a, rows_total, block_m, s);
     if (fp8) return q ? launch_contig_t<true, false, false, false, 2>(a, rows_total, block_m, s)
                       : launch_contig_t<true, false, false, false, 1>(a, rows_total, block_m, s);
     return q ? launch_contig_t<false, false, false, false, 2>(a, rows_total, block_m, s)

@@ -45,7 +45,9 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
 // L1 GEMM with the SwiGLU epilogue: [G, N, K] weights whose N columns interleave
 // gate and up in groups of 16; C receives [rows_total, N / 2] bf16, or e4m3 codes
 // with fp32 1x128 scales in C_scale when that is set
-hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, int64_t rows_total, int block_m, hipStream_t s);
+// w4: fp8 activations with E8M0 scales and packed E2M1 weights [G, N, K/2]
+hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int64_t rows_total, int block_m,
+                                    hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);
 int masked_block_m();

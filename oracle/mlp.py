@@ -51,6 +51,16 @@ def swiglu_rows(A: torch.Tensor, W1: torch.Tensor, counts: Sequence[int], rows: 
     return silu(g) * u
 
 
+def swiglu_rows_fp4(A: torch.Tensor, A_scale, W1: torch.Tensor, W1_scale, counts: Sequence[int],
+                    rows: Sequence[int], seg_align: int = 1) -> np.ndarray:
+    """As swiglu_rows for fp8 activations times packed E2M1 gate/up weights
+    W1 [G, 2I, K/2] (same row order) with power-of-two scales given as fp32."""
+    from . import fp4
+    c = fp4.contiguous_fp8_fp4(A, A_scale, W1, W1_scale, counts, rows, seg_align=seg_align)
+    g, u = split_gate_up(c)
+    return silu(g) * u
+
+
 def _e4m3_positive() -> np.ndarray:
     """Values of the non-negative finite e4m3 codes 0x00 .. 0x7E, ascending with the code."""
     return np.array([og.dec_e4m3(c) for c in range(0x7F)], dtype=np.float64)

@@ -929,6 +929,67 @@ def test_swiglu_e4m3_h_and_fp8_down_projection(block_m):
     assert ey <= P.TOL["fp8"], ey
 
 
+def run_mlp_fp4(counts, K, I, N2, block_m, seed):
+    """L1 with fp4 gate/up weights (fp8 activations, E8M0 scales) and the e4m3 H
+    epilogue, then the fp8 L2 on H."""
+    G, R = len(counts), sum(counts)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=seed, device="cuda", l2="fp8",
+                             w1_format="e2m1")
+    ws = mg.workspace(G, R)
+    mg.schedule(inp["counts"], R, ws, block_m=block_m, N=2 * I)
+    H = torch.empty((R, I), dtype=torch.float8_e4m3fn, device="cuda")
+    Hs = torch.full((R, I // 128), float("nan"), device="cuda")
+    Y = P.sentinel_like((R, N2))
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale_e8m0"], inp["W1_scale_e8m0"],
+                                     block_m=block_m, H_scale=Hs)
+    mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=block_m,
+                                         b_layout=mg.B_NK)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), counts)
+    return inp, H, Hs, Y
+
+
+@pytest.mark.parametrize("block_m", [0, 64, 256, mg.BLOCK_M_PER_EXPERT])
+def test_swiglu_fp4_weights(block_m):
+    """Expert MLP with fp4 gate/up weights: H (e4m3) and y on every valid row."""
+    counts = [70, 0, 300, 6, 129, 3]                     # 508 rows: a multiple of 4 (E8M0 scale rows)
+    K, I, N2 = 256, 256, 512
+    announce("expert MLP fp4 L1", counts, "block_m", block_m)
+    inp, H, Hs, Y = run_mlp_fp4(counts, K, I, N2, block_m, seed=26)
+    rows = list(range(sum(counts)))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    h = omlp.swiglu_rows_fp4(cpu["A"], cpu["A_scale"], cpu["W1"], cpu["W1_scale"], counts, rows)
+    q, s = check_fp8_h(H, Hs, h, rows)
+    qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
+    y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
+                      A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
+    assert og.rel_frobenius(P.rows_as_float(Y, rows), y) <= P.TOL["fp8"]
+
+
+def test_expert_mlp_fp4_full_size():
+    """fp4 gate/up weights at the DeepSeek-V3 expert shape on the Zipf histogram
+    (the configuration bench.py --mlp --weights e2m1 times); sampled rows."""
+    counts = wl.workload(3).counts
+    K, I, N2 = 7168, 2048, 7168
+    announce("expert MLP fp4 L1 full size")
+    inp, H, Hs, Y = run_mlp_fp4(counts, K, I, N2, 0, seed=27)
+    rows = P.sample_rows_contiguous(counts, 1, 256, extra=24, seed=19)
+    got_y = P.rows_as_float(Y, rows)
+    cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("W_gate", "W_up")}
+    del inp
+    h = omlp.swiglu_rows_fp4(cpu["A"], cpu["A_scale"], cpu["W1"], cpu["W1_scale"], counts, rows)
+    q, s = check_fp8_h(H, Hs, h, rows)
+    offs = acc.segment_offsets(counts, 1)
+    ex = [next(e for e in range(len(counts)) if offs[e] <= r < offs[e] + counts[e]) for r in rows]
+    y = np.empty((len(rows), N2))
+    for e in sorted(set(ex)):
+        idx = [i for i, x in enumerate(ex) if x == e]
+        w2e = cpu["W2"][e].float().double().numpy() * np.repeat(
+            np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0), 128, 1).T
+        y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
+    assert og.rel_frobenius(got_y, y) <= P.TOL["fp8"]
+
+
 def test_expert_mlp_fp8_full_size():
     """Both GEMMs fp8 at the DeepSeek-V3 expert shape on the Zipf histogram; sampled rows."""
     counts = wl.workload(3).counts

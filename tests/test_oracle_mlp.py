@@ -114,3 +114,18 @@ def test_quantize_groups_definition():
     assert q[0, 127] == 448.0 and q[1, 128] == -448.0  # the group's amax maps to the largest code
     assert np.all(np.abs(q[0, :128] * s[0, 0] - h[0, :128]) <= np.abs(h[0, :128]) / 16 + 1e-12)
     assert not q[0, 128:].any()
+
+
+def test_fp4_swiglu_oracle_matches_the_e4m3_route():
+    """fp4 gate/up weights: every E2M1 value is exact in e4m3, so the same
+    weights re-encoded as e4m3 through the C-oracle route give the same h."""
+    from oracle import fp4
+    counts = [3, 0, 2]
+    inp = wl.materialize_mlp(counts, K=256, I=64, N2=64, dtype="fp8", seed=2, w1_format="e2m1")
+    rows = list(range(5))
+    h4 = mlp.swiglu_rows_fp4(inp["A"], inp["A_scale"], inp["W1"], inp["W1_scale"], counts, rows)
+    w1_vals = torch.from_numpy(fp4.dec_e2m1_packed(inp["W1"].numpy())).float()       # [G, 2I, K]
+    w1_e4m3 = w1_vals.to(torch.float8_e4m3fn)
+    assert torch.equal(w1_e4m3.float(), w1_vals)
+    h8 = mlp.swiglu_rows(inp["A"], w1_e4m3, counts, rows, A_scale=inp["A_scale"], W1_scale=inp["W1_scale"])
+    assert np.allclose(h4, h8, rtol=1e-12, atol=1e-14)

@@ -357,7 +357,7 @@ def _valid_row_mask(wl: Workload, device) -> torch.Tensor:
 
 
 def materialize_mlp(counts: Sequence[int], K: int, I: int, N2: int, dtype: str = "bf16", seed: int = 6,
-                    device="cpu", l2: str = "bf16") -> Dict[str, Optional[torch.Tensor]]:
+                    device="cpu", l2: str = "bf16", w1_format: str = "e4m3") -> Dict[str, Optional[torch.Tensor]]:
     """Operands of an expert MLP (L1 -> SwiGLU -> L2), contiguous layout, packed segments.
 
     A [rows, K] ~ N(0, 1); gate and up weights [G, I, K] ~ N(0, 1)/sqrt(K),
@@ -366,6 +366,9 @@ def materialize_mlp(counts: Sequence[int], K: int, I: int, N2: int, dtype: str =
     dtype "bf16": A, W1 bf16.  "fp8": A e4m3 with fp32 1x128 scales, W1 e4m3
     with fp32 scales per 128x128 block of the interleaved rows.  W2 is bf16,
     or with l2 = "fp8" e4m3 with fp32 scales W2_scale [G, I/128, N2/128].
+    dtype "fp8" with w1_format = "e2m1": A with power-of-two 1x128 scales (also as
+    E8M0 bytes A_scale_e8m0 [K/128, rows]) and W1 packed E2M1 [G, 2I, K/2]
+    with power-of-two 128x128 block scales (W1_scale fp32, W1_scale_e8m0).
     Also returns the plain gate / up weights (W_gate, W_up, as W1's dtype
     before quantization: bf16 or fp32) for checks of the interleave."""
     G, R = len(counts), sum(counts)
@@ -385,6 +388,11 @@ def materialize_mlp(counts: Sequence[int], K: int, I: int, N2: int, dtype: str =
     if dtype == "bf16":
         out.update({"A": to_bf16(a), "A_scale": None, "W1": to_bf16(w1), "W1_scale": None,
                     "W_gate": to_bf16(wg), "W_up": to_bf16(wu)})
+    elif w1_format == "e2m1":
+        qa, sa = quantize_rows_e4m3(a, pow2=True)
+        qw, sw = quantize_blocks_e2m1(w1.transpose(1, 2).contiguous())         # packed [G, 2I, K/2]
+        out.update({"A": qa, "A_scale": sa, "W1": qw, "W1_scale": sw, "W_gate": wg, "W_up": wu,
+                    "A_scale_e8m0": e8m0_bytes(sa.t().contiguous()), "W1_scale_e8m0": e8m0_bytes(sw)})
     else:
         qa, sa = quantize_rows_e4m3(a)
         qw, sw = quantize_blocks_e4m3(w1.transpose(1, 2).contiguous())
