@@ -43,7 +43,7 @@ def log(*a):
 
 
 def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_block_m: int = 0, exemplars=None,
-               hysteresis: int = 0):
+               hysteresis: int = 0, scale_km: bool = False):
     """Returns (scheduler, gemm, workspace) closures for one workload.  With an
     exemplar table the scheduler picks the tile height by exemplar matching."""
     dev = "cuda"
@@ -60,7 +60,8 @@ def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_bloc
 
         def gemm():
             mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"),
-                                                 inp.get("B_scale"), block_m=block_m_hint, b_layout=b_layout)
+                                                 inp.get("B_scale"), block_m=block_m_hint, b_layout=b_layout,
+                                                 scale_km=scale_km)
         return sched, gemm, ws
     if w.layout == "masked":
         C = torch.empty((w.G, w.cap, w.N), dtype=torch.bfloat16, device=dev)
@@ -68,7 +69,7 @@ def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_bloc
 
         def gemm():
             mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], None, inp.get("A_scale"),
-                                   inp.get("B_scale"), b_layout=b_layout)
+                                   inp.get("B_scale"), b_layout=b_layout, scale_km=scale_km)
         return None, gemm, ws
     dW = torch.empty((w.G, w.Mw, w.Nw), dtype=torch.float32, device=dev)
     ws = mg.workspace(w.G, 0)
@@ -102,7 +103,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(w: wl.Workload, b_layout: int):
+def traffic_for(w: wl.Workload, b_layout: int, scale_km: bool = True):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary, if it was taken on this exact kernel source and workload; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -111,7 +112,8 @@ def traffic_for(w: wl.Workload, b_layout: int):
     with open(path) as f:
         t = json.load(f)
     key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}" + ("|e8m0" if w.scales == "e8m0" else "") + \
-        ("|e2m1" if w.weights == "e2m1" else "")
+        ("|e2m1" if w.weights == "e2m1" else "") + \
+        ("|rows" if w.dtype == "fp8" and w.scales != "e8m0" and not scale_km else "")
     e = t.get("entries", {}).get(key)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
@@ -171,12 +173,18 @@ def run_mlp(args):
     inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=14, device="cuda",
                              l2="fp8" if fp8_h else "bf16", w1_format="e2m1" if w4 else "e4m3")
     a_s, w1_s = (inp["A_scale_e8m0"], inp["W1_scale_e8m0"]) if w4 else (inp["A_scale"], inp["W1_scale"])
+    # fp32 scales go over transposed, [K/128, rows]: L1's input and the H scales it writes for L2 (an
+    # fp4-weight L1 takes E8M0 activation scales and writes H scales [rows, I/128])
+    km_l1 = not w4 and args.a_scale == "km"
+    km_l2 = fp8_h and km_l1
+    if km_l1:
+        a_s = a_s.t().contiguous()
     for k in ("W_gate", "W_up"):
         inp.pop(k)
     torch.cuda.empty_cache()
     ws = mg.workspace(G, R)
     H = torch.empty((R, I), dtype=torch.float8_e4m3fn if fp8_h else torch.bfloat16, device="cuda")
-    Hs = torch.empty((R, I // 128), device="cuda") if fp8_h else None
+    Hs = (torch.empty((I // 128, R) if km_l2 else (R, I // 128), device="cuda")) if fp8_h else None
     Y = torch.empty((R, N2), dtype=torch.bfloat16, device="cuda")
     mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
     torch.cuda.synchronize()
@@ -187,11 +195,12 @@ def run_mlp(args):
         mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
 
     def l1():
-        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, a_s, w1_s, block_m=bm, H_scale=Hs)
+        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, a_s, w1_s, block_m=bm, H_scale=Hs,
+                                         scale_km=km_l1)
 
     def l2():
         mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=bm,
-                                             b_layout=mg.B_NK)
+                                             b_layout=mg.B_NK, scale_km=km_l2)
     for _ in range(args.warmup):
         sched(); l1(); l2()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -260,6 +269,8 @@ def main():
     ap.add_argument("--mlp", action="store_true",
                     help="time the expert MLP (scheduler, L1 fp8 with the fused SwiGLU epilogue, L2 bf16) on the "
                          "Zipf histogram at the DeepSeek-V3 expert shape instead of one grouped GEMM")
+    ap.add_argument("--a-scale", choices=("km", "rows"), default="km",
+                    help="fp32 activation-scale layout for fp8: [K/128, rows] (default) or [rows, K/128]")
     ap.add_argument("--mlp-h", choices=("fp8", "bf16"), default="fp8",
                     help="with --mlp: H quantized to e4m3 in L1's epilogue and an fp8 L2 (default), or bf16 H and L2")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -319,12 +330,18 @@ def main():
     exemplars = mg.exemplar_table() if args.block_m == "exemplar" and w.layout == "contiguous" else None
     # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32
     inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) if w.scales == "e8m0" else inp
-    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req, exemplars, 4096)
+    # fp32 activation scales handed over [K/128, rows] (the quantizer upstream writes them so; the
+    # transpose here is input preparation, outside the timed region); the oracle keeps [rows, K/128]
+    scale_km = w.dtype == "fp8" and w.scales != "e8m0" and args.a_scale == "km"
+    if scale_km:
+        a_s = inp["A_scale"]
+        inp_gpu = dict(inp, A_scale=a_s.reshape(-1, a_s.shape[-1]).t().contiguous())
+    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req, exemplars, 4096, scale_km=scale_km)
     if sched is not None:
         sched()
         torch.cuda.synchronize()
         st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req, exemplars, 4096)
+        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req, exemplars, 4096, scale_km=scale_km)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -380,7 +397,8 @@ def main():
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
                    "weights": ("[G,N,K/2] packed e2m1" if w.weights == "e2m1" else "[G,N,K]")
                    if b_layout == mg.B_NK else "[G,K,N]",
-                   "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else "fp32")
+                   "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else
+                              "fp32, activation scales [K/128, rows]" if scale_km else "fp32")
                    if w.dtype == "fp8" else None,
                    "cache": "cold (512 MiB written between steps)" if args.cold else "warm",
                    "tile_choice": "exemplar table (MI355X)" if exemplars is not None else
@@ -405,7 +423,7 @@ def main():
     else:
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": peak,
                            "unit": "TFLOP/s", "frac": round(achieved_tflops / peak, 4), "traffic": None}
-    tr = traffic_for(w, b_layout)
+    tr = traffic_for(w, b_layout, scale_km)
     if tr is not None:
         out["roofline"]["traffic"] = tr
     out["gemm_kernel_ms"] = round(gemm_avg, 4)

@@ -57,11 +57,18 @@ typedef enum {
  * byte, element 2i in the low nibble, stored [G, N, K/2] (b_layout must be
  * MOEGG_B_NK), with E8M0 weight-block scales [G, K/128, N/128].  The same
  * gfx950 MFMA takes the fp4 operand directly.  Contiguous and masked layouts. */
+/* MOEGG_FP8_E4M3_SCALE_KM is MOEGG_FP8_E4M3 with the fp32 activation
+ * scales stored transposed, [K/128, rows] (the record's note that SM100 wants
+ * a transposed LHS scale layout; here for fp32 scales).  One K step's scales
+ * of a tile's rows are then contiguous: the kernel fetches them as a few
+ * cache lines instead of one line per row.  Same arithmetic as
+ * MOEGG_FP8_E4M3.  Contiguous and masked layouts and the SwiGLU call. */
 typedef enum {
     MOEGG_BF16 = 0,
     MOEGG_FP8_E4M3 = 1,
     MOEGG_FP8_E4M3_E8M0 = 2,
-    MOEGG_FP8_E4M3_FP4_E2M1 = 3
+    MOEGG_FP8_E4M3_FP4_E2M1 = 3,
+    MOEGG_FP8_E4M3_SCALE_KM = 4
 } moegg_dtype_t;
 
 /* How each expert's weight B_e is stored.
@@ -219,11 +226,13 @@ moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, vo
  *            as in moegg_schedule.  seg_align = 1 packs them back to back.  A
  *            larger seg_align puts every segment start at a multiple of it.
  *   A_scale  MOEGG_FP8_E4M3: fp32 [rows_total, K/128], one scale per 1x128
- *            group.  MOEGG_FP8_E4M3_E8M0: E8M0 bytes [K/128, rows_total]
- *            (transposed).  NULL for bf16.
+ *            group.  MOEGG_FP8_E4M3_SCALE_KM: the same scales as fp32
+ *            [K/128, rows_total].  MOEGG_FP8_E4M3_E8M0: E8M0 bytes
+ *            [K/128, rows_total] (transposed).  NULL for bf16.
  *   B        [G, K, N] or [G, N, K] (b_layout), same dtype as A.
  *            MOEGG_FP8_E4M3_FP4_E2M1: packed E2M1 bytes [G, N, K/2].
- *   B_scale  MOEGG_FP8_E4M3: fp32 [G, K/128, N/128], one per 128x128 block.
+ *   B_scale  MOEGG_FP8_E4M3 and MOEGG_FP8_E4M3_SCALE_KM: fp32
+ *            [G, K/128, N/128], one per 128x128 block.
  *            MOEGG_FP8_E4M3_E8M0 and MOEGG_FP8_E4M3_FP4_E2M1: E8M0 bytes,
  *            same shape.  NULL for bf16.
  *   C        bf16 [rows_total, N], row-major.  Only the rows of valid
@@ -289,9 +298,10 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  * Driven by the tile list an earlier moegg_schedule or
  * moegg_grouped_gemm_contiguous call left in `ws` (same G, rows_total).
  *   A        [rows_total, K] as for the contiguous call: bf16, e4m3 with
- *            fp32 1x128 scales, or (MOEGG_FP8_E4M3_FP4_E2M1) e4m3 with E8M0
- *            scale bytes [K/128, rows_total].  MOEGG_FP8_E4M3_E8M0 is not
- *            supported here.
+ *            fp32 1x128 scales ([rows_total, K/128], or [K/128, rows_total]
+ *            with MOEGG_FP8_E4M3_SCALE_KM), or (MOEGG_FP8_E4M3_FP4_E2M1) e4m3
+ *            with E8M0 scale bytes [K/128, rows_total].  MOEGG_FP8_E4M3_E8M0
+ *            is not supported here.
  *   W1       [G, 2I, K] (K-contiguous; b_layout must be MOEGG_B_NK): for
  *            q = 0 .. I/16 - 1 and w = 0 .. 15, row 32q + w is gate column
  *            16q + w and row 32q + 16 + w is up column 16q + w.  W1_scale
@@ -303,8 +313,9 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  *                h[R, c] = silu(g) * u,  silu(g) = g / (1 + e^-g)
  *            with fp32 accumulation and fp32 SwiGLU.  H_scale NULL: H is bf16,
  *            H[R, c] = bf16_rne(h).  H_scale set: H holds e4m3 codes and
- *            H_scale fp32 [rows_total, I/128] one scale per 1x128 group, the
- *            input format of the fp8 contiguous call:
+ *            H_scale fp32 [rows_total, I/128] (MOEGG_FP8_E4M3_SCALE_KM:
+ *            [I/128, rows_total]) one scale per 1x128 group, the input
+ *            format of the fp8 contiguous call with the same dtype:
  *                s = amax over the group of |h| / 448 (1 if the amax is 0),
  *                H[R, c] = e4m3_rne(clamp(h / s, -448, 448)).
  *            Other rows untouched.
@@ -322,7 +333,8 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
  * Masked layout for decode under graph capture (DeepGEMM record,
  * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
  * computes only the valid portions, with no CPU sync).
- *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (MOEGG_FP8_E4M3), E8M0
+ *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (MOEGG_FP8_E4M3),
+ *            fp32 [K/128, G * cap] (MOEGG_FP8_E4M3_SCALE_KM), E8M0
  *            bytes [K/128, G * cap] (MOEGG_FP8_E4M3_E8M0 and
  *            MOEGG_FP8_E4M3_FP4_E2M1; G * cap % 4 == 0), or NULL (bf16).
  *   B        as for the contiguous call.  B_scale as for the contiguous call.

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libmoegg.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moegg.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1 = 0, 1, 2, 3
+BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1, FP8_E4M3_SCALE_KM = 0, 1, 2, 3, 4
 B_KN, B_NK = 0, 1
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP, FLAG_BAD_EXEMPLAR = 0x1, 0x2, 0x4, 0x8
 Q_VALUES = (8, 16, 32, 64, 128, 256)
@@ -126,16 +126,26 @@ def _check(status: int, what: str):
         raise MoeggError(status, what)
 
 
-def _dtype(t: torch.Tensor, scale: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None) -> int:
+def _dtype(t: torch.Tensor, scale: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+           scale_km: bool = False) -> int:
     """Operand type code: fp8 with uint8 (E8M0) scales is MOEGG_FP8_E4M3_E8M0,
-    and with uint8 weights (packed E2M1 [G, N, K/2]) MOEGG_FP8_E4M3_FP4_E2M1."""
+    and with uint8 weights (packed E2M1 [G, N, K/2]) MOEGG_FP8_E4M3_FP4_E2M1.
+    scale_km: fp32 activation scales stored [K/128, rows]
+    (MOEGG_FP8_E4M3_SCALE_KM)."""
     if t.dtype == torch.bfloat16:
-        return BF16
-    if t.dtype == torch.float8_e4m3fn:
+        code = BF16
+    elif t.dtype == torch.float8_e4m3fn:
         if w is not None and w.dtype == torch.uint8:
-            return FP8_E4M3_FP4_E2M1
-        return FP8_E4M3_E8M0 if scale is not None and scale.dtype == torch.uint8 else FP8_E4M3
-    raise TypeError(f"bf16 or float8_e4m3fn operands expected, got {t.dtype}")
+            code = FP8_E4M3_FP4_E2M1
+        else:
+            code = FP8_E4M3_E8M0 if scale is not None and scale.dtype == torch.uint8 else FP8_E4M3
+    else:
+        raise TypeError(f"bf16 or float8_e4m3fn operands expected, got {t.dtype}")
+    if scale_km:
+        if code != FP8_E4M3:
+            raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
+        return FP8_E4M3_SCALE_KM
+    return code
 
 
 def workspace_bytes(G: int, max_rows: int) -> int:
@@ -200,23 +210,25 @@ def selection_read(ws: torch.Tensor, stream=None) -> Selection:
 
 
 def grouped_gemm_contiguous_scheduled(A, B, C, G: int, ws, A_scale=None, B_scale=None, block_m: int = 0,
-                                      b_layout: int = B_KN, stream=None):
-    """The contiguous GEMM from the tile list already in ws (see moegg.h)."""
+                                      b_layout: int = B_KN, stream=None, scale_km: bool = False):
+    """The contiguous GEMM from the tile list already in ws (see moegg.h).
+    scale_km: A_scale is fp32 [K/128, rows] (MOEGG_FP8_E4M3_SCALE_KM)."""
     K = A.shape[1]
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_contiguous_scheduled(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, A.shape[0], K, N, _dtype(A, A_scale, B), b_layout, block_m,
-        _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_contiguous_scheduled")
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, A.shape[0], K, N, _dtype(A, A_scale, B, scale_km), b_layout,
+        block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_contiguous_scheduled")
 
 
 def grouped_gemm_contiguous(A, B, C, m_sizes, ws, A_scale=None, B_scale=None, seg_align: int = 1,
-                            block_m: int = 0, b_layout: int = B_KN, stream=None):
-    """C[rows of expert e] = A[rows of expert e] @ B_e (see moegg.h)."""
+                            block_m: int = 0, b_layout: int = B_KN, stream=None, scale_km: bool = False):
+    """C[rows of expert e] = A[rows of expert e] @ B_e (see moegg.h).
+    scale_km: A_scale is fp32 [K/128, rows] (MOEGG_FP8_E4M3_SCALE_KM)."""
     K = A.shape[1]
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_contiguous(
         _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), m_sizes.numel(), A.shape[0], K, N,
-        seg_align, _dtype(A, A_scale, B), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
+        seg_align, _dtype(A, A_scale, B, scale_km), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
         "moegg_grouped_gemm_contiguous")
 
 
@@ -232,25 +244,28 @@ def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor
 
 
 def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=None, block_m: int = 0,
-                                  H_scale=None, stream=None):
+                                  H_scale=None, stream=None, scale_km: bool = False):
     """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h).
-    H bf16 [rows, I]; or, with H_scale (fp32 [rows, I/128]), H float8_e4m3fn codes."""
+    H bf16 [rows, I]; or, with H_scale (fp32 [rows, I/128]), H float8_e4m3fn codes.
+    scale_km: A_scale fp32 [K/128, rows] in, H_scale [I/128, rows] out."""
     K = A.shape[1]
     I = W1.shape[1] // 2
     if (H_scale is None) != (H.dtype == torch.bfloat16):
         raise ValueError("H: bf16 without H_scale, float8_e4m3fn with it")
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
-        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I, _dtype(A, A_scale, W1),
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I,
+        _dtype(A, A_scale, W1, scale_km),
         B_NK, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 
 def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, b_layout: int = B_KN,
-                        stream=None):
-    """C[e, r] = A[e, r] @ B_e for r < masked_m[e] (see moegg.h)."""
+                        stream=None, scale_km: bool = False):
+    """C[e, r] = A[e, r] @ B_e for r < masked_m[e] (see moegg.h).
+    scale_km: A_scale is fp32 [K/128, G * cap] (MOEGG_FP8_E4M3_SCALE_KM)."""
     G, cap, K = A.shape
     N = B.shape[2] if b_layout == B_KN else B.shape[1]
     _check(lib().moegg_grouped_gemm_masked(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, _dtype(A, A_scale, B), b_layout,
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, _dtype(A, A_scale, B, scale_km), b_layout,
         _p(ws), 0 if ws is None else ws.numel(), _stream(stream)), "moegg_grouped_gemm_masked")
 
 

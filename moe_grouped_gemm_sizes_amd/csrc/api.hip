@@ -44,7 +44,7 @@ moegg_status_t check_common(const void* A, const void* A_scale, const void* B, c
     if (!A || !B || !C) return MOEGG_ERR_INVALID_ARG;
     if (G < 1 || G > kMaxExperts || K < 1 || N < 1) return MOEGG_ERR_INVALID_ARG;
     if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3 && dtype != MOEGG_FP8_E4M3_E8M0 &&
-        dtype != MOEGG_FP8_E4M3_FP4_E2M1)
+        dtype != MOEGG_FP8_E4M3_FP4_E2M1 && dtype != MOEGG_FP8_E4M3_SCALE_KM)
         return MOEGG_ERR_INVALID_ARG;
     if (b_layout != MOEGG_B_KN && b_layout != MOEGG_B_NK) return MOEGG_ERR_INVALID_ARG;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
@@ -156,6 +156,7 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
     hipError_t e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, block_m, N / 256, 0, ws, L.max_tiles, s);
     if (e != hipSuccess) return hip_status(e, "scheduler launch");
     ContigArgs a{A, A_scale, B, B_scale, C, m_sizes, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
+    a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
     e = launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
                           b_layout == MOEGG_B_KN, rows_total, block_m, s);
     if (debug_on())
@@ -179,6 +180,7 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
     ContigArgs a{A, A_scale, B, B_scale, C, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
+    a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
     return hip_status(launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
                                         b_layout == MOEGG_B_KN, rows_total, block_m, (hipStream_t)stream),
                       "scheduled contiguous GEMM launch");
@@ -205,6 +207,7 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
     ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total,
                  H_scale};
+    a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
     return hip_status(launch_contiguous_swiglu(a, dtype != MOEGG_BF16, dtype == MOEGG_FP8_E4M3_FP4_E2M1, rows_total,
                                                block_m, (hipStream_t)stream),
                       "SwiGLU GEMM launch");
@@ -233,6 +236,7 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
         if (e != hipSuccess) return hip_status(e, "masked stats launch");
     }
     ContigArgs a{A, A_scale, B, B_scale, C, masked_m, (const unsigned char*)ws, G, K, N, cap, G * cap};
+    a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
     e = launch_masked(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
                       b_layout == MOEGG_B_KN, s);
     return hip_status(e, "masked GEMM launch");

@@ -331,7 +331,10 @@ struct TileGemm {
     v4f acc[C::NB][C::MB];
 
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-    uint32_t a_row_bytes, b_row_bytes, b_col_byte, sa_row_bytes;
+    uint32_t a_row_bytes, b_row_bytes, b_col_byte;
+    // fp32 activation scales: byte stride between tile rows and between K steps
+    // ([rows, K/128]: K/128 * 4 and 4; [K/128, rows_total]: 4 and rows_total * 4)
+    uint32_t sa_row_bytes, sa_step_bytes;
     uint32_t sb_col_byte;      // byte offset of this column tile's first weight-scale block in a K row
     uint32_t sb_row_bytes;     // weight-scale bytes per K step (N / 128 floats)
     int wm, wn, r16;
@@ -357,14 +360,16 @@ struct TileGemm {
             ss_step = act ? sa_step_e8 : sb_row_bytes;
             ss_dst = C::A_BYTES + C::B_BYTES + (act ? wave * 256 : C::SA_BYTES);
         } else if constexpr (C::FP8) {
-            // waves below BM/64: one 4-byte activation scale per tile row; the other
+            // waves below BM/64: one 4-byte activation scale per tile row (the
+            // step's scales of the tile are one contiguous run when stored
+            // [K/128, rows_total], one cache line per row otherwise); the other
             // waves: the weight-block scales of this column tile (all write the same
             // values to the same slots).  The weight-scale K row sits in voffset, so
             // the range check clamps lanes past the expert's scales.
             const bool act = wave < C::BM / 64;
             rss = act ? rsa : rsb;
             ss_voff = act ? (wave * 64 + lane) * sa_row_bytes : sb_col_byte + lane * 4;
-            ss_step = act ? 4u : sb_row_bytes;
+            ss_step = act ? sa_step_bytes : sb_row_bytes;
             ss_dst = C::A_BYTES + C::B_BYTES + (act ? wave * 256 : C::SA_BYTES);
         }
     }
@@ -653,7 +658,8 @@ struct TileGemm {
     // scale), clamped to +-448, round to nearest even (e4m3_code).  Codes go to rh (4 per
     // lane and 16-column block), the scale to rs[row, group].
     __device__ __forceinline__ void store_swiglu_e4m3(__amdgpu_buffer_rsrc_t rh, uint32_t row_bytes,
-                                                      __amdgpu_buffer_rsrc_t rs, uint32_t s_row_bytes, int group,
+                                                      __amdgpu_buffer_rsrc_t rs, uint32_t s_row_bytes,
+                                                      uint32_t s_group_bytes, int group,
                                                       char* lds, int rows_valid) {
         static_assert(C::NB % 2 == 0 && C::BN == 256, "one 128-wide group per tile row");
         const int lane = threadIdx.x & 63, g = lane >> 4;
@@ -702,7 +708,7 @@ struct TileGemm {
                 }
                 if (wn == 0 && g == 0)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, scale), rs,
-                                                          row * s_row_bytes + group * 4, 0, 0);
+                                                          row * s_row_bytes + group * s_group_bytes, 0, 0);
             }
         }
     }
@@ -736,7 +742,8 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
     }
     tg.rsa = tg.rb;
     tg.rsb = tg.rb;
-    tg.sa_row_bytes = (uint32_t)KB * 4;
+    tg.sa_row_bytes = p.a_scale_km ? 4u : (uint32_t)KB * 4;
+    tg.sa_step_bytes = p.a_scale_km ? (uint32_t)p.rows_total * 4 : 4u;
     tg.sb_row_bytes = (uint32_t)(p.N / 128) * 4;
     tg.sb_col_byte = (uint32_t)(n0 / 128) * 4;
     if constexpr (C::E8M0) {
@@ -754,7 +761,12 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         tg.sb_col = n0 / 128;
         tg.rsb = make_rsrc((const unsigned char*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * (p.N / 128));
     } else if constexpr (C::FP8) {
-        tg.rsa = make_rsrc((const float*)p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
+        // rows past rows_valid: zeros from the range check ([rows, K/128]), or the
+        // neighbouring rows' scales ([K/128, rows_total]), which only ever meet
+        // those rows' zero activations and are never stored
+        tg.rsa = p.a_scale_km
+                     ? make_rsrc((const float*)p.A_scale + row_start, (uint32_t)(((int64_t)KB * p.rows_total - row_start) * 4))
+                     : make_rsrc((const float*)p.A_scale + (size_t)row_start * KB, (uint32_t)rows_valid * KB * 4);
         // this expert's weight scales [K/128, N/128]; slots past the row read as zero
         tg.rsb = make_rsrc((const float*)p.B_scale + (size_t)e * KB * (p.N / 128), (uint32_t)KB * tg.sb_row_bytes);
     }
@@ -763,11 +775,15 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         // output H e4m3 [rows_total, N / 2] and its scales [rows_total, N / 256]: the tile's
         // BN / 2 = 128 outputs per row are one scale group (group ct)
         const uint32_t h_row_bytes = (uint32_t)p.N / 2;
-        const uint32_t s_row_bytes = (uint32_t)(p.N / 256) * 4;
+        // [rows_total, N / 256], or [N / 256, rows_total] with a_scale_km
+        const uint32_t s_row_bytes = p.a_scale_km ? 4u : (uint32_t)(p.N / 256) * 4;
+        const uint32_t s_group_bytes = p.a_scale_km ? (uint32_t)p.rows_total * 4 : 4u;
         auto rh = make_rsrc((char*)p.C + (size_t)row_start * h_row_bytes + (size_t)ct * (C::BN / 2),
                             (uint32_t)(rows_valid - 1) * h_row_bytes + C::BN / 2);
-        auto rs = make_rsrc((char*)p.C_scale + (size_t)row_start * s_row_bytes, (uint32_t)rows_valid * s_row_bytes);
-        tg.store_swiglu_e4m3(rh, h_row_bytes, rs, s_row_bytes, ct, lds, rows_valid);
+        auto rs = p.a_scale_km
+                      ? make_rsrc((float*)p.C_scale + row_start, (uint32_t)(((int64_t)(p.N / 256) * p.rows_total - row_start) * 4))
+                      : make_rsrc((char*)p.C_scale + (size_t)row_start * s_row_bytes, (uint32_t)rows_valid * s_row_bytes);
+        tg.store_swiglu_e4m3(rh, h_row_bytes, rs, s_row_bytes, s_group_bytes, ct, lds, rows_valid);
     } else if constexpr (SWIGLU == 1) {
         // output H [rows_total, N / 2]: the tile's BN interleaved columns give BN / 2 outputs
         const uint32_t h_row_bytes = (uint32_t)p.N;              // N / 2 bf16

@@ -10,7 +10,7 @@ namespace moegg {
 
 struct ContigArgs {
     const void* A;
-    const void* A_scale;          // fp32 [rows, K/128], or E8M0 bytes [K/128, rows_total]
+    const void* A_scale;          // fp32 [rows, K/128] or [K/128, rows_total], or E8M0 bytes [K/128, rows_total]
     const void* B;
     const void* B_scale;          // fp32 or E8M0 bytes [G, K/128, N/128]
     void* C;
@@ -19,6 +19,7 @@ struct ContigArgs {
     int G, K, N, cap;             // cap: masked layout only
     int rows_total;               // rows of A and C (masked layout: G * cap)
     void* C_scale;                // SwiGLU with e4m3 output: fp32 [rows_total, N / 256] scales, else NULL
+    int a_scale_km;               // fp32 activation scales (and C_scale) stored [K/128, rows_total]
 };
 
 struct KGroupedArgs {

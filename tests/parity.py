@@ -49,14 +49,18 @@ def sample_rows_contiguous(counts: Sequence[int], seg_align: int, block_m: int, 
     return sorted(rows)
 
 
-def run_contiguous(w: wl.Workload, inp: Dict, block_m: int = 0, b_layout: int = mg.B_KN):
+def run_contiguous(w: wl.Workload, inp: Dict, block_m: int = 0, b_layout: int = mg.B_KN, scale_km: bool = False):
+    """scale_km: hand the fp32 activation scales over transposed, [K/128, rows]."""
     A, B = inp["A"], inp["B"]
     if b_layout == mg.B_NK:
         B = B.transpose(1, 2).contiguous()
     C = sentinel_like((w.rows_total, w.N))
     ws = mg.workspace(w.G, w.rows_total)
-    mg.grouped_gemm_contiguous(A, B, C, inp["counts"], ws, A_scale=inp.get("A_scale"), B_scale=inp.get("B_scale"),
-                               seg_align=w.seg_align, block_m=block_m, b_layout=b_layout)
+    a_scale = inp.get("A_scale")
+    if scale_km:
+        a_scale = a_scale.t().contiguous()
+    mg.grouped_gemm_contiguous(A, B, C, inp["counts"], ws, A_scale=a_scale, B_scale=inp.get("B_scale"),
+                               seg_align=w.seg_align, block_m=block_m, b_layout=b_layout, scale_km=scale_km)
     torch.cuda.synchronize()
     return C, ws
 

@@ -65,6 +65,9 @@ def contiguous(**kw):
     (dict(layout=3), mg.ERR_INVALID_ARG),
     (dict(dtype=mg.FP8_E4M3), mg.ERR_INVALID_ARG),                 # fp8 without scales
     (dict(dtype=mg.FP8_E4M3, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_SCALE_KM), mg.ERR_INVALID_ARG),         # transposed fp32 scales, none given
+    (dict(dtype=mg.FP8_E4M3_SCALE_KM, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_SCALE_KM, A_scale=ctypes.c_void_p(0x100002), B_scale=FAKE), mg.ERR_INVALID_ARG),
     (dict(dtype=mg.FP8_E4M3_E8M0), mg.ERR_INVALID_ARG),            # E8M0 without scales
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=768), mg.ERR_UNSUPPORTED),   # N % 512
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=512, rows=130), mg.ERR_UNSUPPORTED),  # rows % 4
@@ -198,3 +201,15 @@ def test_k_grouped_accepts_null_operands_only_without_rows():
     # T = 0: X and dY are never read, so NULL passes validation (and fails later only on the workspace)
     assert f(None, None, FAKE, FAKE, 16, 0, 2048, 7168, None, 0, None) == mg.ERR_WORKSPACE
     assert f(None, None, FAKE, FAKE, 16, 1, 2048, 7168, None, 0, None) == mg.ERR_INVALID_ARG
+
+
+def test_scale_km_dtype_code():
+    """scale_km selects the transposed-fp32-scale format, and only for e4m3 with fp32 scales."""
+    import torch
+    a8, s = torch.empty(2, 128, dtype=torch.float8_e4m3fn), torch.empty(1, 2)
+    assert mg._dtype(a8, s, None, True) == mg.FP8_E4M3_SCALE_KM
+    assert mg._dtype(a8, s) == mg.FP8_E4M3
+    with pytest.raises(ValueError):
+        mg._dtype(torch.empty(2, 2, dtype=torch.bfloat16), None, None, True)
+    with pytest.raises(ValueError):
+        mg._dtype(a8, s.to(torch.uint8), None, True)
