@@ -607,21 +607,42 @@ struct TileGemm {
     }
 
     // bf16 epilogue: rows < rows_valid of the tile; C rows are row_bytes apart.
-    __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
+    // The tile goes through LDS (free once every wave's last DMAs have landed:
+    // the barrier after each wave's final vmcnt wait) as bf16 [BM][BN], 16-byte
+    // chunks XOR-swizzled by row & 15, so that the global stores write whole
+    // rows, 16 bytes per lane, rather than 8-byte pieces of 16 rows per
+    // instruction.  Stores past the valid rows fall outside rc and are dropped;
+    // whole 16-row groups past them are skipped.
+    __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid,
+                                               char* lds) {
+        static_assert(C::BM * C::BN * 2 <= C::LDS_BYTES, "the C tile fits in the ring");
+        constexpr int RB = C::BN * 2;                    // bytes per tile row in LDS
+        constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+        static_assert(CPR >= 16 && C::THREADS % CPR == 0, "row swizzle");
         const int g = (threadIdx.x & 63) >> 4;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < C::MB; ++j) {
             const int row = wm * C::WTM + j * 16 + r16;
-            if (row < rows_valid) {
 #pragma unroll
-                for (int i = 0; i < C::NB; ++i) {
-                    const int col = wn * C::WTN + i * 16 + 4 * g;
-                    v2i d;
-                    d.x = (int)pack_bf16x2(acc[i][j].x, acc[i][j].y);
-                    d.y = (int)pack_bf16x2(acc[i][j].z, acc[i][j].w);
-                    __builtin_amdgcn_raw_buffer_store_b64(d, rc, row * row_bytes + col * 2, 0, 0);
-                }
+            for (int i = 0; i < C::NB; ++i) {
+                const int col = wn * C::WTN + i * 16 + 4 * g;
+                v2i d;
+                d.x = (int)pack_bf16x2(acc[i][j].x, acc[i][j].y);
+                d.y = (int)pack_bf16x2(acc[i][j].z, acc[i][j].w);
+                const int chunk = (col >> 3) ^ (row & 15);
+                *(MOEGG_LDS v2i*)(lds + row * RB + chunk * 16 + (col & 7) * 2) = d;
             }
+        }
+        __syncthreads();
+        constexpr int ROWS_PER_PASS = C::THREADS / CPR;
+        const int c = threadIdx.x % CPR;
+#pragma unroll 4
+        for (int r0 = 0; r0 < C::BM; r0 += ROWS_PER_PASS) {
+            if (r0 >= rows_valid) break;
+            const int row = r0 + threadIdx.x / CPR;
+            const v4i v = lds_read_b128(lds + row * RB + ((c ^ (row & 15)) << 4));
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row * row_bytes + c * 16, 0, 0);
         }
     }
 
@@ -794,7 +815,7 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         const uint32_t c_row_bytes = (uint32_t)p.N * 2;
         auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
                             (uint32_t)(rows_valid - 1) * c_row_bytes + C::BN * 2);
-        tg.store_bf16(rc, c_row_bytes, rows_valid);
+        tg.store_bf16(rc, c_row_bytes, rows_valid, lds);
     }
 }
 
