@@ -971,16 +971,38 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
         }
         wait_vmcnt<0>();
     }
-    // fp32 epilogue: lane holds dW[i][j..j+3]
+    // fp32 epilogue (lane holds dW[i][j..j+3]) through LDS in two passes of
+    // BM / 2 rows, which is what the ring holds: the waves owning those rows
+    // write them as [BM/2][BN] fp32 with 16-byte chunks XOR-swizzled by
+    // row & 15, then every lane stores 16 bytes of a whole row, so each store
+    // instruction writes 1 KB of consecutive bytes instead of 64-byte pieces of
+    // 16 rows.  The first barrier also covers every wave's last DMAs.
+    static_assert(C::WAVES_M % 2 == 0 && (C::BM / 2) * C::BN * 4 <= C::LDS_BYTES, "epilogue passes");
+    constexpr int RB = C::BN * 4, CPR = RB / 16, HALF_ROWS = C::BM / 2;
+    static_assert(CPR >= 16 && C::THREADS % CPR == 0, "row swizzle");
     const int r16 = lane & 15, g = lane >> 4;
     float* out = p.dW + (size_t)e * p.Mw * p.Nw;
+    const int c = tid % CPR;
 #pragma unroll
-    for (int j = 0; j < C::MB; ++j) {
-        const int i = i0 + wm * C::WTM + j * 16 + r16;
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        if (wm / (C::WAVES_M / 2) == h) {
 #pragma unroll
-        for (int n = 0; n < C::NB; ++n) {
-            const int col = j0 + wn * C::WTN + n * 16 + 4 * g;
-            *(v4f*)(out + (size_t)i * p.Nw + col) = acc[n][j];
+            for (int j = 0; j < C::MB; ++j) {
+                const int row = (wm % (C::WAVES_M / 2)) * C::WTM + j * 16 + r16;
+#pragma unroll
+                for (int n = 0; n < C::NB; ++n) {
+                    const int chunk = ((wn * C::WTN + n * 16 + 4 * g) >> 2) ^ (row & 15);
+                    *(MOEGG_LDS v4f*)(lds + row * RB + chunk * 16) = acc[n][j];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r0 = 0; r0 < HALF_ROWS; r0 += C::THREADS / CPR) {
+            const int row = r0 + tid / CPR;
+            const v4f v = *(const MOEGG_LDS v4f*)(lds + row * RB + ((c ^ (row & 15)) << 4));
+            *(v4f*)(out + (size_t)(i0 + h * HALF_ROWS + row) * p.Nw + j0 + c * 4) = v;
         }
     }
 }
