@@ -606,19 +606,44 @@ struct TileGemm {
         dispatch<C::MB>(lds, mba, nks);
     }
 
+    // ---- epilogues staged through LDS
+    // An output tile of BM rows of RB bytes is written to LDS first, 16-byte
+    // chunks XOR-swizzled by the row (row & 15, or & 7 for 8-chunk rows), then
+    // stored as whole rows, 16 bytes per lane, so each store instruction writes
+    // THREADS * 16 consecutive-row bytes instead of a few bytes of each of 16
+    // rows.  Byte b of tile row r sits at lds_off<RB>(r, b).
+    template <int RB>
+    __device__ __forceinline__ static int lds_off(int row, int byte) {
+        constexpr int CPR = RB / 16;
+        static_assert(CPR >= 8 && C::THREADS % CPR == 0, "row swizzle");
+        return row * RB + ((((byte >> 4) ^ (row & (CPR >= 16 ? 15 : 7)))) << 4) + (byte & 15);
+    }
+
+    // Stores rows < rows_valid of the staged tile (after a barrier that
+    // published it); output rows are row_bytes apart in rc.  Stores past the
+    // valid rows fall outside rc and are dropped; whole passes past them are
+    // skipped.
+    template <int RB>
+    __device__ __forceinline__ static void store_staged(const char* lds, __amdgpu_buffer_rsrc_t rc,
+                                                        uint32_t row_bytes, int rows_valid) {
+        constexpr int CPR = RB / 16, ROWS_PER_PASS = C::THREADS / CPR;
+        static_assert(C::BM * RB <= C::LDS_BYTES, "the staged tile fits in the ring");
+        const int c = threadIdx.x % CPR;
+#pragma unroll 4
+        for (int r0 = 0; r0 < C::BM; r0 += ROWS_PER_PASS) {
+            if (r0 >= rows_valid) break;
+            const int row = r0 + threadIdx.x / CPR;
+            const v4i v = lds_read_b128(lds + lds_off<RB>(row, c * 16));
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row * row_bytes + c * 16, 0, 0);
+        }
+    }
+
     // bf16 epilogue: rows < rows_valid of the tile; C rows are row_bytes apart.
-    // The tile goes through LDS (free once every wave's last DMAs have landed:
-    // the barrier after each wave's final vmcnt wait) as bf16 [BM][BN], 16-byte
-    // chunks XOR-swizzled by row & 15, so that the global stores write whole
-    // rows, 16 bytes per lane, rather than 8-byte pieces of 16 rows per
-    // instruction.  Stores past the valid rows fall outside rc and are dropped;
-    // whole 16-row groups past them are skipped.
+    // The first barrier makes the ring free: every wave's last DMAs have landed
+    // (each waited for its own before it).
     __device__ __forceinline__ void store_bf16(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid,
                                                char* lds) {
-        static_assert(C::BM * C::BN * 2 <= C::LDS_BYTES, "the C tile fits in the ring");
-        constexpr int RB = C::BN * 2;                    // bytes per tile row in LDS
-        constexpr int CPR = RB / 16;                     // 16-byte chunks per row
-        static_assert(CPR >= 16 && C::THREADS % CPR == 0, "row swizzle");
+        constexpr int RB = C::BN * 2;
         const int g = (threadIdx.x & 63) >> 4;
         __syncthreads();
 #pragma unroll
@@ -630,20 +655,11 @@ struct TileGemm {
                 v2i d;
                 d.x = (int)pack_bf16x2(acc[i][j].x, acc[i][j].y);
                 d.y = (int)pack_bf16x2(acc[i][j].z, acc[i][j].w);
-                const int chunk = (col >> 3) ^ (row & 15);
-                *(MOEGG_LDS v2i*)(lds + row * RB + chunk * 16 + (col & 7) * 2) = d;
+                *(MOEGG_LDS v2i*)(lds + lds_off<RB>(row, col * 2)) = d;
             }
         }
         __syncthreads();
-        constexpr int ROWS_PER_PASS = C::THREADS / CPR;
-        const int c = threadIdx.x % CPR;
-#pragma unroll 4
-        for (int r0 = 0; r0 < C::BM; r0 += ROWS_PER_PASS) {
-            if (r0 >= rows_valid) break;
-            const int row = r0 + threadIdx.x / CPR;
-            const v4i v = lds_read_b128(lds + row * RB + ((c ^ (row & 15)) << 4));
-            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row * row_bytes + c * 16, 0, 0);
-        }
+        store_staged<RB>(lds, rc, row_bytes, rows_valid);
     }
 
     // SwiGLU epilogue: the tile's columns come in groups of 32, gate columns
@@ -651,24 +667,27 @@ struct TileGemm {
     // gate and up values of the same 16 outputs in the same lanes.  Writes
     // silu(gate) * up as bf16: 4 consecutive outputs per lane, rows <
     // rows_valid, output row_bytes apart, BN / 2 outputs per tile.
-    __device__ __forceinline__ void store_swiglu(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid) {
+    __device__ __forceinline__ void store_swiglu(__amdgpu_buffer_rsrc_t rc, uint32_t row_bytes, int rows_valid,
+                                                 char* lds) {
         static_assert(C::NB % 2 == 0, "gate/up block pairs");
+        constexpr int RB = C::BN;                        // BN / 2 bf16 outputs per row
         const int g = (threadIdx.x & 63) >> 4;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < C::MB; ++j) {
             const int row = wm * C::WTM + j * 16 + r16;
-            if (row < rows_valid) {
 #pragma unroll
-                for (int ip = 0; ip < C::NB / 2; ++ip) {
-                    const v4f gt = acc[2 * ip][j], up = acc[2 * ip + 1][j];
-                    const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
-                    v2i d;
-                    d.x = (int)pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y);
-                    d.y = (int)pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w);
-                    __builtin_amdgcn_raw_buffer_store_b64(d, rc, row * row_bytes + col * 2, 0, 0);
-                }
+            for (int ip = 0; ip < C::NB / 2; ++ip) {
+                const v4f gt = acc[2 * ip][j], up = acc[2 * ip + 1][j];
+                const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
+                v2i d;
+                d.x = (int)pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y);
+                d.y = (int)pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w);
+                *(MOEGG_LDS v2i*)(lds + lds_off<RB>(row, col * 2)) = d;
             }
         }
+        __syncthreads();
+        store_staged<RB>(lds, rc, row_bytes, rows_valid);
     }
 
     // SwiGLU epilogue with H quantized for an e4m3 down projection: the tile's
@@ -676,8 +695,9 @@ struct TileGemm {
     // over the lane's 4 x NB / 2 values, the four lane groups holding the row
     // (lane shuffles) and the WAVES_N wave columns (through LDS, which no stage
     // uses any more); scale = amax / 448 (1 when amax = 0); code = e4m3(h /
-    // scale), clamped to +-448, round to nearest even (e4m3_code).  Codes go to rh (4 per
-    // lane and 16-column block), the scale to rs[row, group].
+    // scale), clamped to +-448, round to nearest even (e4m3_code).  The codes are
+    // staged in LDS behind the amax exchange and stored to rh as whole rows; the
+    // scale goes to rs[row, group].
     __device__ __forceinline__ void store_swiglu_e4m3(__amdgpu_buffer_rsrc_t rh, uint32_t row_bytes,
                                                       __amdgpu_buffer_rsrc_t rs, uint32_t s_row_bytes,
                                                       uint32_t s_group_bytes, int group,
@@ -705,6 +725,11 @@ struct TileGemm {
         // every wave's DMAs have landed once all waves pass this barrier
         __syncthreads();
         float* red = (float*)lds;                             // [WAVES_N][BM]
+        // the staged codes [BM][BN / 2] follow the amax exchange
+        constexpr int RED_BYTES = 4096;
+        static_assert(C::WAVES_N * C::BM * 4 <= RED_BYTES && RED_BYTES + C::BM * C::BN / 2 <= C::LDS_BYTES,
+                      "epilogue LDS");
+        char* codes = lds + RED_BYTES;
         if (g == 0) {
 #pragma unroll
             for (int j = 0; j < C::MB; ++j) red[wn * C::BM + wm * C::WTM + j * 16 + r16] = amax[j];
@@ -717,21 +742,23 @@ struct TileGemm {
 #pragma unroll
             for (int w = 0; w < C::WAVES_N; ++w) m = fmaxf(m, red[w * C::BM + row]);
             const float scale = m > 0.f ? m / 448.f : 1.f;
-            if (row < rows_valid) {
+            // codes of every row go to the staged tile (rows past the valid ones
+            // are never stored; the clamp turns a NaN into -448 first)
 #pragma unroll
-                for (int ip = 0; ip < C::NB / 2; ++ip) {
-                    uint32_t v = 0;
+            for (int ip = 0; ip < C::NB / 2; ++ip) {
+                uint32_t v = 0;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        v |= e4m3_code(fminf(fmaxf(h[j][ip][t] / scale, -448.f), 448.f)) << (8 * t);
-                    const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
-                    __builtin_amdgcn_raw_buffer_store_b32((int)v, rh, row * row_bytes + col, 0, 0);
-                }
-                if (wn == 0 && g == 0)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, scale), rs,
-                                                          row * s_row_bytes + group * s_group_bytes, 0, 0);
+                for (int t = 0; t < 4; ++t)
+                    v |= e4m3_code(fminf(fmaxf(h[j][ip][t] / scale, -448.f), 448.f)) << (8 * t);
+                const int col = wn * C::WTN / 2 + ip * 16 + 4 * g;
+                *(MOEGG_LDS uint32_t*)(codes + lds_off<C::BN / 2>(row, col)) = v;
             }
+            if (row < rows_valid && wn == 0 && g == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, scale), rs,
+                                                      row * s_row_bytes + group * s_group_bytes, 0, 0);
         }
+        __syncthreads();
+        store_staged<C::BN / 2>(codes, rh, row_bytes, rows_valid);
     }
 };
 
@@ -810,7 +837,7 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         const uint32_t h_row_bytes = (uint32_t)p.N;              // N / 2 bf16
         auto rh = make_rsrc((char*)p.C + (size_t)row_start * h_row_bytes + (size_t)n0,
                             (uint32_t)(rows_valid - 1) * h_row_bytes + C::BN);
-        tg.store_swiglu(rh, h_row_bytes, rows_valid);
+        tg.store_swiglu(rh, h_row_bytes, rows_valid, lds);
     } else {
         const uint32_t c_row_bytes = (uint32_t)p.N * 2;
         auto rc = make_rsrc((char*)p.C + (size_t)row_start * c_row_bytes + (size_t)n0 * 2,
