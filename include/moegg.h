@@ -246,7 +246,9 @@ moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, vo
  * the two powers of two instead: the same value up to fp32 rounding order.
  * Constraints: K % 128 == 0 and N % 256 == 0 for fp8.  K % 64 == 0 and
  * N % 256 == 0 for bf16.  E8M0 scales also need N % 512 == 0, N <= 32768
- * and rows_total % 4 == 0 (UNSUPPORTED otherwise); fp4 weights also need
+ * and rows_total % 4 == 0 (UNSUPPORTED otherwise); scales stored [K/128,
+ * rows_total] (E8M0, MOEGG_FP8_E4M3_SCALE_KM) must span at most 4 GiB
+ * (UNSUPPORTED otherwise); fp4 weights also need
  * b_layout = MOEGG_B_NK (UNSUPPORTED otherwise).  16-byte aligned
  * operands, 4-byte aligned scales.  G = 1..4096.
  * block_m: 64, 128 or 256; 0 = choose one height on the device from the

@@ -2,6 +2,8 @@
 // workspace layout and kernel launches.  No call here allocates device
 // memory or synchronizes, except the two *_read calls.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -36,6 +38,14 @@ moegg_status_t hip_status(hipError_t e, const char* what) {
 
 // Block scales stored as E8M0 exponent bytes.
 bool e8m0_scales(moegg_dtype_t d) { return d == MOEGG_FP8_E4M3_E8M0 || d == MOEGG_FP8_E4M3_FP4_E2M1; }
+
+// Scales stored [groups, rows] (E8M0 bytes, or fp32 with MOEGG_FP8_E4M3_SCALE_KM)
+// are addressed with 32-bit buffer offsets across the whole array, so
+// groups * rows elements must stay within 4 GiB.
+bool transposed_scales_fit(moegg_dtype_t d, int64_t groups, int64_t rows) {
+    const int64_t esz = d == MOEGG_FP8_E4M3_SCALE_KM ? 4 : e8m0_scales(d) ? 1 : 0;
+    return groups * rows * esz <= (int64_t)UINT32_MAX;
+}
 
 // Shared checks for the contiguous and masked calls.
 moegg_status_t check_common(const void* A, const void* A_scale, const void* B, const void* B_scale,
@@ -146,6 +156,7 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX || seg_align < 1) return MOEGG_ERR_INVALID_ARG;
     if (e8m0_scales(dtype) && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (!transposed_scales_fit(dtype, K / 128, rows_total)) return MOEGG_ERR_UNSUPPORTED;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
@@ -174,6 +185,7 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
     if (st != MOEGG_OK) return st;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     if (e8m0_scales(dtype) && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (!transposed_scales_fit(dtype, K / 128, rows_total)) return MOEGG_ERR_UNSUPPORTED;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
@@ -198,6 +210,8 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     if (st != MOEGG_OK) return st;
     if (dtype == MOEGG_FP8_E4M3_E8M0) return MOEGG_ERR_UNSUPPORTED;
     if (dtype == MOEGG_FP8_E4M3_FP4_E2M1 && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    // A_scale [K/128, rows_total] in; with MOEGG_FP8_E4M3_SCALE_KM also H_scale [I/128, rows_total] out
+    if (!transposed_scales_fit(dtype, std::max(K, I) / 128, rows_total)) return MOEGG_ERR_UNSUPPORTED;
     if (b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
@@ -223,6 +237,7 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     if (cap < 1 || (int64_t)G * cap > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     // E8M0 activation scales [K/128, G * cap] are read four bytes at a time
     if (e8m0_scales(dtype) && ((int64_t)G * cap) % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
+    if (!transposed_scales_fit(dtype, K / 128, (int64_t)G * cap)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if ((int64_t)masked_block_m() * K * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;

@@ -68,6 +68,10 @@ def contiguous(**kw):
     (dict(dtype=mg.FP8_E4M3_SCALE_KM), mg.ERR_INVALID_ARG),         # transposed fp32 scales, none given
     (dict(dtype=mg.FP8_E4M3_SCALE_KM, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
     (dict(dtype=mg.FP8_E4M3_SCALE_KM, A_scale=ctypes.c_void_p(0x100002), B_scale=FAKE), mg.ERR_INVALID_ARG),
+    # transposed scales beyond 32-bit offsets: K/128 * rows fp32 scales over 4 GiB, E8M0 bytes over 4 GiB
+    (dict(dtype=mg.FP8_E4M3_SCALE_KM, A_scale=FAKE, B_scale=FAKE, K=7168, rows=20_000_000), mg.ERR_UNSUPPORTED),
+    (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=512, K=131072, rows=40_000_000),
+     mg.ERR_UNSUPPORTED),
     (dict(dtype=mg.FP8_E4M3_E8M0), mg.ERR_INVALID_ARG),            # E8M0 without scales
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=768), mg.ERR_UNSUPPORTED),   # N % 512
     (dict(dtype=mg.FP8_E4M3_E8M0, A_scale=FAKE, B_scale=FAKE, N=512, rows=130), mg.ERR_UNSUPPORTED),  # rows % 4
