@@ -50,6 +50,8 @@ def lib():
         L.oracle_masked.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i64, vp]
         L.oracle_k_grouped.restype = i32
         L.oracle_k_grouped.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, i64, vp]
+        L.oracle_k_grouped_fp8.restype = i32
+        L.oracle_k_grouped_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i64, vp, vp, i64, vp]
         L.oracle_threads.restype = i32
         _lib = L
     return _lib
@@ -123,6 +125,29 @@ def k_grouped(X, dY, t_sizes: Sequence[int], experts: Sequence[int], is_: Sequen
                                 len(e), ctypes.c_void_p(out.ctypes.data))
     if rc != 0:
         raise ValueError("oracle_k_grouped rejected its arguments")
+    return out
+
+
+def k_grouped_fp8(X, X_scale, dY, dY_scale, t_sizes: Sequence[int], experts: Sequence[int],
+                  is_: Sequence[int]) -> np.ndarray:
+    """Rows dW[e, i, :] of the K-grouped weight gradient on e4m3 operands with
+    fp32 scales per 128-row group of each expert's segment (see oracle.c):
+    X e4m3 [T, Mw], X_scale fp32 [n_groups, Mw], dY e4m3 [T, Nw], dY_scale fp32
+    [n_groups, Nw]."""
+    X, dY = X.contiguous(), dY.contiguous()
+    assert X.dtype == torch.float8_e4m3fn and dY.dtype == torch.float8_e4m3fn
+    Xs, dYs = X_scale.float().contiguous(), dY_scale.float().contiguous()
+    T, Mw = X.shape
+    Nw = dY.shape[1]
+    assert Xs.shape[0] == dYs.shape[0] and Xs.shape[1] == Mw and dYs.shape[1] == Nw
+    t = torch.tensor(list(t_sizes), dtype=torch.int32)
+    e = torch.tensor(list(experts), dtype=torch.int32)
+    i = torch.tensor(list(is_), dtype=torch.int32)
+    out = np.empty((len(e), Nw), dtype=np.float64)
+    rc = lib().oracle_k_grouped_fp8(_ptr(X), _ptr(Xs), _ptr(dY), _ptr(dYs), _ptr(t), len(t_sizes), T, Mw, Nw,
+                                    Xs.shape[0], _ptr(e), _ptr(i), len(e), ctypes.c_void_p(out.ctypes.data))
+    if rc != 0:
+        raise ValueError("oracle_k_grouped_fp8 rejected its arguments")
     return out
 
 

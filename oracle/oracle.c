@@ -179,6 +179,60 @@ int oracle_k_grouped(const uint16_t* X, const uint16_t* dY, const int32_t* t_siz
     return bad ? -1 : 0;
 }
 
+/*
+ * K-grouped weight gradient with e4m3 operands and fp32 scales along the
+ * reduction axis (DeepGEMM record, "Workarounds": the K-grouped MoE weight
+ * backward next to FP8 with per-group scaling).  The reduction axis is the
+ * token axis, so each scale group is 128 consecutive rows of one expert's
+ * segment and one column:
+ *   - expert e's segment starts at off[e] = sum_{j<e} t_j and holds t_e rows;
+ *   - its groups are its rows 0..127, 128..255, ... counted from the segment
+ *     start (the last group may hold fewer than 128 rows);
+ *   - groups are numbered across experts in order: expert e's first group is
+ *     goff[e] = sum_{j<e} ceil(t_j / 128);
+ *   - Xs[g, i] scales column i of X in group g, dYs[g, j] column j of dY.
+ * Then
+ *     dW[e, i, j] = sum over expert e's rows t of
+ *                   (dec(X[t, i]) * Xs[g(t), i]) * (dec(dY[t, j]) * dYs[g(t), j])
+ * with g(t) = goff[e] + (t - off[e]) / 128, summed in fp64, t ascending.
+ * Xs is [n_groups, Mw] and dYs [n_groups, Nw]; n_groups must cover every
+ * group.  An expert with no rows gets 0.  Each request (experts[i], is[i])
+ * gets the dW row dW[e, i, :].
+ */
+int oracle_k_grouped_fp8(const uint8_t* X, const float* Xs, const uint8_t* dY, const float* dYs,
+                         const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw, int64_t n_groups,
+                         const int32_t* experts, const int32_t* is, int64_t nreq, double* out) {
+    if (G <= 0 || Mw <= 0 || Nw <= 0 || n_groups < 0) return -1;
+    int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    int64_t* goff = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    if (!off || !goff) { free(off); free(goff); return -1; }
+    off[0] = 0;
+    goff[0] = 0;
+    for (int e = 0; e < G; ++e) {
+        if (t_sizes[e] < 0) { free(off); free(goff); return -1; }
+        off[e + 1] = off[e] + t_sizes[e];
+        goff[e + 1] = goff[e] + (t_sizes[e] + 127) / 128;
+    }
+    if (off[G] > T || goff[G] > n_groups) { free(off); free(goff); return -1; }
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t q = 0; q < nreq; ++q) {
+        int e = experts[q], i = is[q];
+        double* o = out + q * (int64_t)Nw;
+        if (e < 0 || e >= G || i < 0 || i >= Mw) { bad = 1; continue; }
+        for (int j = 0; j < Nw; ++j) o[j] = 0.0;
+        for (int64_t t = off[e]; t < off[e + 1]; ++t) {
+            int64_t g = goff[e] + (t - off[e]) / 128;
+            double x = oracle_dec_e4m3(X[t * Mw + i]) * (double)Xs[g * Mw + i];
+            for (int j = 0; j < Nw; ++j)
+                o[j] += x * (oracle_dec_e4m3(dY[t * Nw + j]) * (double)dYs[g * Nw + j]);
+        }
+    }
+    free(off);
+    free(goff);
+    return bad ? -1 : 0;
+}
+
 /* Number of OpenMP threads a parallel region uses (1 without OpenMP). */
 int oracle_threads(void) {
     int n = 1;

@@ -217,6 +217,40 @@ def quantize_blocks_e4m3(w: torch.Tensor, pow2: bool = False):
     return q, s
 
 
+def k_group_starts(counts: Sequence[int]) -> List[int]:
+    """First scale group of each expert's segment along the token axis, and the
+    total: groups are 128 consecutive rows of one segment, counted from the
+    segment start, so expert e starts at sum over j < e of ceil(t_j / 128)."""
+    starts = [0]
+    for t in counts:
+        starts.append(starts[-1] + (max(int(t), 0) + SCALE_GROUP - 1) // SCALE_GROUP)
+    return starts
+
+
+def quantize_k_groups_e4m3(x: torch.Tensor, counts: Sequence[int]):
+    """Operand [T, M] of the K-grouped weight gradient, rows grouped by expert ->
+    (e4m3 codes [T, M], fp32 scales [n_groups, M]).
+
+    Each scale covers one column over a group of up to 128 consecutive rows of
+    one expert's segment (groups restart at every segment start; the last group
+    of a segment may be short): s = amax / 448, 1 for an all-zero group."""
+    T, M = x.shape
+    starts = k_group_starts(counts)
+    q = torch.empty((T, M), dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.ones((max(starts[-1], 1), M), dtype=torch.float32, device=x.device)
+    off = 0
+    for e, t in enumerate(counts):
+        for gi in range(starts[e + 1] - starts[e]):
+            r0, r1 = off + gi * SCALE_GROUP, min(off + (gi + 1) * SCALE_GROUP, off + t)
+            blk = x[r0:r1].float()
+            amax = blk.abs().amax(dim=0, keepdim=True)
+            sg = _scale_for(amax, False)
+            q[r0:r1] = _to_e4m3(blk / sg)
+            s[starts[e] + gi] = sg.squeeze(0)
+        off += t
+    return q, s
+
+
 # ---------------------------------------------------------------- workloads
 
 
@@ -306,8 +340,14 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
     s = wl.seed * 1000
     if wl.layout == "k_grouped":
         T = sum(wl.counts)
-        out["X"] = to_bf16(_values((T, wl.Mw), wl, T, s + 1, device))
-        out["dY"] = to_bf16(_values((T, wl.Nw), wl, T, s + 2, device))
+        x = _values((T, wl.Mw), wl, T, s + 1, device)
+        dy = _values((T, wl.Nw), wl, T, s + 2, device)
+        if wl.dtype == "fp8":
+            # e4m3 with fp32 scales per 128-row group of each expert's segment
+            out["X"], out["X_scale"] = quantize_k_groups_e4m3(x, wl.counts)
+            out["dY"], out["dY_scale"] = quantize_k_groups_e4m3(dy, wl.counts)
+        else:
+            out["X"], out["dY"] = to_bf16(x), to_bf16(dy)
         return out
     if wl.layout == "contiguous":
         a_shape = (wl.rows_total, wl.K)
