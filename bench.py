@@ -75,7 +75,8 @@ def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_bloc
     ws = mg.workspace(w.G, 0)
 
     def gemm():
-        mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws)
+        mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws, inp.get("X_scale"),
+                                  inp.get("dY_scale"))
     return None, gemm, ws
 
 
@@ -84,6 +85,9 @@ def algorithmic_bytes(w: wl.Workload) -> int:
     active = sum(1 for c in w.counts if c > 0)
     U = sum(w.counts)
     if w.layout == "k_grouped":
+        if w.dtype == "fp8":
+            groups = mg.k_scale_groups(w.counts)
+            return U * (w.Mw + w.Nw) + groups * (w.Mw + w.Nw) * 4 + w.G * w.Mw * w.Nw * 4
         return U * (w.Mw + w.Nw) * 2 + w.G * w.Mw * w.Nw * 4
     esz = 1 if w.dtype == "fp8" else 2
     w_bytes = w.K * w.N // 2 if w.weights == "e2m1" else w.K * w.N * esz
@@ -260,6 +264,10 @@ def main():
                             "workloads 2-5, whose operands (0.8-2.2 GB) are streamed once per layer in a model")
     cache.add_argument("--warm", dest="cold", action="store_false",
                        help="back-to-back steps, operands left in L2 and MALL; the default for workload 1")
+    ap.add_argument("--dtype", choices=("as-stated", "fp8"), default="as-stated",
+                    help="fp8: run the masked decode (4) or the K-grouped weight-gradient (5) workload on e4m3 "
+                         "operands with fp32 scales (per 1x128 activation group and 128x128 weight block; "
+                         "K-grouped: per 128-row group of each expert's segment and column)")
     ap.add_argument("--scales", choices=("fp32", "e8m0"), default="fp32",
                     help="fp8 block scales: fp32 (the workload as stated, promoted on the VALU), or powers of two "
                          "as E8M0 bytes, applied by the MFMA (contiguous fp8 workloads only)")
@@ -298,6 +306,12 @@ def main():
         run_mlp(args)
         return
     w = wl.workload(args.config)
+    if args.dtype == "fp8":
+        if w.layout == "contiguous":
+            print("--dtype fp8 applies to the masked (4) and K-grouped (5) workloads", file=sys.stderr)
+            sys.exit(2)
+        if w.dtype != "fp8":
+            w.dtype, w.name = "fp8", w.name.replace("bf16", "fp8")
     if args.weights == "e2m1":
         args.scales = "e8m0"
         w.weights = "e2m1"
@@ -332,7 +346,7 @@ def main():
     inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) if w.scales == "e8m0" else inp
     # fp32 activation scales handed over [K/128, rows] (the quantizer upstream writes them so; the
     # transpose here is input preparation, outside the timed region); the oracle keeps [rows, K/128]
-    scale_km = w.dtype == "fp8" and w.scales != "e8m0" and args.a_scale == "km"
+    scale_km = w.dtype == "fp8" and w.scales != "e8m0" and args.a_scale == "km" and w.layout != "k_grouped"
     if scale_km:
         a_s = inp["A_scale"]
         inp_gpu = dict(inp, A_scale=a_s.reshape(-1, a_s.shape[-1]).t().contiguous())
@@ -392,6 +406,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp8_e4m3 x fp4_e2m1" if w.weights == "e2m1" else "fp8_e4m3") if w.dtype == "fp8" else "bf16",
+        # operands' storage type; accumulation is fp32 and the output bf16 (fp32 dW for the K-grouped gradient)
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,

@@ -82,6 +82,9 @@ typedef enum { MOEGG_B_KN = 0, MOEGG_B_NK = 1 } moegg_b_layout_t;
 #define MOEGG_FLAG_ROWS_OVERFLOW   0x2u  /* segments ran past rows_total / T; truncated */
 #define MOEGG_FLAG_COUNT_OVER_CAP  0x4u  /* a masked count > cap was read as cap      */
 #define MOEGG_FLAG_BAD_EXEMPLAR    0x8u  /* an exemplar named an invalid block_m      */
+#define MOEGG_FLAG_SCALE_GROUPS    0x10u /* K-grouped fp8: the histogram needs more scale
+                                            groups than the scale arrays hold; the
+                                            missing groups' scales read as 0           */
 
 /* block_m value for per-expert tile heights: every expert gets 256-row tiles,
  * and its remainder rows one tile of the smallest height in {64, 128, 256}
@@ -116,6 +119,28 @@ typedef struct {
     int32_t block_m;         /* tile height used                                              */
     uint32_t error_flags;    /* MOEGG_FLAG_* bits                                             */
 } moegg_stats_t;
+
+/*
+ * Ratios derived from one moegg_stats_t, for reports ("MoE GroupGEMM padding
+ * under expert skew": section "Calculate padded token columns" for the padding
+ * fraction (P - U) / P and the useful share U / P; section "Summarize skew
+ * without losing the histogram" for effective experts U^2 / sum m_e^2; section
+ * "Padding is not the whole cost model" for physical versus effective work).
+ * Each is computed from the exact integers in extended precision and rounded
+ * once to double.  A ratio whose denominator is 0 reads 0.
+ */
+typedef struct {
+    double effective_experts;             /* U^2 / sum_sq                             */
+    double padding_fraction[MOEGG_NUM_Q]; /* (P(q) - U) / P(q), q = 8 .. 256          */
+    double useful_share[MOEGG_NUM_Q];     /* U / P(q): the aggregate M-occupancy      */
+    double exec_padding_fraction;         /* (P_exec - U) / P_exec: rows the MFMAs ran */
+                                          /* without a valid row                       */
+    double physical_over_effective;       /* P_exec / U: physical / effective work     */
+} moegg_report_t;
+
+/* Fill *h_out from *h_stats.  Pure host function (no stream, no device).
+ * MOEGG_ERR_INVALID_ARG for NULL pointers or negative counts in *h_stats. */
+moegg_status_t moegg_stats_report(const moegg_stats_t* h_stats, moegg_report_t* h_out);
 
 /* One entry of the device tile list: expert, tile index within the expert,
  * first row of the tile in A/C, and valid rows (1..block_m). */
@@ -370,6 +395,39 @@ moegg_status_t moegg_grouped_gemm_masked(
 moegg_status_t moegg_grouped_gemm_k_grouped(
     const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G, int64_t T,
     int Mw, int Nw, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * K-grouped weight gradient on e4m3 operands with fp32 scales (DeepGEMM
+ * record, "Workarounds": the K-grouped MoE weight backward next to FP8 with
+ * per-group scaling).  The scale groups lie along the reduction (token) axis:
+ * one group is up to 128 consecutive rows of one expert's segment, counted
+ * from the segment's first row, so groups restart at every segment start and
+ * the last group of a segment may be short.  Groups are numbered across
+ * experts in order: expert e's first group is
+ *     goff[e] = sum_{j<e} ceil(t_j / 128)
+ * (over the counts as used: negative counts read as 0, segments truncated at
+ * T).  Each scale covers one column over one group.
+ *   X         e4m3 [T, Mw], dY e4m3 [T, Nw]: rows grouped by expert in expert
+ *             order, t_sizes[e] rows each (device int32 [G]).
+ *   X_scale   fp32 [scale_groups, Mw]; row g scales X's columns over group g.
+ *   dY_scale  fp32 [scale_groups, Nw]; likewise for dY.
+ *   dW        fp32 [G, Mw, Nw], overwritten:
+ *               dW[e, i, j] = sum over expert e's rows t of
+ *                   (X[t, i] * X_scale[g(t), i]) * (dY[t, j] * dY_scale[g(t), j])
+ *             with g(t) = goff[e] + (t - first row of e) / 128.  Each group's
+ *             fp32 partial sum of code products is multiplied by its two
+ *             scales and added to the fp32 accumulator.  t_e = 0 writes zeros.
+ *   scale_groups  rows of the scale arrays, at least sum_e ceil(t_e / 128)
+ *             (at most T / 128 + G).  A histogram that needs more sets
+ *             MOEGG_FLAG_SCALE_GROUPS; the missing groups' scales read as 0.
+ * Experts are started longest first.  Constraints: as for
+ * moegg_grouped_gemm_k_grouped; scale arrays 4-byte aligned, and
+ * scale_groups * max(Mw, Nw) * 4 < 2^31 (UNSUPPORTED otherwise).
+ */
+moegg_status_t moegg_grouped_gemm_k_grouped_fp8(
+    const void* X, const float* X_scale, const void* dY, const float* dY_scale, float* dW,
+    const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw, int64_t scale_groups,
+    void* ws, size_t ws_bytes, void* stream);
 
 /* Copy the stats of the last scheduled call on `ws` to the host.
  * Synchronizes `stream`. */

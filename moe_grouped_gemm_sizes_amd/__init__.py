@@ -12,8 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
-from fractions import Fraction
-from typing import List, Optional, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -25,6 +24,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1, FP8_E4M3_SCALE_KM = 0, 1, 2, 3, 4
 B_KN, B_NK = 0, 1
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP, FLAG_BAD_EXEMPLAR = 0x1, 0x2, 0x4, 0x8
+FLAG_SCALE_GROUPS = 0x10
 Q_VALUES = (8, 16, 32, 64, 128, 256)
 BLOCK_M_PER_EXPERT = -1          # per-expert tile heights (include/moegg.h)
 
@@ -39,6 +39,12 @@ class _Stats(ctypes.Structure):
     _fields_ = [("U", ctypes.c_int64), ("P_exec", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("active", ctypes.c_int64), ("sum_sq", ctypes.c_int64), ("capacity_rows", ctypes.c_int64),
                 ("P_at", ctypes.c_int64 * 6), ("block_m", ctypes.c_int32), ("error_flags", ctypes.c_uint32)]
+
+
+class _Report(ctypes.Structure):
+    _fields_ = [("effective_experts", ctypes.c_double), ("padding_fraction", ctypes.c_double * 6),
+                ("useful_share", ctypes.c_double * 6), ("exec_padding_fraction", ctypes.c_double),
+                ("physical_over_effective", ctypes.c_double)]
 
 
 class _Tile(ctypes.Structure):
@@ -59,13 +65,34 @@ class Stats:
     block_m: int
     error_flags: int
 
-    @property
-    def effective_experts(self) -> Fraction:
-        return Fraction(0) if self.sum_sq == 0 else Fraction(self.U * self.U, self.sum_sq)
+    def report(self) -> "Report":
+        """The derived ratios, computed by the library (moegg_stats_report)."""
+        st = _Stats(self.U, self.P_exec, self.tiles, self.active, self.sum_sq, self.capacity_rows,
+                    (ctypes.c_int64 * 6)(*[self.P_at[q] for q in Q_VALUES]), self.block_m, self.error_flags)
+        r = _Report()
+        _check(lib().moegg_stats_report(ctypes.byref(st), ctypes.byref(r)), "moegg_stats_report")
+        return Report(r.effective_experts, {q: r.padding_fraction[i] for i, q in enumerate(Q_VALUES)},
+                      {q: r.useful_share[i] for i, q in enumerate(Q_VALUES)}, r.exec_padding_fraction,
+                      r.physical_over_effective)
 
-    def padding_fraction(self, q: int) -> Fraction:
-        p = self.P_at[q]
-        return Fraction(0) if p == 0 else Fraction(p - self.U, p)
+    @property
+    def effective_experts(self) -> float:
+        return self.report().effective_experts
+
+    def padding_fraction(self, q: int) -> float:
+        return self.report().padding_fraction[q]
+
+
+@dataclass
+class Report:
+    """Ratios derived from Stats by the library: effective experts U^2 / sum m^2,
+    padding fraction (P(q) - U) / P(q), useful share U / P(q), the executed rows'
+    padding fraction and physical / effective work."""
+    effective_experts: float
+    padding_fraction: dict
+    useful_share: dict
+    exec_padding_fraction: float
+    physical_over_effective: float
 
 
 _lib = None
@@ -87,7 +114,10 @@ EXPORTS = {
     "moegg_grouped_gemm_masked": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _VP, _SZ, _VP]),
     "moegg_grouped_gemm_k_grouped": (_I32, [_VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_grouped_gemm_k_grouped_fp8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I64,
+                                                _VP, _SZ, _VP]),
     "moegg_stats_read": (_I32, [_VP, ctypes.POINTER(_Stats), _VP]),
+    "moegg_stats_report": (_I32, [ctypes.POINTER(_Stats), ctypes.POINTER(_Report)]),
     "moegg_tile_list_read": (_I32, [_VP, ctypes.POINTER(_Tile), _I64, ctypes.POINTER(_I64), _VP]),
 }
 
@@ -126,26 +156,98 @@ def _check(status: int, what: str):
         raise MoeggError(status, what)
 
 
-def _dtype(t: torch.Tensor, scale: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
-           scale_km: bool = False) -> int:
-    """Operand type code: fp8 with uint8 (E8M0) scales is MOEGG_FP8_E4M3_E8M0,
-    and with uint8 weights (packed E2M1 [G, N, K/2]) MOEGG_FP8_E4M3_FP4_E2M1.
-    scale_km: fp32 activation scales stored [K/128, rows]
-    (MOEGG_FP8_E4M3_SCALE_KM)."""
-    if t.dtype == torch.bfloat16:
-        code = BF16
-    elif t.dtype == torch.float8_e4m3fn:
-        if w is not None and w.dtype == torch.uint8:
-            code = FP8_E4M3_FP4_E2M1
-        else:
-            code = FP8_E4M3_E8M0 if scale is not None and scale.dtype == torch.uint8 else FP8_E4M3
-    else:
-        raise TypeError(f"bf16 or float8_e4m3fn operands expected, got {t.dtype}")
-    if scale_km:
-        if code != FP8_E4M3:
+_E4M3 = torch.float8_e4m3fn
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape: Sequence[Optional[int]], dtypes):
+    """ValueError unless `t` is a tensor of this shape (None matches any extent) and one of `dtypes`.
+    The library sees only pointers, so every extent it will index is checked here."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: tensor expected")
+    if t.dim() != len(shape) or any(x is not None and d != x for d, x in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if x is None else str(x) for x in shape) + "]"
+        raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+
+
+def _none(t, name: str, why: str):
+    if t is not None:
+        raise ValueError(f"{name}: must be None {why}")
+
+
+def _one_device(*ts):
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(str(d) for d in devs)}")
+
+
+def _ws(ws, G: int, max_rows: int):
+    _need(ws, "ws", [None], (torch.uint8,))
+    # the library checks the byte count too; this names the problem
+    need = workspace_bytes(G, max_rows)
+    if ws.numel() < need:
+        raise ValueError(f"ws: {ws.numel()} bytes, need {need} (workspace_bytes({G}, {max_rows}))")
+
+
+def _counts(t, name: str, G: Optional[int] = None):
+    _need(t, name, [G], (torch.int32,))
+    if t.numel() < 1:
+        raise ValueError(f"{name}: at least one expert expected")
+
+
+def _operands(rows: int, K: int, A, A_scale, B, B_scale, G: int, b_layout: int, scale_km: bool,
+              a_scale_rows_shape=None) -> Tuple[int, int]:
+    """Operand type code and N, after checking B, A_scale and B_scale against A's
+    dtype, `rows` rows of K and G experts.  a_scale_rows_shape: the shape of a
+    row-major fp32 activation-scale array ([rows, K/128] unless given).
+    Formats (include/moegg.h): bf16 x bf16, no scales; e4m3 x e4m3 with fp32
+    scales ([rows, K/128], or [K/128, rows] with scale_km) or E8M0 bytes
+    ([K/128, rows]); e4m3 x packed E2M1 [G, N, K/2] (uint8) with E8M0 bytes."""
+    if b_layout not in (B_KN, B_NK):
+        raise ValueError(f"b_layout: {b_layout}")
+    if A.dtype == torch.bfloat16:
+        _need(B, "B", [G, None, None], (torch.bfloat16,))
+        _none(A_scale, "A_scale", "for bf16 operands")
+        _none(B_scale, "B_scale", "for bf16 operands")
+        if scale_km:
             raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
-        return FP8_E4M3_SCALE_KM
-    return code
+        N = B.shape[2] if b_layout == B_KN else B.shape[1]
+        _need(B, "B", [G, K, N] if b_layout == B_KN else [G, N, K], (torch.bfloat16,))
+        return BF16, N
+    if A.dtype != _E4M3:
+        raise ValueError(f"A: bf16 or float8_e4m3fn expected, got {A.dtype}")
+    if K % 128:
+        raise ValueError(f"K = {K}: e4m3 operands need K % 128 == 0")
+    _need(B, "B", [G, None, None], (_E4M3, torch.uint8))
+    if A_scale is None or B_scale is None:
+        raise ValueError("e4m3 operands need A_scale and B_scale")
+    if B.dtype == torch.uint8:                              # packed E2M1 weights [G, N, K/2]
+        if b_layout != B_NK:
+            raise ValueError("packed E2M1 weights are stored [G, N, K/2]: b_layout must be B_NK")
+        N = B.shape[1]
+        _need(B, "B", [G, N, K // 2], (torch.uint8,))
+        _need(A_scale, "A_scale", [K // 128, rows], (torch.uint8,))
+        _need(B_scale, "B_scale", [G, K // 128, N // 128], (torch.uint8,))
+        if scale_km:
+            raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
+        return FP8_E4M3_FP4_E2M1, N
+    N = B.shape[2] if b_layout == B_KN else B.shape[1]
+    _need(B, "B", [G, K, N] if b_layout == B_KN else [G, N, K], (_E4M3,))
+    if N % 128:
+        raise ValueError(f"N = {N}: e4m3 operands need N % 128 == 0")
+    if A_scale.dtype == torch.uint8:                        # E8M0 exponent bytes
+        if scale_km:
+            raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
+        _need(A_scale, "A_scale", [K // 128, rows], (torch.uint8,))
+        _need(B_scale, "B_scale", [G, K // 128, N // 128], (torch.uint8,))
+        return FP8_E4M3_E8M0, N
+    if scale_km:
+        _need(A_scale, "A_scale", [K // 128, rows], (torch.float32,))
+    else:
+        _need(A_scale, "A_scale", a_scale_rows_shape or [rows, K // 128], (torch.float32,))
+    _need(B_scale, "B_scale", [G, K // 128, N // 128], (torch.float32,))
+    return (FP8_E4M3_SCALE_KM if scale_km else FP8_E4M3), N
 
 
 def workspace_bytes(G: int, max_rows: int) -> int:
@@ -161,6 +263,9 @@ def workspace(G: int, max_rows: int, device="cuda") -> torch.Tensor:
 
 def schedule(m_sizes: torch.Tensor, rows_total: int, ws: torch.Tensor, seg_align: int = 1, block_m: int = 0,
              N: int = 256, stream=None):
+    _counts(m_sizes, "m_sizes")
+    _ws(ws, m_sizes.numel(), rows_total)
+    _one_device(m_sizes, ws)
     _check(lib().moegg_schedule(_p(m_sizes), m_sizes.numel(), rows_total, seg_align, block_m, N, _p(ws),
                                 ws.numel(), _stream(stream)), "moegg_schedule")
 
@@ -184,6 +289,9 @@ def schedule_exemplar(m_sizes: torch.Tensor, rows_total: int, ws: torch.Tensor, 
     """moegg_schedule with the tile height matched to an exemplar on the device (see moegg.h)."""
     if exemplars.dtype != torch.int32 or exemplars.dim() != 2 or exemplars.shape[1] != EXEMPLAR_FIELDS:
         raise ValueError("exemplars: int32 [n, 10] expected")
+    _counts(m_sizes, "m_sizes")
+    _ws(ws, m_sizes.numel(), rows_total)
+    _one_device(m_sizes, ws, exemplars)
     _check(lib().moegg_schedule_exemplar(_p(m_sizes), m_sizes.numel(), rows_total, seg_align, N, _p(exemplars),
                                          exemplars.shape[0], hysteresis, _p(ws), ws.numel(), _stream(stream)),
            "moegg_schedule_exemplar")
@@ -213,10 +321,14 @@ def grouped_gemm_contiguous_scheduled(A, B, C, G: int, ws, A_scale=None, B_scale
                                       b_layout: int = B_KN, stream=None, scale_km: bool = False):
     """The contiguous GEMM from the tile list already in ws (see moegg.h).
     scale_km: A_scale is fp32 [K/128, rows] (MOEGG_FP8_E4M3_SCALE_KM)."""
-    K = A.shape[1]
-    N = B.shape[2] if b_layout == B_KN else B.shape[1]
+    _need(A, "A", [None, None], (torch.bfloat16, _E4M3))
+    rows, K = A.shape
+    code, N = _operands(rows, K, A, A_scale, B, B_scale, G, b_layout, scale_km)
+    _need(C, "C", [rows, N], (torch.bfloat16,))
+    _ws(ws, G, rows)
+    _one_device(A, A_scale, B, B_scale, C, ws)
     _check(lib().moegg_grouped_gemm_contiguous_scheduled(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, A.shape[0], K, N, _dtype(A, A_scale, B, scale_km), b_layout,
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), G, rows, K, N, code, b_layout,
         block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_contiguous_scheduled")
 
 
@@ -224,11 +336,17 @@ def grouped_gemm_contiguous(A, B, C, m_sizes, ws, A_scale=None, B_scale=None, se
                             block_m: int = 0, b_layout: int = B_KN, stream=None, scale_km: bool = False):
     """C[rows of expert e] = A[rows of expert e] @ B_e (see moegg.h).
     scale_km: A_scale is fp32 [K/128, rows] (MOEGG_FP8_E4M3_SCALE_KM)."""
-    K = A.shape[1]
-    N = B.shape[2] if b_layout == B_KN else B.shape[1]
+    _counts(m_sizes, "m_sizes")
+    G = m_sizes.numel()
+    _need(A, "A", [None, None], (torch.bfloat16, _E4M3))
+    rows, K = A.shape
+    code, N = _operands(rows, K, A, A_scale, B, B_scale, G, b_layout, scale_km)
+    _need(C, "C", [rows, N], (torch.bfloat16,))
+    _ws(ws, G, rows)
+    _one_device(A, A_scale, B, B_scale, C, m_sizes, ws)
     _check(lib().moegg_grouped_gemm_contiguous(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), m_sizes.numel(), A.shape[0], K, N,
-        seg_align, _dtype(A, A_scale, B, scale_km), b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), G, rows, K, N,
+        seg_align, code, b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
         "moegg_grouped_gemm_contiguous")
 
 
@@ -248,13 +366,22 @@ def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=N
     """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h).
     H bf16 [rows, I]; or, with H_scale (fp32 [rows, I/128]), H float8_e4m3fn codes.
     scale_km: A_scale fp32 [K/128, rows] in, H_scale [I/128, rows] out."""
-    K = A.shape[1]
-    I = W1.shape[1] // 2
-    if (H_scale is None) != (H.dtype == torch.bfloat16):
-        raise ValueError("H: bf16 without H_scale, float8_e4m3fn with it")
+    _need(A, "A", [None, None], (torch.bfloat16, _E4M3))
+    rows, K = A.shape
+    _need(W1, "W1", [G, None, None], (torch.bfloat16, _E4M3, torch.uint8))
+    code, N = _operands(rows, K, A, A_scale, W1, W1_scale, G, B_NK, scale_km)
+    if N % 256:
+        raise ValueError(f"W1: {N} interleaved gate/up rows, a multiple of 256 expected")
+    I = N // 2
+    if H_scale is None:
+        _need(H, "H", [rows, I], (torch.bfloat16,))
+    else:
+        _need(H, "H", [rows, I], (_E4M3,))
+        _need(H_scale, "H_scale", [I // 128, rows] if scale_km else [rows, I // 128], (torch.float32,))
+    _ws(ws, G, rows)
+    _one_device(A, A_scale, W1, W1_scale, H, H_scale, ws)
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
-        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, A.shape[0], K, I,
-        _dtype(A, A_scale, W1, scale_km),
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, rows, K, I, code,
         B_NK, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 
@@ -262,20 +389,52 @@ def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, 
                         stream=None, scale_km: bool = False):
     """C[e, r] = A[e, r] @ B_e for r < masked_m[e] (see moegg.h).
     scale_km: A_scale is fp32 [K/128, G * cap] (MOEGG_FP8_E4M3_SCALE_KM)."""
+    _need(A, "A", [None, None, None], (torch.bfloat16, _E4M3))
     G, cap, K = A.shape
-    N = B.shape[2] if b_layout == B_KN else B.shape[1]
+    _counts(masked_m, "masked_m", G)
+    code, N = _operands(G * cap, K, A, A_scale, B, B_scale, G, b_layout, scale_km,
+                        a_scale_rows_shape=[G, cap, K // 128])
+    _need(C, "C", [G, cap, N], (torch.bfloat16,))
+    if ws is not None:
+        _ws(ws, G, G * cap)
+    _one_device(A, A_scale, B, B_scale, C, masked_m, ws)
     _check(lib().moegg_grouped_gemm_masked(
-        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, _dtype(A, A_scale, B, scale_km), b_layout,
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(masked_m), G, cap, K, N, code, b_layout,
         _p(ws), 0 if ws is None else ws.numel(), _stream(stream)), "moegg_grouped_gemm_masked")
 
 
-def grouped_gemm_k_grouped(X, dY, dW, t_sizes, ws, stream=None):
-    """dW[e] = X_e^T @ dY_e over expert e's rows (see moegg.h)."""
+def k_scale_groups(t_sizes: Sequence[int]) -> int:
+    """Rows the K-grouped fp8 scale arrays need: sum over experts of ceil(t_e / 128)."""
+    return sum((max(int(t), 0) + 127) // 128 for t in t_sizes)
+
+
+def grouped_gemm_k_grouped(X, dY, dW, t_sizes, ws, X_scale=None, dY_scale=None, stream=None):
+    """dW[e] = X_e^T @ dY_e over expert e's rows (see moegg.h).  bf16 X and dY;
+    or e4m3 X and dY with fp32 scales X_scale [S, Mw], dY_scale [S, Nw], one row
+    per 128-row group of each expert's segment (k_scale_groups gives S)."""
+    _counts(t_sizes, "t_sizes")
+    G = t_sizes.numel()
+    _need(X, "X", [None, None], (torch.bfloat16, _E4M3))
     T, Mw = X.shape
+    _need(dY, "dY", [T, None], (X.dtype,))
     Nw = dY.shape[1]
-    _check(lib().moegg_grouped_gemm_k_grouped(
-        _p(X), _p(dY), _p(dW), _p(t_sizes), t_sizes.numel(), T, Mw, Nw, _p(ws), ws.numel(), _stream(stream)),
-        "moegg_grouped_gemm_k_grouped")
+    _need(dW, "dW", [G, Mw, Nw], (torch.float32,))
+    _ws(ws, G, 0)
+    if X.dtype == torch.bfloat16:
+        _none(X_scale, "X_scale", "for bf16 operands")
+        _none(dY_scale, "dY_scale", "for bf16 operands")
+        _one_device(X, dY, dW, t_sizes, ws)
+        _check(lib().moegg_grouped_gemm_k_grouped(
+            _p(X), _p(dY), _p(dW), _p(t_sizes), G, T, Mw, Nw, _p(ws), ws.numel(), _stream(stream)),
+            "moegg_grouped_gemm_k_grouped")
+        return
+    _need(X_scale, "X_scale", [None, Mw], (torch.float32,))
+    S = X_scale.shape[0]
+    _need(dY_scale, "dY_scale", [S, Nw], (torch.float32,))
+    _one_device(X, X_scale, dY, dY_scale, dW, t_sizes, ws)
+    _check(lib().moegg_grouped_gemm_k_grouped_fp8(
+        _p(X), _p(X_scale), _p(dY), _p(dY_scale), _p(dW), _p(t_sizes), G, T, Mw, Nw, S, _p(ws), ws.numel(),
+        _stream(stream)), "moegg_grouped_gemm_k_grouped_fp8")
 
 
 def stats_read(ws: torch.Tensor, stream=None) -> Stats:

@@ -257,23 +257,67 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     return hip_status(e, "masked GEMM launch");
 }
 
-moegg_status_t moegg_grouped_gemm_k_grouped(const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G,
-                                            int64_t T, int Mw, int Nw, void* ws, size_t ws_bytes, void* stream) {
+// Shared by the bf16 and fp8 K-grouped calls.  esz: operand bytes per element.
+static moegg_status_t k_grouped_call(const void* X, const float* X_scale, const void* dY, const float* dY_scale,
+                                     float* dW, const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw,
+                                     int64_t scale_groups, bool fp8, void* ws, size_t ws_bytes, void* stream) {
     // with T = 0 no row is read, so X and dY may be NULL (an empty tensor's pointer)
     if ((T > 0 && (!X || !dY)) || !dW || !t_sizes) return MOEGG_ERR_INVALID_ARG;
     if (G < 1 || G > kMaxExperts || T < 0 || Mw < 1 || Nw < 1) return MOEGG_ERR_INVALID_ARG;
     if (Mw % 256 != 0 || Nw % 256 != 0) return MOEGG_ERR_UNSUPPORTED;
     if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(dW, 16) || !aligned(t_sizes, 4))
         return MOEGG_ERR_INVALID_ARG;
-    if (T * Mw * 2 > kMaxBufferBytes || T * Nw * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    const int64_t esz = fp8 ? 1 : 2;
+    if (T * Mw * esz > kMaxBufferBytes || T * Nw * esz > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
+    if (fp8) {
+        if (scale_groups < 0 || (T > 0 && (scale_groups < 1 || !X_scale || !dY_scale))) return MOEGG_ERR_INVALID_ARG;
+        if (!aligned(X_scale, 4) || !aligned(dY_scale, 4)) return MOEGG_ERR_INVALID_ARG;
+        // scale offsets are 32-bit; the parked offset 2^31 must lie past both arrays
+        if (scale_groups * (int64_t)std::max(Mw, Nw) * 4 >= 0x80000000ll) return MOEGG_ERR_UNSUPPORTED;
+    }
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     const WsLayout L = ws_layout(G, 0);
     if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_sched_k_grouped(t_sizes, G, T, ws, s);
+    hipError_t e = launch_sched_k_grouped(t_sizes, G, T, fp8 ? scale_groups : 0, ws, s);
     if (e != hipSuccess) return hip_status(e, "K-grouped scheduler launch");
-    KGroupedArgs a{X, dY, dW, (const unsigned char*)ws, G, Mw, Nw};
-    return hip_status(launch_k_grouped(a, s), "K-grouped GEMM launch");
+    KGroupedArgs a{X, dY, dW, (const unsigned char*)ws, G, Mw, Nw, X_scale, dY_scale, scale_groups};
+    return hip_status(launch_k_grouped(a, fp8, s), "K-grouped GEMM launch");
+}
+
+moegg_status_t moegg_grouped_gemm_k_grouped(const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G,
+                                            int64_t T, int Mw, int Nw, void* ws, size_t ws_bytes, void* stream) {
+    return k_grouped_call(X, nullptr, dY, nullptr, dW, t_sizes, G, T, Mw, Nw, 0, false, ws, ws_bytes, stream);
+}
+
+moegg_status_t moegg_grouped_gemm_k_grouped_fp8(const void* X, const float* X_scale, const void* dY,
+                                                const float* dY_scale, float* dW, const int32_t* t_sizes, int G,
+                                                int64_t T, int Mw, int Nw, int64_t scale_groups, void* ws,
+                                                size_t ws_bytes, void* stream) {
+    return k_grouped_call(X, X_scale, dY, dY_scale, dW, t_sizes, G, T, Mw, Nw, scale_groups, true, ws, ws_bytes,
+                          stream);
+}
+
+moegg_status_t moegg_stats_report(const moegg_stats_t* h_stats, moegg_report_t* h_out) {
+    if (!h_stats || !h_out) return MOEGG_ERR_INVALID_ARG;
+    const moegg_stats_t& st = *h_stats;
+    if (st.U < 0 || st.sum_sq < 0 || st.P_exec < 0) return MOEGG_ERR_INVALID_ARG;
+    for (int i = 0; i < MOEGG_NUM_Q; ++i)
+        if (st.P_at[i] < 0) return MOEGG_ERR_INVALID_ARG;
+    // U <= 2^31, so U^2 and every difference below are exact in a 64-bit mantissa
+    auto ratio = [](long double num, long double den) -> double {
+        return den == 0 ? 0.0 : (double)(num / den);
+    };
+    const long double U = (long double)st.U;
+    h_out->effective_experts = ratio(U * U, (long double)st.sum_sq);
+    for (int i = 0; i < MOEGG_NUM_Q; ++i) {
+        const long double P = (long double)st.P_at[i];
+        h_out->padding_fraction[i] = ratio(P - U, P);
+        h_out->useful_share[i] = ratio(U, P);
+    }
+    h_out->exec_padding_fraction = ratio((long double)st.P_exec - U, (long double)st.P_exec);
+    h_out->physical_over_effective = ratio((long double)st.P_exec, U);
+    return MOEGG_OK;
 }
 
 moegg_status_t moegg_stats_read(const void* ws, moegg_stats_t* h_out, void* stream) {

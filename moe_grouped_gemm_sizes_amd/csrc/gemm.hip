@@ -80,13 +80,16 @@ __device__ __forceinline__ int swz_mn(int k) {
     return 0;
 }
 
-// Tile configuration of the K-grouped weight gradient (bf16 operands, both
+// Tile configuration of the K-grouped weight gradient (both operands
 // M/N-contiguous): 512 threads as WAVES_M x WAVES_N waves over a BM x BN tile
-// of dW; a stage holds KSTEP rows of the reduction axis of both operands.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// of dW; a stage holds KSTEP rows of the reduction axis of both operands (128
+// bytes of each column: 64 bf16 rows, or 128 e4m3 rows = one scale group), and
+// with fp8 the group's scales of the tile's columns, [X scales | dY scales].
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool FP8_ = false>
 struct KCfg {
-    static constexpr int ESZ = 2;
-    static constexpr int KSTEP = 64;                   // reduction rows per stage (128 bytes of bf16 K)
+    static constexpr bool FP8 = FP8_;
+    static constexpr int ESZ = FP8 ? 1 : 2;
+    static constexpr int KSTEP = 128 / ESZ;            // reduction rows per stage
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M * WAVES_N;
@@ -96,13 +99,15 @@ struct KCfg {
     static constexpr int MB = WTM / 16, NB = WTN / 16;             // 16x16 blocks per wave
     static constexpr int A_BYTES = BM * KSTEP * ESZ;
     static constexpr int B_BYTES = BN * KSTEP * ESZ;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int S_BYTES = FP8 ? (BM + BN) * 4 : 0;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int A_LOADS = A_BYTES / 16 / THREADS;         // 16-byte DMAs per thread per stage
     static constexpr int B_LOADS = B_BYTES / 16 / THREADS;
-    static constexpr int OPS = A_LOADS + B_LOADS;
+    static constexpr int OPS = A_LOADS + B_LOADS + (FP8 ? 1 : 0);  // fp8: one 4-byte scale DMA
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(!FP8 || BM + BN == THREADS, "one scale per thread per stage");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(OPS * (STAGES - 2) < 64, "vmcnt range");
 };
@@ -918,6 +923,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigA
 // dW[e, i, j] = sum over expert e's rows t of X[t, i] * dY[t, j].
 // Both operands are M/N-contiguous: the dY tile is the MFMA A operand (so each
 // lane holds 4 consecutive j), the X tile the MFMA B operand.
+// fp8 (C::FP8): X and dY are e4m3 codes; a stage is one 128-row scale group of
+// the expert's segment (groups restart at its first row), and each group's
+// partial sum is promoted as acc += (p * sy[g, j]) * sx[g, i], the group's
+// scales of the lane's four columns j and its row i.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -935,7 +944,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
     const int64_t t0 = offs[e];
     const int64_t te = max((int64_t)0, min(offs[e + 1], offs[p.G]) - t0);
     const int i0 = it * C::BM, j0 = jt * C::BN;
-    const uint32_t x_row = (uint32_t)p.Mw * 2, y_row = (uint32_t)p.Nw * 2;
+    const uint32_t x_row = (uint32_t)p.Mw * C::ESZ, y_row = (uint32_t)p.Nw * C::ESZ;
     auto rx = make_rsrc((const char*)p.X + t0 * x_row, (uint32_t)(te * x_row));
     auto ry = make_rsrc((const char*)p.dY + t0 * y_row, (uint32_t)(te * y_row));
     const int nks = (int)((te + C::KSTEP - 1) / C::KSTEP);
@@ -948,9 +957,32 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int r16 = lane & 15, g4 = (lane >> 4) * 4;
+    // fp8: the scale DMA of this wave, fixed per tile.  Waves below BM / 64 load
+    // the X scales of the tile's BM columns, the others the dY scales; scale row
+    // (group) groups[e] + ks, one 4-byte DMA per thread per stage.  A group past
+    // the scale arrays reads 0 (MOEGG_FLAG_SCALE_GROUPS).
+    __amdgpu_buffer_rsrc_t rss = make_rsrc(nullptr, 0);
+    uint32_t ss_voff = 0, ss_step = 0, ss_dst = 0;
+    if constexpr (C::FP8) {
+        const int64_t g0 = ((const int64_t*)(p.ws + L.groups))[e];
+        const bool xs = wave < C::BM / 64;
+        const uint32_t srow = xs ? (uint32_t)p.Mw * 4 : (uint32_t)p.Nw * 4;
+        rss = xs ? make_rsrc(p.X_scale, (uint32_t)(p.scale_groups * srow))
+                 : make_rsrc(p.dY_scale, (uint32_t)(p.scale_groups * srow));
+        const int col = (xs ? i0 : j0) + (xs ? wave : wave - C::BM / 64) * 64 + lane;
+        // a group index past the arrays is parked past the buffer and reads 0
+        ss_voff = g0 < p.scale_groups ? (uint32_t)(g0 * srow) + col * 4 : 0x80000000u;
+        ss_step = srow;
+        ss_dst = C::A_BYTES + C::B_BYTES + wave * 256;
+    }
     auto issue = [&](int ks, char* __restrict__ base) {
-        load_tile_mn<C, C::BM * 2>(rx, x_row, ks * C::KSTEP, i0 * 2, base, C::A_LOADS);
-        load_tile_mn<C, C::BN * 2>(ry, y_row, ks * C::KSTEP, j0 * 2, base + C::A_BYTES, C::B_LOADS);
+        load_tile_mn<C, C::BM * C::ESZ>(rx, x_row, ks * C::KSTEP, i0 * C::ESZ, base, C::A_LOADS);
+        load_tile_mn<C, C::BN * C::ESZ>(ry, y_row, ks * C::KSTEP, j0 * C::ESZ, base + C::A_BYTES, C::B_LOADS);
+        if constexpr (C::FP8) {
+            const uint32_t v = ss_voff >= 0x80000000u ? ss_voff : ss_voff + (uint32_t)ks * ss_step;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (MOEGG_LDS void*)(base + ss_dst), 4, v, 0, 0, 0);
+        }
     };
     // Same pipeline as the contiguous kernel: loads run STAGES - 1 steps ahead,
     // the DMAs of a step are issued after the first MFMA block of the step
@@ -966,24 +998,59 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
         // the read stage and the DMA stage of a step differ (see TileGemm::step)
         auto step = [&](const char* __restrict__ tx, char* __restrict__ wr, int next) {
             const char* ty = tx + C::A_BYTES;
-            // both K halves of this wave's X fragments, then the dY blocks one
-            // ahead of their MFMAs
-            v4i xa[2][C::MB];
+            if constexpr (C::FP8) {
+                // this wave's X fragments and row scales, then the dY blocks one ahead
+                // of their MFMAs; each block's partials promoted with the group's scales
+                const float* sx = (const float*)(ty + C::B_BYTES);
+                const float* sy = sx + C::BM;
+                v8i xa[C::MB];
+                float sxj[C::MB];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+                for (int j = 0; j < C::MB; ++j) {
+                    xa[j] = frag_mn_fp8<C::BM>(tx, wm * C::WTM + j * 16);
+                    sxj[j] = sx[wm * C::WTM + j * 16 + r16];
+                }
+                auto fragy = [&](int i) { return frag_mn_fp8<C::BN>(ty, wn * C::WTN + i * 16); };
+                v8i yb[2];
+                yb[0] = fragy(0);
+                v4f pp[C::MB];
+                static_for<0, C::NB>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (i + 1 < C::NB) yb[(i + 1) & 1] = fragy(i + 1);
+                    const v4f syi = *(const MOEGG_LDS v4f*)(sy + wn * C::WTN + i * 16 + g4);
 #pragma unroll
-                for (int j = 0; j < C::MB; ++j) xa[kk][j] = frag_mn_bf16<C::BM * 2>(tx, wm * C::WTM + j * 16, kk);
-            auto fragy = [&](int i, int kk) { return frag_mn_bf16<C::BN * 2>(ty, wn * C::WTN + i * 16, kk); };
-            v4i yb[2];
-            yb[0] = fragy(0, 0);
-            static_for<0, 2 * C::NB>([&](auto U) {
-                constexpr int u = decltype(U)::value, i = u >> 1, kk = u & 1;
-                if constexpr (u + 1 < 2 * C::NB) yb[(u + 1) & 1] = fragy((u + 1) >> 1, (u + 1) & 1);
+                    for (int j = 0; j < C::MB; ++j) pp[j] = mfma_fp8(yb[i & 1], xa[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (i == 0) issue(next, wr);
 #pragma unroll
-                for (int j = 0; j < C::MB; ++j) acc[i][j] = mfma_bf16(yb[u & 1], xa[kk][j], acc[i][j]);
-                if constexpr (u == 0) issue(next, wr);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                    for (int j = 0; j < C::MB; ++j) {
+                        const v4f q = pp[j] * syi;
+                        acc[i][j].x = __builtin_fmaf(q.x, sxj[j], acc[i][j].x);
+                        acc[i][j].y = __builtin_fmaf(q.y, sxj[j], acc[i][j].y);
+                        acc[i][j].z = __builtin_fmaf(q.z, sxj[j], acc[i][j].z);
+                        acc[i][j].w = __builtin_fmaf(q.w, sxj[j], acc[i][j].w);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else {
+                // both K halves of this wave's X fragments, then the dY blocks one
+                // ahead of their MFMAs
+                v4i xa[2][C::MB];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int j = 0; j < C::MB; ++j) xa[kk][j] = frag_mn_bf16<C::BM * 2>(tx, wm * C::WTM + j * 16, kk);
+                auto fragy = [&](int i, int kk) { return frag_mn_bf16<C::BN * 2>(ty, wn * C::WTN + i * 16, kk); };
+                v4i yb[2];
+                yb[0] = fragy(0, 0);
+                static_for<0, 2 * C::NB>([&](auto U) {
+                    constexpr int u = decltype(U)::value, i = u >> 1, kk = u & 1;
+                    if constexpr (u + 1 < 2 * C::NB) yb[(u + 1) & 1] = fragy((u + 1) >> 1, (u + 1) & 1);
+#pragma unroll
+                    for (int j = 0; j < C::MB; ++j) acc[i][j] = mfma_bf16(yb[u & 1], xa[kk][j], acc[i][j]);
+                    if constexpr (u == 0) issue(next, wr);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
         };
         for (int ks = 0; ks < nks; ++ks) {
             __builtin_amdgcn_s_setprio(1);
@@ -1007,7 +1074,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
     static_assert(C::WAVES_M % 2 == 0 && (C::BM / 2) * C::BN * 4 <= C::LDS_BYTES, "epilogue passes");
     constexpr int RB = C::BN * 4, CPR = RB / 16, HALF_ROWS = C::BM / 2;
     static_assert(CPR >= 16 && C::THREADS % CPR == 0, "row swizzle");
-    const int r16 = lane & 15, g = lane >> 4;
+    const int g = lane >> 4;
     float* out = p.dW + (size_t)e * p.Mw * p.Nw;
     const int c = tid % CPR;
 #pragma unroll
@@ -1041,6 +1108,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 // start-up and epilogue of the other, and a CU keeps twice the bytes in flight.
 template <bool FP8, bool E8 = false, bool W4 = false> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4, 2, E8, W4>;
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
+using KGroupedFp8Cfg = KCfg<256, 256, 4, 2, 2, true>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
 // attribute, not a stream operation).
@@ -1130,14 +1198,18 @@ hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool
                 : launch_one<MaskedCfg<false>, false, true>(a, grid, s);
 }
 
-hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s) {
-    using C = KGroupedCfg;
+template <class C>
+static hipError_t launch_k_grouped_t(const KGroupedArgs& a, hipStream_t s) {
     auto k = k_grouped_kernel<C>;
     hipError_t err = allow_lds<k_grouped_kernel<C>>(C::LDS_BYTES);
     if (err != hipSuccess) return err;
     const int64_t items = (int64_t)a.G * (a.Mw / C::BM) * (a.Nw / C::BN);
     hipLaunchKernelGGL(k, dim3(round256(items)), dim3(C::THREADS), C::LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, hipStream_t s) {
+    return fp8 ? launch_k_grouped_t<KGroupedFp8Cfg>(a, s) : launch_k_grouped_t<KGroupedCfg>(a, s);
 }
 
 }  // namespace moegg

@@ -28,6 +28,9 @@ struct KGroupedArgs {
     float* dW;
     const unsigned char* ws;
     int G, Mw, Nw;
+    const float* X_scale;          // fp8: [scale_groups, Mw] fp32, else NULL
+    const float* dY_scale;         // fp8: [scale_groups, Nw] fp32, else NULL
+    int64_t scale_groups;          // rows of the fp8 scale arrays
 };
 
 // mode 0: contiguous (tile list); mode 1: masked (stats only).
@@ -39,7 +42,9 @@ hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int se
 hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_total, int seg_align, int n_col_tiles,
                                  const moegg_exemplar_t* exemplars, int n_ex, int hysteresis, void* ws,
                                  int64_t max_tiles, hipStream_t stream);
-hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void* ws, hipStream_t stream);
+// scale_groups: rows of the K-grouped fp8 scale arrays (0 for bf16)
+hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, int64_t scale_groups, void* ws,
+                                  hipStream_t stream);
 // w4: packed E2M1 weights [G, N, K/2] (needs fp8 activations, E8M0 scales, !b_kn)
 hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,
                              int block_m, hipStream_t s);
@@ -50,7 +55,7 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
 hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int64_t rows_total, int block_m,
                                     hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
-hipError_t launch_k_grouped(const KGroupedArgs& a, hipStream_t s);
+hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, hipStream_t s);
 int masked_block_m();
 int masked_block_n();
 

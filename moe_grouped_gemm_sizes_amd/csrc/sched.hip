@@ -385,19 +385,24 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
 }
 
 // K-grouped weight gradient: row offsets of each expert's segment along the
-// reduction axis, and the expert order for launch (longest first, ties by
-// expert index).
+// reduction axis, the first 128-row scale group of each segment (fp8 operands:
+// groups restart at every segment start), and the expert order for launch
+// (longest first, ties by expert index).  The order comes from a bitonic sort
+// of 64-bit keys (count << 32 | (4095 - expert)) in LDS, descending.
+// scale_groups: rows of the fp8 scale arrays (0 for bf16); a histogram needing
+// more groups than that sets MOEGG_FLAG_SCALE_GROUPS.
 __global__ __launch_bounds__(kSchedThreads) void sched_k_grouped_kernel(
-    const int32_t* __restrict__ t_sizes, int G, int64_t T, unsigned char* __restrict__ ws) {
+    const int32_t* __restrict__ t_sizes, int G, int64_t T, int64_t scale_groups, unsigned char* __restrict__ ws) {
     __shared__ int64_t wave_buf[kWaves];
     __shared__ int64_t sums_buf[kWaves][3];
-    __shared__ int32_t m_s[kMaxExperts];
+    __shared__ int64_t key_s[kMaxExperts];
     __shared__ unsigned int flags_s;
     const int t = threadIdx.x;
     WsLayout L = ws_layout(G, 0);
     moegg_stats_t* st = (moegg_stats_t*)(ws + L.stats);
     Control* ctl = (Control*)(ws + L.control);
     int64_t* offsets = (int64_t*)(ws + L.offsets);
+    int64_t* groups = (int64_t*)(ws + L.groups);
     int32_t* order = (int32_t*)(ws + L.order);
     if (t == 0) flags_s = 0;
     unsigned int flags = 0;
@@ -408,40 +413,64 @@ __global__ __launch_bounds__(kSchedThreads) void sched_k_grouped_kernel(
     for (int e = e0; e < e1; ++e) {
         int32_t m = t_sizes[e];
         if (m < 0) { m = 0; flags |= MOEGG_FLAG_NEGATIVE_COUNT; }
-        m_s[e] = m;
+        key_s[e] = m;
         local += m;
     }
     int64_t tot;
     int64_t base = block_exclusive_scan(local, wave_buf, &tot);
+    // segments truncated at T: the counts that are actually used, then their groups
     int64_t v[3] = {0, 0, 0};
+    int64_t grp_local = 0;
 #pragma unroll 1
     for (int e = e0; e < e1; ++e) {
-        const int32_t m_in = m_s[e];
-        int32_t m = m_in;
+        const int64_t m_in = key_s[e];
+        int64_t m = m_in;
         int64_t room = T - base;
         if (room < 0) room = 0;
-        if ((int64_t)m > room) { m = (int32_t)room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
+        if (m > room) { m = room; flags |= MOEGG_FLAG_ROWS_OVERFLOW; }
         offsets[e] = base;
-        m_s[e] = m;
+        key_s[e] = m;
         v[0] += m;
         v[1] += m > 0;
-        v[2] += (int64_t)m * m;
+        v[2] += m * m;
+        grp_local += (m + 127) / 128;
         base += m_in;
     }
-    // offsets[e] are the layout's segment starts; segments truncated at T end there
-    if (t == 0) offsets[G] = tot < T ? tot : T;
-    if (flags) atomicOr(&flags_s, flags);
-    block_sums<3>(v, sums_buf);        // its barriers also publish m_s and flags_s
-    // rank = number of experts that come before e in longest-first order
-    for (int e = t; e < G; e += kSchedThreads) {
-        const int32_t me = m_s[e];
-        int r = 0;
-        for (int j = 0; j < G; ++j) {
-            const int32_t mj = m_s[j];
-            r += (mj > me) || (mj == me && j < e);
-        }
-        order[r] = e;
+    int64_t grp_tot;
+    int64_t gbase = block_exclusive_scan(grp_local, wave_buf, &grp_tot);   // barriers publish key_s too
+#pragma unroll 1
+    for (int e = e0; e < e1; ++e) {
+        groups[e] = gbase;
+        gbase += (key_s[e] + 127) / 128;
     }
+    // offsets[e] are the layout's segment starts; segments truncated at T end there
+    if (t == 0) {
+        offsets[G] = tot < T ? tot : T;
+        groups[G] = grp_tot;
+    }
+    if (scale_groups > 0 && grp_tot > scale_groups) flags |= MOEGG_FLAG_SCALE_GROUPS;
+    if (flags) atomicOr(&flags_s, flags);
+    block_sums<3>(v, sums_buf);        // its barriers also publish flags_s
+    // longest first: sort keys descending over the next power of two (padding -1 sorts last)
+    int P = 1;
+    while (P < G) P <<= 1;
+    for (int e = t; e < P; e += kSchedThreads)
+        key_s[e] = e < G ? (key_s[e] << 32) | (int64_t)(kMaxExperts - 1 - e) : -1;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < P; i += kSchedThreads) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const int64_t a = key_s[i], b = key_s[l];
+                    const bool down = (i & k) == 0;
+                    if (down ? a < b : a > b) { key_s[i] = b; key_s[l] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int r = t; r < G; r += kSchedThreads) order[r] = kMaxExperts - 1 - (int32_t)(key_s[r] & 0xFFFFFFFF);
     if (t == 0) {
         st->U = v[0];
         st->P_exec = v[0];
@@ -481,9 +510,10 @@ hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_tota
     return hipGetLastError();
 }
 
-hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, void* ws, hipStream_t stream) {
+hipError_t launch_sched_k_grouped(const int32_t* t_sizes, int G, int64_t T, int64_t scale_groups, void* ws,
+                                  hipStream_t stream) {
     hipLaunchKernelGGL(sched_k_grouped_kernel, dim3(1), dim3(kSchedThreads), 0, stream, t_sizes, G, T,
-                       (unsigned char*)ws);
+                       scale_groups, (unsigned char*)ws);
     return hipGetLastError();
 }
 

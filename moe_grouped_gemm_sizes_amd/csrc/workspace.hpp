@@ -4,6 +4,7 @@
 //   [128, 256)  control block: tile count, chosen block_m, candidate tile counts
 //   [256, ...)  int64 offsets[G + 1]  (segment starts / K-grouped row offsets)
 //   [...]       int32 order[G]        (K-grouped: experts, longest first)
+//   [...]       int64 groups[G + 1]   (K-grouped fp8: first 128-row scale group of each expert)
 //   [...]       moegg_tile_t tiles[max_tiles]
 // Every region starts on a 256-byte boundary.
 #pragma once
@@ -43,7 +44,7 @@ static_assert(sizeof(Control) == 128, "control block");
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-    size_t stats, control, offsets, order, tiles, total;
+    size_t stats, control, offsets, order, groups, tiles, total;
     int64_t max_tiles;
 };
 
@@ -53,7 +54,8 @@ __host__ __device__ inline WsLayout ws_layout(int G, int64_t max_rows) {
     L.control = 128;
     L.offsets = 256;
     L.order = L.offsets + align256(sizeof(int64_t) * (size_t)(G + 1));
-    L.tiles = L.order + align256(sizeof(int32_t) * (size_t)G);
+    L.groups = L.order + align256(sizeof(int32_t) * (size_t)G);
+    L.tiles = L.groups + align256(sizeof(int64_t) * (size_t)(G + 1));
     L.max_tiles = (max_rows + kMinBlockM - 1) / kMinBlockM + G;
     L.total = L.tiles + align256(sizeof(moegg_tile_t) * (size_t)L.max_tiles);
     return L;

@@ -61,6 +61,29 @@ int main(void) {
            MOEGG_ERR_UNSUPPORTED);
     EXPECT(moegg_grouped_gemm_k_grouped(NULL, NULL, fake, fake, 16, 1, 2048, 7168, fake, ws, NULL),
            MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, fake, fake, fake, fake, fake, 16, 100, 2048, 7168, 0, fake, ws,
+                                            NULL), MOEGG_ERR_INVALID_ARG);          /* rows but no scale groups */
+    EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, NULL, fake, fake, fake, fake, 16, 100, 2048, 7168, 16, fake, ws,
+                                            NULL), MOEGG_ERR_INVALID_ARG);          /* missing X scales */
+    EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, odd, fake, fake, fake, fake, 16, 100, 2048, 7168, 16, fake, ws,
+                                            NULL), MOEGG_ERR_INVALID_ARG);          /* misaligned scales */
+    EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, fake, fake, fake, fake, fake, 16, 100, 2048, 7168, 80000, fake,
+                                            ws, NULL), MOEGG_ERR_UNSUPPORTED);      /* scale offsets past 2^31 */
+    EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, fake, fake, fake, fake, fake, 16, 100, 2000, 7168, 16, fake, ws,
+                                            NULL), MOEGG_ERR_UNSUPPORTED);
+    {
+        moegg_stats_t st = {0};
+        moegg_report_t rep;
+        st.U = 132;
+        st.sum_sq = 2180;
+        st.P_exec = 192;
+        st.P_at[0] = 160;
+        EXPECT(moegg_stats_report(&st, &rep), MOEGG_OK);
+        if (rep.padding_fraction[0] != 28.0 / 160.0 || rep.padding_fraction[1] != 0.0) ++fails;
+        EXPECT(moegg_stats_report(NULL, &rep), MOEGG_ERR_INVALID_ARG);
+        st.U = -1;
+        EXPECT(moegg_stats_report(&st, &rep), MOEGG_ERR_INVALID_ARG);
+    }
     EXPECT(moegg_stats_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
     EXPECT(moegg_selection_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
     int64_t n = 0;

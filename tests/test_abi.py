@@ -12,7 +12,7 @@ import moe_grouped_gemm_sizes_amd as mg
 def declared_functions():
     src = open(mg.HEADER_PATH).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moegg_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moegg_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_exports():
@@ -210,10 +210,70 @@ def test_k_grouped_accepts_null_operands_only_without_rows():
 def test_scale_km_dtype_code():
     """scale_km selects the transposed-fp32-scale format, and only for e4m3 with fp32 scales."""
     import torch
-    a8, s = torch.empty(2, 128, dtype=torch.float8_e4m3fn), torch.empty(1, 2)
-    assert mg._dtype(a8, s, None, True) == mg.FP8_E4M3_SCALE_KM
-    assert mg._dtype(a8, s) == mg.FP8_E4M3
+    G, rows, K, N = 2, 4, 128, 256
+    a8 = torch.empty(rows, K, dtype=torch.float8_e4m3fn)
+    b8 = torch.empty(G, K, N, dtype=torch.float8_e4m3fn)
+    bs = torch.empty(G, 1, 2)
+    assert mg._operands(rows, K, a8, torch.empty(1, rows), b8, bs, G, mg.B_KN, True) == (mg.FP8_E4M3_SCALE_KM, N)
+    assert mg._operands(rows, K, a8, torch.empty(rows, 1), b8, bs, G, mg.B_KN, False) == (mg.FP8_E4M3, N)
     with pytest.raises(ValueError):
-        mg._dtype(torch.empty(2, 2, dtype=torch.bfloat16), None, None, True)
+        mg._operands(rows, K, torch.empty(rows, K, dtype=torch.bfloat16), None,
+                     torch.empty(G, K, N, dtype=torch.bfloat16), None, G, mg.B_KN, True)
     with pytest.raises(ValueError):
-        mg._dtype(a8, s.to(torch.uint8), None, True)
+        mg._operands(rows, K, a8, torch.empty(1, rows, dtype=torch.uint8), b8, bs.to(torch.uint8), G, mg.B_KN, True)
+
+
+def _stats_from_oracle(counts):
+    from oracle import accounting as acc
+    s = acc.summary(counts)
+    P = [s["P"][q] for q in mg.Q_VALUES]
+    return mg.Stats(s["U"], s["P"][16], s["tiles"][256], s["active"], s["sum_sq"], 0,
+                    dict(zip(mg.Q_VALUES, P)), 256, 0), s
+
+
+@pytest.mark.parametrize("counts", [
+    [17, 17, 17, 17, 16, 16, 16, 16], [100, 32, 0, 0, 0, 0, 0, 0], [0, 0, 0], [1],
+    [4, 1026, 1799, 166, 694, 753, 0, 16, 0, 240, 1119, 19, 6, 0, 46, 659,
+     10, 0, 112, 808, 181, 0, 28, 22, 90, 0, 176, 0, 37, 5, 10, 22],
+    [2 ** 31 - 1, 3],
+])
+def test_stats_report_matches_the_exact_ratios(counts):
+    """moegg_stats_report (host C) against the oracle's exact Fractions: each ratio
+    is the exact one rounded to double (within one ulp)."""
+    import math
+    from fractions import Fraction
+    from oracle import accounting as acc
+    st, s = _stats_from_oracle(counts)
+    r = st.report()
+
+    def close(got, exact):
+        return got == float(exact) or abs(got - float(exact)) <= math.ulp(float(exact))
+    assert close(r.effective_experts, s["effective_experts"])
+    for q in mg.Q_VALUES:
+        assert close(r.padding_fraction[q], acc.padding_fraction(counts, q))
+        P = s["P"][q]
+        assert close(r.useful_share[q], Fraction(s["U"], P) if P else 0)
+    P16 = s["P"][16]
+    assert close(r.exec_padding_fraction, Fraction(P16 - s["U"], P16) if P16 else 0)
+    assert close(r.physical_over_effective, Fraction(P16, s["U"]) if s["U"] else 0)
+
+
+def test_stats_report_worked_values():
+    """The padding page's printed values, through the library's report."""
+    st, _ = _stats_from_oracle([17, 17, 17, 17, 16, 16, 16, 16])
+    r = st.report()
+    assert [round(100 * r.padding_fraction[q], 2) for q in (8, 16, 32)] == [17.5, 31.25, 48.44]
+    assert round(100 * r.useful_share[8], 1) == 82.5 and round(100 * r.useful_share[32], 1) == 51.6
+    assert 7.9 < r.effective_experts < 8
+    st, _ = _stats_from_oracle([100, 32, 0, 0, 0, 0, 0, 0])
+    r = st.report()
+    assert round(100 * r.padding_fraction[8], 1) == 2.9 and round(100 * r.padding_fraction[32], 1) == 17.5
+    assert round(r.effective_experts, 2) == 1.58
+
+
+def test_stats_report_rejects_bad_input():
+    L = mg.lib()
+    assert L.moegg_stats_report(None, None) == mg.ERR_INVALID_ARG
+    st = mg._Stats()
+    st.U = -1
+    assert L.moegg_stats_report(ctypes.byref(st), ctypes.byref(mg._Report())) == mg.ERR_INVALID_ARG

@@ -1,0 +1,183 @@
+"""The Python binding checks every tensor it hands to the C ABI (CPU only).
+
+The library sees plain pointers, so a buffer that is too small or of the wrong
+type would make a kernel read or write outside it.  The binding therefore
+checks the shape, dtype and device of every operand against the sizes it
+passes, and raises ValueError naming the argument before any library call.
+Each case below builds a correct set of (CPU) tensors, changes one of them,
+and expects that argument's name in the error; the unchanged set gets as far as
+the device check.
+"""
+import pytest
+import torch
+
+import moe_grouped_gemm_sizes_amd as mg
+
+E4M3 = torch.float8_e4m3fn
+G, ROWS, K, N = 3, 40, 256, 512
+
+
+def t(*shape, dtype=torch.float32):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def contiguous_args(dtype="bf16", b_layout=mg.B_KN):
+    kw = dict(m_sizes=t(G, dtype=torch.int32), ws=t(mg.workspace_bytes(G, ROWS), dtype=torch.uint8),
+              C=t(ROWS, N, dtype=torch.bfloat16), b_layout=b_layout)
+    bshape = (G, K, N) if b_layout == mg.B_KN else (G, N, K)
+    if dtype == "bf16":
+        kw.update(A=t(ROWS, K, dtype=torch.bfloat16), B=t(*bshape, dtype=torch.bfloat16))
+    elif dtype == "fp8":
+        kw.update(A=t(ROWS, K, dtype=E4M3), B=t(*bshape, dtype=E4M3), A_scale=t(ROWS, K // 128),
+                  B_scale=t(G, K // 128, N // 128))
+    elif dtype == "fp8_km":
+        kw.update(A=t(ROWS, K, dtype=E4M3), B=t(*bshape, dtype=E4M3), A_scale=t(K // 128, ROWS),
+                  B_scale=t(G, K // 128, N // 128), scale_km=True)
+    elif dtype == "e8m0":
+        kw.update(A=t(ROWS, K, dtype=E4M3), B=t(*bshape, dtype=E4M3), A_scale=t(K // 128, ROWS, dtype=torch.uint8),
+                  B_scale=t(G, K // 128, N // 128, dtype=torch.uint8))
+    elif dtype == "fp4":
+        kw.update(A=t(ROWS, K, dtype=E4M3), B=t(G, N, K // 2, dtype=torch.uint8),
+                  A_scale=t(K // 128, ROWS, dtype=torch.uint8), B_scale=t(G, K // 128, N // 128, dtype=torch.uint8),
+                  b_layout=mg.B_NK)
+    return kw
+
+
+def call_contiguous(kw):
+    mg.grouped_gemm_contiguous(**kw)
+
+
+@pytest.mark.parametrize("dtype,layout", [("bf16", mg.B_KN), ("bf16", mg.B_NK), ("fp8", mg.B_NK),
+                                          ("fp8_km", mg.B_KN), ("e8m0", mg.B_NK), ("fp4", mg.B_NK)])
+def test_contiguous_correct_arguments_reach_the_device_check(dtype, layout):
+    with pytest.raises(ValueError, match="device tensor expected"):
+        call_contiguous(contiguous_args(dtype, layout))
+
+
+@pytest.mark.parametrize("dtype,change,name", [
+    ("bf16", dict(C=t(ROWS - 1, N, dtype=torch.bfloat16)), "C: shape"),
+    ("bf16", dict(C=t(ROWS, N, dtype=torch.float32)), "C: dtype"),
+    ("bf16", dict(B=t(G + 1, K, N, dtype=torch.bfloat16)), "B: shape"),
+    ("bf16", dict(B=t(G, K + 64, N, dtype=torch.bfloat16)), "B: shape"),
+    ("bf16", dict(B=t(G, K, N, dtype=E4M3)), "B: dtype"),
+    ("bf16", dict(A_scale=t(ROWS, 2)), "A_scale: must be None"),
+    ("bf16", dict(m_sizes=t(G, dtype=torch.int64)), "m_sizes: dtype"),
+    ("bf16", dict(m_sizes=t(G, 1, dtype=torch.int32)), "m_sizes: shape"),
+    ("bf16", dict(ws=t(64, dtype=torch.uint8)), "ws: 64 bytes"),
+    ("bf16", dict(A=t(ROWS, K)), "A: dtype"),
+    ("fp8", dict(A_scale=t(ROWS, K // 128 + 1)), "A_scale: shape"),
+    ("fp8", dict(A_scale=t(K // 128, ROWS)), "A_scale: shape"),
+    ("fp8", dict(B_scale=t(G, K // 128, N // 256)), "B_scale: shape"),
+    ("fp8", dict(B_scale=None), "need A_scale and B_scale"),
+    ("fp8", dict(B=t(G, K, N, dtype=torch.bfloat16)), "B: dtype"),
+    ("fp8_km", dict(A_scale=t(ROWS, K // 128)), "A_scale: shape"),
+    ("e8m0", dict(B_scale=t(G, K // 128, N // 128)), "B_scale: dtype"),
+    ("e8m0", dict(A_scale=t(ROWS, K // 128, dtype=torch.uint8)), "A_scale: shape"),
+    ("fp4", dict(B=t(G, N, K, dtype=torch.uint8)), "B: shape"),
+    ("fp4", dict(b_layout=mg.B_KN), "b_layout must be B_NK"),
+])
+def test_contiguous_mismatch_raises(dtype, change, name):
+    kw = contiguous_args(dtype, mg.B_KN if dtype in ("bf16", "fp8_km") else mg.B_NK)
+    kw.update(change)
+    with pytest.raises(ValueError, match=name):
+        call_contiguous(kw)
+
+
+def test_contiguous_scheduled_checks_against_G():
+    kw = contiguous_args("bf16")
+    kw.pop("m_sizes")
+    with pytest.raises(ValueError, match="device tensor expected"):
+        mg.grouped_gemm_contiguous_scheduled(G=G, **kw)
+    with pytest.raises(ValueError, match="B: shape"):
+        mg.grouped_gemm_contiguous_scheduled(G=G + 1, **kw)
+
+
+def masked_args(dtype="bf16"):
+    cap = 16
+    kw = dict(masked_m=t(G, dtype=torch.int32), C=t(G, cap, N, dtype=torch.bfloat16),
+              ws=t(mg.workspace_bytes(G, G * cap), dtype=torch.uint8), b_layout=mg.B_KN)
+    if dtype == "bf16":
+        kw.update(A=t(G, cap, K, dtype=torch.bfloat16), B=t(G, K, N, dtype=torch.bfloat16))
+    else:
+        kw.update(A=t(G, cap, K, dtype=E4M3), B=t(G, K, N, dtype=E4M3), A_scale=t(G, cap, K // 128),
+                  B_scale=t(G, K // 128, N // 128))
+    return kw
+
+
+@pytest.mark.parametrize("dtype,change,name", [
+    ("bf16", dict(C=t(G, 15, N, dtype=torch.bfloat16)), "C: shape"),
+    ("bf16", dict(masked_m=t(G + 1, dtype=torch.int32)), "masked_m: shape"),
+    ("bf16", dict(B=t(G, K, N + 128, dtype=torch.bfloat16)), "C: shape"),
+    ("bf16", dict(ws=t(8, dtype=torch.uint8)), "ws: 8 bytes"),
+    ("fp8", dict(A_scale=t(G * 16, K // 128)), "A_scale: shape"),
+    ("fp8", dict(B_scale=t(G, K // 128, 1)), "B_scale: shape"),
+])
+def test_masked_mismatch_raises(dtype, change, name):
+    kw = masked_args(dtype)
+    with pytest.raises(ValueError, match="device tensor expected"):
+        mg.grouped_gemm_masked(**kw)
+    kw.update(change)
+    with pytest.raises(ValueError, match=name):
+        mg.grouped_gemm_masked(**kw)
+
+
+def swiglu_args():
+    I = 256
+    return dict(A=t(ROWS, K, dtype=E4M3), W1=t(G, 2 * I, K, dtype=E4M3), H=t(ROWS, I, dtype=E4M3),
+                G=G, ws=t(mg.workspace_bytes(G, ROWS), dtype=torch.uint8), A_scale=t(ROWS, K // 128),
+                W1_scale=t(G, K // 128, 2 * I // 128), H_scale=t(ROWS, I // 128))
+
+
+@pytest.mark.parametrize("change,name", [
+    (dict(H=t(ROWS, 128, dtype=E4M3)), "H: shape"),
+    (dict(H_scale=t(2, ROWS)), "H_scale: shape"),
+    (dict(H=t(ROWS, 256, dtype=torch.bfloat16)), "H: dtype"),
+    (dict(W1=t(G, 384, K, dtype=E4M3), W1_scale=t(G, K // 128, 3)), "multiple of 256"),
+])
+def test_swiglu_mismatch_raises(change, name):
+    kw = swiglu_args()
+    with pytest.raises(ValueError, match="device tensor expected"):
+        mg.grouped_gemm_swiglu_scheduled(**kw)
+    kw.update(change)
+    with pytest.raises(ValueError, match=name):
+        mg.grouped_gemm_swiglu_scheduled(**kw)
+
+
+def k_grouped_args(fp8=False):
+    T, Mw, Nw = 300, 256, 512
+    d = E4M3 if fp8 else torch.bfloat16
+    kw = dict(X=t(T, Mw, dtype=d), dY=t(T, Nw, dtype=d), dW=t(G, Mw, Nw), t_sizes=t(G, dtype=torch.int32),
+              ws=t(mg.workspace_bytes(G, 0), dtype=torch.uint8))
+    if fp8:
+        kw.update(X_scale=t(6, Mw), dY_scale=t(6, Nw))
+    return kw
+
+
+@pytest.mark.parametrize("fp8,change,name", [
+    (False, dict(dW=t(G, 256, 256)), "dW: shape"),
+    (False, dict(dW=t(G, 256, 512, dtype=torch.bfloat16)), "dW: dtype"),
+    (False, dict(dY=t(299, 512, dtype=torch.bfloat16)), "dY: shape"),
+    (False, dict(X_scale=t(6, 256)), "X_scale: must be None"),
+    (True, dict(dY=t(300, 512, dtype=torch.bfloat16)), "dY: dtype"),
+    (True, dict(X_scale=t(6, 512)), "X_scale: shape"),
+    (True, dict(dY_scale=t(5, 512)), "dY_scale: shape"),
+    (True, dict(X_scale=None), "X_scale: tensor expected"),
+])
+def test_k_grouped_mismatch_raises(fp8, change, name):
+    kw = k_grouped_args(fp8)
+    with pytest.raises(ValueError, match="device tensor expected"):
+        mg.grouped_gemm_k_grouped(**kw)
+    kw.update(change)
+    with pytest.raises(ValueError, match=name):
+        mg.grouped_gemm_k_grouped(**kw)
+
+
+def test_schedule_checks_counts_and_workspace():
+    with pytest.raises(ValueError, match="m_sizes: dtype"):
+        mg.schedule(t(4, dtype=torch.int64), 100, t(4096, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="ws: 16 bytes"):
+        mg.schedule(t(4, dtype=torch.int32), 100, t(16, dtype=torch.uint8))
+
+
+def test_k_scale_groups():
+    assert mg.k_scale_groups([0, 1, 128, 129, 256, -5]) == 0 + 1 + 1 + 2 + 2 + 0

@@ -167,9 +167,7 @@ def test_contiguous_small_full_compare(case, block_m, b_layout):
     ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
     valid = ~np.isnan(ref[:, 0])
     got = P.rows_as_float(C, rows)
-    assert np.isfinite(got[valid]).all()
-    err = og.rel_frobenius(got[valid], ref[valid])
-    assert err <= P.TOL[dtype], err
+    P.check_gemm(got[valid], ref[valid], dtype, what=f"small {name} block_m={block_m} layout={b_layout}")
     assert P.untouched_rows_ok(C, counts, align)
 
 
@@ -211,7 +209,7 @@ def test_contiguous_maximum_expert_count():
     assert mg.tile_list_read(ws, st.tiles + 4) == acc.tile_list(counts, 64, 1)
     rows = list(range(w.rows_total))
     ref = P.oracle_contiguous_rows(w, {k: P.cpu(v) for k, v in inp.items()}, rows)
-    assert og.rel_frobenius(P.rows_as_float(C, rows), ref) <= P.TOL["bf16"]
+    P.check_gemm(P.rows_as_float(C, rows), ref, "bf16", what="G=4096")
 
 
 def test_contiguous_e8m0_widest_output():
@@ -226,7 +224,7 @@ def test_contiguous_e8m0_widest_output():
     rows = P.sample_rows_contiguous(counts, 1, 64, extra=16, seed=3)
     cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
     ref = P.oracle_contiguous_rows(w, cpu, rows)
-    assert og.rel_frobenius(P.rows_as_float(C, rows), ref) <= P.TOL["fp8"]
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what="e8m0 N=32768")
 
 
 def test_contiguous_deterministic_and_empty():
@@ -251,6 +249,20 @@ def test_contiguous_deterministic_and_empty():
 # ----------------------------------------------------------------- contiguous, full-size configs
 
 
+def full_size_rows(w):
+    """Rows compared at full size: one per 16-row block of every expert segment
+    (every MFMA row block of every tile at every height), whole rows."""
+    return list(range(w.rows_total)) if w.rows_total <= 512 else P.rows_every_block(w.counts, w.seg_align, w.seed)
+
+
+def full_size_ref(w, inp, rows, tag=""):
+    """The oracle's rows for a full-size seeded workload, computed once per session."""
+    def compute():
+        cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+        return P.oracle_contiguous_rows(w, cpu, rows)
+    return P.cached((w.name, w.scales, w.weights, tag, tuple(rows)), compute)
+
+
 @pytest.mark.parametrize("n", [1, 2, 3])
 @pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
 def test_contiguous_config_full_size(n, b_layout):
@@ -263,16 +275,10 @@ def test_contiguous_config_full_size(n, b_layout):
     assert st.block_m == P.choice_rule(w.counts, w.N // 256)
     if n == 1:
         assert [st.P_at[q] for q in (8, 16, 32)] == [160, 192, 256]
-    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256 if st.block_m < 0 else st.block_m, extra=48, seed=n) \
-        if n > 1 else list(range(w.rows_total))
-    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    rows = full_size_rows(w)
+    ref = full_size_ref(w, inp, rows)
     del inp
-    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"config {n}: block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL[w.dtype], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, w.dtype, what=f"config {n} block_m={st.block_m} layout={b_layout}")
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
@@ -294,13 +300,7 @@ def test_contiguous_every_tile_height_long_k(dtype, b_layout, block_m):
     del inp
     ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
     got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    # no element may be off by more than a few bf16 ulps of the row scale
-    worst = float(np.max(np.abs(got - ref) / (np.abs(ref).max(axis=1, keepdims=True) + 1e-30)))
-    print(f"long K {dtype} layout={b_layout} block_m={block_m}: rel_frobenius={err:.3e} worst={worst:.3e}", flush=True)
-    assert err <= P.TOL[dtype], err
-    assert worst <= 0.05, worst
+    P.check_gemm(got, ref, dtype, what=f"long K {dtype} layout={b_layout} block_m={block_m}")
 
 
 @pytest.mark.parametrize("n", [2, 3])
@@ -314,15 +314,10 @@ def test_contiguous_per_expert_full_size(n, b_layout):
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts, mg.BLOCK_M_PER_EXPERT)
     assert mg.tile_list_read(ws, st.tiles) == acc.tile_list_per_expert(w.counts, w.seg_align)
-    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 64, extra=48, seed=n)
-    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    rows = full_size_rows(w)
+    ref = full_size_ref(w, inp, rows)
     del inp
-    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"per-expert config {n}: rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL[w.dtype], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, w.dtype, what=f"per-expert config {n} layout={b_layout}")
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
@@ -343,9 +338,7 @@ def check_masked(w, inp, C, counts):
                     A_scale=inp_cpu.get("A_scale"), B_scale=inp_cpu.get("B_scale"))
     idx = torch.tensor([e * w.cap + r for e, r in reqs], device="cuda")
     got = C.reshape(w.G * w.cap, -1)[idx].float().cpu().double().numpy()
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    assert err <= P.TOL[w.dtype], err
+    P.check_gemm(got, ref, w.dtype, what=f"masked G={w.G} cap={w.cap} K={w.K} N={w.N}")
     # rows past masked_m keep the sentinel
     inval = torch.tensor([e * w.cap + r for e in range(w.G) for r in range(w.cap)
                           if r >= min(max(counts[e], 0), w.cap)], device="cuda")
@@ -388,8 +381,7 @@ def check_masked_fp4(w, inp, C, counts, pairs=None):
     ref = fp4.masked_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, pairs)
     idx = torch.tensor([e * w.cap + r for e, r in pairs], device="cuda")
     got = C.reshape(w.G * w.cap, -1)[idx].float().cpu().double().numpy()
-    assert np.isfinite(got).all()
-    assert og.rel_frobenius(got, ref) <= P.TOL["fp8"]
+    P.check_gemm(got, ref, "fp8", what=f"masked fp8 x fp4 G={w.G} cap={w.cap}")
 
 
 @pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK])
@@ -433,6 +425,52 @@ def test_masked_config_full_size(b_layout):
     mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, b_layout=b_layout)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
+    check_masked(w, inp, C, w.counts)
+
+
+def test_masked_counts_out_of_range_are_clamped():
+    """masked_m above cap reads as cap and below 0 as 0: the stats carry both
+    flags and the clamped accounting, the kernel writes exactly the clamped
+    rows (every row of an over-cap expert, none of a negative one), and nothing
+    is read or written past the capacity buffer."""
+    counts = [300, -5, 40, 256, 0, 257, -1, 1]
+    cap = 256
+    clamped = [min(max(c, 0), cap) for c in counts]
+    announce("masked clamp", counts, "cap", cap)
+    w, inp = masked_case(counts, cap, 256, 256, "bf16")
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws)
+    torch.cuda.synchronize()
+    st = mg.stats_read(ws)
+    assert st.error_flags == mg.FLAG_NEGATIVE_COUNT | mg.FLAG_COUNT_OVER_CAP, hex(st.error_flags)
+    ref = acc.summary(clamped)
+    assert (st.U, st.active, st.sum_sq, st.P_at) == (ref["U"], ref["active"], ref["sum_sq"], ref["P"])
+    assert st.capacity_rows == w.G * cap - ref["U"]
+    check_masked(w, inp, C, counts)          # valid rows = the clamped counts; the rest keep the sentinel
+    # without a workspace (no stats) the kernel clamps the same way
+    C2 = P.sentinel_like((w.G, w.cap, w.N))
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C2, inp["counts"])
+    torch.cuda.synchronize()
+    assert torch.equal(C2.view(torch.int16), C.view(torch.int16))
+
+
+@pytest.mark.parametrize("scale_km", [False, True])
+def test_masked_fp8_fp32_scales_full_size(scale_km):
+    """The masked decode workload's shape (32 experts, cap 256, K 2048, N 7168,
+    Poisson(24) counts) with e4m3 operands and fp32 scales, activation scales
+    [G, cap, K/128] or transposed [K/128, G * cap]: every valid row."""
+    w0 = wl.workload(4)
+    announce("masked fp8 fp32 scales full size", "scale_km", scale_km)
+    w = wl.Workload("masked fp8", "masked", "fp8", w0.counts, K=w0.K, N=w0.N, cap=w0.cap, seed=w0.seed)
+    inp = wl.materialize(w, "cuda")
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    a_scale = inp["A_scale"].reshape(w.G * w.cap, -1).t().contiguous() if scale_km else inp["A_scale"]
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws, a_scale, inp["B_scale"], mg.B_KN,
+                           scale_km=scale_km)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), w.counts)
     check_masked(w, inp, C, w.counts)
 
 
@@ -511,10 +549,7 @@ def test_contiguous_graph_replay(dtype):
         rows = [r for e, s0 in enumerate(acc.segment_offsets(counts, 1)[:-1]) for r in range(s0, s0 + counts[e])]
         if rows:
             ref = P.oracle_contiguous_rows(wc, cpu, rows)
-            got = P.rows_as_float(C, rows)
-            assert np.isfinite(got).all()
-            err = og.rel_frobenius(got, ref)
-            assert err <= P.TOL[dtype], (counts, err)
+            P.check_gemm(P.rows_as_float(C, rows), ref, dtype, what=f"graph replay {counts}")
         assert P.untouched_rows_ok(C, counts, 1), counts
 
 
@@ -547,11 +582,7 @@ def test_contiguous_fp8_e8m0(block_m, b_layout):
     rows = list(range(w.rows_total))
     cpu = {k: P.cpu(v) for k, v in inp.items()}
     ref = P.oracle_contiguous_rows(w, cpu, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"e8m0 block_m={st.block_m} layout={b_layout} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL["fp8"], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what=f"e8m0 block_m={st.block_m} layout={b_layout}")
 
 
 def test_contiguous_fp8_e8m0_full_size():
@@ -563,15 +594,10 @@ def test_contiguous_fp8_e8m0_full_size():
     C, ws = run_contiguous_e8m0(w, inp, 0, mg.B_NK)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
-    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256, extra=48, seed=13)
-    inp_cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
+    rows = full_size_rows(w)
+    ref = full_size_ref(w, inp, rows)
     del inp
-    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"e8m0 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL["fp8"], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what=f"e8m0 full size block_m={st.block_m}")
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
@@ -597,18 +623,15 @@ def test_contiguous_fp8_fp4(block_m):
     w = wl.Workload("f4", "contiguous", "fp8", counts, K=512, N=512, values="normal", seed=9, scales="e8m0",
                     weights="e2m1")
     inp = wl.materialize(w, "cuda")
-    assert mg._dtype(inp["A"], inp["A_scale_e8m0"], inp["B"]) == mg.FP8_E4M3_FP4_E2M1
+    assert mg._operands(w.rows_total, w.K, inp["A"], inp["A_scale_e8m0"], inp["B"], inp["B_scale_e8m0"], w.G,
+                        mg.B_NK, False)[0] == mg.FP8_E4M3_FP4_E2M1
     C, ws = run_contiguous_fp4(w, inp, block_m)
     st = mg.stats_read(ws)
     P.check_stats(st, counts)
     rows = list(range(w.rows_total))
     cpu = {k: P.cpu(v) for k, v in inp.items()}
     ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"fp4 block_m={st.block_m} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL["fp8"], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what=f"fp4 block_m={st.block_m}")
     assert P.untouched_rows_ok(C, counts, 1)
 
 
@@ -649,9 +672,7 @@ def test_contiguous_fp8_fp4_aligned_segments():
     rows = [r for e, s0 in enumerate(acc.segment_offsets(counts, 64)[:-1]) for r in range(s0, s0 + counts[e])]
     cpu = {k: P.cpu(v) for k, v in inp.items()}
     ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], counts, rows, seg_align=64)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    assert og.rel_frobenius(got, ref) <= P.TOL["fp8"]
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what="fp4 aligned 64")
     assert P.untouched_rows_ok(C, counts, 64)
 
 
@@ -665,15 +686,11 @@ def test_contiguous_fp8_fp4_full_size():
     C, ws = run_contiguous_fp4(w, inp, 0)
     st = mg.stats_read(ws)
     P.check_stats(st, w.counts)
-    rows = P.sample_rows_contiguous(w.counts, w.seg_align, 256, extra=48, seed=13)
+    rows = full_size_rows(w)
     cpu = {k: P.cpu(v) for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}
     del inp
     ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], w.counts, rows)
-    got = P.rows_as_float(C, rows)
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    print(f"fp4 full size block_m={st.block_m} rows={len(rows)} rel_frobenius={err:.3e}", flush=True)
-    assert err <= P.TOL["fp8"], err
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what=f"fp4 full size block_m={st.block_m}")
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
 
 
@@ -818,8 +835,7 @@ def test_exemplar_selection_in_a_graph():
         prev = idx
         rows = P.sample_rows_contiguous(counts, 1, 64, extra=16, seed=5)
         ref = og.contiguous(cpu["A"], cpu["B"], counts, rows)
-        err = og.rel_frobenius(P.rows_as_float(C, rows), ref)
-        assert err <= P.TOL["bf16"], err
+        P.check_gemm(P.rows_as_float(C, rows), ref, "bf16", what=f"exemplar graph {counts}")
 
 
 # ----------------------------------------------------------------- expert MLP: L1 -> SwiGLU -> L2
@@ -859,11 +875,10 @@ def test_swiglu_and_down_projection(dtype, block_m):
     h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
     y = omlp.down_rows(h, cpu["W2"], counts, rows)
     got_h, got_y = P.rows_as_float(H, rows), P.rows_as_float(Y, rows)
-    assert np.isfinite(got_h).all() and np.isfinite(got_y).all()
-    eh, ey = og.rel_frobenius(got_h, h), og.rel_frobenius(got_y, y)
-    print(f"mlp {dtype} block_m={block_m} h {eh:.3e} y {ey:.3e}", flush=True)
-    assert eh <= P.TOL[dtype], eh
+    P.check_gemm(got_h, h, dtype, what=f"mlp {dtype} block_m={block_m} h")
+    ey = og.rel_frobenius(got_y, y)
     assert ey <= (TOL_MLP_BF16 if dtype == "bf16" else P.TOL["fp8"]), ey
+    assert P.elementwise_ratio(got_y, y, "chain") <= 1.0
 
 
 def dequant_h(H, Hs):
@@ -925,8 +940,7 @@ def test_swiglu_e4m3_h_and_fp8_down_projection(block_m):
     qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
     y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
                       A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
-    ey = og.rel_frobenius(P.rows_as_float(Y, rows), y)
-    assert ey <= P.TOL["fp8"], ey
+    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain", what=f"mlp fp8 H block_m={block_m} y")
 
 
 def run_mlp_fp4(counts, K, I, N2, block_m, seed):
@@ -963,7 +977,7 @@ def test_swiglu_fp4_weights(block_m):
     qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
     y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
                       A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
-    assert og.rel_frobenius(P.rows_as_float(Y, rows), y) <= P.TOL["fp8"]
+    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain", what=f"mlp fp4 L1 block_m={block_m} y")
 
 
 def test_expert_mlp_fp4_full_size():
@@ -987,7 +1001,7 @@ def test_expert_mlp_fp4_full_size():
         w2e = cpu["W2"][e].float().double().numpy() * np.repeat(
             np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0), 128, 1).T
         y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
-    assert og.rel_frobenius(got_y, y) <= P.TOL["fp8"]
+    P.check_gemm(got_y, y, "fp8", bound="chain", what="mlp fp4 L1 full size y")
 
 
 def test_expert_mlp_fp8_full_size():
@@ -1023,8 +1037,7 @@ def test_expert_mlp_fp8_full_size():
         w2e = w2[e].float().double().numpy() * np.repeat(np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0),
                                                           128, 1).T
         y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
-    ey = og.rel_frobenius(got_y, y)
-    assert ey <= P.TOL["fp8"], ey
+    P.check_gemm(got_y, y, "fp8", bound="chain", what="mlp fp8 full size y")
 
 
 def test_swiglu_leaves_other_rows_alone_and_handles_empty():
@@ -1043,7 +1056,7 @@ def test_swiglu_leaves_other_rows_alone_and_handles_empty():
     assert bool((H[37:].view(torch.int16) == P.SENTINEL_BITS).all())
     cpu = {k: P.cpu(v) for k, v in inp.items()}
     h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, list(range(37)))
-    assert og.rel_frobenius(P.rows_as_float(H, range(37)), h) <= P.TOL["bf16"]
+    P.check_gemm(P.rows_as_float(H, range(37)), h, "bf16", what="mlp gaps h")
     ws0 = mg.workspace(4, R)
     mg.schedule(torch.zeros(4, dtype=torch.int32, device="cuda"), R, ws0, block_m=0, N=2 * I)
     H0 = P.sentinel_like((R, I))
@@ -1067,56 +1080,72 @@ def test_expert_mlp_full_size():
     del inp
     h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
     y = omlp.down_rows(h, cpu["W2"], counts, rows)
-    eh, ey = og.rel_frobenius(got_h, h), og.rel_frobenius(got_y, y)
-    print(f"mlp full size rows={len(rows)} h {eh:.3e} y {ey:.3e}", flush=True)
-    assert eh <= P.TOL["fp8"] and ey <= P.TOL["fp8"], (eh, ey)
+    P.check_gemm(got_h, h, "fp8", what="mlp full size h")
+    P.check_gemm(got_y, y, "fp8", bound="chain", what="mlp full size y")
 
 
 # ----------------------------------------------------------------- K-grouped
 
 
-def run_k_grouped(t_sizes, Mw, Nw, seed=5, values="normal_unit"):
-    w = wl.Workload("kg", "k_grouped", "bf16", t_sizes, Mw=Mw, Nw=Nw, values=values, seed=seed)
+def run_k_grouped(t_sizes, Mw, Nw, seed=5, values="normal_unit", dtype="bf16"):
+    w = wl.Workload("kg", "k_grouped", dtype, t_sizes, Mw=Mw, Nw=Nw, values=values, seed=seed)
     inp = wl.materialize(w, "cuda")
     dW = torch.full((w.G, Mw, Nw), float("nan"), device="cuda")
     ws = mg.workspace(w.G, 0)
-    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws)
+    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws, inp.get("X_scale"), inp.get("dY_scale"))
     torch.cuda.synchronize()
     return w, inp, dW, ws
 
 
-def check_k_grouped(w, inp, dW, pairs):
+def k_grouped_ref(w, inp, pairs):
     X, dY = P.cpu(inp["X"]), P.cpu(inp["dY"])
-    ref = og.k_grouped(X, dY, w.counts, [e for e, _ in pairs], [i for _, i in pairs])
+    if w.dtype == "fp8":
+        return og.k_grouped_fp8(X, P.cpu(inp["X_scale"]), dY, P.cpu(inp["dY_scale"]), w.counts,
+                                [e for e, _ in pairs], [i for _, i in pairs])
+    return og.k_grouped(X, dY, w.counts, [e for e, _ in pairs], [i for _, i in pairs])
+
+
+def check_k_grouped(w, inp, dW, pairs, ref=None):
+    """dW rows against the oracle: fp32 output, so only fp32 accumulation separates them
+    (rel. Frobenius <= 1e-4 and the fp32 per-element bound)."""
+    ref = k_grouped_ref(w, inp, pairs) if ref is None else ref
     got = dW[torch.tensor([e for e, _ in pairs]), torch.tensor([i for _, i in pairs])].cpu().double().numpy()
-    assert np.isfinite(got).all()
-    err = og.rel_frobenius(got, ref)
-    assert err <= 1e-4, err          # fp32 output: no bf16 rounding anywhere, only fp32 accumulation
-    return err
+    return P.check_gemm(got, ref, "fp32", bound="fp32", what=f"k-grouped {w.dtype} G={w.G} Mw={w.Mw} Nw={w.Nw}")
 
 
-def test_k_grouped_small():
-    t = [100, 0, 37, 200, 1]
-    announce("k-grouped small", t)
-    w, inp, dW, ws = run_k_grouped(t, 256, 512)
+def k_rows_every_block(G, Mw, seed):
+    """One dW row from every 16-row block of every 256-row i-tile of every expert."""
+    rng = random.Random(seed)
+    return [(e, b + rng.randrange(16)) for e in range(G) for b in range(0, Mw, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_grouped_small(dtype):
+    t = [100, 0, 37, 200, 1, 129]
+    announce("k-grouped small", dtype, t)
+    w, inp, dW, ws = run_k_grouped(t, 512, 512, dtype=dtype)
     pairs = [(e, i) for e in range(w.G) for i in range(w.Mw)]
     check_k_grouped(w, inp, dW, pairs)
     assert not dW[1].any()                        # t_e = 0 -> zeros
     st = mg.stats_read(ws)
-    assert st.U == sum(t) and st.active == 4 and st.sum_sq == sum(x * x for x in t)
+    assert st.U == sum(t) and st.active == 5 and st.sum_sq == sum(x * x for x in t) and st.error_flags == 0
 
 
-def test_k_grouped_config_full_size():
-    w = wl.workload(5)
-    announce("k-grouped config 5", w.counts)
-    w, inp, dW, ws = run_k_grouped(w.counts, w.Mw, w.Nw)
-    rng = random.Random(5)
-    pairs = [(e, i) for e in range(w.G) for i in (0, w.Mw - 1, rng.randrange(w.Mw))]
-    err = check_k_grouped(w, inp, dW, pairs)
-    print(f"config 5: rel_frobenius={err:.3e}", flush=True)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_grouped_config_full_size(dtype):
+    """The Dirichlet weight-gradient workload (16 experts, 65536 rows, dW [16, 2048,
+    7168]): one dW row from every 16-row block of every i-tile of every expert,
+    whole rows, so every 16 x 16 MFMA block of every tile is compared."""
+    w0 = wl.workload(5)
+    announce("k-grouped config 5", dtype, w0.counts)
+    w, inp, dW, ws = run_k_grouped(w0.counts, w0.Mw, w0.Nw, dtype=dtype)
+    pairs = k_rows_every_block(w.G, w.Mw, seed=5)
+    check_k_grouped(w, inp, dW, pairs)
     for e, t in enumerate(w.counts):
         if t == 0:
             assert not dW[e].any()
+    st = mg.stats_read(ws)
+    assert st.U == sum(w.counts) and st.error_flags == 0
 
 
 def test_k_grouped_integer_exact_and_ragged():
@@ -1139,36 +1168,116 @@ def test_k_grouped_integer_exact_and_ragged():
     assert np.array_equal(got, ref)
 
 
-def test_k_grouped_empty_truncated_and_deterministic():
+def test_k_grouped_fp8_integer_exact():
+    """e4m3 codes in {-1, 0, 1} with power-of-two scales 2^-3..2^3 per group and
+    column: every product and every partial sum is a multiple of 2^-6 well
+    inside fp32's exact range, so GPU == oracle bit for bit.  Segment lengths
+    straddle the 128-row scale group (1, 127, 128, 129, 255, 0, 300): a group
+    index off by one anywhere changes the result."""
+    t = [1, 127, 128, 129, 255, 0, 300]
+    T, Mw, Nw = sum(t), 256, 512
+    announce("k-grouped fp8 integer exact", t)
+    g = torch.Generator().manual_seed(10)
+    X = torch.randint(-1, 2, (T, Mw), generator=g).float().to(torch.float8_e4m3fn)
+    dY = torch.randint(-1, 2, (T, Nw), generator=g).float().to(torch.float8_e4m3fn)
+    S = mg.k_scale_groups(t)
+    sx = torch.exp2(torch.randint(-3, 4, (S, Mw), generator=g).float())
+    sy = torch.exp2(torch.randint(-3, 4, (S, Nw), generator=g).float())
+    dW = torch.full((len(t), Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(len(t), 0)
+    mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws,
+                              sx.cuda(), sy.cuda())
+    torch.cuda.synchronize()
+    pairs = [(e, i) for e in range(len(t)) for i in range(Mw)]
+    ref = og.k_grouped_fp8(X, sx, dY, sy, t, [e for e, _ in pairs], [i for _, i in pairs])
+    got = dW.cpu().double().numpy().reshape(len(t) * Mw, Nw)
+    assert np.array_equal(got, ref)
+    assert mg.stats_read(ws).error_flags == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_grouped_empty_truncated_and_deterministic(dtype):
     """All experts empty -> dW all zero; counts past T are truncated (flag set);
     two runs give identical bits."""
-    announce("k-grouped empty / truncated / deterministic")
+    announce("k-grouped empty / truncated / deterministic", dtype)
     Mw, Nw = 256, 256
-    X = torch.randn(0, Mw).to(torch.bfloat16).cuda()
-    dY = torch.randn(0, Nw).to(torch.bfloat16).cuda()
+    d = torch.float8_e4m3fn if dtype == "fp8" else torch.bfloat16
+    scales = lambda S: (torch.ones(S, Mw, device="cuda"), torch.ones(S, Nw, device="cuda")) \
+        if dtype == "fp8" else (None, None)
+    X = torch.zeros(0, Mw).to(d).cuda()
+    dY = torch.zeros(0, Nw).to(d).cuda()
     dW = torch.full((3, Mw, Nw), float("nan"), device="cuda")
     ws = mg.workspace(3, 0)
-    mg.grouped_gemm_k_grouped(X, dY, dW, torch.zeros(3, dtype=torch.int32, device="cuda"), ws)
+    mg.grouped_gemm_k_grouped(X, dY, dW, torch.zeros(3, dtype=torch.int32, device="cuda"), ws, *scales(1))
     torch.cuda.synchronize()
     assert not dW.any()
     assert mg.stats_read(ws).U == 0
     # counts summing past T: the last segment is cut at T
     t, T = [50, 80, 40], 100
+    clamped = [50, 50, 0]                                   # the reading the device takes
     g = torch.Generator().manual_seed(4)
-    X = torch.randn(T, Mw, generator=g).to(torch.bfloat16)
-    dY = torch.randn(T, Nw, generator=g).to(torch.bfloat16)
+    x, dy = torch.randn(T, Mw, generator=g), torch.randn(T, Nw, generator=g)
+    if dtype == "fp8":
+        X, sx = wl.quantize_k_groups_e4m3(x, clamped)
+        dY, sy = wl.quantize_k_groups_e4m3(dy, clamped)
+        sc = (sx.cuda(), sy.cuda())
+    else:
+        X, dY, sc = x.to(torch.bfloat16), dy.to(torch.bfloat16), (None, None)
     outs = []
     for _ in range(2):
         dW = torch.full((3, Mw, Nw), float("nan"), device="cuda")
-        mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws)
+        mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws,
+                                  *sc)
         torch.cuda.synchronize()
         outs.append(dW.cpu())
     st = mg.stats_read(ws)
     assert st.error_flags & mg.FLAG_ROWS_OVERFLOW and st.U == T
     assert torch.equal(outs[0], outs[1])
-    clamped = [50, 50, 0]                                   # the reading the device takes
     pairs = [(e, i) for e in range(2) for i in range(0, Mw, 7)]
-    ref = og.k_grouped(X, dY, clamped, [e for e, _ in pairs], [i for _, i in pairs])
+    if dtype == "fp8":
+        ref = og.k_grouped_fp8(X, sx, dY, sy, clamped, [e for e, _ in pairs], [i for _, i in pairs])
+    else:
+        ref = og.k_grouped(X, dY, clamped, [e for e, _ in pairs], [i for _, i in pairs])
     got = outs[0][torch.tensor([e for e, _ in pairs]), torch.tensor([i for _, i in pairs])].double().numpy()
-    assert og.rel_frobenius(got, ref) <= 1e-4
+    P.check_gemm(got, ref, "fp32", bound="fp32", what=f"k-grouped truncated {dtype}")
     assert not outs[0][2].any()                             # the segment that starts at T is empty
+
+
+def test_k_grouped_fp8_too_few_scale_groups_is_flagged():
+    """Scale arrays with fewer rows than the histogram's groups: the call runs, the
+    missing groups read as zero scales, and MOEGG_FLAG_SCALE_GROUPS is set."""
+    t = [200, 100]                                          # 2 + 1 = 3 groups
+    announce("k-grouped fp8 scale groups flag", t)
+    Mw = Nw = 256
+    g = torch.Generator().manual_seed(12)
+    X, sx = wl.quantize_k_groups_e4m3(torch.randn(300, Mw, generator=g), t)
+    dY, sy = wl.quantize_k_groups_e4m3(torch.randn(300, Nw, generator=g), t)
+    dW = torch.full((2, Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(2, 0)
+    mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws,
+                              sx[:2].contiguous().cuda(), sy[:2].contiguous().cuda())
+    torch.cuda.synchronize()
+    assert mg.stats_read(ws).error_flags & mg.FLAG_SCALE_GROUPS
+    assert bool(torch.isfinite(dW).all())
+    # expert 0 (groups 0 and 1) is complete; expert 1's group 2 is missing and reads as 0
+    pairs = [(0, i) for i in range(0, Mw, 5)]
+    ref = og.k_grouped_fp8(X, sx, dY, sy, t, [e for e, _ in pairs], [i for _, i in pairs])
+    got = dW[0, 0:Mw:5].cpu().double().numpy()
+    P.check_gemm(got, ref, "fp32", bound="fp32", what="k-grouped fp8 complete expert")
+    assert not dW[1].any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_grouped_maximum_expert_count(dtype):
+    """G = 4096 experts with tiny ragged segments (a third empty): the expert
+    order comes from the scheduler's sort; every expert's dW, zeros included."""
+    rng = random.Random(43)
+    t = [0 if rng.random() < 0.33 else rng.randint(1, 3) for _ in range(4096)]
+    announce("k-grouped G=4096", dtype, sum(t))
+    w, inp, dW, ws = run_k_grouped(t, 256, 256, seed=43, dtype=dtype)
+    rows = [(e, i) for e in range(w.G) for i in range(0, w.Mw, 37)]
+    check_k_grouped(w, inp, dW, rows)
+    empty = torch.tensor([e for e, x in enumerate(t) if x == 0], device="cuda")
+    assert not dW[empty].any()
+    st = mg.stats_read(ws)
+    assert st.U == sum(t) and st.active == sum(1 for x in t if x) and st.error_flags == 0
