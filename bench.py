@@ -163,6 +163,101 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
             "sample": f"{len(sample)} output rows x {w.N} columns of this workload (fp64 oracle, {dt:.1f} s)"}
 
 
+def time_candidates(w: wl.Workload, inp, b_layout: int, scale_km: bool, args):
+    """Every candidate tile height of the contiguous GEMM timed on its own (the padding page,
+    "Build a routing-shaped benchmark": P, padding fraction, tiles, latency, effective and physical
+    throughput per candidate), outside the headline's timed steps, same cache mode."""
+    rows = []
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
+    for bm in (64, 128, 256, mg.BLOCK_M_PER_EXPERT):
+        sched, gemm, ws = build_step(w, inp, bm, b_layout, bm, None, 0, scale_km=scale_km)
+        for _ in range(3):
+            sched(); gemm()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for i, (a, b) in enumerate(ev):
+            if scratch is not None:
+                scratch.fill_(i & 255)
+            sched()
+            a.record()
+            gemm()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+        st = mg.stats_read(ws)
+        rep = st.report()
+        q = 256 if bm == mg.BLOCK_M_PER_EXPERT else bm
+        rows.append({"block_m": "per-expert" if bm == mg.BLOCK_M_PER_EXPERT else bm, "tiles": st.tiles,
+                     "P_at_block_m": st.P_at[q], "padding_fraction_at_block_m": round(rep.padding_fraction[q], 6),
+                     "P_exec": st.P_exec, "active_experts": st.active,
+                     "effective_experts": round(rep.effective_experts, 4), "gemm_ms_median": round(ms, 4),
+                     "effective_tflops": round(w.useful_flops() / (ms * 1e-3) / 1e12, 2),
+                     "physical_tflops": round(2.0 * st.P_exec * w.K * w.N / (ms * 1e-3) / 1e12, 2)})
+        del ws
+    return rows
+
+
+def sample_sclk(step, seconds: float = 0.4):
+    """The shader clock under this workload: the current DPM level of the GPU's
+    sclk (sysfs pp_dpm_sclk), sampled from a thread while about `seconds` of
+    steps run back to back after the timed region."""
+    import glob
+    import re
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+    def read():
+        for pth in paths:
+            try:
+                with open(pth) as f:
+                    for line in f:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                return int(m.group(1))
+            except OSError:
+                pass
+        return None
+    if not paths or read() is None:
+        return {"mhz_median": None, "source": "pp_dpm_sclk not readable on this host"}
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-4)
+    samples, done = [], threading.Event()
+
+    def sampler():
+        while not done.is_set():
+            v = read()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.002)
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    for _ in range(int(seconds / per) + 1):
+        step()
+    torch.cuda.synchronize()
+    done.set()
+    th.join()
+    samples.sort()
+    return {"mhz_median": samples[len(samples) // 2] if samples else None,
+            "mhz_min": samples[0] if samples else None, "mhz_max": samples[-1] if samples else None,
+            "samples": len(samples), "source": "pp_dpm_sclk current level while steps run back to back"}
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "cpu_affinity": len(os.sched_getaffinity(0))}
+
+
 def run_mlp(args):
     """Expert MLP on the Zipf histogram (64 experts, 32768 rows), DeepSeek-V3 expert shape: K 7168, I 2048,
     N2 7168.  One step: scheduler, L1 (fp8 e4m3, fp32 scales) with the fused SwiGLU epilogue writing H, L2 on H
@@ -257,6 +352,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-candidates", action="store_true",
+                    help="skip the per-candidate report (each tile height timed on its own after the timed steps)")
     cache = ap.add_mutually_exclusive_group()
     cache.add_argument("--cold", dest="cold", action="store_true", default=None,
                        help="write a 512 MiB scratch buffer between steps (more than L2 + MALL), and time each "
@@ -338,7 +435,8 @@ def main():
         inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
     torch.cuda.synchronize()
 
-    # first pass: learn the device's tile-height choice (outside timing)
+    # the tile height stays on the device: the timed step is the scheduler, then the GEMM with block_m = 0
+    # (one launch that runs whatever height the scheduler chose) unless --block-m fixes a height
     bm_req = {"auto": 0, "exemplar": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] \
         if not args.block_m.isdigit() else int(args.block_m)
     exemplars = mg.exemplar_table() if args.block_m == "exemplar" and w.layout == "contiguous" else None
@@ -350,12 +448,7 @@ def main():
     if scale_km:
         a_s = inp["A_scale"]
         inp_gpu = dict(inp, A_scale=a_s.reshape(-1, a_s.shape[-1]).t().contiguous())
-    sched, gemm, ws = build_step(w, inp_gpu, 0, b_layout, bm_req, exemplars, 4096, scale_km=scale_km)
-    if sched is not None:
-        sched()
-        torch.cuda.synchronize()
-        st0 = mg.stats_read(ws)
-        sched, gemm, ws = build_step(w, inp_gpu, st0.block_m, b_layout, bm_req, exemplars, 4096, scale_km=scale_km)
+    sched, gemm, ws = build_step(w, inp_gpu, bm_req, b_layout, bm_req, exemplars, 4096, scale_km=scale_km)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         if sched is not None:
@@ -422,11 +515,15 @@ def main():
     }
     if w.layout == "contiguous":
         phys = 2.0 * st.P_exec * w.K * w.N / (ms_step * 1e-3) / 1e12
-        bm_q = 256 if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m
+        rep = st.report()                       # ratios derived by the library (moegg_stats_report)
         out.update({"physical_tflops": round(phys, 2),
                     "block_m": "per-expert" if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m,
-                    "P_exec": st.P_exec, "padding_fraction_at_block_m": float(st.padding_fraction(bm_q)),
-                    "effective_experts": round(float(st.effective_experts), 3)})
+                    "U": st.U, "P_exec": st.P_exec, "active_experts": st.active,
+                    # rows the MFMAs ran without a valid row: every height skips 16-row blocks past a tile's
+                    # valid rows, so the executed rows are P(16) whatever the height
+                    "padding_fraction_exec": round(rep.exec_padding_fraction, 6),
+                    "padding_fraction_by_q": {q: round(v, 6) for q, v in rep.padding_fraction.items()},
+                    "effective_experts": round(rep.effective_experts, 4)})
     # roofline of the dominant kernel (the GEMM), from HIP events on its own stream
     achieved_tflops = flops / (gemm_avg * 1e-3) / 1e12
     bytes_alg = algorithmic_bytes(w)
@@ -444,6 +541,11 @@ def main():
     out["gemm_kernel_ms"] = round(gemm_avg, 4)
     out["algorithmic_bytes"] = bytes_alg
     out["wall_s_timed"] = round(wall, 4)
+    # after the timed steps: the other candidate heights, and the clock under this load
+    if w.layout == "contiguous" and exemplars is None and not args.no_candidates:
+        out["candidates"] = time_candidates(w, inp_gpu, b_layout, scale_km, args)
+    out["sclk"] = sample_sclk(lambda: (sched() if sched is not None else None, gemm()))
+    out["host"] = host_info()
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 18                         # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -292,8 +292,9 @@ moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, vo
  * chosen only when strictly cheaper; stats block_m then reads
  * MOEGG_BLOCK_M_PER_EXPERT.  Padding alone does not pick the kernel
  * ("Padding is not the whole cost model", MoE GroupGEMM padding page).  The
- * grid size is fixed from host arguments alone, so the call is
- * graph-capturable.
+ * GEMM is one launch whose grid size comes from host arguments alone (sized
+ * for the longest tile list, 64-row tiles; workgroups past the list the
+ * device chose exit at once), so the call is graph-capturable.
  */
 moegg_status_t moegg_grouped_gemm_contiguous(
     const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,
@@ -307,10 +308,12 @@ moegg_status_t moegg_grouped_gemm_contiguous(
  * MoE layer runs several grouped GEMMs over one routing histogram (gate/up,
  * then down projection); they can share one schedule.  Arguments are those of
  * moegg_grouped_gemm_contiguous, without m_sizes and seg_align.  The
- * schedule must come from the same G and rows_total.  block_m = 0 launches
- * every candidate (the three heights and the per-expert kernel), and the one
- * matching the schedule does the work.  Any other block_m launches only that
- * kernel; if it differs from the schedule's, nothing is written.
+ * schedule must come from the same G and rows_total.  block_m = 0 runs
+ * whatever height the schedule used, in one launch whose grid depends only on
+ * G, rows_total and N (so a captured graph stays valid when the counts and
+ * the device's choice change between replays).  Any other block_m runs only
+ * that height (MOEGG_BLOCK_M_PER_EXPERT: per-expert heights); if it differs
+ * from the schedule's, nothing is written.
  */
 moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
     const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,

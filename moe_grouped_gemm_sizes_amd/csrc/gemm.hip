@@ -889,29 +889,39 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
     contig_tile<C, B_KN, SWIGLU>(p, lds, e, row_start, rows_valid, ct);
 }
 
-// Per-expert tile heights (block_m = MOEGG_BLOCK_M_PER_EXPERT): the tile list
-// is the one of 256-row tiles, ordered tiles of more than 128 valid rows first,
-// then tails of 65..128 rows, then tails of 1..64 rows.  Each tile runs with the
-// smallest configuration that covers its valid rows, so an expert's remainder
-// does not pay for a 256-row tile, and the 128- and 64-row configurations'
-// deeper stage rings keep their loads further ahead.  All three share one
-// launch; the configuration is uniform per workgroup.
+// One launch for any tile height the scheduler chose (block_m = 0, the
+// choice made on the device) and for per-expert heights
+// (MOEGG_BLOCK_M_PER_EXPERT).  The grid is sized from host arguments for the
+// longest list any height can produce (64-row tiles); each workgroup runs one
+// work item with the configuration of the chosen height, or under per-expert
+// heights with the smallest one that holds the tile's valid rows, and
+// workgroups past the list exit after reading the control block.  (A grid
+// sized for 256-row tiles with a loop over items spilled registers: the
+// compiler kept tile setup of all three configurations live across the loop.)
+// The per-expert list orders tiles of more than 128 valid rows first, then
+// tails of 65..128 rows, then tails of 1..64 rows, so an expert's remainder
+// does not pay for a 256-row tile and the 128- and 64-row configurations'
+// deeper stage rings keep their loads further ahead.  Nothing here depends on
+// the host knowing the height, so the call is graph-capturable.
 template <bool FP8, bool B_KN, bool E8, bool W4, int SWIGLU = 0>
-__global__ __launch_bounds__(512, 1) void grouped_gemm_per_expert_kernel(ContigArgs p) {
+__global__ __launch_bounds__(512, 1) void grouped_gemm_auto_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / 256;
     const WsLayout L = ws_layout(p.G, 0);
     const Control* ctl = (const Control*)(p.ws + L.control);
-    if (ctl->block_m != MOEGG_BLOCK_M_PER_EXPERT) return;
+    const int bm = ctl->block_m;
+    if (p.req_block_m != 0 && p.req_block_m != bm) return;   // asked for another height than scheduled
     const int n_rt = ctl->n_tiles;
+    const moegg_tile_t* tiles = (const moegg_tile_t*)(p.ws + L.tiles);
     const int item = block_to_item(blockIdx.x);
     if (item >= n_rt * n_ct) return;
     int rt, ct;
     item_to_tiles(item, n_rt, n_ct, rt, ct);
-    const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
-    if (t.rows_valid > 128)
+    const moegg_tile_t t = tiles[rt];
+    const int h = bm == MOEGG_BLOCK_M_PER_EXPERT ? (t.rows_valid > 128 ? 256 : t.rows_valid > 64 ? 128 : 64) : bm;
+    if (h == 256)
         contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else if (t.rows_valid > 64)
+    else if (h == 128)
         contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
     else
         contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
@@ -1130,36 +1140,28 @@ static hipError_t launch_one(const ContigArgs& a, int grid, hipStream_t s) {
 
 static int round256(int64_t x) { return (int)((x + 255) / 256 * 256); }
 
-// Launch the contiguous GEMM for tile height block_m (0 = every candidate;
-// the ones the device did not choose exit at entry).
+// Launch the contiguous GEMM for tile height block_m.  0 (the height the
+// device chose) and per-expert heights run in one launch of the auto kernel;
+// an explicit 64, 128 or 256 runs that height's own kernel, which writes
+// nothing unless the schedule used the same height.
 template <bool FP8, bool B_KN, bool E8, bool W4 = false, int SW = 0>
 static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int block_m, hipStream_t s) {
     const int64_t n_ct = a.N / 256;
-    hipError_t err = hipSuccess;
     auto grid_for = [&](int q) { return round256(((rows_total + q - 1) / q + a.G) * n_ct); };
-    // block_m = 0 launches every candidate; the one matching the schedule does the work
     if (block_m == MOEGG_BLOCK_M_PER_EXPERT || block_m == 0) {
+        ContigArgs b = a;
+        b.req_block_m = block_m;
         constexpr int lds = std::max({Contig256<FP8, E8, W4>::LDS_BYTES, Contig128<FP8, E8, W4>::LDS_BYTES,
                                       Contig64<FP8, E8, W4>::LDS_BYTES});
-        err = allow_lds<grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4, SW>>(lds);
+        hipError_t err = allow_lds<grouped_gemm_auto_kernel<FP8, B_KN, E8, W4, SW>>(lds);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((grouped_gemm_per_expert_kernel<FP8, B_KN, E8, W4, SW>), dim3(grid_for(256)), dim3(512),
-                           lds, s, a);
-        err = hipGetLastError();
-        if (err != hipSuccess || block_m != 0) return err;
+        hipLaunchKernelGGL((grouped_gemm_auto_kernel<FP8, B_KN, E8, W4, SW>), dim3(grid_for(64)), dim3(512), lds,
+                           s, b);
+        return hipGetLastError();
     }
-    if (block_m == 0 || block_m == 256) {
-        err = launch_one<Contig256<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(256), s);
-        if (err != hipSuccess) return err;
-    }
-    if (block_m == 0 || block_m == 128) {
-        err = launch_one<Contig128<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(128), s);
-        if (err != hipSuccess) return err;
-    }
-    if (block_m == 0 || block_m == 64) {
-        err = launch_one<Contig64<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(64), s);
-    }
-    return err;
+    if (block_m == 256) return launch_one<Contig256<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(256), s);
+    if (block_m == 128) return launch_one<Contig128<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(128), s);
+    return launch_one<Contig64<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(64), s);
 }
 
 hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,

@@ -12,11 +12,14 @@ And, for every element of every compared row (check_gemm):
   2^-8 of its magnitude; the rms term holds the fp32 accumulation error, about
   1e-5 of the row's rms at K = 7168, with a wide margin);
 - fp32 output:              |C - C_ref| <= 2^-20 |C_ref| + 2^-12 rms(row);
-- second GEMM of the expert MLP (its input H was rounded once more, to bf16 or
-  e4m3): |y - y_ref| <= 2^-8 |y_ref| + 2^-5 rms(row).
+- second GEMM of the expert MLP, whose input H was rounded once more:
+  bf16 H: |y - y_ref| <= 2^-8 |y_ref| + 2^-5 rms(row);
+  e4m3 H (y_ref from the oracle's own codes, about 0.15 % of which sit one
+  e4m3 step, up to 2^-3 of the value, from the GPU's): 2^-8 |y_ref| + 2^-4 rms(row).
 Measured on CPU emulations of the same arithmetic (fp32 accumulation, one
 final rounding) at K = 7168: the largest element uses 0.96, 0.94 and 0.38 of
-these bounds.  One wrong 16 x 16 MFMA block, or one K step of it missing,
+the first three; on MI355X the single GEMMs reach 0.94 of theirs and the e4m3
+chain at full size 0.60 of its own.  One wrong 16 x 16 MFMA block, or one K step of it missing,
 moves its elements by a sizeable fraction of the row's rms and fails them.
 """
 from __future__ import annotations
@@ -33,7 +36,8 @@ from oracle import accounting as acc
 from oracle import gemm as og
 
 TOL = {"bf16": 2e-3, "fp8": 2e-2, "fp32": 1e-4}
-ELEM = {"bf16": (2.0 ** -8, 2.0 ** -10), "fp32": (2.0 ** -20, 2.0 ** -12), "chain": (2.0 ** -8, 2.0 ** -5)}
+ELEM = {"bf16": (2.0 ** -8, 2.0 ** -10), "fp32": (2.0 ** -20, 2.0 ** -12), "chain": (2.0 ** -8, 2.0 ** -5),
+        "chain_e4m3": (2.0 ** -8, 2.0 ** -4)}
 SENTINEL_BITS = 0x7BAD          # a finite bf16 pattern the kernels never produce here by chance
 
 

@@ -940,7 +940,7 @@ def test_swiglu_e4m3_h_and_fp8_down_projection(block_m):
     qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
     y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
                       A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
-    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain", what=f"mlp fp8 H block_m={block_m} y")
+    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain_e4m3", what=f"mlp fp8 H block_m={block_m} y")
 
 
 def run_mlp_fp4(counts, K, I, N2, block_m, seed):
@@ -977,7 +977,7 @@ def test_swiglu_fp4_weights(block_m):
     qa = torch.from_numpy(q).float().to(torch.float8_e4m3fn).contiguous()
     y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
                       A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
-    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain", what=f"mlp fp4 L1 block_m={block_m} y")
+    P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain_e4m3", what=f"mlp fp4 L1 block_m={block_m} y")
 
 
 def test_expert_mlp_fp4_full_size():
@@ -1001,7 +1001,7 @@ def test_expert_mlp_fp4_full_size():
         w2e = cpu["W2"][e].float().double().numpy() * np.repeat(
             np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0), 128, 1).T
         y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
-    P.check_gemm(got_y, y, "fp8", bound="chain", what="mlp fp4 L1 full size y")
+    P.check_gemm(got_y, y, "fp8", bound="chain_e4m3", what="mlp fp4 L1 full size y")
 
 
 def test_expert_mlp_fp8_full_size():
@@ -1037,7 +1037,7 @@ def test_expert_mlp_fp8_full_size():
         w2e = w2[e].float().double().numpy() * np.repeat(np.repeat(cpu["W2_scale"][e].double().numpy(), 128, 0),
                                                           128, 1).T
         y[idx] = (q[idx] * np.repeat(s[idx], 128, axis=1)) @ w2e.T
-    P.check_gemm(got_y, y, "fp8", bound="chain", what="mlp fp8 full size y")
+    P.check_gemm(got_y, y, "fp8", bound="chain_e4m3", what="mlp fp8 full size y")
 
 
 def test_swiglu_leaves_other_rows_alone_and_handles_empty():

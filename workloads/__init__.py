@@ -34,6 +34,8 @@ distributions stand in for real routing traces (none ship with the pages):
 """
 from __future__ import annotations
 
+import json
+import os
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
@@ -293,8 +295,20 @@ class Workload:
         return 2 * sum(self.counts) * self.K * self.N
 
 
+FIXTURE_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden",
+                            "histograms.json")
+
+
+def fixture_counts(name: str) -> List[int]:
+    """Counts of a seeded histogram as frozen in tests/golden/histograms.json
+    (written by tests/golden/make_histograms.py from the generators above)."""
+    with open(FIXTURE_PATH) as f:
+        return [int(c) for c in json.load(f)[name]["counts"]]
+
+
 def workload(n: int) -> Workload:
-    """The five benchmark problems, by number 1..5."""
+    """The five benchmark problems, by number 1..5.  Workloads 3-5 take their
+    histograms from the frozen fixture."""
     if n == 1:
         return Workload("near-uniform 8 experts bf16 contiguous", "contiguous", "bf16",
                         hist_near_uniform(), K=512, N=256, values="uniform", seed=1)
@@ -303,13 +317,13 @@ def workload(n: int) -> Workload:
                         hist_issue_32(), K=7168, N=4096, seg_align=128, values="normal", seed=2)
     if n == 3:
         return Workload("zipf 64 experts fp8 contiguous", "contiguous", "fp8",
-                        hist_zipf(3), K=7168, N=4096, values="normal", seed=3)
+                        fixture_counts("zipf64"), K=7168, N=4096, values="normal", seed=3)
     if n == 4:
         return Workload("masked decode 32 experts bf16", "masked", "bf16",
-                        hist_poisson_masked(4), K=2048, N=7168, cap=256, values="normal", seed=4)
+                        fixture_counts("poisson32"), K=2048, N=7168, cap=256, values="normal", seed=4)
     if n == 5:
         return Workload("k-grouped weight gradient 16 experts bf16", "k_grouped", "bf16",
-                        hist_dirichlet(5), Mw=2048, Nw=7168, values="normal_unit", seed=5)
+                        fixture_counts("dirichlet16"), Mw=2048, Nw=7168, values="normal_unit", seed=5)
     raise ValueError(f"no workload {n}")
 
 
