@@ -303,6 +303,30 @@ moegg_status_t moegg_grouped_gemm_contiguous(
     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moegg_grouped_gemm_contiguous for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture that may not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, computation, constraints and errors as
+ * moegg_grouped_gemm_contiguous, without ws and ws_bytes.  The scheduler's
+ * workspace is a fixed array of MOEGG_NOALLOC_SCRATCH_BYTES in each GPU's
+ * memory, held by the library until the process ends; problems whose
+ * workspace (moegg_workspace_bytes(G, rows_total)) exceeds it return
+ * MOEGG_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing: on its first use on a GPU it looks up the array's address there
+ * (the calling thread's current device, which `stream` must belong to).
+ * Every call on one GPU uses the same array and each call rewrites what the
+ * GEMM reads, so calls in order on one GPU are independent; calls that overlap
+ * on one GPU (concurrent streams, several threads) race.  The stats and tile
+ * list it leaves there are not readable through moegg_stats_read.
+ */
+#define MOEGG_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+moegg_status_t moegg_grouped_gemm_contiguous_noalloc(
+    const void* A, const void* A_scale, const void* B, const void* B_scale, void* C,
+    const int32_t* m_sizes, int G, int64_t rows_total, int K, int N, int seg_align,
+    moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m, void* stream);
+
+/*
  * The contiguous GEMM alone, driven by the tile list that an earlier
  * moegg_schedule or moegg_grouped_gemm_contiguous call left in `ws`.  One
  * MoE layer runs several grouped GEMMs over one routing histogram (gate/up,

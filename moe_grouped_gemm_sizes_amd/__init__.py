@@ -109,6 +109,8 @@ EXPORTS = {
                                                        _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_contiguous": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                              _I32, _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_grouped_gemm_contiguous_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
+                                                     _I32, _I32, _I32, _VP]),
     "moegg_grouped_gemm_swiglu_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                                    _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_masked": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -348,6 +350,25 @@ def grouped_gemm_contiguous(A, B, C, m_sizes, ws, A_scale=None, B_scale=None, se
         _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), G, rows, K, N,
         seg_align, code, b_layout, block_m, _p(ws), ws.numel(), _stream(stream)),
         "moegg_grouped_gemm_contiguous")
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20          # MOEGG_NOALLOC_SCRATCH_BYTES
+
+
+def grouped_gemm_contiguous_noalloc(A, B, C, m_sizes, A_scale=None, B_scale=None, seg_align: int = 1,
+                                    block_m: int = 0, b_layout: int = B_KN, stream=None, scale_km: bool = False):
+    """grouped_gemm_contiguous without a workspace: the library's fixed per-GPU
+    scratch array holds the schedule (see moegg.h); nothing is allocated."""
+    _counts(m_sizes, "m_sizes")
+    G = m_sizes.numel()
+    _need(A, "A", [None, None], (torch.bfloat16, _E4M3))
+    rows, K = A.shape
+    code, N = _operands(rows, K, A, A_scale, B, B_scale, G, b_layout, scale_km)
+    _need(C, "C", [rows, N], (torch.bfloat16,))
+    _one_device(A, A_scale, B, B_scale, C, m_sizes)
+    _check(lib().moegg_grouped_gemm_contiguous_noalloc(
+        _p(A), _p(A_scale), _p(B), _p(B_scale), _p(C), _p(m_sizes), G, rows, K, N,
+        seg_align, code, b_layout, block_m, _stream(stream)), "moegg_grouped_gemm_contiguous_noalloc")
 
 
 def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:

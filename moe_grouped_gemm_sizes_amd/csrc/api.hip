@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -146,11 +147,14 @@ moegg_status_t moegg_selection_read(const void* ws, moegg_selection_t* h_out, vo
     return MOEGG_OK;
 }
 
-moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale, const void* B,
-                                             const void* B_scale, void* C, const int32_t* m_sizes, int G,
-                                             int64_t rows_total, int K, int N, int seg_align,
-                                             moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
-                                             void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the contiguous call, everything but the workspace.
+moegg_status_t check_contiguous(const void* A, const void* A_scale, const void* B, const void* B_scale,
+                                const void* C, const int32_t* m_sizes, int G, int64_t rows_total, int K, int N,
+                                int seg_align, moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m) {
     if (!m_sizes || !aligned(m_sizes, 4)) return MOEGG_ERR_INVALID_ARG;
     moegg_status_t st = check_common(A, A_scale, B, B_scale, C, G, K, N, dtype, b_layout, 256);
     if (st != MOEGG_OK) return st;
@@ -160,10 +164,15 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     if (256ll * K * esz > kMaxBufferBytes || 256ll * N * 2 > kMaxBufferBytes) return MOEGG_ERR_UNSUPPORTED;
-    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    return MOEGG_OK;
+}
+
+// Scheduler + contiguous GEMM on a checked problem, with the workspace at ws.
+moegg_status_t launch_contiguous_call(const void* A, const void* A_scale, const void* B, const void* B_scale,
+                                      void* C, const int32_t* m_sizes, int G, int64_t rows_total, int K, int N,
+                                      int seg_align, moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
+                                      void* ws, hipStream_t s) {
     const WsLayout L = ws_layout(G, rows_total);
-    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, block_m, N / 256, 0, ws, L.max_tiles, s);
     if (e != hipSuccess) return hip_status(e, "scheduler launch");
     ContigArgs a{A, A_scale, B, B_scale, C, m_sizes, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
@@ -174,6 +183,80 @@ moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale,
         fprintf(stderr, "moegg: contiguous G=%d rows=%lld K=%d N=%d align=%d dtype=%d b_layout=%d block_m=%d\n", G,
                 (long long)rows_total, K, N, seg_align, (int)dtype, (int)b_layout, block_m);
     return hip_status(e, "contiguous GEMM launch");
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ allocation-free variant
+//
+// The workspace of moegg_grouped_gemm_contiguous_noalloc: a fixed array in
+// each GPU's memory, for callers that cannot allocate.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address on a
+// GPU comes from hipGetSymbolAddress with that GPU current, looked up once per
+// GPU and kept in scratch_ptr, and only that address is ever handed to a
+// kernel.  Calls on one GPU share the array: the scheduler writes every field
+// the GEMM reads (stats, control block, offsets, tile list) before the GEMM
+// runs, so nothing needs clearing, but calls that overlap on one GPU race.
+namespace {
+constexpr size_t kNoAllocScratchBytes = MOEGG_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the calling thread's current GPU.
+hipError_t scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+moegg_status_t moegg_grouped_gemm_contiguous(const void* A, const void* A_scale, const void* B,
+                                             const void* B_scale, void* C, const int32_t* m_sizes, int G,
+                                             int64_t rows_total, int K, int N, int seg_align,
+                                             moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
+                                             void* ws, size_t ws_bytes, void* stream) {
+    moegg_status_t st = check_contiguous(A, A_scale, B, B_scale, C, m_sizes, G, rows_total, K, N, seg_align, dtype,
+                                         b_layout, block_m);
+    if (st != MOEGG_OK) return st;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
+    return launch_contiguous_call(A, A_scale, B, B_scale, C, m_sizes, G, rows_total, K, N, seg_align, dtype,
+                                  b_layout, block_m, ws, (hipStream_t)stream);
+}
+
+moegg_status_t moegg_grouped_gemm_contiguous_noalloc(const void* A, const void* A_scale, const void* B,
+                                                     const void* B_scale, void* C, const int32_t* m_sizes, int G,
+                                                     int64_t rows_total, int K, int N, int seg_align,
+                                                     moegg_dtype_t dtype, moegg_b_layout_t b_layout, int block_m,
+                                                     void* stream) {
+    moegg_status_t st = check_contiguous(A, A_scale, B, B_scale, C, m_sizes, G, rows_total, K, N, seg_align, dtype,
+                                         b_layout, block_m);
+    if (st != MOEGG_OK) return st;
+    if (ws_layout(G, rows_total).total > kNoAllocScratchBytes) return MOEGG_ERR_WORKSPACE;
+    void* ws = nullptr;
+    hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch lookup");
+    return launch_contiguous_call(A, A_scale, B, B_scale, C, m_sizes, G, rows_total, K, N, seg_align, dtype,
+                                  b_layout, block_m, ws, (hipStream_t)stream);
 }
 
 moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void* A_scale, const void* B,

@@ -84,6 +84,12 @@ int main(void) {
         st.U = -1;
         EXPECT(moegg_stats_report(&st, &rep), MOEGG_ERR_INVALID_ARG);
     }
+    /* allocation-free variant: argument errors, and a workspace beyond its fixed array, before any HIP call */
+    EXPECT(moegg_grouped_gemm_contiguous_noalloc(NULL, NULL, fake, NULL, fake, fake, 8, 132, 512, 256, 1, MOEGG_BF16,
+                                                 MOEGG_B_KN, 0, NULL), MOEGG_ERR_INVALID_ARG);
+    EXPECT(moegg_grouped_gemm_contiguous_noalloc(fake, NULL, fake, NULL, fake, fake, 64, 8 << 20, 256, 256, 1,
+                                                 MOEGG_BF16, MOEGG_B_KN, 0, NULL), MOEGG_ERR_WORKSPACE);
+    if (moegg_workspace_bytes(64, 8 << 20) <= MOEGG_NOALLOC_SCRATCH_BYTES) ++fails;
     EXPECT(moegg_stats_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
     EXPECT(moegg_selection_read(NULL, NULL, NULL), MOEGG_ERR_INVALID_ARG);
     int64_t n = 0;
