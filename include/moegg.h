@@ -3,9 +3,10 @@
  *
  * The operation: expert e multiplies its m_e routed rows [m_e, K] by its own
  * weight B_e [K, N].  N and K are shared by all experts.  The counts m_e are
- * ragged, skewed and often zero.  Grouping tokens by expert changes the
- * tiling, not the math.  Only M is grouped, because experts share one N and
- * one K.  (DeepGEMM grouped/masked MoE GEMM record, "Arithmetic intensity".)
+ * ragged, skewed and often zero.  Gathering each expert's tokens into one GEMM
+ * alters how the work is tiled; every output is still the same product.  Only
+ * M is grouped, because experts share one N and one K.  (DeepGEMM
+ * grouped/masked MoE GEMM record, "Arithmetic intensity".)
  *
  * Conventions for every call below:
  *   - Pointers are device pointers unless the name starts with h_.
@@ -385,8 +386,9 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
 
 /*
  * Masked layout for decode under graph capture (DeepGEMM record,
- * "Workarounds" and "Arithmetic intensity": the kernel takes a mask and
- * computes only the valid portions, with no CPU sync).
+ * "Workarounds" and "Arithmetic intensity": the kernel reads the per-expert
+ * valid counts on the device and works on those rows only, so the token
+ * counts never travel to the host).
  *   A        [G, cap, K].  A_scale fp32 [G, cap, K/128] (MOEGG_FP8_E4M3),
  *            fp32 [K/128, G * cap] (MOEGG_FP8_E4M3_SCALE_KM), E8M0
  *            bytes [K/128, G * cap] (MOEGG_FP8_E4M3_E8M0 and

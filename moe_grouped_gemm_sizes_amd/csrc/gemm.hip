@@ -6,9 +6,9 @@
 //   - masked: a capacity buffer [G, cap, K] plus per-expert valid counts,
 //     read at run time, with a fixed grid for graph replay.
 //   - K-grouped weight gradient: the reduction axis is split by expert.
-// "Grouped GEMM changes the tiling, not the math" (same record, "Arithmetic
-// intensity"): every valid output is a plain dot product over K, accumulated
-// in fp32.
+// Grouping alters only how the work is tiled, not what each output is (same
+// record, "Arithmetic intensity"): every valid output is a plain dot product
+// over K, accumulated in fp32.
 //
 // Kernel structure (one 512-thread workgroup per output tile):
 //   - Stage loads go straight from HBM to LDS (buffer_load_dwordx4 ... lds).

@@ -9,8 +9,9 @@ row R of expert e and each column n:
 
 with dec8 the oracle's own OCP E4M3FN decoder (gemm.dec_e4m3) and dec4 the
 OCP E2M1 decoder below.  Weights are stored [G, N, K/2], two codes per byte,
-element 2i in the low nibble.  A library matmul serves as the sum over each
-128-wide K group; nothing else is blocked or reordered.
+element 2i in the low nibble.  Both operands are dequantized in fp64 exactly as
+the formula reads (each code times its own group's scale), and a library
+float64 matmul takes the sum over k; nothing is blocked or reordered.
 """
 from __future__ import annotations
 
@@ -50,6 +51,18 @@ def _e4m3_table() -> np.ndarray:
     return np.array([og.dec_e4m3(c) for c in range(256)], dtype=np.float64)
 
 
+def _dequant_rows(codes: np.ndarray, scales: np.ndarray, dec8: np.ndarray) -> np.ndarray:
+    """e4m3 codes [m, K] and their 1x128 scales [m, K/128] -> values [m, K] (fp64)."""
+    return dec8[codes] * np.repeat(scales, 128, axis=1)
+
+
+def _dequant_weight(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """One expert's packed E2M1 weights [N, K/2] and block scales [K/128, N/128] -> W [N, K] (fp64)."""
+    w = dec_e2m1_packed(packed)                                      # [N, K]
+    s = np.repeat(np.repeat(scales, 128, axis=0), 128, axis=1)       # [K, N]: the scale of each (k, n)
+    return w * s.T
+
+
 def contiguous_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, W_scale: torch.Tensor,
                        counts: Sequence[int], rows: Sequence[int], seg_align: int = 1) -> np.ndarray:
     """Rows `rows` of C for the contiguous layout (segment starts as in the tile
@@ -60,7 +73,6 @@ def contiguous_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, 
     sa = A_scale.double().numpy()
     w = W.contiguous().numpy()
     sb = W_scale.double().numpy()
-    K = a_codes.shape[1]
     N = w.shape[1]
     offs = acc.segment_offsets(counts, seg_align)
     out = np.zeros((len(rows), N), dtype=np.float64)
@@ -73,15 +85,9 @@ def contiguous_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, 
         by_e.setdefault(expert_of[r], []).append(i)
     for e, idx in by_e.items():
         rr = [rows[i] for i in idx]
-        a = dec8[a_codes[rr]]                                  # [m, K]
-        we = dec_e2m1_packed(w[e])                             # [N, K]
-        res = np.zeros((len(rr), N), dtype=np.float64)
-        for kb in range(K // 128):
-            ks = slice(kb * 128, (kb + 1) * 128)
-            part = a[:, ks] @ we[:, ks].T                      # [m, N], the group's sum
-            colscale = np.repeat(sb[e, kb], 128)[:N]           # weight block scale per column
-            res += part * sa[rr, kb][:, None] * colscale[None, :]
-        out[idx] = res
+        a = _dequant_rows(a_codes[rr], sa[rr], dec8)                  # [m, K]
+        we = _dequant_weight(w[e], sb[e])                             # [N, K]
+        out[idx] = a @ we.T
     return out
 
 
@@ -89,14 +95,13 @@ def masked_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, W_sc
                    masked_m: Sequence[int], pairs: Sequence[tuple]) -> np.ndarray:
     """Masked layout: C[e, r, n] for each (e, r) in `pairs` (r < masked_m[e]).
     A: e4m3 codes [G, cap, K]; A_scale fp32 [G, cap, K/128]; W packed E2M1
-    [G, N, K/2]; W_scale fp32 [G, K/128, N/128].  Same sum as
+    [G, N, K/2]; W_scale fp32 [G, K/128, N/128].  Same product as
     contiguous_fp8_fp4, with row r of expert e at A[e, r]."""
     dec8 = _e4m3_table()
     a_codes = A.contiguous().view(torch.uint8).numpy()
     sa = A_scale.double().numpy()
     w = W.contiguous().numpy()
     sb = W_scale.double().numpy()
-    K = a_codes.shape[2]
     N = w.shape[1]
     out = np.zeros((len(pairs), N), dtype=np.float64)
     by_e = {}
@@ -105,13 +110,7 @@ def masked_fp8_fp4(A: torch.Tensor, A_scale: torch.Tensor, W: torch.Tensor, W_sc
         by_e.setdefault(e, []).append(i)
     for e, idx in by_e.items():
         rr = [pairs[i][1] for i in idx]
-        a = dec8[a_codes[e, rr]]                               # [m, K]
-        we = dec_e2m1_packed(w[e])                             # [N, K]
-        res = np.zeros((len(rr), N), dtype=np.float64)
-        for kb in range(K // 128):
-            ks = slice(kb * 128, (kb + 1) * 128)
-            part = a[:, ks] @ we[:, ks].T
-            colscale = np.repeat(sb[e, kb], 128)[:N]
-            res += part * sa[e, rr, kb][:, None] * colscale[None, :]
-        out[idx] = res
+        a = _dequant_rows(a_codes[e, rr], sa[e, rr], dec8)
+        we = _dequant_weight(w[e], sb[e])
+        out[idx] = a @ we.T
     return out

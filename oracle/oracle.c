@@ -6,8 +6,9 @@
  * product path never calls it, and the two share no code.
  *
  * What it computes, from the pages:
- *   - "Grouped GEMM changes the tiling, not the math" (DeepGEMM grouped/masked
- *     MoE GEMM record, "Arithmetic intensity").  Each expert e multiplies its
+ *   - Grouping routes each expert's tokens into one GEMM; it alters how the
+ *     work is tiled, while every output stays the same product (DeepGEMM
+ *     grouped/masked MoE GEMM record, "Arithmetic intensity").  Each expert e multiplies its
  *     own routed rows by its own weight, and all experts share K and N.  So
  *     every valid output element is the plain dot product
  *         C[row, n] = sum_k A[row, k] * B_e[k, n]

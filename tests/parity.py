@@ -33,6 +33,7 @@ import torch
 import moe_grouped_gemm_sizes_amd as mg
 import workloads as wl
 from oracle import accounting as acc
+from oracle import choice as ochoice
 from oracle import gemm as og
 
 TOL = {"bf16": 2e-3, "fp8": 2e-2, "fp32": 1e-4}
@@ -174,15 +175,5 @@ def untouched_rows_ok(C: torch.Tensor, counts: Sequence[int], seg_align: int) ->
 
 
 def choice_rule(counts, n_col_tiles):
-    """The documented tile-height rule: cost(q) = ceil(tiles(q) * cols / 256) * (q + 64), ties to larger q;
-    per-expert heights (classes of 256-row tiles, 65..128-row and 1..64-row remainders, each class costed as
-    its own waves) only when strictly cheaper."""
-    waves = lambda tiles, q: -(-tiles * n_col_tiles // 256) * (q + 64)
-    costs = {q: waves(acc.tiles_for(counts, q), q) for q in (64, 128, 256)}
-    best = min(costs.values())
-    uniform = max(q for q, c in costs.items() if c == best)
-    rem = [m - (-(-m // 256) - 1) * 256 for m in counts if m > 0]
-    n128 = sum(1 for r in rem if 64 < r <= 128)
-    n64 = sum(1 for r in rem if r <= 64)
-    pe = waves(acc.tiles_for(counts, 256) - n128 - n64, 256) + waves(n128, 128) + waves(n64, 64)
-    return mg.BLOCK_M_PER_EXPERT if pe < best else uniform
+    """The documented tile-height rule, from the oracle (oracle/choice.py)."""
+    return ochoice.choose(counts, n_col_tiles)
