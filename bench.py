@@ -141,9 +141,6 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     else:
-        if cpu["B"].shape[1] != w.K:                     # weights were repacked to [G,N,K]
-            cpu["B"] = cpu["B"].transpose(1, 2).contiguous()
-
         def run(rows):
             og.contiguous(cpu["A"], cpu["B"], w.counts, rows, seg_align=w.seg_align,
                           A_scale=cpu.get("A_scale"), B_scale=cpu.get("B_scale"))
@@ -352,6 +349,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the clock sample (about 0.4 s of extra back-to-back steps after the timed ones)")
     ap.add_argument("--no-candidates", action="store_true",
                     help="skip the per-candidate report (each tile height timed on its own after the timed steps)")
     cache = ap.add_mutually_exclusive_group()
@@ -386,10 +385,12 @@ def main():
                     help="tile height: auto = chosen on the device by the cost rule; exemplar = chosen on the "
                          "device by matching the histogram to the MI355X exemplar table (hysteresis 4096); "
                          "per-expert = 256-row tiles plus a remainder tile per expert sized 64/128/256")
-    ap.add_argument("--b-layout", choices=("auto", "kn", "nk"), default="auto",
+    ap.add_argument("--b-layout", choices=("auto", "kn", "nk", "kn-panel", "nk-panel"), default="auto",
                     help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE weights "
                          "are usually kept in; repacking is one-time, outside the timed steps).  auto: nk for "
-                         "the contiguous workloads, kn (as the masked workload prints it) for the masked one")
+                         "the contiguous workloads, kn (as the masked workload prints it) for the masked one.  "
+                         "kn-panel / nk-panel: the same weights repacked in column panels of the call's tile "
+                         "width, so that each K step's weight tile is one contiguous block (one-time repack)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -425,14 +426,23 @@ def main():
         args.cold = args.config != 1
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
+    # auto: K-contiguous [G,N,K] for the contiguous workloads; for the decode workload its [G,K,N] weights
+    # repacked once into 128-column panels, which it streams (fp4 weights come as [G,N,K/2] only)
     layout = args.b_layout if args.b_layout != "auto" else \
-        ("kn" if w.layout == "masked" and w.weights != "e2m1" else "nk")
+        ("kn-panel" if w.layout == "masked" and w.weights != "e2m1" else "nk")
     if w.weights == "e2m1" and layout != "nk":
         print("fp4 weights are stored [G,N,K/2] only", file=sys.stderr)
         sys.exit(2)
-    b_layout = mg.B_NK if layout == "nk" else mg.B_KN
+    b_layout = {"kn": mg.B_KN, "nk": mg.B_NK, "kn-panel": mg.B_KN_PANEL, "nk-panel": mg.B_NK_PANEL}[layout]
+    oracle_inp = dict(inp)                # the oracle reads the weights as drawn, [G, K, N]
     if b_layout == mg.B_NK and "B" in inp and w.weights != "e2m1":
         inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
+    elif b_layout in (mg.B_KN_PANEL, mg.B_NK_PANEL):
+        if w.weights == "e2m1" or w.layout == "k_grouped":
+            print("panel layouts apply to e4m3 / bf16 weights of the contiguous and masked workloads", file=sys.stderr)
+            sys.exit(2)
+        inp["B"] = mg.pack_panels(inp["B"], b_layout,
+                                  mg.PANEL_MASKED if w.layout == "masked" else mg.PANEL_CONTIGUOUS)
     torch.cuda.synchronize()
 
     # the tile height stays on the device: the timed step is the scheduler, then the GEMM with block_m = 0
@@ -503,8 +513,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "experts": w.G, "routed_rows": U,
                    "K": w.K or None, "N": w.N or None, "layout": w.layout, "seed": w.seed,
-                   "weights": ("[G,N,K/2] packed e2m1" if w.weights == "e2m1" else "[G,N,K]")
-                   if b_layout == mg.B_NK else "[G,K,N]",
+                   "weights": {mg.B_KN: "[G,K,N]", mg.B_KN_PANEL: "[G,N/P,K,P] column panels",
+                               mg.B_NK_PANEL: "[G,N/P,K/S,P,S] column panels by K step",
+                               mg.B_NK: "[G,N,K/2] packed e2m1" if w.weights == "e2m1" else "[G,N,K]"}[b_layout],
                    "scales": ("e8m0 (powers of two, applied by the MFMA)" if w.scales == "e8m0" else
                               "fp32, activation scales [K/128, rows]" if scale_km else "fp32")
                    if w.dtype == "fp8" else None,
@@ -544,7 +555,7 @@ def main():
     # after the timed steps: the other candidate heights, and the clock under this load
     if w.layout == "contiguous" and exemplars is None and not args.no_candidates:
         out["candidates"] = time_candidates(w, inp_gpu, b_layout, scale_km, args)
-    out["sclk"] = sample_sclk(lambda: (sched() if sched is not None else None, gemm()))
+    out["sclk"] = None if args.no_sclk else sample_sclk(lambda: (sched() if sched is not None else None, gemm()))
     out["host"] = host_info()
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 18                         # fp32 elements
@@ -556,7 +567,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
-        out["cpu_baseline"] = cpu_baseline(w, inp)
+        out["cpu_baseline"] = cpu_baseline(w, oracle_inp)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -75,8 +75,22 @@ typedef enum {
 /* How each expert's weight B_e is stored.
  *   MOEGG_B_KN: B[G, K, N], N contiguous.
  *   MOEGG_B_NK: B[G, N, K], K contiguous.
- * The fp8 block scales are [G, K/128, N/128] in both cases. */
-typedef enum { MOEGG_B_KN = 0, MOEGG_B_NK = 1 } moegg_b_layout_t;
+ *   MOEGG_B_KN_PANEL: B[G, N/P, K, P]: the columns in panels of P, each panel
+ *     K rows of P contiguous elements, panels back to back.
+ *   MOEGG_B_NK_PANEL: B[G, N/P, K/S, P, S], S = 128 bytes of K (64 bf16, 128
+ *     e4m3): each panel of P columns stored one K step at a time, so the
+ *     weights one tile loads per K step are one contiguous block.
+ * P is the column tile of the call: 256 for the contiguous and SwiGLU calls,
+ * 128 for the masked call.  The panel layouts are one-time weight repacks,
+ * like the choice between [G,K,N] and [G,N,K]; they change where a weight
+ * sits, not the arithmetic.  The fp8 block scales are [G, K/128, N/128] in
+ * every layout. */
+typedef enum {
+    MOEGG_B_KN = 0,
+    MOEGG_B_NK = 1,
+    MOEGG_B_KN_PANEL = 2,
+    MOEGG_B_NK_PANEL = 3
+} moegg_b_layout_t;
 
 /* error_flags bits */
 #define MOEGG_FLAG_NEGATIVE_COUNT  0x1u  /* a count < 0 was read as 0                 */

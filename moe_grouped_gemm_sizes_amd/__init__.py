@@ -22,7 +22,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moegg.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3, FP8_E4M3_E8M0, FP8_E4M3_FP4_E2M1, FP8_E4M3_SCALE_KM = 0, 1, 2, 3, 4
-B_KN, B_NK = 0, 1
+B_KN, B_NK, B_KN_PANEL, B_NK_PANEL = 0, 1, 2, 3
+PANEL_CONTIGUOUS, PANEL_MASKED = 256, 128     # panel width P of the contiguous / SwiGLU and the masked calls
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP, FLAG_BAD_EXEMPLAR = 0x1, 0x2, 0x4, 0x8
 FLAG_SCALE_GROUPS = 0x10
 Q_VALUES = (8, 16, 32, 64, 128, 256)
@@ -166,11 +167,11 @@ def _need(t: Optional[torch.Tensor], name: str, shape: Sequence[Optional[int]], 
     The library sees only pointers, so every extent it will index is checked here."""
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name}: tensor expected")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
     if t.dim() != len(shape) or any(x is not None and d != x for d, x in zip(t.shape, shape)):
         want = "[" + ", ".join("*" if x is None else str(x) for x in shape) + "]"
         raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
-    if t.dtype not in dtypes:
-        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
 
 
 def _none(t, name: str, why: str):
@@ -198,32 +199,68 @@ def _counts(t, name: str, G: Optional[int] = None):
         raise ValueError(f"{name}: at least one expert expected")
 
 
+def pack_panels(B: torch.Tensor, b_layout: int, P: int) -> torch.Tensor:
+    """Weights [G, K, N] -> the paneled layout the kernels stream (include/moegg.h):
+    B_KN_PANEL [G, N/P, K, P]; B_NK_PANEL [G, N/P, K/S, P, S] with S = 128 bytes of
+    K.  P: PANEL_CONTIGUOUS for the contiguous and SwiGLU calls, PANEL_MASKED for
+    the masked call.  A one-time weight transform."""
+    G, K, N = B.shape
+    if N % P:
+        raise ValueError(f"N = {N} is not a multiple of the panel width {P}")
+    if b_layout == B_KN_PANEL:
+        return B.reshape(G, K, N // P, P).permute(0, 2, 1, 3).contiguous()
+    if b_layout == B_NK_PANEL:
+        S = 128 // B.element_size()
+        if K % S:
+            raise ValueError(f"K = {K} is not a multiple of {S}")
+        return B.reshape(G, K // S, S, N // P, P).permute(0, 3, 1, 4, 2).contiguous()
+    raise ValueError(f"b_layout {b_layout} is not a panel layout")
+
+
+def _weight_n(B, K: int, G: int, b_layout: int, P: int, dtypes) -> int:
+    """N of weights B in layout b_layout, after checking B's shape against K and G."""
+    if b_layout == B_KN:
+        _need(B, "B", [G, K, None], dtypes)
+        return B.shape[2]
+    if b_layout == B_NK:
+        _need(B, "B", [G, None, K], dtypes)
+        return B.shape[1]
+    if b_layout == B_KN_PANEL:
+        _need(B, "B", [G, None, K, P], dtypes)
+        return B.shape[1] * P
+    if b_layout == B_NK_PANEL:
+        S = 128 // B.element_size()
+        _need(B, "B", [G, None, K // S, P, S], dtypes)
+        if K % S:
+            raise ValueError(f"K = {K}: the panel layout needs K % {S} == 0")
+        return B.shape[1] * P
+    raise ValueError(f"b_layout: {b_layout}")
+
+
 def _operands(rows: int, K: int, A, A_scale, B, B_scale, G: int, b_layout: int, scale_km: bool,
-              a_scale_rows_shape=None) -> Tuple[int, int]:
+              a_scale_rows_shape=None, P: int = PANEL_CONTIGUOUS) -> Tuple[int, int]:
     """Operand type code and N, after checking B, A_scale and B_scale against A's
     dtype, `rows` rows of K and G experts.  a_scale_rows_shape: the shape of a
     row-major fp32 activation-scale array ([rows, K/128] unless given).
     Formats (include/moegg.h): bf16 x bf16, no scales; e4m3 x e4m3 with fp32
     scales ([rows, K/128], or [K/128, rows] with scale_km) or E8M0 bytes
     ([K/128, rows]); e4m3 x packed E2M1 [G, N, K/2] (uint8) with E8M0 bytes."""
-    if b_layout not in (B_KN, B_NK):
+    if b_layout not in (B_KN, B_NK, B_KN_PANEL, B_NK_PANEL):
         raise ValueError(f"b_layout: {b_layout}")
     if A.dtype == torch.bfloat16:
-        _need(B, "B", [G, None, None], (torch.bfloat16,))
         _none(A_scale, "A_scale", "for bf16 operands")
         _none(B_scale, "B_scale", "for bf16 operands")
         if scale_km:
             raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
-        N = B.shape[2] if b_layout == B_KN else B.shape[1]
-        _need(B, "B", [G, K, N] if b_layout == B_KN else [G, N, K], (torch.bfloat16,))
-        return BF16, N
+        return BF16, _weight_n(B, K, G, b_layout, P, (torch.bfloat16,))
     if A.dtype != _E4M3:
         raise ValueError(f"A: bf16 or float8_e4m3fn expected, got {A.dtype}")
     if K % 128:
         raise ValueError(f"K = {K}: e4m3 operands need K % 128 == 0")
-    _need(B, "B", [G, None, None], (_E4M3, torch.uint8))
     if A_scale is None or B_scale is None:
         raise ValueError("e4m3 operands need A_scale and B_scale")
+    if not isinstance(B, torch.Tensor):
+        raise ValueError("B: tensor expected")
     if B.dtype == torch.uint8:                              # packed E2M1 weights [G, N, K/2]
         if b_layout != B_NK:
             raise ValueError("packed E2M1 weights are stored [G, N, K/2]: b_layout must be B_NK")
@@ -234,8 +271,7 @@ def _operands(rows: int, K: int, A, A_scale, B, B_scale, G: int, b_layout: int, 
         if scale_km:
             raise ValueError("scale_km applies to e4m3 operands with fp32 scales")
         return FP8_E4M3_FP4_E2M1, N
-    N = B.shape[2] if b_layout == B_KN else B.shape[1]
-    _need(B, "B", [G, K, N] if b_layout == B_KN else [G, N, K], (_E4M3,))
+    N = _weight_n(B, K, G, b_layout, P, (_E4M3,))
     if N % 128:
         raise ValueError(f"N = {N}: e4m3 operands need N % 128 == 0")
     if A_scale.dtype == torch.uint8:                        # E8M0 exponent bytes
@@ -383,14 +419,15 @@ def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor
 
 
 def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=None, block_m: int = 0,
-                                  H_scale=None, stream=None, scale_km: bool = False):
+                                  H_scale=None, stream=None, scale_km: bool = False, b_layout: int = B_NK):
     """H = silu(A W_gate) * (A W_up) per expert, from the tile list in ws (see moegg.h).
     H bf16 [rows, I]; or, with H_scale (fp32 [rows, I/128]), H float8_e4m3fn codes.
     scale_km: A_scale fp32 [K/128, rows] in, H_scale [I/128, rows] out."""
     _need(A, "A", [None, None], (torch.bfloat16, _E4M3))
     rows, K = A.shape
-    _need(W1, "W1", [G, None, None], (torch.bfloat16, _E4M3, torch.uint8))
-    code, N = _operands(rows, K, A, A_scale, W1, W1_scale, G, B_NK, scale_km)
+    if b_layout not in (B_NK, B_NK_PANEL):
+        raise ValueError("W1: [G, 2I, K] (B_NK) or its panels (B_NK_PANEL)")
+    code, N = _operands(rows, K, A, A_scale, W1, W1_scale, G, b_layout, scale_km)
     if N % 256:
         raise ValueError(f"W1: {N} interleaved gate/up rows, a multiple of 256 expected")
     I = N // 2
@@ -403,7 +440,7 @@ def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=N
     _one_device(A, A_scale, W1, W1_scale, H, H_scale, ws)
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
         _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, rows, K, I, code,
-        B_NK, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
+        b_layout, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
 
 
 def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, b_layout: int = B_KN,
@@ -414,7 +451,7 @@ def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, 
     G, cap, K = A.shape
     _counts(masked_m, "masked_m", G)
     code, N = _operands(G * cap, K, A, A_scale, B, B_scale, G, b_layout, scale_km,
-                        a_scale_rows_shape=[G, cap, K // 128])
+                        a_scale_rows_shape=[G, cap, K // 128], P=PANEL_MASKED)
     _need(C, "C", [G, cap, N], (torch.bfloat16,))
     if ws is not None:
         _ws(ws, G, G * cap)

@@ -37,6 +37,10 @@ moegg_status_t hip_status(hipError_t e, const char* what) {
     return MOEGG_ERR_HIP;
 }
 
+// Weight layouts: N-contiguous rows (plain or in column panels), and whether paneled.
+bool layout_kn(moegg_b_layout_t l) { return l == MOEGG_B_KN || l == MOEGG_B_KN_PANEL; }
+bool layout_panel(moegg_b_layout_t l) { return l == MOEGG_B_KN_PANEL || l == MOEGG_B_NK_PANEL; }
+
 // Block scales stored as E8M0 exponent bytes.
 bool e8m0_scales(moegg_dtype_t d) { return d == MOEGG_FP8_E4M3_E8M0 || d == MOEGG_FP8_E4M3_FP4_E2M1; }
 
@@ -57,14 +61,16 @@ moegg_status_t check_common(const void* A, const void* A_scale, const void* B, c
     if (dtype != MOEGG_BF16 && dtype != MOEGG_FP8_E4M3 && dtype != MOEGG_FP8_E4M3_E8M0 &&
         dtype != MOEGG_FP8_E4M3_FP4_E2M1 && dtype != MOEGG_FP8_E4M3_SCALE_KM)
         return MOEGG_ERR_INVALID_ARG;
-    if (b_layout != MOEGG_B_KN && b_layout != MOEGG_B_NK) return MOEGG_ERR_INVALID_ARG;
+    if (b_layout != MOEGG_B_KN && b_layout != MOEGG_B_NK && b_layout != MOEGG_B_KN_PANEL &&
+        b_layout != MOEGG_B_NK_PANEL)
+        return MOEGG_ERR_INVALID_ARG;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
     const bool w4 = dtype == MOEGG_FP8_E4M3_FP4_E2M1;
     if (dtype != MOEGG_BF16) {
         if (!A_scale || !B_scale) return MOEGG_ERR_INVALID_ARG;
         if (!aligned(A_scale, 4) || !aligned(B_scale, 4)) return MOEGG_ERR_INVALID_ARG;
     }
-    if (w4 && b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;      // packed E2M1 is K-contiguous
+    if (w4 && b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;      // packed E2M1 is [G, N, K/2] only
     // E8M0 scale rows are read four bytes at a time: N / 128 bytes per weight-scale row
     if (e8m0_scales(dtype) && (N % 512 != 0 || N / 128 > 256)) return MOEGG_ERR_UNSUPPORTED;
     if (K % (128 / esz) != 0 || N % col_tile != 0) return MOEGG_ERR_UNSUPPORTED;
@@ -177,8 +183,9 @@ moegg_status_t launch_contiguous_call(const void* A, const void* A_scale, const 
     if (e != hipSuccess) return hip_status(e, "scheduler launch");
     ContigArgs a{A, A_scale, B, B_scale, C, m_sizes, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
     a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
+    a.b_panel = layout_panel(b_layout);
     e = launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
-                          b_layout == MOEGG_B_KN, rows_total, block_m, s);
+                          layout_kn(b_layout), rows_total, block_m, s);
     if (debug_on())
         fprintf(stderr, "moegg: contiguous G=%d rows=%lld K=%d N=%d align=%d dtype=%d b_layout=%d block_m=%d\n", G,
                 (long long)rows_total, K, N, seg_align, (int)dtype, (int)b_layout, block_m);
@@ -276,8 +283,9 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(const void* A, const void
     if (ws_bytes < ws_layout(G, rows_total).total) return MOEGG_ERR_WORKSPACE;
     ContigArgs a{A, A_scale, B, B_scale, C, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total};
     a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
+    a.b_panel = layout_panel(b_layout);
     return hip_status(launch_contiguous(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
-                                        b_layout == MOEGG_B_KN, rows_total, block_m, (hipStream_t)stream),
+                                        layout_kn(b_layout), rows_total, block_m, (hipStream_t)stream),
                       "scheduled contiguous GEMM launch");
 }
 
@@ -295,7 +303,7 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     if (dtype == MOEGG_FP8_E4M3_FP4_E2M1 && rows_total % 4 != 0) return MOEGG_ERR_UNSUPPORTED;
     // A_scale [K/128, rows_total] in; with MOEGG_FP8_E4M3_SCALE_KM also H_scale [I/128, rows_total] out
     if (!transposed_scales_fit(dtype, std::max(K, I) / 128, rows_total)) return MOEGG_ERR_UNSUPPORTED;
-    if (b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;
+    if (b_layout != MOEGG_B_NK && b_layout != MOEGG_B_NK_PANEL) return MOEGG_ERR_UNSUPPORTED;
     if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
     if (!valid_block_m(block_m)) return MOEGG_ERR_UNSUPPORTED;
     const int esz = dtype == MOEGG_BF16 ? 2 : 1;
@@ -305,6 +313,7 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
     ContigArgs a{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, N, 0, (int)rows_total,
                  H_scale};
     a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
+    a.b_panel = layout_panel(b_layout);
     return hip_status(launch_contiguous_swiglu(a, dtype != MOEGG_BF16, dtype == MOEGG_FP8_E4M3_FP4_E2M1, rows_total,
                                                block_m, (hipStream_t)stream),
                       "SwiGLU GEMM launch");
@@ -335,8 +344,9 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     }
     ContigArgs a{A, A_scale, B, B_scale, C, masked_m, (const unsigned char*)ws, G, K, N, cap, G * cap};
     a.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
+    a.b_panel = layout_panel(b_layout);
     e = launch_masked(a, dtype != MOEGG_BF16, e8m0_scales(dtype), dtype == MOEGG_FP8_E4M3_FP4_E2M1,
-                      b_layout == MOEGG_B_KN, s);
+                      layout_kn(b_layout), s);
     return hip_status(e, "masked GEMM launch");
 }
 

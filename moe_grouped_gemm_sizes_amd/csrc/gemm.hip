@@ -327,8 +327,11 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 // barrier per step publishes the stage of step ks + 1.
 // The wave runs at raised priority (s_setprio) from the barrier to the end of
 // its MFMAs, so a SIMD's two waves drain their MFMA work ahead of the barrier.
-template <class C, bool B_KN>
+// WNT: the weight panel is read by this tile only, so its loads stream
+// (non-temporal); see load16_to_lds_cp.
+template <class C, bool B_KN, bool WNT = false>
 struct TileGemm {
+    static constexpr int WCP = WNT ? CP_NT : CP_DEFAULT;
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     static constexpr int HSEG = C::WTN / 2;                        // weight rows per wave column half
     static_assert(B_KN || C::W4 || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
@@ -337,6 +340,7 @@ struct TileGemm {
 
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
     uint32_t a_row_bytes, b_row_bytes, b_col_byte;
+    uint32_t b_step_bytes;     // K-contiguous weights: bytes between one K step's rows and the next's
     // fp32 activation scales: byte stride between tile rows and between K steps
     // ([rows, K/128]: K/128 * 4 and 4; [K/128, rows_total]: 4 and rows_total * 4)
     uint32_t sa_row_bytes, sa_step_bytes;
@@ -403,19 +407,19 @@ struct TileGemm {
             static_assert(!B_KN, "fp4 weights are K-contiguous");
             const int f = J * C::THREADS + tid;
             const int row = f >> 2;
-            load16_to_lds_so(rb, row * b_row_bytes + (((f & 3) ^ swz_w4(row)) << 4), ks * C::WROW,
+            load16_to_lds_cp<WCP>(rb, row * b_row_bytes + (((f & 3) ^ swz_w4(row)) << 4), ks * C::WROW,
                              base + (J * C::THREADS + wave * 64) * 16);
         } else if constexpr (B_KN) {
             constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
             const int r0 = tid / CPR;
             const int c = (tid % CPR) ^ swz_mn<C::ESZ, RB>(r0 + J * RPO);
-            load16_to_lds_so(rb, r0 * b_row_bytes + b_col_byte + c * 16, (ks * C::KSTEP + J * RPO) * b_row_bytes,
+            load16_to_lds_cp<WCP>(rb, r0 * b_row_bytes + b_col_byte + c * 16, (ks * C::KSTEP + J * RPO) * b_row_bytes,
                              base + (J * C::THREADS + wave * 64) * 16);
         } else {
             constexpr int h = J & 1, q = J >> 1, SPO = (C::THREADS / 8) / HSEG;
             auto row_of = [](int lr) { return (q * SPO + lr / HSEG) * C::WTN + h * HSEG + lr % HSEG; };
             const int row = row_of(tid >> 3);
-            load16_to_lds_so(rb, row * b_row_bytes + (((tid & 7) ^ swz_k<C::ESZ>(row)) << 4), ks * 128,
+            load16_to_lds_cp<WCP>(rb, row * b_row_bytes + (((tid & 7) ^ swz_k<C::ESZ>(row)) << 4), ks * b_step_bytes,
                              base + row_of(wave * 8) * 128);
         }
     }
@@ -523,16 +527,30 @@ struct TileGemm {
 #pragma unroll
                 for (int b = 0; b < NSB; ++b) s[b][j] = as * bsc[b];
             }
-            v4f p[MBA];
-            static_for<0, C::NB>([&](auto I) {
+            // Software-pipelined promotion: block i's MFMAs are interleaved with the
+            // promotion of block i - 1's partials, which finished a block earlier, so
+            // the four FMAs that follow each MFMA never wait on a result and run on
+            // the VALU while the MFMA occupies the matrix pipe.  Each accumulator
+            // still receives the same products in the same order.
+            v4f p[2][MBA];
+            static_for<0, C::NB + 1>([&](auto I) {
                 constexpr int i = decltype(I)::value;
+                constexpr int ip = i - 1;                               // block promoted now
+                constexpr int sbp = ip >= 0 && NSB > 1 ? ip * 16 / 128 : 0;
                 if constexpr (i + 1 < C::NB) xb[(i + 1) & 1] = fragb(i + 1);
 #pragma unroll
-                for (int j = 0; j < MBA; ++j) p[j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int j = 0; j < MBA; ++j) {
+                    if constexpr (i < C::NB) p[i & 1][j] = mfma_fp8(xb[i & 1], ya[j], v4f{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (ip >= 0) promote(acc[ip][j], p[ip & 1][j], s[sbp][j]);
+                }
                 if constexpr (i == 0) issue_all(wr, next);
-                constexpr int sb = NSB > 1 ? i * 16 / 128 : 0;
+                if constexpr (i > 0 && i < C::NB) {
 #pragma unroll
-                for (int j = 0; j < MBA; ++j) promote(acc[i][j], p[j], s[sb][j]);
+                    for (int j = 0; j < MBA; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // then four VALU ops
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {
@@ -769,12 +787,12 @@ struct TileGemm {
 
 // One output tile: rows [row_start, row_start + rows_valid) of expert e's
 // segment, column tile ct.
-template <class C, bool B_KN, int SWIGLU = 0>
+template <class C, bool B_KN, int SWIGLU = 0, bool WNT = false>
 __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows_valid,
                                             int ct) {
     const int n0 = ct * C::BN;
     const int KB = p.K / 128;
-    TileGemm<C, B_KN> tg;
+    TileGemm<C, B_KN, WNT> tg;
     tg.a_row_bytes = (uint32_t)p.K * C::ESZ;
     tg.ra = make_rsrc((const char*)p.A + (size_t)row_start * tg.a_row_bytes, (uint32_t)rows_valid * tg.a_row_bytes);
     const size_t b_expert_bytes = C::W4 ? (size_t)p.K * p.N / 2 : (size_t)p.K * p.N * C::ESZ;
@@ -785,12 +803,26 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
         tg.rb = make_rsrc(b_base + (size_t)n0 * tg.b_row_bytes, (uint32_t)C::BN * tg.b_row_bytes);
         tg.b_col_byte = 0;
     } else if constexpr (B_KN) {
-        tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
-        tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
-        tg.b_col_byte = (uint32_t)n0 * C::ESZ;
+        if (p.b_panel) {
+            // [G, N / BN, K, BN]: this column tile's panel, K rows of BN columns back to back
+            tg.rb = make_rsrc(b_base + (size_t)ct * p.K * C::BN * C::ESZ, (uint32_t)p.K * C::BN * C::ESZ);
+            tg.b_row_bytes = (uint32_t)C::BN * C::ESZ;
+            tg.b_col_byte = 0;
+        } else {
+            tg.rb = make_rsrc(b_base, (uint32_t)b_expert_bytes);
+            tg.b_row_bytes = (uint32_t)p.N * C::ESZ;
+            tg.b_col_byte = (uint32_t)n0 * C::ESZ;
+        }
     } else {
         tg.rb = make_rsrc(b_base + (size_t)n0 * p.K * C::ESZ, (uint32_t)C::BN * p.K * C::ESZ);
-        tg.b_row_bytes = (uint32_t)p.K * C::ESZ;
+        if (p.b_panel) {
+            // [G, N / BN, K / KSTEP, BN, KSTEP]: one K step of the column tile's BN rows back to back
+            tg.b_row_bytes = 128;
+            tg.b_step_bytes = (uint32_t)C::BN * 128;
+        } else {
+            tg.b_row_bytes = (uint32_t)p.K * C::ESZ;
+            tg.b_step_bytes = 128;
+        }
         tg.b_col_byte = 0;
     }
     tg.rsa = tg.rb;
@@ -866,6 +898,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
         ct = blockIdx.x - e * n_ct;
         if (e >= p.G) return;
         const int m = min(max(p.counts[e], 0), p.cap);
+        if (m == 0) return;
+        if (m <= C::BM) {
+            // one row tile: the weight panel is read once, so it streams
+            contig_tile<C, B_KN, 0, true>(p, lds, e, e * p.cap, m, ct);
+            return;
+        }
 #pragma unroll 1
         for (int rt = 0; rt * C::BM < m; ++rt) {
             if (rt > 0) __syncthreads();         // the previous tile's LDS is free
@@ -918,13 +956,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_auto_kernel(ContigArgs p)
     int rt, ct;
     item_to_tiles(item, n_rt, n_ct, rt, ct);
     const moegg_tile_t t = tiles[rt];
-    const int h = bm == MOEGG_BLOCK_M_PER_EXPERT ? (t.rows_valid > 128 ? 256 : t.rows_valid > 64 ? 128 : 64) : bm;
-    if (h == 256)
+    if (bm == MOEGG_BLOCK_M_PER_EXPERT) {
+        // the per-expert list runs every expert's tail (1..128 rows) after all full tiles, so the
+        // tail's weight panel is read once more by that tile alone: it streams
+        if (t.rows_valid > 128)
+            contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        else if (t.rows_valid > 64)
+            contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        else
+            contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    } else if (bm == 256) {
         contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else if (h == 128)
+    } else if (bm == 128) {
         contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    else
+    } else {
         contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+    }
 }
 
 // ---------------------------------------------------------------- K-grouped

@@ -21,6 +21,7 @@ struct ContigArgs {
     void* C_scale;                // SwiGLU with e4m3 output: fp32 [rows_total, N / 256] scales, else NULL
     int a_scale_km;               // fp32 activation scales (and C_scale) stored [K/128, rows_total]
     int req_block_m;              // contiguous: height the caller asked for (0 = whatever the schedule chose)
+    int b_panel;                  // weights stored in column panels of the kernel's tile width (see moegg.h)
 };
 
 struct KGroupedArgs {

@@ -62,7 +62,7 @@ def contiguous(**kw):
     (dict(K=100), mg.ERR_UNSUPPORTED),
     (dict(N=200), mg.ERR_UNSUPPORTED),
     (dict(dtype=7), mg.ERR_INVALID_ARG),
-    (dict(layout=3), mg.ERR_INVALID_ARG),
+    (dict(layout=7), mg.ERR_INVALID_ARG),
     (dict(dtype=mg.FP8_E4M3), mg.ERR_INVALID_ARG),                 # fp8 without scales
     (dict(dtype=mg.FP8_E4M3, A_scale=FAKE, B_scale=FAKE, K=192), mg.ERR_UNSUPPORTED),
     (dict(dtype=mg.FP8_E4M3_SCALE_KM), mg.ERR_INVALID_ARG),         # transposed fp32 scales, none given

@@ -181,3 +181,33 @@ def test_schedule_checks_counts_and_workspace():
 
 def test_k_scale_groups():
     assert mg.k_scale_groups([0, 1, 128, 129, 256, -5]) == 0 + 1 + 1 + 2 + 2 + 0
+
+
+def test_pack_panels_index_mapping():
+    """pack_panels places B[e, k, n] where the panel layouts say (checked element by element)."""
+    G, K, N = 2, 256, 512
+    B = torch.arange(G * K * N, dtype=torch.int64).reshape(G, K, N)
+    kn = mg.pack_panels(B, mg.B_KN_PANEL, 256)
+    assert kn.shape == (G, N // 256, K, 256)
+    for e, k, n in [(0, 0, 0), (1, 255, 511), (0, 17, 300), (1, 128, 255), (1, 3, 256)]:
+        assert kn[e, n // 256, k, n % 256] == B[e, k, n]
+    Bh = B.to(torch.int16)                                   # 2-byte elements: S = 64
+    nk = mg.pack_panels(Bh, mg.B_NK_PANEL, 128)
+    assert nk.shape == (G, N // 128, K // 64, 128, 64)
+    for e, k, n in [(0, 0, 0), (1, 255, 511), (0, 70, 300), (1, 191, 129)]:
+        assert nk[e, n // 128, k // 64, n % 128, k % 64] == Bh[e, k, n]
+    B8 = B.to(torch.uint8)                                   # 1-byte elements: S = 128
+    nk8 = mg.pack_panels(B8, mg.B_NK_PANEL, 256)
+    assert nk8.shape == (G, N // 256, K // 128, 256, 128)
+    assert nk8[1, 1, 1, 7, 5] == B8[1, 128 + 5, 256 + 7]
+
+
+def test_panel_shapes_are_checked():
+    kw = contiguous_args("bf16")
+    kw["b_layout"] = mg.B_KN_PANEL
+    kw["B"] = t(G, N // 256, K, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor expected"):
+        call_contiguous(kw)
+    kw["B"] = t(G, N // 128, K, 128, dtype=torch.bfloat16)     # masked panel width on a contiguous call
+    with pytest.raises(ValueError, match="B: shape"):
+        call_contiguous(kw)

@@ -1281,3 +1281,102 @@ def test_k_grouped_maximum_expert_count(dtype):
     assert not dW[empty].any()
     st = mg.stats_read(ws)
     assert st.U == sum(t) and st.active == sum(1 for x in t if x) and st.error_flags == 0
+
+
+# ----------------------------------------------------------------- weights in column panels
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("b_layout", [mg.B_KN_PANEL, mg.B_NK_PANEL])
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+def test_contiguous_panel_layouts(dtype, b_layout, block_m):
+    """The same weights repacked in 256-column panels: every valid row against the
+    oracle (which reads them as [G, K, N]); rows outside segments untouched."""
+    counts = [300, 0, 17, 513, 64, 1]
+    announce("contiguous panels", dtype, b_layout, block_m, counts)
+    w, inp = small_contig(counts, 512, 768, dtype)
+    B = mg.pack_panels(inp["B"], b_layout, mg.PANEL_CONTIGUOUS)
+    C = P.sentinel_like((w.rows_total, w.N))
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.grouped_gemm_contiguous(inp["A"], B, C, inp["counts"], ws, A_scale=inp.get("A_scale"),
+                               B_scale=inp.get("B_scale"), block_m=block_m, b_layout=b_layout)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), counts)
+    rows = list(range(w.rows_total))
+    ref = P.oracle_contiguous_rows(w, {k: P.cpu(v) for k, v in inp.items()}, rows)
+    valid = ~np.isnan(ref[:, 0])
+    P.check_gemm(P.rows_as_float(C, rows)[valid], ref[valid], dtype, what=f"panels {dtype} {b_layout} {block_m}")
+    assert P.untouched_rows_ok(C, counts, 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("b_layout", [mg.B_KN_PANEL, mg.B_NK_PANEL])
+def test_masked_panel_layouts(dtype, b_layout):
+    """128-column panels in the masked layout, with experts of one row tile (weights
+    streamed) and of several (64, 65, 130 rows)."""
+    counts = [3, 0, 64, 65, 130, 1]
+    announce("masked panels", dtype, b_layout, counts)
+    w, inp = masked_case(counts, 160, 512, 256, dtype)
+    B = mg.pack_panels(inp["B"], b_layout, mg.PANEL_MASKED)
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], None, inp.get("A_scale"), inp.get("B_scale"), b_layout)
+    torch.cuda.synchronize()
+    check_masked(w, inp, C, counts)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_masked_panel_full_size(dtype):
+    """The decode workload (32 experts, cap 256, K 2048, N 7168) with weights in
+    128-column panels, as the benchmark runs it: every valid row."""
+    w0 = wl.workload(4)
+    announce("masked panels full size", dtype)
+    w = wl.Workload("masked " + dtype, "masked", dtype, w0.counts, K=w0.K, N=w0.N, cap=w0.cap, seed=w0.seed)
+    inp = wl.materialize(w, "cuda")
+    B = mg.pack_panels(inp["B"], mg.B_KN_PANEL, mg.PANEL_MASKED)
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, inp.get("A_scale"), inp.get("B_scale"),
+                           mg.B_KN_PANEL)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), w.counts)
+    check_masked(w, inp, C, w.counts)
+
+
+def test_contiguous_panel_full_size():
+    """The Zipf fp8 workload with weights in K-step panels, device-chosen height:
+    one row from every 16-row block of every expert segment."""
+    w = wl.workload(3)
+    announce("contiguous nk panels full size", w.name)
+    inp = wl.materialize(w, "cuda")
+    B = mg.pack_panels(inp["B"], mg.B_NK_PANEL, mg.PANEL_CONTIGUOUS)
+    C = P.sentinel_like((w.rows_total, w.N))
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.grouped_gemm_contiguous(inp["A"], B, C, inp["counts"], ws, A_scale=inp["A_scale"], B_scale=inp["B_scale"],
+                               b_layout=mg.B_NK_PANEL)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), w.counts)
+    rows = full_size_rows(w)
+    ref = full_size_ref(w, inp, rows)
+    del inp
+    P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what="nk panels full size")
+    assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_swiglu_panel_layout(dtype):
+    """L1 with the SwiGLU epilogue reading W1 in K-step panels, bit for bit the
+    [G, 2I, K] result."""
+    counts = [70, 0, 300, 6, 129, 3]
+    K, I, N2 = 256, 256, 512
+    G, R = len(counts), sum(counts)
+    announce("swiglu panels", dtype, counts)
+    inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype=dtype, seed=12, device="cuda")
+    ws = mg.workspace(G, R)
+    mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
+    H0, H1 = P.sentinel_like((R, I)), P.sentinel_like((R, I))
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H0, G, ws, inp["A_scale"], inp["W1_scale"])
+    W1p = mg.pack_panels(inp["W1"].transpose(1, 2).contiguous(), mg.B_NK_PANEL, mg.PANEL_CONTIGUOUS)
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], W1p, H1, G, ws, inp["A_scale"], inp["W1_scale"],
+                                     b_layout=mg.B_NK_PANEL)
+    torch.cuda.synchronize()
+    assert torch.equal(H0.view(torch.int16), H1.view(torch.int16))
