@@ -297,6 +297,8 @@ def run_mlp(args):
     def l2():
         mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=bm,
                                              b_layout=mg.B_NK, scale_km=km_l2)
+    if args.mlp_fused:
+        return run_mlp_fused(args, inp, counts, K, I, N2, a_s, w1_s, km_l1, ws, H, Hs, Y)
     for _ in range(args.warmup):
         sched(); l1(); l2()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -342,6 +344,67 @@ def run_mlp(args):
     print(json.dumps(out), flush=True)
 
 
+def run_mlp_fused(args, inp, counts, K, I, N2, a_s, w1_s, km, ws, H, Hs, Y):
+    """The expert MLP in one persistent launch (moegg_expert_mlp_fused: scheduler, sync clear, one kernel with
+    both GEMMs), and beside it the same work as three launches from the same 256-row schedule, each timed
+    cold over the same steps."""
+    G, R = len(counts), sum(counts)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        mg.expert_mlp_fused(inp["A"], inp["W1"], inp["W2"], H, Y, inp["counts"], ws, a_s, w1_s, inp["W2_scale"],
+                            Hs, scale_km=km)
+
+    def chain():
+        mg.schedule(inp["counts"], R, ws, block_m=256, N=2 * I)
+        mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, a_s, w1_s, block_m=256, H_scale=Hs,
+                                         scale_km=km)
+        mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=256,
+                                             b_layout=mg.B_NK, scale_km=km)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scratch.fill_(i & 255)
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    t_wall = time.perf_counter()
+    ms = timed(fused)
+    wall = time.perf_counter() - t_wall
+    st = mg.stats_read(ws)
+    if st.error_flags:
+        raise RuntimeError(f"fused expert MLP: error flags {st.error_flags:#x}")
+    chain_ms = timed(chain)
+    f1, f2 = 2.0 * R * K * 2 * I, 2.0 * R * I * N2
+    tf = (f1 + f2) / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "effective TFLOPS (valid rows), expert MLP L1 -> SwiGLU -> L2 in one launch",
+        "value": round(tf, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "zipf 64 experts expert MLP (L1 fp8 + SwiGLU, e4m3 H, L2 fp8), one launch",
+                   "experts": G, "routed_rows": R, "K": K, "I": I, "N2": N2, "layout": "contiguous", "seed": 3,
+                   "weights": "W1 [G,2I,K] gate/up interleaved, W2 [G,N2,I]",
+                   "scales": "[K/128, rows]" if km else "[rows, K/128]",
+                   "cache": "cold (512 MiB written between steps)"},
+        "block_m": 256,
+        "three_launch_ms_block_m_256": round(chain_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK["fp8"], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK["fp8"], 4), "traffic": None,
+                     "kernel": "fused expert MLP (both GEMMs; scheduler and sync clear included)"},
+        "wall_s_timed": round(wall, 4), "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +438,9 @@ def main():
                          "Zipf histogram at the DeepSeek-V3 expert shape instead of one grouped GEMM")
     ap.add_argument("--a-scale", choices=("km", "rows"), default="km",
                     help="fp32 activation-scale layout for fp8: [K/128, rows] (default) or [rows, K/128]")
+    ap.add_argument("--mlp-fused", action="store_true",
+                    help="with --mlp: the expert MLP in one persistent launch (fp8 H), timed beside the same "
+                         "work as three launches from the 256-row schedule")
     ap.add_argument("--mlp-h", choices=("fp8", "bf16"), default="fp8",
                     help="with --mlp: H quantized to e4m3 in L1's epilogue and an fp8 L2 (default), or bf16 H and L2")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -400,6 +466,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     mg.lib()
+    if args.mlp_fused and (not args.mlp or args.mlp_h != "fp8" or args.weights != "e4m3"):
+        print("--mlp-fused goes with --mlp, fp8 H and e4m3 weights", file=sys.stderr)
+        sys.exit(2)
     if args.mlp:
         run_mlp(args)
         return

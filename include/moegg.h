@@ -100,6 +100,9 @@ typedef enum {
 #define MOEGG_FLAG_SCALE_GROUPS    0x10u /* K-grouped fp8: the histogram needs more scale
                                             groups than the scale arrays hold; the
                                             missing groups' scales read as 0           */
+#define MOEGG_FLAG_SYNC_TIMEOUT    0x20u /* fused expert MLP: a down-projection tile gave up
+                                            waiting for its H rows (bounded wait); its
+                                            output rows are unspecified               */
 
 /* block_m value for per-expert tile heights: every expert gets 256-row tiles,
  * and its remainder rows one tile of the smallest height in {64, 128, 256}
@@ -397,6 +400,47 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
     const void* A, const void* A_scale, const void* W1, const void* W1_scale, void* H, void* H_scale,
     int G, int64_t rows_total, int K, int I, moegg_dtype_t dtype, moegg_b_layout_t b_layout,
     int block_m, const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert MLP in one launch: the SwiGLU projection and the down projection of
+ * every expert in one persistent kernel (the DeepGEMM record's "Arithmetic
+ * intensity" section: Mega MoE fuses linear 1, SwiGLU and linear 2 so the
+ * activations between them need not round-trip HBM; the dispatch and combine
+ * it also fuses are inter-GPU and not part of this call).  It computes
+ * exactly what moegg_grouped_gemm_contiguous with block_m = 256 (scheduler),
+ * moegg_grouped_gemm_swiglu_scheduled (H = SwiGLU projection, e4m3 H with fp32
+ * scales) and moegg_grouped_gemm_contiguous_scheduled on H compute in turn,
+ * bit for bit, from one stream-ordered call:
+ *   A        e4m3 [rows_total, K], A_scale fp32 [rows_total, K/128]
+ *            (MOEGG_FP8_E4M3_SCALE_KM: [K/128, rows_total]).
+ *   W1       e4m3 [G, 2I, K] with gate/up rows interleaved as for the SwiGLU
+ *            call, W1_scale fp32 [G, K/128, 2I/128].
+ *   W2       e4m3 [G, N2, I], W2_scale fp32 [G, I/128, N2/128].
+ *            b_layout: MOEGG_B_NK for both weights, or MOEGG_B_NK_PANEL with
+ *            P = 256 for both.
+ *   H        e4m3 [rows_total, I], H_scale fp32 [rows_total, I/128]
+ *            (SCALE_KM: [I/128, rows_total]): caller-owned intermediate,
+ *            written and read back by the kernel; valid rows hold the SwiGLU
+ *            call's output afterwards.
+ *   Y        bf16 [rows_total, N2]: valid rows = H W2 per expert (fp32
+ *            accumulation, one bf16 rounding); other rows untouched.
+ *   m_sizes, G, rows_total, seg_align: as for the contiguous call (the tile
+ *            list is always 256 rows tall).
+ *   dtype    MOEGG_FP8_E4M3 or MOEGG_FP8_E4M3_SCALE_KM (else UNSUPPORTED).
+ *   ws       moegg_workspace_bytes(G, rows_total), 256-byte aligned; also
+ *            holds the row tiles' completion counters and work queues.
+ * Constraints: K % 128 == 0, I % 128 == 0, N2 % 256 == 0, every pointer
+ * 16-byte aligned (scales 4).  One workgroup per compute unit; a row tile's
+ * down-projection tiles wait (bounded) for all of its SwiGLU tiles.  A wait
+ * that exceeds its bound sets MOEGG_FLAG_SYNC_TIMEOUT in the stats (the
+ * affected Y rows are then unspecified); moegg_stats_read shows it.  Calls that
+ * share ws must not overlap.
+ */
+moegg_status_t moegg_expert_mlp_fused(
+    const void* A, const float* A_scale, const void* W1, const float* W1_scale, const void* W2,
+    const float* W2_scale, void* H, float* H_scale, void* Y, const int32_t* m_sizes, int G,
+    int64_t rows_total, int K, int I, int N2, int seg_align, moegg_dtype_t dtype,
+    moegg_b_layout_t b_layout, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Masked layout for decode under graph capture (DeepGEMM record,

@@ -26,6 +26,7 @@ B_KN, B_NK, B_KN_PANEL, B_NK_PANEL = 0, 1, 2, 3
 PANEL_CONTIGUOUS, PANEL_MASKED = 256, 128     # panel width P of the contiguous / SwiGLU and the masked calls
 FLAG_NEGATIVE_COUNT, FLAG_ROWS_OVERFLOW, FLAG_COUNT_OVER_CAP, FLAG_BAD_EXEMPLAR = 0x1, 0x2, 0x4, 0x8
 FLAG_SCALE_GROUPS = 0x10
+FLAG_SYNC_TIMEOUT = 0x20
 Q_VALUES = (8, 16, 32, 64, 128, 256)
 BLOCK_M_PER_EXPERT = -1          # per-expert tile heights (include/moegg.h)
 
@@ -114,6 +115,8 @@ EXPORTS = {
                                                      _I32, _I32, _I32, _VP]),
     "moegg_grouped_gemm_swiglu_scheduled": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I32,
                                                    _I32, _I32, _VP, _SZ, _VP]),
+    "moegg_expert_mlp_fused": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32,
+                                      _I32, _I32, _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_masked": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                          _VP, _SZ, _VP]),
     "moegg_grouped_gemm_k_grouped": (_I32, [_VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _VP, _SZ, _VP]),
@@ -441,6 +444,36 @@ def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=N
     _check(lib().moegg_grouped_gemm_swiglu_scheduled(
         _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(H), _p(H_scale), G, rows, K, I, code,
         b_layout, block_m, _p(ws), ws.numel(), _stream(stream)), "moegg_grouped_gemm_swiglu_scheduled")
+
+
+def expert_mlp_fused(A, W1, W2, H, Y, m_sizes, ws, A_scale, W1_scale, W2_scale, H_scale, seg_align: int = 1,
+                     b_layout: int = B_NK, scale_km: bool = False, stream=None):
+    """Y = SwiGLU(A W1) W2 per expert in one persistent launch (see moegg.h): e4m3 A [rows, K], W1
+    [G, 2I, K] (gate/up interleaved), W2 [G, N2, I], fp32 scales; H e4m3 [rows, I] with H_scale the
+    caller's intermediate, written and read back by the kernel; Y bf16 [rows, N2].  b_layout B_NK or
+    B_NK_PANEL (P = PANEL_CONTIGUOUS) for both weights; scale_km: A_scale [K/128, rows] in and
+    H_scale [I/128, rows]."""
+    _need(A, "A", [None, None], (_E4M3,))
+    rows, K = A.shape
+    if b_layout not in (B_NK, B_NK_PANEL):
+        raise ValueError("W1, W2: [G, N, K] (B_NK) or its panels (B_NK_PANEL)")
+    _counts(m_sizes, "m_sizes")
+    G = m_sizes.numel()
+    code, N = _operands(rows, K, A, A_scale, W1, W1_scale, G, b_layout, scale_km)
+    if N % 256:
+        raise ValueError(f"W1: {N} interleaved gate/up rows, a multiple of 256 expected")
+    I = N // 2
+    _need(H, "H", [rows, I], (_E4M3,))
+    code2, N2 = _operands(rows, I, H, H_scale, W2, W2_scale, G, b_layout, scale_km)
+    if code2 != code or N2 % 256:
+        raise ValueError(f"W2: e4m3 [G, N2, I] with N2 % 256 == 0 expected, got N2 = {N2}")
+    _need(Y, "Y", [rows, N2], (torch.bfloat16,))
+    _ws(ws, G, rows)
+    _one_device(A, A_scale, W1, W1_scale, W2, W2_scale, H, H_scale, Y, m_sizes, ws)
+    _check(lib().moegg_expert_mlp_fused(
+        _p(A), _p(A_scale), _p(W1), _p(W1_scale), _p(W2), _p(W2_scale), _p(H), _p(H_scale), _p(Y),
+        _p(m_sizes), G, rows, K, I, N2, seg_align, code, b_layout, _p(ws), ws.numel(), _stream(stream)),
+        "moegg_expert_mlp_fused")
 
 
 def grouped_gemm_masked(A, B, C, masked_m, ws=None, A_scale=None, B_scale=None, b_layout: int = B_KN,

@@ -319,6 +319,57 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(const void* A, const void* A_
                       "SwiGLU GEMM launch");
 }
 
+moegg_status_t moegg_expert_mlp_fused(const void* A, const float* A_scale, const void* W1, const float* W1_scale,
+                                     const void* W2, const float* W2_scale, void* H, float* H_scale, void* Y,
+                                     const int32_t* m_sizes, int G, int64_t rows_total, int K, int I, int N2,
+                                     int seg_align, moegg_dtype_t dtype, moegg_b_layout_t b_layout, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    if (!m_sizes || !aligned(m_sizes, 4) || seg_align < 1) return MOEGG_ERR_INVALID_ARG;
+    if (I < 1 || (int64_t)I * 2 > INT32_MAX || N2 < 1) return MOEGG_ERR_INVALID_ARG;
+    if (dtype != MOEGG_FP8_E4M3 && dtype != MOEGG_FP8_E4M3_SCALE_KM) return MOEGG_ERR_UNSUPPORTED;
+    if (b_layout != MOEGG_B_NK && b_layout != MOEGG_B_NK_PANEL) return MOEGG_ERR_UNSUPPORTED;
+    if (!H_scale || !aligned(H_scale, 4)) return MOEGG_ERR_INVALID_ARG;
+    if (rows_total < 0 || rows_total > INT32_MAX) return MOEGG_ERR_INVALID_ARG;
+    // L1: A [rows, K] x W1 [G, 2I, K] -> H; L2: H [rows, I] x W2 [G, N2, I] -> Y
+    moegg_status_t st = check_common(A, A_scale, W1, W1_scale, H, G, K, 2 * I, dtype, b_layout, 256);
+    if (st != MOEGG_OK) return st;
+    st = check_common(H, H_scale, W2, W2_scale, Y, G, I, N2, dtype, b_layout, 256);
+    if (st != MOEGG_OK) return st;
+    if (!transposed_scales_fit(dtype, std::max(K, I) / 128, rows_total)) return MOEGG_ERR_UNSUPPORTED;
+    if (256ll * std::max(K, I) > kMaxBufferBytes || 256ll * std::max(2 * I, 2 * N2) > kMaxBufferBytes)
+        return MOEGG_ERR_UNSUPPORTED;
+    if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
+    const WsLayout L = ws_layout(G, rows_total);
+    if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
+    if (((rows_total + 255) / 256 + G) * (int64_t)(2 * I / 256 + N2 / 256) > INT32_MAX) return MOEGG_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e, "device query");
+    e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, 256, 2 * I / 256, 0, ws, L.max_tiles, s);
+    if (e != hipSuccess) return hip_status(e, "scheduler launch");
+    uint32_t* sync = (uint32_t*)((unsigned char*)ws + L.sync);
+    e = launch_zero(sync, L.max_tiles + kSyncExtra, s);
+    if (e != hipSuccess) return hip_status(e, "sync clear launch");
+    MlpArgs a{};
+    a.l1 = ContigArgs{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, 2 * I, 0,
+                      (int)rows_total, H_scale};
+    a.l2 = ContigArgs{H, H_scale, W2, W2_scale, Y, nullptr, (const unsigned char*)ws, G, I, N2, 0, (int)rows_total};
+    a.l1.a_scale_km = a.l2.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
+    a.l1.b_panel = a.l2.b_panel = layout_panel(b_layout);
+    a.sync = sync;
+    a.max_tiles = (int)L.max_tiles;
+    a.n_queues = std::min(std::max(cus / 32, 1), kSyncExtra);
+    // one workgroup per work item: at most ceil(rows_total / 256) + G row tiles, each with 2I/256 + N2/256 items
+    const int64_t items = ((rows_total + 255) / 256 + G) * (int64_t)(2 * I / 256 + N2 / 256);
+    e = launch_mlp_fused(a, (int)std::min<int64_t>(items, INT32_MAX), s);
+    if (debug_on())
+        fprintf(stderr, "moegg: expert MLP fused G=%d rows=%lld K=%d I=%d N2=%d dtype=%d b_layout=%d CUs=%d\n", G,
+                (long long)rows_total, K, I, N2, (int)dtype, (int)b_layout, cus);
+    return hip_status(e, "fused expert MLP launch");
+}
+
 moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, const void* B, const void* B_scale,
                                          void* C, const int32_t* masked_m, int G, int cap, int K, int N,
                                          moegg_dtype_t dtype, moegg_b_layout_t b_layout, void* ws,

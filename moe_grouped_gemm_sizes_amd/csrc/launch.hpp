@@ -24,6 +24,15 @@ struct ContigArgs {
     int b_panel;                  // weights stored in column panels of the kernel's tile width (see moegg.h)
 };
 
+// Expert MLP in one persistent launch: l1 is the SwiGLU projection (C = H,
+// C_scale = H_scale, N = 2I), l2 the down projection on H (A = H, K = I, N = N2).
+struct MlpArgs {
+    ContigArgs l1, l2;
+    uint32_t* sync;               // per-row-tile completion counters [max_tiles], then the queue heads
+    int max_tiles;
+    int n_queues;                 // one work queue per XCD
+};
+
 struct KGroupedArgs {
     const void* X;
     const void* dY;
@@ -58,6 +67,11 @@ hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int6
                                     hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, hipStream_t s);
+// n_words 32-bit zeros at p (a fill kernel: graph-capturable, no memset node)
+hipError_t launch_zero(uint32_t* p, int64_t n_words, hipStream_t s);
+// the fused expert MLP on fp8 operands (e4m3 A, W1, H, W2 with fp32 scales); one workgroup per
+// work item, n_workgroups at least the items the schedule can produce
+hipError_t launch_mlp_fused(const MlpArgs& a, int n_workgroups, hipStream_t s);
 int masked_block_m();
 int masked_block_n();
 

@@ -6,7 +6,10 @@
 //   [...]       int32 order[G]        (K-grouped: experts, longest first)
 //   [...]       int64 groups[G + 1]   (K-grouped fp8: first 128-row scale group of each expert)
 //   [...]       moegg_tile_t tiles[max_tiles]
-// Every region starts on a 256-byte boundary.
+//   [...]       uint32 sync[max_tiles + 16]   (fused expert MLP: per-row-tile completion counters, then
+//                                              one queue head per XCD)
+// Every region starts on a 256-byte boundary.  The regions up to `tiles` depend
+// on G alone; `sync` follows the tile list, so its offset also depends on max_rows.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -19,6 +22,7 @@ constexpr int kMaxExperts = 4096;
 constexpr int kMinBlockM = 64;     // smallest schedulable tile height
 constexpr int kExecRows = 16;      // MFMA row block: rows are executed in 16s
 constexpr int kNumCand = 3;        // candidate tile heights 64, 128, 256
+constexpr int kSyncExtra = 16;     // sync words past the per-tile counters: queue heads
 
 // Tag of a valid exemplar-selector state in the control block.
 constexpr uint64_t kSelectorTag = 0x4D4F454753454C31ull;
@@ -44,7 +48,7 @@ static_assert(sizeof(Control) == 128, "control block");
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-    size_t stats, control, offsets, order, groups, tiles, total;
+    size_t stats, control, offsets, order, groups, tiles, sync, total;
     int64_t max_tiles;
 };
 
@@ -57,7 +61,8 @@ __host__ __device__ inline WsLayout ws_layout(int G, int64_t max_rows) {
     L.groups = L.order + align256(sizeof(int32_t) * (size_t)G);
     L.tiles = L.groups + align256(sizeof(int64_t) * (size_t)(G + 1));
     L.max_tiles = (max_rows + kMinBlockM - 1) / kMinBlockM + G;
-    L.total = L.tiles + align256(sizeof(moegg_tile_t) * (size_t)L.max_tiles);
+    L.sync = L.tiles + align256(sizeof(moegg_tile_t) * (size_t)L.max_tiles);
+    L.total = L.sync + align256(sizeof(uint32_t) * (size_t)(L.max_tiles + kSyncExtra));
     return L;
 }
 

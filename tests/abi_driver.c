@@ -84,6 +84,10 @@ int main(void) {
         st.U = -1;
         EXPECT(moegg_stats_report(&st, &rep), MOEGG_ERR_INVALID_ARG);
     }
+    EXPECT(moegg_expert_mlp_fused(fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 8, 132, 512, 256, 512, 1,
+                                  MOEGG_BF16, MOEGG_B_NK, fake, ws, NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_expert_mlp_fused(fake, fake, fake, fake, fake, fake, fake, NULL, fake, fake, 8, 132, 512, 256, 512, 1,
+                                  MOEGG_FP8_E4M3, MOEGG_B_NK, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);
     /* allocation-free variant: argument errors, and a workspace beyond its fixed array, before any HIP call */
     EXPECT(moegg_grouped_gemm_contiguous_noalloc(NULL, NULL, fake, NULL, fake, fake, 8, 132, 512, 256, 1, MOEGG_BF16,
                                                  MOEGG_B_KN, 0, NULL), MOEGG_ERR_INVALID_ARG);

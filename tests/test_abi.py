@@ -193,6 +193,27 @@ def test_swiglu_validation():
     assert call(5, ctypes.c_void_p(0x100002)) == mg.ERR_INVALID_ARG   # H_scale alignment
 
 
+def test_expert_mlp_fused_validation():
+    f = mg.lib().moegg_expert_mlp_fused
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 132, 512, 256, 512, 1, mg.FP8_E4M3,
+          mg.B_NK, FAKE, 1 << 20, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(9, None) == mg.ERR_INVALID_ARG              # m_sizes
+    assert call(0, None) == mg.ERR_INVALID_ARG              # A
+    assert call(7, None) == mg.ERR_INVALID_ARG              # H_scale
+    assert call(13, 0) == mg.ERR_INVALID_ARG                # I
+    assert call(13, 64) == mg.ERR_UNSUPPORTED               # 2I % 256
+    assert call(14, 128) == mg.ERR_UNSUPPORTED              # N2 % 256
+    assert call(16, mg.BF16) == mg.ERR_UNSUPPORTED          # e4m3 with fp32 scales only
+    assert call(17, mg.B_KN) == mg.ERR_UNSUPPORTED          # weights must be K-contiguous
+    assert call(18, None) == mg.ERR_WORKSPACE
+    assert call(19, 1024) == mg.ERR_WORKSPACE               # too small
+
+
 def test_read_validation():
     L = mg.lib()
     assert L.moegg_stats_read(None, None, None) == mg.ERR_INVALID_ARG
