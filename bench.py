@@ -107,6 +107,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_key(w: wl.Workload, b_layout: int, scale_km: bool = True) -> str:
+    """The entry of profiles/traffic.json that holds this workload's counters."""
+    layout = {mg.B_KN: "kn", mg.B_NK: "nk", mg.B_KN_PANEL: "kn-panel", mg.B_NK_PANEL: "nk-panel"}[b_layout]
+    return f"{w.name}|{layout}" + ("|e8m0" if w.scales == "e8m0" else "") + \
+        ("|e2m1" if w.weights == "e2m1" else "") + \
+        ("|rows" if w.dtype == "fp8" and w.scales != "e8m0" and not scale_km else "")
+
+
 def traffic_for(w: wl.Workload, b_layout: int, scale_km: bool = True):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary, if it was taken on this exact kernel source and workload; else None."""
@@ -115,10 +123,7 @@ def traffic_for(w: wl.Workload, b_layout: int, scale_km: bool = True):
         return None
     with open(path) as f:
         t = json.load(f)
-    key = f"{w.name}|{'nk' if b_layout == mg.B_NK else 'kn'}" + ("|e8m0" if w.scales == "e8m0" else "") + \
-        ("|e2m1" if w.weights == "e2m1" else "") + \
-        ("|rows" if w.dtype == "fp8" and w.scales != "e8m0" and not scale_km else "")
-    e = t.get("entries", {}).get(key)
+    e = t.get("entries", {}).get(traffic_key(w, b_layout, scale_km))
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
     return e["hbm_bytes_per_launch"]
@@ -618,6 +623,7 @@ def main():
     tr = traffic_for(w, b_layout, scale_km)
     if tr is not None:
         out["roofline"]["traffic"] = tr
+    out["traffic_key"] = traffic_key(w, b_layout, scale_km)
     out["gemm_kernel_ms"] = round(gemm_avg, 4)
     out["algorithmic_bytes"] = bytes_alg
     out["wall_s_timed"] = round(wall, 4)
