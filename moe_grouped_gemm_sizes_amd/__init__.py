@@ -464,6 +464,7 @@ def expert_mlp_fused(A, W1, W2, H, Y, m_sizes, ws, A_scale, W1_scale, W2_scale, 
         raise ValueError(f"W1: {N} interleaved gate/up rows, a multiple of 256 expected")
     I = N // 2
     _need(H, "H", [rows, I], (_E4M3,))
+    _need(H_scale, "H_scale", [I // 128, rows] if scale_km else [rows, I // 128], (torch.float32,))
     code2, N2 = _operands(rows, I, H, H_scale, W2, W2_scale, G, b_layout, scale_km)
     if code2 != code or N2 % 256:
         raise ValueError(f"W2: e4m3 [G, N2, I] with N2 % 256 == 0 expected, got N2 = {N2}")

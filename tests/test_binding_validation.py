@@ -211,3 +211,37 @@ def test_panel_shapes_are_checked():
     kw["B"] = t(G, N // 128, K, 128, dtype=torch.bfloat16)     # masked panel width on a contiguous call
     with pytest.raises(ValueError, match="B: shape"):
         call_contiguous(kw)
+
+
+def mlp_args(scale_km=False):
+    I, N2 = 256, 512
+    return dict(A=t(ROWS, K, dtype=E4M3), W1=t(G, 2 * I, K, dtype=E4M3), W2=t(G, N2, I, dtype=E4M3),
+                H=t(ROWS, I, dtype=E4M3), Y=t(ROWS, N2, dtype=torch.bfloat16), m_sizes=t(G, dtype=torch.int32),
+                ws=t(mg.workspace_bytes(G, ROWS), dtype=torch.uint8),
+                A_scale=t(K // 128, ROWS) if scale_km else t(ROWS, K // 128), W1_scale=t(G, K // 128, 2 * I // 128),
+                W2_scale=t(G, I // 128, N2 // 128), H_scale=t(I // 128, ROWS) if scale_km else t(ROWS, I // 128),
+                scale_km=scale_km)
+
+
+@pytest.mark.parametrize("scale_km", [False, True])
+def test_expert_mlp_fused_correct_arguments_reach_the_device_check(scale_km):
+    with pytest.raises(ValueError, match="device tensor expected"):
+        mg.expert_mlp_fused(**mlp_args(scale_km))
+
+
+@pytest.mark.parametrize("change,name", [
+    (dict(H=t(ROWS, 384, dtype=E4M3)), "H: shape"),
+    (dict(H_scale=t(ROWS, 1)), "H_scale: shape"),
+    (dict(Y=t(ROWS, 512)), "Y: dtype"),
+    (dict(Y=t(ROWS, 256, dtype=torch.bfloat16)), "Y: shape"),
+    (dict(W2=t(G, 512, 384, dtype=E4M3)), "B: shape"),
+    (dict(W1=t(G, 384, K, dtype=E4M3), W1_scale=t(G, K // 128, 3)), "multiple of 256"),
+    (dict(A=t(ROWS, K, dtype=torch.bfloat16)), "A: dtype"),
+    (dict(m_sizes=t(G, dtype=torch.int64)), "m_sizes: dtype"),
+    (dict(ws=t(16, dtype=torch.uint8)), "ws:"),
+])
+def test_expert_mlp_fused_mismatch_raises(change, name):
+    kw = mlp_args()
+    kw.update(change)
+    with pytest.raises(ValueError, match=name):
+        mg.expert_mlp_fused(**kw)
