@@ -349,6 +349,20 @@ def run_mlp(args):
     print(json.dumps(out), flush=True)
 
 
+def calib_copy(args):
+    """With --calib-copy-mib n: one plain elementwise kernel over n MiB of fp32 after the timed steps (reads n MiB,
+    writes n MiB), so a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) can scale HBM counters by a transfer of
+    known size."""
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 18                         # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def run_mlp_fused(args, inp, counts, K, I, N2, a_s, w1_s, km, ws, H, Hs, Y):
     """The expert MLP in one persistent launch (moegg_expert_mlp_fused: scheduler, sync clear, one kernel with
     both GEMMs), and beside it the same work as three launches from the same 256-row schedule, each timed
@@ -388,6 +402,7 @@ def run_mlp_fused(args, inp, counts, K, I, N2, a_s, w1_s, km, ws, H, Hs, Y):
     if st.error_flags:
         raise RuntimeError(f"fused expert MLP: error flags {st.error_flags:#x}")
     chain_ms = timed(chain)
+    calib_copy(args)
     f1, f2 = 2.0 * R * K * 2 * I, 2.0 * R * I * N2
     tf = (f1 + f2) / (ms * 1e-3) / 1e12
     out = {
@@ -632,14 +647,7 @@ def main():
         out["candidates"] = time_candidates(w, inp_gpu, b_layout, scale_km, args)
     out["sclk"] = None if args.no_sclk else sample_sclk(lambda: (sched() if sched is not None else None, gemm()))
     out["host"] = host_info()
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 18                         # fp32 elements
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)                               # one elementwise kernel: reads n*4, writes n*4 bytes
-        torch.cuda.synchronize()
-        del src, dst
+    calib_copy(args)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
         out["cpu_baseline"] = cpu_baseline(w, oracle_inp)
