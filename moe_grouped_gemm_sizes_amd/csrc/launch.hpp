@@ -24,7 +24,7 @@ struct ContigArgs {
     int b_panel;                  // weights stored in column panels of the kernel's tile width (see moegg.h)
 };
 
-// Expert MLP in one persistent launch: l1 is the SwiGLU projection (C = H,
+// Expert MLP in one launch: l1 is the SwiGLU projection (C = H,
 // C_scale = H_scale, N = 2I), l2 the down projection on H (A = H, K = I, N = N2).
 struct MlpArgs {
     ContigArgs l1, l2;
