@@ -153,6 +153,16 @@ def test_fused_mlp_tiny_and_single_expert():
         check_against_chain(inp, counts, I, N2, mg.B_NK, False)
 
 
+def test_fused_mlp_one_column_tile_each():
+    """I = 128 and N2 = 256: one SwiGLU item and one down-projection item per row tile,
+    so every queue alternates single items of the two phases."""
+    counts = [300, 5, 0, 700, 1]
+    K, I, N2 = 128, 128, 256
+    announce("fused expert MLP one column tile each", counts)
+    inp = operands(counts, K, I, N2, 47, mg.B_NK, False)
+    check_against_chain(inp, counts, I, N2, mg.B_NK, False)
+
+
 def test_fused_mlp_all_experts_empty():
     """Every count 0 on a 4-row buffer: no tile, nothing written, no wait."""
     K, I, N2, G, R = 128, 128, 256, 3, 4
