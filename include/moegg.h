@@ -346,9 +346,12 @@ moegg_status_t moegg_grouped_gemm_contiguous_noalloc(
 
 /*
  * The contiguous GEMM alone, driven by the tile list that an earlier
- * moegg_schedule or moegg_grouped_gemm_contiguous call left in `ws`.  One
- * MoE layer runs several grouped GEMMs over one routing histogram (gate/up,
- * then down projection); they can share one schedule.  Arguments are those of
+ * moegg_schedule or moegg_grouped_gemm_contiguous call left in `ws` (the
+ * M-grouped contiguous layout of the DeepGEMM record, "Workarounds"; the
+ * histogram and the choices made from it stay on the device, the padding
+ * page's "Adapt kernels without adding a CPU stall").  One MoE layer runs
+ * several grouped GEMMs over one routing histogram (gate/up, then down
+ * projection); they can share one schedule.  Arguments are those of
  * moegg_grouped_gemm_contiguous, without m_sizes and seg_align.  The
  * schedule must come from the same G and rows_total.  block_m = 0 runs
  * whatever height the schedule used, in one launch whose grid depends only on
