@@ -79,7 +79,8 @@ def effective_experts(counts: Sequence[int]) -> Fraction:
 
 
 def average_assignments(concurrency: int, top_k: int, experts: int) -> Fraction:
-    """Global concurrency times top-k divided by the expert count."""
+    """Mean routed rows per expert: tokens in flight, each routed to top_k experts,
+    spread over the experts (the padding page's companion average)."""
     return Fraction(concurrency * top_k, experts)
 
 
