@@ -116,7 +116,8 @@ def oracle_y(cpu, q, s, counts, rows, N2):
     return y
 
 
-@pytest.mark.parametrize("b_layout,scale_km", [(mg.B_NK, False), (mg.B_NK, True), (mg.B_NK_PANEL, False)])
+@pytest.mark.parametrize("b_layout,scale_km", [(mg.B_NK, False), (mg.B_NK, True), (mg.B_NK_PANEL, False),
+                                               (mg.B_NK_PANEL, True)])
 def test_fused_mlp_small(b_layout, scale_km):
     """Ragged experts (empty, 3 rows, a 256-row tile plus 44): bit for bit against
     the chain, H and Y on every valid row against the oracle."""
