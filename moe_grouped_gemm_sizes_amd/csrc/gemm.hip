@@ -988,8 +988,9 @@ constexpr int kMlpSpinLimit = 1 << 15;      // polls (with a short sleep each) b
 
 // The expert MLP (the compute half of the DeepGEMM record's Mega MoE: both
 // expert GEMMs and SwiGLU in one kernel, "Arithmetic intensity") in one
-// launch, so the down projection reads H back while it is likely still in L2
-// and the two GEMMs share one tail instead of two.  Each workgroup runs one
+// launch, so the down projection of a row tile starts as soon as its H is
+// complete and the two GEMMs share one tail instead of two.  (H still goes
+// through its buffer: each release writes the XCD's L2 back.)  Each workgroup runs one
 // work item taken from a queue: the row tiles are cut into n_queues
 // consecutive ranges, one queue per XCD, so an expert's row tiles mostly share
 // one XCD's L2.  A workgroup takes a ticket from the queue of the XCD it runs
