@@ -235,3 +235,17 @@ def test_fused_mlp_full_size():
     q, s = check_fp8_h(H, Hs, h, rows)
     P.check_gemm(got_y, oracle_y(cpu, q, s, counts, rows, N2), "fp8", bound="chain_e4m3",
                  what="fused mlp full size y")
+
+
+def test_fused_mlp_full_size_transposed_scales_and_panels():
+    """The configuration bench.py --mlp --mlp-fused times (activation and H scales
+    [K/128, rows]), and with the weights in column panels: bit for bit against the
+    three launches on every row of the Zipf histogram at the DeepSeek-V3 shape."""
+    counts = wl.workload(3).counts
+    K, I, N2 = 7168, 2048, 7168
+    for b_layout in (mg.B_NK, mg.B_NK_PANEL):
+        announce("fused expert MLP full size, scales [K/128, rows]", "b_layout", b_layout)
+        inp = operands(counts, K, I, N2, 48, b_layout, True)
+        check_against_chain(inp, counts, I, N2, b_layout, True)
+        del inp
+        torch.cuda.empty_cache()
