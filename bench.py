@@ -425,6 +425,75 @@ def run_mlp_fused(args, inp, counts, K, I, N2, a_s, w1_s, km, ws, H, Hs, Y):
     print(json.dumps(out), flush=True)
 
 
+def run_decode_buckets(args):
+    """Low-token buckets (the padding page, "Build a routing-shaped benchmark", asks for them beside the large
+    histograms).  Contiguous: the Zipf fp8 shape (64 experts, K 7168, N 4096, fp32 scales [K/128, rows]) at U =
+    32 ... 1024 routed rows, every tile height timed on its own and the device's own choice (block_m = 0).
+    Masked: the decode shape (32 experts, cap 256, K 2048, N 7168, bf16 and fp8 with fp32 scales, weights in
+    128-column panels) at Poisson means 1 ... 128.  Cold caches between calls; one JSON line per bucket; these are memory-bound, so the
+    rate is algorithmic bytes per second against HBM."""
+    args.cold = True
+    for U in (32, 64, 128, 256, 512, 1024):
+        counts = wl.hist_zipf(3, experts=64, total=U)
+        w = wl.Workload(f"zipf 64 experts fp8 contiguous, {U} rows", "contiguous", "fp8", counts, K=7168, N=4096,
+                        values="normal", seed=3)
+        inp = wl.materialize(w, "cuda")
+        inp["B"] = inp["B"].transpose(1, 2).contiguous()
+        a_s = inp["A_scale"]
+        inp = dict(inp, A_scale=a_s.t().contiguous())
+        cands = time_candidates(w, inp, mg.B_NK, True, args)
+        sched, gemm, ws = build_step(w, inp, 0, mg.B_NK, 0, None, 0, scale_km=True)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            sched(); gemm()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i, (a, b) in enumerate(ev):
+            scratch.fill_(i & 255)
+            sched()
+            a.record()
+            gemm()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        st = mg.stats_read(ws)
+        nb = algorithmic_bytes(w)
+        best = min(cands, key=lambda c: c["gemm_ms_median"])
+        print(json.dumps({"bucket": "contiguous", "U": U, "active_experts": st.active,
+                          "effective_experts": round(st.report().effective_experts, 3),
+                          "device_choice": "per-expert" if st.block_m == mg.BLOCK_M_PER_EXPERT else st.block_m,
+                          "device_choice_ms": round(ms, 4), "fastest": best["block_m"],
+                          "fastest_ms": best["gemm_ms_median"], "algorithmic_bytes": nb,
+                          "gbs": round(nb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK, 4),
+                          "candidates": {str(c["block_m"]): c["gemm_ms_median"] for c in cands}}), flush=True)
+        del inp, ws, scratch
+        torch.cuda.empty_cache()
+    for dtype, mean in [(d, m) for d in ("bf16", "fp8") for m in (1, 2, 4, 8, 16, 32, 64, 128)]:
+        counts = wl.hist_poisson_masked(4, experts=32, cap=256, mean=float(mean))
+        w = wl.Workload(f"masked decode 32 experts {dtype}, mean {mean}", "masked", dtype, counts, K=2048, N=7168,
+                        cap=256, values="normal", seed=4)
+        inp = wl.materialize(w, "cuda")
+        inp["B"] = mg.pack_panels(inp["B"], mg.B_KN_PANEL, mg.PANEL_MASKED)
+        _, gemm, _ = build_step(w, inp, 0, mg.B_KN_PANEL)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            gemm()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i, (a, b) in enumerate(ev):
+            scratch.fill_(i & 255)
+            a.record()
+            gemm()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        nb = algorithmic_bytes(w)
+        print(json.dumps({"bucket": "masked", "dtype": dtype, "poisson_mean": mean, "U": sum(counts),
+                          "active_experts": sum(1 for c in counts if c > 0), "ms": round(ms, 4),
+                          "algorithmic_bytes": nb, "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK, 4)}), flush=True)
+        del inp, scratch
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +527,10 @@ def main():
                          "Zipf histogram at the DeepSeek-V3 expert shape instead of one grouped GEMM")
     ap.add_argument("--a-scale", choices=("km", "rows"), default="km",
                     help="fp32 activation-scale layout for fp8: [K/128, rows] (default) or [rows, K/128]")
+    ap.add_argument("--decode-buckets", action="store_true",
+                    help="low-token buckets instead of one workload: the contiguous fp8 shape at 32..1024 routed "
+                         "rows (every tile height and the device's choice) and the masked decode shape at Poisson "
+                         "means 1..128; one JSON line per bucket")
     ap.add_argument("--mlp-fused", action="store_true",
                     help="with --mlp: the expert MLP in one persistent launch (fp8 H), timed beside the same "
                          "work as three launches from the 256-row schedule")
@@ -491,6 +564,9 @@ def main():
         sys.exit(2)
     if args.mlp:
         run_mlp(args)
+        return
+    if args.decode_buckets:
+        run_decode_buckets(args)
         return
     w = wl.workload(args.config)
     if args.dtype == "fp8":

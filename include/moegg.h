@@ -458,10 +458,12 @@ moegg_status_t moegg_expert_mlp_fused(
  *   C        bf16 [G, cap, N].  Only rows r < masked_m[e] are written.
  *   masked_m int32 [G] on the device, read by the kernel at run time.
  * The grid depends only on G and N (one workgroup per expert and 128-column
- * tile, walking that expert's 64-row tiles up to masked_m[e]), so a captured
- * graph stays valid when masked_m changes between replays.  Experts with
- * masked_m[e] = 0 load no weights.  ws may be NULL (no stats).  Otherwise stats are written as for
- * the contiguous call, with block_m = the kernel's row tile.
+ * tile, walking that expert's rows up to masked_m[e] in 128-row tiles, the
+ * last one 64 or 128 rows tall), so a captured graph stays valid when
+ * masked_m changes between replays.  Experts with masked_m[e] = 0 load no
+ * weights.  ws may be NULL (no stats).  Otherwise stats are written as for
+ * the contiguous call, with block_m = 128 and tiles = the sum of
+ * ceil(masked_m[e] / 128).
  * Constraints: as for the contiguous call, plus cap >= 1.
  */
 moegg_status_t moegg_grouped_gemm_masked(

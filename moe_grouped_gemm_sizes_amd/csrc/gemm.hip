@@ -329,10 +329,11 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 // The wave runs at raised priority (s_setprio) from the barrier to the end of
 // its MFMAs, so a SIMD's two waves drain their MFMA work ahead of the barrier.
 // WNT: the weight panel is read by this tile only, so its loads stream
-// (non-temporal); see load16_to_lds_cp.
+// (non-temporal); see load16_to_lds_cp.  Not for fp4 weights: a K step reads
+// half of each 128-byte line, and a streamed line is gone by the next step.
 template <class C, bool B_KN, bool WNT = false>
 struct TileGemm {
-    static constexpr int WCP = WNT ? CP_NT : CP_DEFAULT;
+    static constexpr int WCP = WNT && !C::W4 ? CP_NT : CP_DEFAULT;
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     static constexpr int HSEG = C::WTN / 2;                        // weight rows per wave column half
     static_assert(B_KN || C::W4 || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
@@ -884,48 +885,69 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
     }
 }
 
-// M-grouped contiguous (MASKED = false) or masked (MASKED = true) layout, one
-// tile height.
-template <class C, bool B_KN, bool MASKED, int SWIGLU = 0>
+// M-grouped contiguous layout, one tile height.
+template <class C, bool B_KN, int SWIGLU = 0>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(ContigArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const int n_ct = p.N / C::BN;
-    int e, row_start, rows_valid, ct;
-    if constexpr (MASKED) {
-        // one workgroup per (expert, column tile); it walks the expert's row tiles
-        // up to masked_m, so an empty expert loads no weights and the grid depends
-        // only on G and N
-        e = blockIdx.x / n_ct;
-        ct = blockIdx.x - e * n_ct;
-        if (e >= p.G) return;
-        const int m = min(max(p.counts[e], 0), p.cap);
-        if (m == 0) return;
-        if (m <= C::BM) {
-            // one row tile: the weight panel is read once, so it streams
-            contig_tile<C, B_KN, 0, true>(p, lds, e, e * p.cap, m, ct);
-            return;
-        }
-#pragma unroll 1
-        for (int rt = 0; rt * C::BM < m; ++rt) {
-            if (rt > 0) __syncthreads();         // the previous tile's LDS is free
-            contig_tile<C, B_KN>(p, lds, e, e * p.cap + rt * C::BM, min(C::BM, m - rt * C::BM), ct);
-        }
+    const WsLayout L = ws_layout(p.G, 0);
+    const Control* ctl = (const Control*)(p.ws + L.control);
+    if (ctl->block_m != C::BM) return;       // another candidate height was chosen
+    const int n_rt = ctl->n_tiles;
+    const int item = block_to_item(blockIdx.x);
+    if (item >= n_rt * n_ct) return;
+    int rt, ct;
+    item_to_tiles(item, n_rt, n_ct, rt, ct);
+    const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
+    if (t.tile == 0 && t.rows_valid < C::BM) {
+        // the expert's only tile: this column's weight panel has no other reader, so it streams
+        contig_tile<C, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
         return;
-    } else {
-        const WsLayout L = ws_layout(p.G, 0);
-        const Control* ctl = (const Control*)(p.ws + L.control);
-        if (ctl->block_m != C::BM) return;       // another candidate height was chosen
-        const int n_rt = ctl->n_tiles;
-        const int item = block_to_item(blockIdx.x);
-        if (item >= n_rt * n_ct) return;
-        int rt;
-        item_to_tiles(item, n_rt, n_ct, rt, ct);
-        const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
-        e = t.expert;
-        row_start = t.row_start;
-        rows_valid = t.rows_valid;
     }
-    contig_tile<C, B_KN, SWIGLU>(p, lds, e, row_start, rows_valid, ct);
+    contig_tile<C, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+}
+
+// Masked layout: one workgroup per (expert, 128-column tile).  It reads
+// masked_m[e] itself, so an empty expert loads no weights and the grid depends
+// only on G and N, and it walks the expert's rows in 128-row tiles, the last
+// one 64 or 128 rows tall.  An expert of one tile is its weight panel's only
+// reader, so the panel streams; with several, every tile loads it again.
+// Two workgroups per CU (four waves per SIMD, so at most 128 VGPRs; 80 KB of
+// LDS each): the loads of one overlap the start-up and epilogue of the other.
+// A 256-row height would need a 48 KB stage and one workgroup per CU, which
+// costs the short tiles that decode mostly runs more than it saves.
+template <bool FP8, bool E8 = false, bool W4 = false> using Masked64 = GCfg<FP8, 64, 128, 2, 4, 2, E8, W4>;
+template <bool FP8, bool E8 = false, bool W4 = false> using Masked128 = GCfg<FP8, 128, 128, 4, 2, 2, E8, W4>;
+
+template <bool FP8, bool E8, bool W4, bool NT, bool B_KN>
+__device__ __forceinline__ void masked_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows, int ct) {
+    if (rows > 64)
+        contig_tile<Masked128<FP8, E8, W4>, B_KN, 0, NT>(p, lds, e, row_start, rows, ct);
+    else
+        contig_tile<Masked64<FP8, E8, W4>, B_KN, 0, NT>(p, lds, e, row_start, rows, ct);
+}
+
+template <bool FP8, bool B_KN, bool E8, bool W4>
+__global__ __launch_bounds__(512, 4) void grouped_gemm_masked_kernel(ContigArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    const int n_ct = p.N / 128;
+    const int e = blockIdx.x / n_ct, ct = blockIdx.x - e * n_ct;
+    if (e >= p.G) return;
+    const int m = min(max(p.counts[e], 0), p.cap);
+    if (m == 0) return;
+    const int row0 = e * p.cap;
+    if (m <= 128) {
+        masked_tile<FP8, E8, W4, true, B_KN>(p, lds, e, row0, m, ct);
+        return;
+    }
+    const int last = (m - 1) >> 7;           // tiles before the last
+#pragma unroll 1
+    for (int i = 0; i < last; ++i) {
+        if (i > 0) __syncthreads();         // the previous tile's LDS is free
+        contig_tile<Masked128<FP8, E8, W4>, B_KN>(p, lds, e, row0 + i * 128, 128, ct);
+    }
+    __syncthreads();
+    masked_tile<FP8, E8, W4, false, B_KN>(p, lds, e, row0 + last * 128, m - last * 128, ct);
 }
 
 // One launch for any tile height the scheduler chose (block_m = 0, the
@@ -957,21 +979,36 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_auto_kernel(ContigArgs p)
     int rt, ct;
     item_to_tiles(item, n_rt, n_ct, rt, ct);
     const moegg_tile_t t = tiles[rt];
+    // A weight panel that one tile alone reads streams (non-temporal loads): the per-expert list's tails
+    // (1..128 rows, run after all full tiles) and, at any height, an expert's only tile.
+    const bool alone = t.tile == 0 && t.rows_valid < (bm == MOEGG_BLOCK_M_PER_EXPERT || bm == 256 ? 256 : bm);
     if (bm == MOEGG_BLOCK_M_PER_EXPERT) {
-        // the per-expert list runs every expert's tail (1..128 rows) after all full tiles, so the
-        // tail's weight panel is read once more by that tile alone: it streams
-        if (t.rows_valid > 128)
+        if (t.rows_valid > 128) {
+            if (alone)
+                contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid,
+                                                                        ct);
+            else
+                contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        } else if (t.rows_valid > 64) {
+            contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        } else {
+            contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        }
+    } else if (bm == 256) {
+        if (alone)
+            contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        else
             contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-        else if (t.rows_valid > 64)
+    } else if (bm == 128) {
+        if (alone)
             contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
         else
-            contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    } else if (bm == 256) {
-        contig_tile<Contig256<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
-    } else if (bm == 128) {
-        contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+            contig_tile<Contig128<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
     } else {
-        contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        if (alone)
+            contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU, true>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
+        else
+            contig_tile<Contig64<FP8, E8, W4>, B_KN, SWIGLU>(p, lds, t.expert, t.row_start, t.rows_valid, ct);
     }
 }
 
@@ -1270,10 +1307,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
 // ---------------------------------------------------------------- configs
 
-// Masked decode: short row tiles, narrow column tiles (HBM-bound).
-// Two workgroups per CU, three stages each: the loads of one overlap the
-// start-up and epilogue of the other, and a CU keeps twice the bytes in flight.
-template <bool FP8, bool E8 = false, bool W4 = false> using MaskedCfg = GCfg<FP8, 64, 128, 2, 4, 2, E8, W4>;
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
 using KGroupedFp8Cfg = KCfg<256, 256, 4, 2, 2, true>;
 
@@ -1286,10 +1319,10 @@ static hipError_t allow_lds(int bytes) {
     return once;
 }
 
-template <class C, bool B_KN, bool MASKED, int SWIGLU = 0>
+template <class C, bool B_KN, int SWIGLU = 0>
 static hipError_t launch_one(const ContigArgs& a, int grid, hipStream_t s) {
-    auto k = grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>;
-    hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, MASKED, SWIGLU>>(C::LDS_BYTES);
+    auto k = grouped_gemm_kernel<C, B_KN, SWIGLU>;
+    hipError_t err = allow_lds<grouped_gemm_kernel<C, B_KN, SWIGLU>>(C::LDS_BYTES);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, a);
     return hipGetLastError();
@@ -1316,9 +1349,9 @@ static hipError_t launch_contig_t(const ContigArgs& a, int64_t rows_total, int b
                            s, b);
         return hipGetLastError();
     }
-    if (block_m == 256) return launch_one<Contig256<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(256), s);
-    if (block_m == 128) return launch_one<Contig128<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(128), s);
-    return launch_one<Contig64<FP8, E8, W4>, B_KN, false, SW>(a, grid_for(64), s);
+    if (block_m == 256) return launch_one<Contig256<FP8, E8, W4>, B_KN, SW>(a, grid_for(256), s);
+    if (block_m == 128) return launch_one<Contig128<FP8, E8, W4>, B_KN, SW>(a, grid_for(128), s);
+    return launch_one<Contig64<FP8, E8, W4>, B_KN, SW>(a, grid_for(64), s);
 }
 
 hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, int64_t rows_total,
@@ -1343,18 +1376,25 @@ hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int6
              : launch_contig_t<false, false, false, false, 1>(a, rows_total, block_m, s);
 }
 
-int masked_block_m() { return MaskedCfg<false>::BM; }
-int masked_block_n() { return MaskedCfg<false>::BN; }
+int masked_block_m() { return Masked128<false>::BM; }
+int masked_block_n() { return Masked128<false>::BN; }
+
+template <bool FP8, bool B_KN, bool E8 = false, bool W4 = false>
+static hipError_t launch_masked_t(const ContigArgs& a, hipStream_t s) {
+    constexpr int lds = std::max(Masked128<FP8, E8, W4>::LDS_BYTES, Masked64<FP8, E8, W4>::LDS_BYTES);
+    static_assert(2 * lds <= 160 * 1024, "two workgroups per CU");
+    hipError_t err = allow_lds<grouped_gemm_masked_kernel<FP8, B_KN, E8, W4>>(lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((grouped_gemm_masked_kernel<FP8, B_KN, E8, W4>), dim3(a.G * (a.N / 128)), dim3(512), lds, s,
+                       a);
+    return hipGetLastError();
+}
 
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s) {
-    const int grid = a.G * (a.N / MaskedCfg<false>::BN);
-    if (w4) return b_kn ? hipErrorInvalidValue : launch_one<MaskedCfg<true, true, true>, false, true>(a, grid, s);
-    if (e8m0) return b_kn ? launch_one<MaskedCfg<true, true>, true, true>(a, grid, s)
-                          : launch_one<MaskedCfg<true, true>, false, true>(a, grid, s);
-    if (fp8) return b_kn ? launch_one<MaskedCfg<true>, true, true>(a, grid, s)
-                         : launch_one<MaskedCfg<true>, false, true>(a, grid, s);
-    return b_kn ? launch_one<MaskedCfg<false>, true, true>(a, grid, s)
-                : launch_one<MaskedCfg<false>, false, true>(a, grid, s);
+    if (w4) return b_kn ? hipErrorInvalidValue : launch_masked_t<true, false, true, true>(a, s);
+    if (e8m0) return b_kn ? launch_masked_t<true, true, true>(a, s) : launch_masked_t<true, false, true>(a, s);
+    if (fp8) return b_kn ? launch_masked_t<true, true>(a, s) : launch_masked_t<true, false>(a, s);
+    return b_kn ? launch_masked_t<false, true>(a, s) : launch_masked_t<false, false>(a, s);
 }
 
 template <class C>

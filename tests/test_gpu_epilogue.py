@@ -37,9 +37,9 @@ def test_contiguous_epilogue_row_counts(dtype, block_m):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_masked_epilogue_row_counts(dtype):
-    counts = [1, 31, 32, 33, 63, 64, 65, 0, 96, 128]
+    counts = [1, 31, 32, 33, 63, 64, 65, 0, 96, 128, 129, 161, 255, 256, 257, 289]
     T.announce("epilogue row counts masked", dtype, counts)
-    w, inp = T.masked_case(counts, 128, 256, 256, dtype, seed=22)
+    w, inp = T.masked_case(counts, 320, 256, 256, dtype, seed=22)
     C = P.sentinel_like((w.G, w.cap, w.N))
     ws = mg.workspace(w.G, w.G * w.cap)
     mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws, inp.get("A_scale"), inp.get("B_scale"),

@@ -402,6 +402,49 @@ def test_masked_fp8_fp4():
     assert bool((C.reshape(w.G * w.cap, -1)[inval].view(torch.int16) == P.SENTINEL_BITS).all())
 
 
+# per expert: one tile of each height (1, 64 | 65, 128 rows), then several
+# 128-row tiles with a last one of each height
+MASKED_HEIGHT_COUNTS = [1, 64, 65, 128, 129, 192, 0, 193, 256, 257, 385, 512]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("b_layout", [mg.B_KN, mg.B_NK, mg.B_KN_PANEL, mg.B_NK_PANEL])
+def test_masked_per_expert_heights(dtype, b_layout):
+    """The masked kernel's row tiles around each height it picks (64 and 128,
+    and several 128-row tiles before a last one of each): every valid row, the
+    rows past masked_m untouched, and the stats' tile count."""
+    counts = MASKED_HEIGHT_COUNTS
+    announce("masked per-expert heights", dtype, b_layout, counts)
+    w, inp = masked_case(counts, 512, 512, 256, dtype, seed=26)
+    B = inp["B"]
+    if b_layout in (mg.B_NK, mg.B_NK_PANEL):
+        B = B.transpose(1, 2).contiguous()
+    if b_layout in (mg.B_KN_PANEL, mg.B_NK_PANEL):
+        B = mg.pack_panels(inp["B"], b_layout, mg.PANEL_MASKED)
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], B, C, inp["counts"], ws, inp.get("A_scale"), inp.get("B_scale"), b_layout)
+    torch.cuda.synchronize()
+    P.check_stats(mg.stats_read(ws), counts, 128)
+    check_masked(w, inp, C, counts)
+
+
+@pytest.mark.parametrize("weights", ["e4m3", "e2m1"])
+def test_masked_per_expert_heights_low_precision(weights):
+    """E8M0 scales with e4m3 or fp4 weights at the same row counts."""
+    counts = MASKED_HEIGHT_COUNTS
+    announce("masked per-expert heights", weights, counts)
+    w, inp, C = run_masked_low_precision(counts, 512, 512, 512, weights, mg.B_NK, seed=27)
+    if weights == "e2m1":
+        check_masked_fp4(w, inp, C, counts)
+        inval = torch.tensor([e * w.cap + r for e in range(w.G) for r in range(w.cap) if r >= counts[e]],
+                             device="cuda")
+        assert bool((C.reshape(w.G * w.cap, -1)[inval].view(torch.int16) == P.SENTINEL_BITS).all())
+    else:
+        w.scales = "e8m0"
+        check_masked(w, {k: v for k, v in inp.items() if k not in ("A_scale_e8m0", "B_scale_e8m0")}, C, counts)
+
+
 def test_masked_fp8_fp4_full_size():
     """The masked decode workload (32 experts, cap 256, K 2048, N 7168) with fp8
     activations and fp4 weights; sampled rows."""
