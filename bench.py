@@ -74,9 +74,12 @@ def build_step(w: wl.Workload, inp, block_m_hint: int, b_layout: int, sched_bloc
     dW = torch.empty((w.G, w.Mw, w.Nw), dtype=torch.float32, device=dev)
     ws = mg.workspace(w.G, 0)
 
+    e8 = w.scales == "e8m0"
+
     def gemm():
-        mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws, inp.get("X_scale"),
-                                  inp.get("dY_scale"))
+        mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws,
+                                  inp.get("X_scale_e8m0" if e8 else "X_scale"),
+                                  inp.get("dY_scale_e8m0" if e8 else "dY_scale"))
     return None, gemm, ws
 
 
@@ -87,7 +90,8 @@ def algorithmic_bytes(w: wl.Workload) -> int:
     if w.layout == "k_grouped":
         if w.dtype == "fp8":
             groups = mg.k_scale_groups(w.counts)
-            return U * (w.Mw + w.Nw) + groups * (w.Mw + w.Nw) * 4 + w.G * w.Mw * w.Nw * 4
+            ssz = 1 if w.scales == "e8m0" else 4
+            return U * (w.Mw + w.Nw) + groups * (w.Mw + w.Nw) * ssz + w.G * w.Mw * w.Nw * 4
         return U * (w.Mw + w.Nw) * 2 + w.G * w.Mw * w.Nw * 4
     esz = 1 if w.dtype == "fp8" else 2
     w_bytes = w.K * w.N // 2 if w.weights == "e2m1" else w.K * w.N * esz
@@ -518,7 +522,8 @@ def main():
                          "K-grouped: per 128-row group of each expert's segment and column)")
     ap.add_argument("--scales", choices=("fp32", "e8m0"), default="fp32",
                     help="fp8 block scales: fp32 (the workload as stated, promoted on the VALU), or powers of two "
-                         "as E8M0 bytes, applied by the MFMA (contiguous fp8 workloads only)")
+                         "as E8M0 bytes, applied by the MFMA (the contiguous and masked workloads, and the K-grouped "
+                         "one with --dtype fp8)")
     ap.add_argument("--weights", choices=("e4m3", "e2m1"), default="e4m3",
                     help="fp8 workload weights: e4m3 (as stated), or packed fp4 E2M1 [G,N,K/2] with E8M0 scales "
                          "(implies --scales e8m0; contiguous fp8 workloads only)")
@@ -582,9 +587,9 @@ def main():
         if w.layout == "masked" and w.dtype == "bf16":
             # the decode workload with fp8 activations (power-of-two 1x128 scales) in place of bf16
             w.dtype, w.name = "fp8", w.name.replace("bf16", "fp8")
-        if w.dtype != "fp8" or w.layout == "k_grouped":
-            print("--scales e8m0 / --weights e2m1 apply to the fp8 contiguous and the masked workloads",
-                  file=sys.stderr)
+        if w.dtype != "fp8" or (w.layout == "k_grouped" and w.weights == "e2m1"):
+            print("--scales e8m0 applies to the fp8 workloads (--dtype fp8 for the K-grouped one), --weights e2m1 "
+                  "to the contiguous and masked ones", file=sys.stderr)
             sys.exit(2)
         w.scales = "e8m0"
     if args.cold is None:
@@ -615,8 +620,10 @@ def main():
     bm_req = {"auto": 0, "exemplar": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] \
         if not args.block_m.isdigit() else int(args.block_m)
     exemplars = mg.exemplar_table() if args.block_m == "exemplar" and w.layout == "contiguous" else None
-    # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32
-    inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) if w.scales == "e8m0" else inp
+    # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32 (the K-grouped
+    # step picks its byte arrays itself)
+    inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) \
+        if w.scales == "e8m0" and w.layout != "k_grouped" else inp
     # fp32 activation scales handed over [K/128, rows] (the quantizer upstream writes them so; the
     # transpose here is input preparation, outside the timed region); the oracle keeps [rows, K/128]
     scale_km = w.dtype == "fp8" and w.scales != "e8m0" and args.a_scale == "km" and w.layout != "k_grouped"

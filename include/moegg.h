@@ -521,6 +521,32 @@ moegg_status_t moegg_grouped_gemm_k_grouped_fp8(
     const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw, int64_t scale_groups,
     void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * K-grouped weight gradient on e4m3 operands with E8M0 scales (DeepGEMM
+ * record, "Workarounds": the K-grouped MoE weight backward; the same record
+ * lists packed UE8M0 scale factors as the newer architecture's format).  The
+ * groups are those of moegg_grouped_gemm_k_grouped_fp8; each scale is an
+ * exponent byte b meaning 2^(b - 127).
+ *   X_scale   uint8 [scale_groups, Mw]; row g scales X's columns over group g.
+ *   dY_scale  uint8 [scale_groups, Nw]; likewise for dY.
+ *   dW        fp32 [G, Mw, Nw], overwritten:
+ *               dW[e, i, j] = sum over expert e's rows t of
+ *                   (X[t, i] * 2^(X_scale[g(t), i] - 127)) * (dY[t, j] * 2^(dY_scale[g(t), j] - 127))
+ *             in fp32.  The scales scale exactly (powers of two), so the
+ *             MFMA applies them to each group's products and accumulates
+ *             the group into dW's accumulator directly.  t_e = 0 writes zeros.
+ *   scale_groups  as for moegg_grouped_gemm_k_grouped_fp8.  A histogram that
+ *             needs more sets MOEGG_FLAG_SCALE_GROUPS; the missing groups'
+ *             scale bytes read as 0 (2^-127), which flushes their products to
+ *             zero.
+ * Constraints: as for moegg_grouped_gemm_k_grouped; scale arrays 4-byte
+ * aligned, and scale_groups * max(Mw, Nw) < 2^31 (UNSUPPORTED otherwise).
+ */
+moegg_status_t moegg_grouped_gemm_k_grouped_e8m0(
+    const void* X, const uint8_t* X_scale, const void* dY, const uint8_t* dY_scale, float* dW,
+    const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw, int64_t scale_groups,
+    void* ws, size_t ws_bytes, void* stream);
+
 /* Copy the stats of the last scheduled call on `ws` to the host.
  * Synchronizes `stream`. */
 moegg_status_t moegg_stats_read(const void* ws, moegg_stats_t* h_out, void* stream);

@@ -122,6 +122,8 @@ EXPORTS = {
     "moegg_grouped_gemm_k_grouped": (_I32, [_VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _VP, _SZ, _VP]),
     "moegg_grouped_gemm_k_grouped_fp8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I64,
                                                 _VP, _SZ, _VP]),
+    "moegg_grouped_gemm_k_grouped_e8m0": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I64, _I32, _I32, _I64,
+                                                 _VP, _SZ, _VP]),
     "moegg_stats_read": (_I32, [_VP, ctypes.POINTER(_Stats), _VP]),
     "moegg_stats_report": (_I32, [ctypes.POINTER(_Stats), ctypes.POINTER(_Report)]),
     "moegg_tile_list_read": (_I32, [_VP, ctypes.POINTER(_Tile), _I64, ctypes.POINTER(_I64), _VP]),
@@ -502,8 +504,9 @@ def k_scale_groups(t_sizes: Sequence[int]) -> int:
 
 def grouped_gemm_k_grouped(X, dY, dW, t_sizes, ws, X_scale=None, dY_scale=None, stream=None):
     """dW[e] = X_e^T @ dY_e over expert e's rows (see moegg.h).  bf16 X and dY;
-    or e4m3 X and dY with fp32 scales X_scale [S, Mw], dY_scale [S, Nw], one row
-    per 128-row group of each expert's segment (k_scale_groups gives S)."""
+    or e4m3 X and dY with scales X_scale [S, Mw], dY_scale [S, Nw], one row per
+    128-row group of each expert's segment (k_scale_groups gives S): fp32, or
+    uint8 E8M0 exponent bytes (2^(b - 127))."""
     _counts(t_sizes, "t_sizes")
     G = t_sizes.numel()
     _need(X, "X", [None, None], (torch.bfloat16, _E4M3))
@@ -520,10 +523,15 @@ def grouped_gemm_k_grouped(X, dY, dW, t_sizes, ws, X_scale=None, dY_scale=None, 
             _p(X), _p(dY), _p(dW), _p(t_sizes), G, T, Mw, Nw, _p(ws), ws.numel(), _stream(stream)),
             "moegg_grouped_gemm_k_grouped")
         return
-    _need(X_scale, "X_scale", [None, Mw], (torch.float32,))
+    _need(X_scale, "X_scale", [None, Mw], (torch.float32, torch.uint8))
     S = X_scale.shape[0]
-    _need(dY_scale, "dY_scale", [S, Nw], (torch.float32,))
+    _need(dY_scale, "dY_scale", [S, Nw], (X_scale.dtype,))
     _one_device(X, X_scale, dY, dY_scale, dW, t_sizes, ws)
+    if X_scale.dtype == torch.uint8:
+        _check(lib().moegg_grouped_gemm_k_grouped_e8m0(
+            _p(X), _p(X_scale), _p(dY), _p(dY_scale), _p(dW), _p(t_sizes), G, T, Mw, Nw, S, _p(ws), ws.numel(),
+            _stream(stream)), "moegg_grouped_gemm_k_grouped_e8m0")
+        return
     _check(lib().moegg_grouped_gemm_k_grouped_fp8(
         _p(X), _p(X_scale), _p(dY), _p(dY_scale), _p(dW), _p(t_sizes), G, T, Mw, Nw, S, _p(ws), ws.numel(),
         _stream(stream)), "moegg_grouped_gemm_k_grouped_fp8")

@@ -401,10 +401,11 @@ moegg_status_t moegg_grouped_gemm_masked(const void* A, const void* A_scale, con
     return hip_status(e, "masked GEMM launch");
 }
 
-// Shared by the bf16 and fp8 K-grouped calls.  esz: operand bytes per element.
-static moegg_status_t k_grouped_call(const void* X, const float* X_scale, const void* dY, const float* dY_scale,
+// Shared by the bf16 and fp8 K-grouped calls.  fp8: e4m3 operands with scales, fp32 or (e8m0) exponent bytes.
+static moegg_status_t k_grouped_call(const void* X, const void* X_scale, const void* dY, const void* dY_scale,
                                      float* dW, const int32_t* t_sizes, int G, int64_t T, int Mw, int Nw,
-                                     int64_t scale_groups, bool fp8, void* ws, size_t ws_bytes, void* stream) {
+                                     int64_t scale_groups, bool fp8, bool e8m0, void* ws, size_t ws_bytes,
+                                     void* stream) {
     // with T = 0 no row is read, so X and dY may be NULL (an empty tensor's pointer)
     if ((T > 0 && (!X || !dY)) || !dW || !t_sizes) return MOEGG_ERR_INVALID_ARG;
     if (G < 1 || G > kMaxExperts || T < 0 || Mw < 1 || Nw < 1) return MOEGG_ERR_INVALID_ARG;
@@ -417,7 +418,7 @@ static moegg_status_t k_grouped_call(const void* X, const float* X_scale, const 
         if (scale_groups < 0 || (T > 0 && (scale_groups < 1 || !X_scale || !dY_scale))) return MOEGG_ERR_INVALID_ARG;
         if (!aligned(X_scale, 4) || !aligned(dY_scale, 4)) return MOEGG_ERR_INVALID_ARG;
         // scale offsets are 32-bit; the parked offset 2^31 must lie past both arrays
-        if (scale_groups * (int64_t)std::max(Mw, Nw) * 4 >= 0x80000000ll) return MOEGG_ERR_UNSUPPORTED;
+        if (scale_groups * (int64_t)std::max(Mw, Nw) * (e8m0 ? 1 : 4) >= 0x80000000ll) return MOEGG_ERR_UNSUPPORTED;
     }
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     const WsLayout L = ws_layout(G, 0);
@@ -426,20 +427,29 @@ static moegg_status_t k_grouped_call(const void* X, const float* X_scale, const 
     hipError_t e = launch_sched_k_grouped(t_sizes, G, T, fp8 ? scale_groups : 0, ws, s);
     if (e != hipSuccess) return hip_status(e, "K-grouped scheduler launch");
     KGroupedArgs a{X, dY, dW, (const unsigned char*)ws, G, Mw, Nw, X_scale, dY_scale, scale_groups};
-    return hip_status(launch_k_grouped(a, fp8, s), "K-grouped GEMM launch");
+    return hip_status(launch_k_grouped(a, fp8, e8m0, s), "K-grouped GEMM launch");
 }
 
 moegg_status_t moegg_grouped_gemm_k_grouped(const void* X, const void* dY, float* dW, const int32_t* t_sizes, int G,
                                             int64_t T, int Mw, int Nw, void* ws, size_t ws_bytes, void* stream) {
-    return k_grouped_call(X, nullptr, dY, nullptr, dW, t_sizes, G, T, Mw, Nw, 0, false, ws, ws_bytes, stream);
+    return k_grouped_call(X, nullptr, dY, nullptr, dW, t_sizes, G, T, Mw, Nw, 0, false, false, ws, ws_bytes,
+                          stream);
 }
 
 moegg_status_t moegg_grouped_gemm_k_grouped_fp8(const void* X, const float* X_scale, const void* dY,
                                                 const float* dY_scale, float* dW, const int32_t* t_sizes, int G,
                                                 int64_t T, int Mw, int Nw, int64_t scale_groups, void* ws,
                                                 size_t ws_bytes, void* stream) {
-    return k_grouped_call(X, X_scale, dY, dY_scale, dW, t_sizes, G, T, Mw, Nw, scale_groups, true, ws, ws_bytes,
-                          stream);
+    return k_grouped_call(X, X_scale, dY, dY_scale, dW, t_sizes, G, T, Mw, Nw, scale_groups, true, false, ws,
+                          ws_bytes, stream);
+}
+
+moegg_status_t moegg_grouped_gemm_k_grouped_e8m0(const void* X, const uint8_t* X_scale, const void* dY,
+                                                 const uint8_t* dY_scale, float* dW, const int32_t* t_sizes, int G,
+                                                 int64_t T, int Mw, int Nw, int64_t scale_groups, void* ws,
+                                                 size_t ws_bytes, void* stream) {
+    return k_grouped_call(X, X_scale, dY, dY_scale, dW, t_sizes, G, T, Mw, Nw, scale_groups, true, true, ws,
+                          ws_bytes, stream);
 }
 
 moegg_status_t moegg_stats_report(const moegg_stats_t* h_stats, moegg_report_t* h_out) {

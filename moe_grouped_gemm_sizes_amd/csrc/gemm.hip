@@ -85,10 +85,12 @@ __device__ __forceinline__ int swz_mn(int k) {
 // M/N-contiguous): 512 threads as WAVES_M x WAVES_N waves over a BM x BN tile
 // of dW; a stage holds KSTEP rows of the reduction axis of both operands (128
 // bytes of each column: 64 bf16 rows, or 128 e4m3 rows = one scale group), and
-// with fp8 the group's scales of the tile's columns, [X scales | dY scales].
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool FP8_ = false>
+// with fp8 the group's scales of the tile's columns, [X scales | dY scales]:
+// fp32, or (E8M0) exponent bytes that the MFMA applies itself.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool FP8_ = false, bool E8M0_ = false>
 struct KCfg {
     static constexpr bool FP8 = FP8_;
+    static constexpr bool E8M0 = E8M0_;
     static constexpr int ESZ = FP8 ? 1 : 2;
     static constexpr int KSTEP = 128 / ESZ;            // reduction rows per stage
     static constexpr int BM = BM_, BN = BN_;
@@ -100,7 +102,7 @@ struct KCfg {
     static constexpr int MB = WTM / 16, NB = WTN / 16;             // 16x16 blocks per wave
     static constexpr int A_BYTES = BM * KSTEP * ESZ;
     static constexpr int B_BYTES = BN * KSTEP * ESZ;
-    static constexpr int S_BYTES = FP8 ? (BM + BN) * 4 : 0;
+    static constexpr int S_BYTES = FP8 ? (BM + BN) * (E8M0 ? 1 : 4) : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int A_LOADS = A_BYTES / 16 / THREADS;         // 16-byte DMAs per thread per stage
@@ -108,7 +110,8 @@ struct KCfg {
     static constexpr int OPS = A_LOADS + B_LOADS + (FP8 ? 1 : 0);  // fp8: one 4-byte scale DMA
     static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0, "stage split");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(!FP8 || BM + BN == THREADS, "one scale per thread per stage");
+    static_assert(!FP8 || E8M0 || BM + BN == THREADS, "one scale per thread per stage");
+    static_assert(!E8M0 || (FP8 && BM == 256 && BN == 256 && WAVES % 2 == 0), "E8M0: 256 scale bytes per wave");
     static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(OPS * (STAGES - 2) < 64, "vmcnt range");
 };
@@ -1168,7 +1171,20 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
     // the scale arrays reads 0 (MOEGG_FLAG_SCALE_GROUPS).
     __amdgpu_buffer_rsrc_t rss = make_rsrc(nullptr, 0);
     uint32_t ss_voff = 0, ss_step = 0, ss_dst = 0;
-    if constexpr (C::FP8) {
+    if constexpr (C::E8M0) {
+        // even waves: the tile's 256 X scale bytes of the group (4 per lane), odd
+        // waves: its 256 dY scale bytes; the waves of a parity write the same
+        // bytes to the same slots
+        const int64_t g0 = ((const int64_t*)(p.ws + L.groups))[e];
+        const bool xs = (wave & 1) == 0;
+        const uint32_t srow = xs ? (uint32_t)p.Mw : (uint32_t)p.Nw;
+        rss = xs ? make_rsrc(p.X_scale, (uint32_t)(p.scale_groups * srow))
+                 : make_rsrc(p.dY_scale, (uint32_t)(p.scale_groups * srow));
+        const int col = (xs ? i0 : j0) + lane * 4;
+        ss_voff = g0 < p.scale_groups ? (uint32_t)(g0 * srow) + col : 0x80000000u;
+        ss_step = srow;
+        ss_dst = C::A_BYTES + C::B_BYTES + (xs ? 0 : C::BM);
+    } else if constexpr (C::FP8) {
         const int64_t g0 = ((const int64_t*)(p.ws + L.groups))[e];
         const bool xs = wave < C::BM / 64;
         const uint32_t srow = xs ? (uint32_t)p.Mw * 4 : (uint32_t)p.Nw * 4;
@@ -1202,7 +1218,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
         // the read stage and the DMA stage of a step differ (see TileGemm::step)
         auto step = [&](const char* __restrict__ tx, char* __restrict__ wr, int next) {
             const char* ty = tx + C::A_BYTES;
-            if constexpr (C::FP8) {
+            if constexpr (C::E8M0) {
+                // the group's scale bytes go to the MFMA: scale_a (dY, the A operand)
+                // is each lane's dY column byte, scale_b (X) its X column byte, and the
+                // MFMA adds the scaled group straight into acc: no VALU work per group.
+                // (Adding a zero-started group partial to acc on the VALU instead gives
+                // the fp32-scale kernel's bits but costs 11 %.)
+                const MOEGG_LDS unsigned char* sxb = (const MOEGG_LDS unsigned char*)(ty + C::B_BYTES);
+                const MOEGG_LDS unsigned char* syb = sxb + C::BM;
+                v8i xa[C::MB];
+                int sxj[C::MB];
+#pragma unroll
+                for (int j = 0; j < C::MB; ++j) {
+                    xa[j] = frag_mn_fp8<C::BM>(tx, wm * C::WTM + j * 16);
+                    sxj[j] = sxb[wm * C::WTM + j * 16 + r16];
+                }
+                auto fragy = [&](int i) { return frag_mn_fp8<C::BN>(ty, wn * C::WTN + i * 16); };
+                v8i yb[2];
+                yb[0] = fragy(0);
+                static_for<0, C::NB>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (i + 1 < C::NB) yb[(i + 1) & 1] = fragy(i + 1);
+                    const int syi = syb[wn * C::WTN + i * 16 + r16];
+#pragma unroll
+                    for (int j = 0; j < C::MB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(yb[i & 1], xa[j], acc[i][j], 0,
+                                                                                     0, 0, syi, 0, sxj[j]);
+                    if constexpr (i == 0) issue(next, wr);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            } else if constexpr (C::FP8) {
                 // this wave's X fragments and row scales, then the dY blocks one ahead
                 // of their MFMAs; each block's partials promoted with the group's scales
                 const float* sx = (const float*)(ty + C::B_BYTES);
@@ -1309,6 +1354,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_grouped_kernel(KGroupedArgs p
 
 using KGroupedCfg = KCfg<256, 256, 4, 2, 2>;
 using KGroupedFp8Cfg = KCfg<256, 256, 4, 2, 2, true>;
+using KGroupedE8Cfg = KCfg<256, 256, 4, 2, 2, true, true>;
 
 // Raise a kernel's dynamic LDS limit once per process (it is a function
 // attribute, not a stream operation).
@@ -1422,7 +1468,8 @@ hipError_t launch_mlp_fused(const MlpArgs& a, int n_workgroups, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, bool e8m0, hipStream_t s) {
+    if (e8m0) return launch_k_grouped_t<KGroupedE8Cfg>(a, s);
     return fp8 ? launch_k_grouped_t<KGroupedFp8Cfg>(a, s) : launch_k_grouped_t<KGroupedCfg>(a, s);
 }
 

@@ -39,8 +39,8 @@ struct KGroupedArgs {
     float* dW;
     const unsigned char* ws;
     int G, Mw, Nw;
-    const float* X_scale;          // fp8: [scale_groups, Mw] fp32, else NULL
-    const float* dY_scale;         // fp8: [scale_groups, Nw] fp32, else NULL
+    const void* X_scale;           // fp8: [scale_groups, Mw] fp32 or E8M0 bytes, else NULL
+    const void* dY_scale;          // fp8: [scale_groups, Nw] fp32 or E8M0 bytes, else NULL
     int64_t scale_groups;          // rows of the fp8 scale arrays
 };
 
@@ -66,7 +66,7 @@ hipError_t launch_contiguous(const ContigArgs& a, bool fp8, bool e8m0, bool w4, 
 hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int64_t rows_total, int block_m,
                                     hipStream_t s);
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
-hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, bool e8m0, hipStream_t s);
 // n_words 32-bit zeros at p (a fill kernel: graph-capturable, no memset node)
 hipError_t launch_zero(uint32_t* p, int64_t n_words, hipStream_t s);
 // the fused expert MLP on fp8 operands (e4m3 A, W1, H, W2 with fp32 scales); one workgroup per

@@ -71,6 +71,14 @@ int main(void) {
                                             ws, NULL), MOEGG_ERR_UNSUPPORTED);      /* scale offsets past 2^31 */
     EXPECT(moegg_grouped_gemm_k_grouped_fp8(fake, fake, fake, fake, fake, fake, 16, 100, 2000, 7168, 16, fake, ws,
                                             NULL), MOEGG_ERR_UNSUPPORTED);
+    EXPECT(moegg_grouped_gemm_k_grouped_e8m0(fake, NULL, fake, fake, fake, fake, 16, 100, 2048, 7168, 16, fake, ws,
+                                             NULL), MOEGG_ERR_INVALID_ARG);         /* missing X scales */
+    EXPECT(moegg_grouped_gemm_k_grouped_e8m0(fake, (const uint8_t*)odd, fake, fake, fake, fake, 16, 100, 2048, 7168,
+                                             16, fake, ws, NULL), MOEGG_ERR_INVALID_ARG);   /* misaligned scales */
+    EXPECT(moegg_grouped_gemm_k_grouped_e8m0(fake, fake, fake, fake, fake, fake, 16, 100, 2048, 7168, 300000, fake,
+                                             ws, NULL), MOEGG_ERR_UNSUPPORTED);     /* scale offsets past 2^31 */
+    EXPECT(moegg_grouped_gemm_k_grouped_e8m0(fake, fake, fake, fake, fake, fake, 16, 100, 2048, 7168, 80000, NULL,
+                                             0, NULL), MOEGG_ERR_WORKSPACE);        /* 80000 groups fit bytes */
     {
         moegg_stats_t st = {0};
         moegg_report_t rep;

@@ -162,6 +162,8 @@ def k_grouped_args(fp8=False):
     (True, dict(X_scale=t(6, 512)), "X_scale: shape"),
     (True, dict(dY_scale=t(5, 512)), "dY_scale: shape"),
     (True, dict(X_scale=None), "X_scale: tensor expected"),
+    (True, dict(dY_scale=t(6, 512, dtype=torch.uint8)), "dY_scale: dtype"),
+    (True, dict(X_scale=t(6, 256, dtype=torch.int32)), "X_scale: dtype"),
 ])
 def test_k_grouped_mismatch_raises(fp8, change, name):
     kw = k_grouped_args(fp8)

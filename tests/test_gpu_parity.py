@@ -1130,17 +1130,23 @@ def test_expert_mlp_full_size():
 # ----------------------------------------------------------------- K-grouped
 
 
-def run_k_grouped(t_sizes, Mw, Nw, seed=5, values="normal_unit", dtype="bf16"):
-    w = wl.Workload("kg", "k_grouped", dtype, t_sizes, Mw=Mw, Nw=Nw, values=values, seed=seed)
+def run_k_grouped(t_sizes, Mw, Nw, seed=5, values="normal_unit", dtype="bf16", scales="fp32"):
+    """scales "e8m0": power-of-two scales, passed to the library as exponent bytes
+    (the oracle takes the same scales as fp32 values)."""
+    w = wl.Workload("kg", "k_grouped", dtype, t_sizes, Mw=Mw, Nw=Nw, values=values, seed=seed, scales=scales)
     inp = wl.materialize(w, "cuda")
     dW = torch.full((w.G, Mw, Nw), float("nan"), device="cuda")
     ws = mg.workspace(w.G, 0)
-    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws, inp.get("X_scale"), inp.get("dY_scale"))
+    e8 = scales == "e8m0"
+    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], dW, inp["counts"], ws,
+                              inp.get("X_scale_e8m0" if e8 else "X_scale"), inp.get("dY_scale_e8m0" if e8 else "dY_scale"))
     torch.cuda.synchronize()
     return w, inp, dW, ws
 
 
 def k_grouped_ref(w, inp, pairs):
+    """fp8 with either scale form: the oracle takes the fp32 scales (for E8M0 the
+    powers of two the bytes encode)."""
     X, dY = P.cpu(inp["X"]), P.cpu(inp["dY"])
     if w.dtype == "fp8":
         return og.k_grouped_fp8(X, P.cpu(inp["X_scale"]), dY, P.cpu(inp["dY_scale"]), w.counts,
@@ -1149,11 +1155,17 @@ def k_grouped_ref(w, inp, pairs):
 
 
 def check_k_grouped(w, inp, dW, pairs, ref=None):
-    """dW rows against the oracle: fp32 output, so only fp32 accumulation separates them
-    (rel. Frobenius <= 1e-4 and the fp32 per-element bound)."""
+    """dW rows against the oracle: fp32 output, so only the accumulation separates them
+    (rel. Frobenius <= 1e-4 and the fp32 per-element bound; with e4m3 operands plus
+    the term for the fp8 MFMA's group sums, S from the oracle on |X| and |dY|)."""
     ref = k_grouped_ref(w, inp, pairs) if ref is None else ref
+    abs_sum = None
+    if w.dtype == "fp8":
+        mag = {k: (v.float().abs().to(torch.float8_e4m3fn) if k in ("X", "dY") else v) for k, v in inp.items()}
+        abs_sum = k_grouped_ref(w, mag, pairs)
     got = dW[torch.tensor([e for e, _ in pairs]), torch.tensor([i for _, i in pairs])].cpu().double().numpy()
-    return P.check_gemm(got, ref, "fp32", bound="fp32", what=f"k-grouped {w.dtype} G={w.G} Mw={w.Mw} Nw={w.Nw}")
+    return P.check_gemm(got, ref, "fp32", bound="fp32", what=f"k-grouped {w.dtype} G={w.G} Mw={w.Mw} Nw={w.Nw}",
+                        abs_sum=abs_sum)
 
 
 def k_rows_every_block(G, Mw, seed):
@@ -1189,6 +1201,106 @@ def test_k_grouped_config_full_size(dtype):
             assert not dW[e].any()
     st = mg.stats_read(ws)
     assert st.U == sum(w.counts) and st.error_flags == 0
+
+
+def k_grouped_matches_fp32_scales(inp, dW, ws):
+    """Every element against the fp32-scale call on the same power-of-two scales.
+    The two differ only in where each group's scaled partial sum is rounded (into
+    the accumulator inside the MFMA, or on its own and then added), one rounding
+    of the accumulator per group either way: at most 512 groups (65536 rows) of
+    2^-24 each stay far below 2^-10 of the row's rms, which one wrong 16 x 16
+    block or one lost group exceeds."""
+    ref = torch.full_like(dW, float("nan"))
+    mg.grouped_gemm_k_grouped(inp["X"], inp["dY"], ref, inp["counts"], ws, inp["X_scale"], inp["dY_scale"])
+    torch.cuda.synchronize()
+    rms = ref.double().pow(2).mean(dim=-1, keepdim=True).sqrt()
+    diff = (dW.double() - ref.double()).abs()
+    worst = float(torch.where(diff == 0, torch.zeros_like(diff), diff / (2.0 ** -10 * rms)).max())
+    print(f"e8m0 call against the fp32-scale call: max |diff| / (2^-10 rms(row)) = {worst:.3e}", flush=True)
+    assert bool(torch.isfinite(dW).all()) and worst <= 1.0
+
+
+def test_k_grouped_e8m0_small():
+    """E8M0 scale bytes, applied by the MFMA: ragged segments around the 128-row
+    group, every dW row against the oracle, and every element against the
+    fp32-scale call."""
+    t = [100, 0, 37, 200, 1, 129, 256, 300]
+    announce("k-grouped e8m0 small", t)
+    w, inp, dW, ws = run_k_grouped(t, 512, 512, dtype="fp8", scales="e8m0", seed=28)
+    assert bool((torch.exp2(inp["X_scale_e8m0"].float() - 127) == inp["X_scale"]).all())
+    pairs = [(e, i) for e in range(w.G) for i in range(w.Mw)]
+    check_k_grouped(w, inp, dW, pairs)
+    assert not dW[1].any()
+    st = mg.stats_read(ws)
+    assert st.U == sum(t) and st.error_flags == 0
+    k_grouped_matches_fp32_scales(inp, dW, ws)
+
+
+def test_k_grouped_e8m0_full_size():
+    """The Dirichlet weight-gradient workload with E8M0 scales: one dW row from
+    every 16-row block of every i-tile of every expert against the oracle, and
+    the whole dW against the fp32-scale call."""
+    w0 = wl.workload(5)
+    announce("k-grouped e8m0 config 5", w0.counts)
+    w, inp, dW, ws = run_k_grouped(w0.counts, w0.Mw, w0.Nw, dtype="fp8", scales="e8m0")
+    pairs = k_rows_every_block(w.G, w.Mw, seed=6)
+    check_k_grouped(w, inp, dW, pairs)
+    for e, t in enumerate(w.counts):
+        if t == 0:
+            assert not dW[e].any()
+    assert mg.stats_read(ws).error_flags == 0
+    k_grouped_matches_fp32_scales(inp, dW, ws)
+
+
+def test_k_grouped_e8m0_integer_exact_and_deterministic():
+    """e4m3 codes in {-1, 0, 1} with scale bytes 124..130 (2^-3..2^3) per group
+    and column: every partial sum is exact in fp32, so GPU == oracle bit for bit,
+    and two runs agree.  Segments straddle the 128-row group."""
+    t = [1, 127, 128, 129, 255, 0, 300]
+    T, Mw, Nw = sum(t), 256, 512
+    announce("k-grouped e8m0 integer exact", t)
+    g = torch.Generator().manual_seed(11)
+    X = torch.randint(-1, 2, (T, Mw), generator=g).float().to(torch.float8_e4m3fn)
+    dY = torch.randint(-1, 2, (T, Nw), generator=g).float().to(torch.float8_e4m3fn)
+    S = mg.k_scale_groups(t)
+    bx = torch.randint(124, 131, (S, Mw), generator=g).to(torch.uint8)
+    by = torch.randint(124, 131, (S, Nw), generator=g).to(torch.uint8)
+    outs = []
+    ws = mg.workspace(len(t), 0)
+    for _ in range(2):
+        dW = torch.full((len(t), Mw, Nw), float("nan"), device="cuda")
+        mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws,
+                                  bx.cuda(), by.cuda())
+        torch.cuda.synchronize()
+        outs.append(dW.cpu())
+    assert torch.equal(outs[0], outs[1])
+    pairs = [(e, i) for e in range(len(t)) for i in range(Mw)]
+    sx, sy = torch.exp2(bx.float() - 127), torch.exp2(by.float() - 127)
+    ref = og.k_grouped_fp8(X, sx, dY, sy, t, [e for e, _ in pairs], [i for _, i in pairs])
+    assert np.array_equal(outs[0].double().numpy().reshape(len(t) * Mw, Nw), ref)
+    assert mg.stats_read(ws).error_flags == 0
+
+
+def test_k_grouped_e8m0_too_few_scale_groups_is_flagged():
+    """E8M0 scale arrays short of the histogram's groups: the flag is set and the
+    missing groups' bytes read as 0 (2^-127), which flushes their products to 0."""
+    t = [200, 100]
+    announce("k-grouped e8m0 scale groups flag", t)
+    Mw = Nw = 256
+    g = torch.Generator().manual_seed(13)
+    X, sx = wl.quantize_k_groups_e4m3(torch.randn(300, Mw, generator=g), t, pow2=True)
+    dY, sy = wl.quantize_k_groups_e4m3(torch.randn(300, Nw, generator=g), t, pow2=True)
+    bx, by = wl.e8m0_bytes(sx), wl.e8m0_bytes(sy)
+    dW = torch.full((2, Mw, Nw), float("nan"), device="cuda")
+    ws = mg.workspace(2, 0)
+    mg.grouped_gemm_k_grouped(X.cuda(), dY.cuda(), dW, torch.tensor(t, dtype=torch.int32, device="cuda"), ws,
+                              bx[:2].contiguous().cuda(), by[:2].contiguous().cuda())
+    torch.cuda.synchronize()
+    assert mg.stats_read(ws).error_flags & mg.FLAG_SCALE_GROUPS
+    pairs = [(0, i) for i in range(0, Mw, 5)]
+    ref = og.k_grouped_fp8(X, sx, dY, sy, t, [e for e, _ in pairs], [i for _, i in pairs])
+    P.check_gemm(dW[0, 0:Mw:5].cpu().double().numpy(), ref, "fp32", bound="fp32", what="k-grouped e8m0 complete")
+    assert not dW[1].any()
 
 
 def test_k_grouped_integer_exact_and_ragged():

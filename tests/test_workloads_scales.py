@@ -44,3 +44,23 @@ def test_pow2_scale_is_the_next_power_of_two():
     assert float(s[0, 0]) == 4.0 and float(q.float()[0, 0]) == 448.0
     _, s = wl.quantize_rows_e4m3(torch.zeros(1, 128), pow2=True)
     assert float(s[0, 0]) == 1.0
+
+
+def test_k_grouped_pow2_scales_and_bytes_agree():
+    """K-grouped operands with E8M0 scales: one byte per (group, column), decoding
+    to the fp32 power-of-two scale of that group; scaled codes fit e4m3."""
+    t = [100, 0, 37, 200, 129]
+    w = wl.Workload("kg e8", "k_grouped", "fp8", t, Mw=256, Nw=512, values="normal_unit", seed=5, scales="e8m0")
+    inp = wl.materialize(w, "cpu")
+    S = wl.k_group_starts(t)[-1]
+    for name, M in (("X", 256), ("dY", 512)):
+        s, b = inp[name + "_scale"], inp[name + "_scale_e8m0"]
+        assert s.shape == b.shape == (S, M) and b.dtype == torch.uint8
+        assert torch.equal(torch.exp2(b.double() - 127).float(), s)
+        assert bool((torch.log2(s) == torch.round(torch.log2(s))).all())
+        assert float(inp[name].float().abs().max()) <= 448.0
+    # without e8m0 the scales are amax / 448 and no bytes are drawn
+    w.scales = "fp32"
+    inp = wl.materialize(w, "cpu")
+    assert "X_scale_e8m0" not in inp and not bool((torch.log2(inp["X_scale"]) ==
+                                                   torch.round(torch.log2(inp["X_scale"]))).all())

@@ -229,13 +229,14 @@ def k_group_starts(counts: Sequence[int]) -> List[int]:
     return starts
 
 
-def quantize_k_groups_e4m3(x: torch.Tensor, counts: Sequence[int]):
+def quantize_k_groups_e4m3(x: torch.Tensor, counts: Sequence[int], pow2: bool = False):
     """Operand [T, M] of the K-grouped weight gradient, rows grouped by expert ->
     (e4m3 codes [T, M], fp32 scales [n_groups, M]).
 
     Each scale covers one column over a group of up to 128 consecutive rows of
     one expert's segment (groups restart at every segment start; the last group
-    of a segment may be short): s = amax / 448, 1 for an all-zero group."""
+    of a segment may be short): s = amax / 448 (with pow2 the smallest power of
+    two at or above it), 1 for an all-zero group."""
     T, M = x.shape
     starts = k_group_starts(counts)
     q = torch.empty((T, M), dtype=torch.float8_e4m3fn, device=x.device)
@@ -246,7 +247,7 @@ def quantize_k_groups_e4m3(x: torch.Tensor, counts: Sequence[int]):
             r0, r1 = off + gi * SCALE_GROUP, min(off + (gi + 1) * SCALE_GROUP, off + t)
             blk = x[r0:r1].float()
             amax = blk.abs().amax(dim=0, keepdim=True)
-            sg = _scale_for(amax, False)
+            sg = _scale_for(amax, pow2)
             q[r0:r1] = _to_e4m3(blk / sg)
             s[starts[e] + gi] = sg.squeeze(0)
         off += t
@@ -341,6 +342,9 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
     contiguous: A [rows_total, K], B [G, K, N], counts int32 [G]
     masked:     A [G, cap, K],     B [G, K, N], counts int32 [G]
     k_grouped:  X [T, Mw], dY [T, Nw],          counts int32 [G]
+                (fp8: X_scale [n_groups, Mw], dY_scale [n_groups, Nw] fp32; with
+                scales == "e8m0" powers of two, and X_scale_e8m0 / dY_scale_e8m0
+                the same as exponent bytes)
     fp8 adds A_scale [..., K/128] and B_scale [G, K/128, N/128] (fp32).  With
     scales == "e8m0" those are powers of two, and A_scale_e8m0 [K/128, rows]
     (contiguous layout) and B_scale_e8m0 [G, K/128, N/128] hold the same
@@ -357,9 +361,14 @@ def materialize(wl: Workload, device="cpu", nan_padding: bool = True) -> Dict[st
         x = _values((T, wl.Mw), wl, T, s + 1, device)
         dy = _values((T, wl.Nw), wl, T, s + 2, device)
         if wl.dtype == "fp8":
-            # e4m3 with fp32 scales per 128-row group of each expert's segment
-            out["X"], out["X_scale"] = quantize_k_groups_e4m3(x, wl.counts)
-            out["dY"], out["dY_scale"] = quantize_k_groups_e4m3(dy, wl.counts)
+            # e4m3 with fp32 scales per 128-row group of each expert's segment; with
+            # scales == "e8m0" powers of two, also as exponent bytes [n_groups, M]
+            pow2 = wl.scales == "e8m0"
+            out["X"], out["X_scale"] = quantize_k_groups_e4m3(x, wl.counts, pow2)
+            out["dY"], out["dY_scale"] = quantize_k_groups_e4m3(dy, wl.counts, pow2)
+            if pow2:
+                out["X_scale_e8m0"] = e8m0_bytes(out["X_scale"])
+                out["dY_scale_e8m0"] = e8m0_bytes(out["dY_scale"])
         else:
             out["X"], out["dY"] = to_bf16(x), to_bf16(dy)
         return out
