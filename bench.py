@@ -299,9 +299,15 @@ def run_mlp(args):
     def sched():
         mg.schedule(inp["counts"], R, ws, block_m=0, N=2 * I)
 
+    w1_layout = mg.B_NK
+    if w4 and not args.mlp_fused:
+        # fp4 gate/up weights repacked once into 256-row panels: whole lines per K step
+        inp["W1"] = mg.pack_panels(inp["W1"], mg.B_NK_PANEL, mg.PANEL_CONTIGUOUS)
+        w1_layout = mg.B_NK_PANEL
+
     def l1():
         mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, a_s, w1_s, block_m=bm, H_scale=Hs,
-                                         scale_km=km_l1)
+                                         scale_km=km_l1, b_layout=w1_layout)
 
     def l2():
         mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=bm,
@@ -552,7 +558,7 @@ def main():
     ap.add_argument("--b-layout", choices=("auto", "kn", "nk", "kn-panel", "nk-panel"), default="auto",
                     help="weight storage: [G,K,N] (kn) or [G,N,K] (nk, the K-contiguous form fp8 MoE weights "
                          "are usually kept in; repacking is one-time, outside the timed steps).  auto: nk for "
-                         "the contiguous workloads, kn (as the masked workload prints it) for the masked one.  "
+                         "the contiguous workloads, kn-panel for the masked one, nk-panel for fp4 weights.  "
                          "kn-panel / nk-panel: the same weights repacked in column panels of the call's tile "
                          "width, so that each K step's weight tile is one contiguous block (one-time repack)")
     args = ap.parse_args()
@@ -597,19 +603,20 @@ def main():
     log(f"workload {args.config}: {w.name}, G={w.G}, U={sum(w.counts)}")
     inp = wl.materialize(w, "cuda")
     # auto: K-contiguous [G,N,K] for the contiguous workloads; for the decode workload its [G,K,N] weights
-    # repacked once into 128-column panels, which it streams (fp4 weights come as [G,N,K/2] only)
+    # repacked once into 128-column panels, which it streams; fp4 weights, drawn [G,N,K/2], repacked once
+    # into panels of the call's column tile, so that each K step reads whole lines
     layout = args.b_layout if args.b_layout != "auto" else \
-        ("kn-panel" if w.layout == "masked" and w.weights != "e2m1" else "nk")
-    if w.weights == "e2m1" and layout != "nk":
-        print("fp4 weights are stored [G,N,K/2] only", file=sys.stderr)
+        ("nk-panel" if w.weights == "e2m1" else "kn-panel" if w.layout == "masked" else "nk")
+    if w.weights == "e2m1" and layout not in ("nk", "nk-panel"):
+        print("fp4 weights are stored [G,N,K/2] (nk) or in its panels (nk-panel)", file=sys.stderr)
         sys.exit(2)
     b_layout = {"kn": mg.B_KN, "nk": mg.B_NK, "kn-panel": mg.B_KN_PANEL, "nk-panel": mg.B_NK_PANEL}[layout]
     oracle_inp = dict(inp)                # the oracle reads the weights as drawn, [G, K, N]
     if b_layout == mg.B_NK and "B" in inp and w.weights != "e2m1":
         inp["B"] = inp["B"].transpose(1, 2).contiguous()       # static weights, stored K-contiguous
     elif b_layout in (mg.B_KN_PANEL, mg.B_NK_PANEL):
-        if w.weights == "e2m1" or w.layout == "k_grouped":
-            print("panel layouts apply to e4m3 / bf16 weights of the contiguous and masked workloads", file=sys.stderr)
+        if w.layout == "k_grouped":
+            print("panel layouts apply to the contiguous and masked workloads", file=sys.stderr)
             sys.exit(2)
         inp["B"] = mg.pack_panels(inp["B"], b_layout,
                                   mg.PANEL_MASKED if w.layout == "masked" else mg.PANEL_CONTIGUOUS)

@@ -55,9 +55,10 @@ typedef enum {
  * record lists for SM100 (FP8 x FP4): activations as for
  * MOEGG_FP8_E4M3_E8M0, weights as OCP E2M1 (fp4: sign, 2 exponent bits with
  * bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two per
- * byte, element 2i in the low nibble, stored [G, N, K/2] (b_layout must be
- * MOEGG_B_NK), with E8M0 weight-block scales [G, K/128, N/128].  The same
- * gfx950 MFMA takes the fp4 operand directly.  Contiguous and masked layouts. */
+ * byte, element 2i in the low nibble, stored [G, N, K/2] (MOEGG_B_NK) or in
+ * its panels [G, N/P, K/128, P, 64] (MOEGG_B_NK_PANEL), with E8M0
+ * weight-block scales [G, K/128, N/128].  The same gfx950 MFMA takes the fp4
+ * operand directly.  Contiguous and masked layouts and the SwiGLU call. */
 /* MOEGG_FP8_E4M3_SCALE_KM is MOEGG_FP8_E4M3 with the fp32 activation
  * scales stored transposed, [K/128, rows] (the record's note that SM100 wants
  * a transposed LHS scale layout; here for fp32 scales).  One K step's scales
@@ -77,9 +78,10 @@ typedef enum {
  *   MOEGG_B_NK: B[G, N, K], K contiguous.
  *   MOEGG_B_KN_PANEL: B[G, N/P, K, P]: the columns in panels of P, each panel
  *     K rows of P contiguous elements, panels back to back.
- *   MOEGG_B_NK_PANEL: B[G, N/P, K/S, P, S], S = 128 bytes of K (64 bf16, 128
- *     e4m3): each panel of P columns stored one K step at a time, so the
- *     weights one tile loads per K step are one contiguous block.
+ *   MOEGG_B_NK_PANEL: B[G, N/P, K/S, P, S], S = one K step: 128 bytes of K
+ *     (64 bf16, 128 e4m3), or 64 bytes (128 packed fp4 codes): each panel of
+ *     P columns stored one K step at a time, so the weights one tile loads
+ *     per K step are one contiguous block of whole cache lines.
  * P is the column tile of the call: 256 for the contiguous and SwiGLU calls,
  * 128 for the masked call.  The panel layouts are one-time weight repacks,
  * like the choice between [G,K,N] and [G,N,K]; they change where a weight

@@ -207,8 +207,16 @@ def _counts(t, name: str, G: Optional[int] = None):
 def pack_panels(B: torch.Tensor, b_layout: int, P: int) -> torch.Tensor:
     """Weights [G, K, N] -> the paneled layout the kernels stream (include/moegg.h):
     B_KN_PANEL [G, N/P, K, P]; B_NK_PANEL [G, N/P, K/S, P, S] with S = 128 bytes of
-    K.  P: PANEL_CONTIGUOUS for the contiguous and SwiGLU calls, PANEL_MASKED for
-    the masked call.  A one-time weight transform."""
+    K.  Packed E2M1 weights (uint8) come as they are stored, [G, N, K/2], and go to
+    B_NK_PANEL [G, N/P, K/128, P, 64].  P: PANEL_CONTIGUOUS for the contiguous and
+    SwiGLU calls, PANEL_MASKED for the masked call.  A one-time weight transform."""
+    if B.dtype == torch.uint8:
+        if b_layout != B_NK_PANEL:
+            raise ValueError("packed E2M1 weights have the B_NK_PANEL panel layout only")
+        G, N, KB = B.shape
+        if N % P or KB % 64:
+            raise ValueError(f"[G, N, K/2] = {list(B.shape)}: N % {P} and K/2 % 64 must be 0")
+        return B.reshape(G, N // P, P, KB // 64, 64).permute(0, 1, 3, 2, 4).contiguous()
     G, K, N = B.shape
     if N % P:
         raise ValueError(f"N = {N} is not a multiple of the panel width {P}")
@@ -249,7 +257,8 @@ def _operands(rows: int, K: int, A, A_scale, B, B_scale, G: int, b_layout: int, 
     row-major fp32 activation-scale array ([rows, K/128] unless given).
     Formats (include/moegg.h): bf16 x bf16, no scales; e4m3 x e4m3 with fp32
     scales ([rows, K/128], or [K/128, rows] with scale_km) or E8M0 bytes
-    ([K/128, rows]); e4m3 x packed E2M1 [G, N, K/2] (uint8) with E8M0 bytes."""
+    ([K/128, rows]); e4m3 x packed E2M1 [G, N, K/2] (uint8) or its panels with E8M0
+    bytes."""
     if b_layout not in (B_KN, B_NK, B_KN_PANEL, B_NK_PANEL):
         raise ValueError(f"b_layout: {b_layout}")
     if A.dtype == torch.bfloat16:
@@ -266,11 +275,15 @@ def _operands(rows: int, K: int, A, A_scale, B, B_scale, G: int, b_layout: int, 
         raise ValueError("e4m3 operands need A_scale and B_scale")
     if not isinstance(B, torch.Tensor):
         raise ValueError("B: tensor expected")
-    if B.dtype == torch.uint8:                              # packed E2M1 weights [G, N, K/2]
-        if b_layout != B_NK:
-            raise ValueError("packed E2M1 weights are stored [G, N, K/2]: b_layout must be B_NK")
-        N = B.shape[1]
-        _need(B, "B", [G, N, K // 2], (torch.uint8,))
+    if B.dtype == torch.uint8:                              # packed E2M1 weights [G, N, K/2] or its panels
+        if b_layout == B_NK:
+            N = B.shape[1]
+            _need(B, "B", [G, N, K // 2], (torch.uint8,))
+        elif b_layout == B_NK_PANEL:
+            _need(B, "B", [G, None, K // 128, P, 64], (torch.uint8,))
+            N = B.shape[1] * P
+        else:
+            raise ValueError("packed E2M1 weights are [G, N, K/2] (B_NK) or its panels (B_NK_PANEL)")
         _need(A_scale, "A_scale", [K // 128, rows], (torch.uint8,))
         _need(B_scale, "B_scale", [G, K // 128, N // 128], (torch.uint8,))
         if scale_km:

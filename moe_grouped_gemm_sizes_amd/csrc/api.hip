@@ -70,7 +70,8 @@ moegg_status_t check_common(const void* A, const void* A_scale, const void* B, c
         if (!A_scale || !B_scale) return MOEGG_ERR_INVALID_ARG;
         if (!aligned(A_scale, 4) || !aligned(B_scale, 4)) return MOEGG_ERR_INVALID_ARG;
     }
-    if (w4 && b_layout != MOEGG_B_NK) return MOEGG_ERR_UNSUPPORTED;      // packed E2M1 is [G, N, K/2] only
+    // packed E2M1 is [G, N, K/2] or its panels [G, N/P, K/128, P, 64]
+    if (w4 && b_layout != MOEGG_B_NK && b_layout != MOEGG_B_NK_PANEL) return MOEGG_ERR_UNSUPPORTED;
     // E8M0 scale rows are read four bytes at a time: N / 128 bytes per weight-scale row
     if (e8m0_scales(dtype) && (N % 512 != 0 || N / 128 > 256)) return MOEGG_ERR_UNSUPPORTED;
     if (K % (128 / esz) != 0 || N % col_tile != 0) return MOEGG_ERR_UNSUPPORTED;

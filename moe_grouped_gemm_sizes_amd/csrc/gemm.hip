@@ -332,11 +332,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 // The wave runs at raised priority (s_setprio) from the barrier to the end of
 // its MFMAs, so a SIMD's two waves drain their MFMA work ahead of the barrier.
 // WNT: the weight panel is read by this tile only, so its loads stream
-// (non-temporal); see load16_to_lds_cp.  Not for fp4 weights: a K step reads
-// half of each 128-byte line, and a streamed line is gone by the next step.
+// (non-temporal); see load16_to_lds_cp.
 template <class C, bool B_KN, bool WNT = false>
 struct TileGemm {
-    static constexpr int WCP = WNT && !C::W4 ? CP_NT : CP_DEFAULT;
+    static constexpr int WCP = WNT ? CP_NT : CP_DEFAULT;
     static constexpr int NSB = C::WTN >= 128 ? C::WTN / 128 : 1;   // weight-scale blocks per wave tile
     static constexpr int HSEG = C::WTN / 2;                        // weight rows per wave column half
     static_assert(B_KN || C::W4 || (C::B_OPS % 2 == 0 && (C::THREADS / 8) % HSEG == 0 && HSEG % 16 == 0),
@@ -412,7 +411,7 @@ struct TileGemm {
             static_assert(!B_KN, "fp4 weights are K-contiguous");
             const int f = J * C::THREADS + tid;
             const int row = f >> 2;
-            load16_to_lds_cp<WCP>(rb, row * b_row_bytes + (((f & 3) ^ swz_w4(row)) << 4), ks * C::WROW,
+            load16_to_lds_cp<WCP>(rb, row * b_row_bytes + (((f & 3) ^ swz_w4(row)) << 4), ks * b_step_bytes,
                              base + (J * C::THREADS + wave * 64) * 16);
         } else if constexpr (B_KN) {
             constexpr int RB = C::BN * C::ESZ, CPR = RB / 16, RPO = C::THREADS / CPR;
@@ -795,6 +794,15 @@ struct TileGemm {
 template <class C, bool B_KN, int SWIGLU = 0, bool WNT = false>
 __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int e, int row_start, int rows_valid,
                                             int ct) {
+    if constexpr (C::W4 && WNT) {
+        // fp4 weights stream only in panels: stored [G, N, K/2], a K step reads half of each
+        // 128-byte line, and a line loaded non-temporally is gone before the next step reads
+        // its other half
+        if (!p.b_panel) {
+            contig_tile<C, B_KN, SWIGLU, false>(p, lds, e, row_start, rows_valid, ct);
+            return;
+        }
+    }
     const int n0 = ct * C::BN;
     const int KB = p.K / 128;
     TileGemm<C, B_KN, WNT> tg;
@@ -803,9 +811,19 @@ __device__ __forceinline__ void contig_tile(const ContigArgs& p, char* lds, int 
     const size_t b_expert_bytes = C::W4 ? (size_t)p.K * p.N / 2 : (size_t)p.K * p.N * C::ESZ;
     const char* b_base = (const char*)p.B + (size_t)e * b_expert_bytes;
     if constexpr (C::W4) {
-        // packed E2M1 [G, N, K/2]: this column tile's BN rows of K/2 bytes
-        tg.b_row_bytes = (uint32_t)p.K / 2;
-        tg.rb = make_rsrc(b_base + (size_t)n0 * tg.b_row_bytes, (uint32_t)C::BN * tg.b_row_bytes);
+        if (p.b_panel) {
+            // packed E2M1 [G, N / BN, K / 128, BN, 64]: one K step of the column tile's BN rows back to
+            // back, so a step reads whole 128-byte lines
+            tg.rb = make_rsrc(b_base + (size_t)ct * C::BN * (p.K / 2), (uint32_t)C::BN * (p.K / 2));
+            tg.b_row_bytes = C::WROW;
+            tg.b_step_bytes = (uint32_t)C::BN * C::WROW;
+        } else {
+            // packed E2M1 [G, N, K/2]: this column tile's BN rows of K/2 bytes; a step reads
+            // 64 bytes of each, half a line
+            tg.b_row_bytes = (uint32_t)p.K / 2;
+            tg.rb = make_rsrc(b_base + (size_t)n0 * tg.b_row_bytes, (uint32_t)C::BN * tg.b_row_bytes);
+            tg.b_step_bytes = C::WROW;
+        }
         tg.b_col_byte = 0;
     } else if constexpr (B_KN) {
         if (p.b_panel) {

@@ -74,7 +74,8 @@ def test_contiguous_correct_arguments_reach_the_device_check(dtype, layout):
     ("e8m0", dict(B_scale=t(G, K // 128, N // 128)), "B_scale: dtype"),
     ("e8m0", dict(A_scale=t(ROWS, K // 128, dtype=torch.uint8)), "A_scale: shape"),
     ("fp4", dict(B=t(G, N, K, dtype=torch.uint8)), "B: shape"),
-    ("fp4", dict(b_layout=mg.B_KN), "b_layout must be B_NK"),
+    ("fp4", dict(b_layout=mg.B_KN), r"\(B_NK\) or its panels"),
+    ("fp4", dict(b_layout=mg.B_NK_PANEL), "B: shape"),
 ])
 def test_contiguous_mismatch_raises(dtype, change, name):
     kw = contiguous_args(dtype, mg.B_KN if dtype in ("bf16", "fp8_km") else mg.B_NK)
@@ -198,10 +199,10 @@ def test_pack_panels_index_mapping():
     assert nk.shape == (G, N // 128, K // 64, 128, 64)
     for e, k, n in [(0, 0, 0), (1, 255, 511), (0, 70, 300), (1, 191, 129)]:
         assert nk[e, n // 128, k // 64, n % 128, k % 64] == Bh[e, k, n]
-    B8 = B.to(torch.uint8)                                   # 1-byte elements: S = 128
-    nk8 = mg.pack_panels(B8, mg.B_NK_PANEL, 256)
+    B8 = B.to(torch.uint8).view(torch.float8_e4m3fn)         # 1-byte elements: S = 128
+    nk8 = mg.pack_panels(B8, mg.B_NK_PANEL, 256).view(torch.uint8)
     assert nk8.shape == (G, N // 256, K // 128, 256, 128)
-    assert nk8[1, 1, 1, 7, 5] == B8[1, 128 + 5, 256 + 7]
+    assert nk8[1, 1, 1, 7, 5] == B8.view(torch.uint8)[1, 128 + 5, 256 + 7]
 
 
 def test_panel_shapes_are_checked():
@@ -247,3 +248,18 @@ def test_expert_mlp_fused_mismatch_raises(change, name):
     kw.update(change)
     with pytest.raises(ValueError, match=name):
         mg.expert_mlp_fused(**kw)
+
+
+def test_pack_panels_fp4():
+    """Packed E2M1 [G, N, K/2] -> [G, N/P, K/128, P, 64]: K step s of panel p holds
+    rows p*P .. p*P+P-1, bytes 64 s .. 64 s + 63 of each, in row order."""
+    G, N, K, P = 2, 512, 512, 256
+    B = torch.randint(0, 256, (G, N, K // 2), dtype=torch.uint8)
+    Q = mg.pack_panels(B, mg.B_NK_PANEL, P)
+    assert Q.shape == (G, N // P, K // 128, P, 64)
+    for g, p, s, r in ((0, 0, 0, 0), (1, 1, 3, 255), (0, 1, 2, 17), (1, 0, 1, 200)):
+        assert torch.equal(Q[g, p, s, r], B[g, p * P + r, 64 * s:64 * s + 64])
+    with pytest.raises(ValueError, match="B_NK_PANEL panel layout only"):
+        mg.pack_panels(B, mg.B_KN_PANEL, P)
+    with pytest.raises(ValueError, match="must be 0"):
+        mg.pack_panels(B[:, :, :96].contiguous(), mg.B_NK_PANEL, P)

@@ -647,12 +647,14 @@ def test_contiguous_fp8_e8m0_full_size():
 # ----------------------------------------------------------------- fp8 x fp4 (E2M1 weights)
 
 
-def run_contiguous_fp4(w, inp, block_m):
+def run_contiguous_fp4(w, inp, block_m, b_layout=mg.B_NK):
+    """b_layout B_NK_PANEL: the packed weights cut into 256-row panels first."""
     C = P.sentinel_like((w.rows_total, w.N))
     ws = mg.workspace(w.G, w.rows_total)
-    mg.grouped_gemm_contiguous(inp["A"], inp["B"], C, inp["counts"], ws, A_scale=inp["A_scale_e8m0"],
+    B = inp["B"] if b_layout == mg.B_NK else mg.pack_panels(inp["B"], mg.B_NK_PANEL, mg.PANEL_CONTIGUOUS)
+    mg.grouped_gemm_contiguous(inp["A"], B, C, inp["counts"], ws, A_scale=inp["A_scale_e8m0"],
                                B_scale=inp["B_scale_e8m0"], seg_align=w.seg_align, block_m=block_m,
-                               b_layout=mg.B_NK)
+                               b_layout=b_layout)
     torch.cuda.synchronize()
     return C, ws
 
@@ -703,6 +705,34 @@ def test_contiguous_fp8_fp4_integer_exact(block_m):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("block_m", [0, 64, 128, 256, mg.BLOCK_M_PER_EXPERT])
+def test_contiguous_fp4_panels_bit_exact(block_m):
+    """fp4 weights in 256-row panels (one K step of a panel = 16 KB of whole
+    lines) give the same bits as [G, N, K/2] at every height."""
+    counts = [70, 0, 300, 6, 129, 3]
+    announce("contiguous fp4 panels", counts, "block_m", block_m)
+    w = wl.Workload("f4p", "contiguous", "fp8", counts, K=512, N=512, values="normal", seed=29, scales="e8m0",
+                    weights="e2m1")
+    inp = wl.materialize(w, "cuda")
+    C0, _ = run_contiguous_fp4(w, inp, block_m)
+    C1, _ = run_contiguous_fp4(w, inp, block_m, mg.B_NK_PANEL)
+    assert torch.equal(C0.view(torch.int16), C1.view(torch.int16))
+
+
+def test_masked_fp4_panels_bit_exact():
+    """The masked call with fp4 weights in 128-row panels: the same bits as
+    [G, N, K/2], with experts of one and of several row tiles."""
+    counts = [3, 0, 64, 65, 130, 1, 257]
+    announce("masked fp4 panels", counts)
+    w, inp, C0 = run_masked_low_precision(counts, 320, 512, 512, "e2m1", mg.B_NK, seed=30)
+    C1 = P.sentinel_like((w.G, w.cap, w.N))
+    mg.grouped_gemm_masked(inp["A"], mg.pack_panels(inp["B"], mg.B_NK_PANEL, mg.PANEL_MASKED), C1, inp["counts"],
+                           None, inp["A_scale_e8m0"], inp["B_scale_e8m0"], mg.B_NK_PANEL)
+    torch.cuda.synchronize()
+    assert torch.equal(C0.view(torch.int16), C1.view(torch.int16))
+    check_masked_fp4(w, inp, C1, counts)
+
+
 def test_contiguous_fp8_fp4_aligned_segments():
     """fp4 weights with segments aligned to 64 rows (gaps between experts stay untouched)."""
     counts = [70, 0, 300, 6, 129, 3]
@@ -735,6 +765,10 @@ def test_contiguous_fp8_fp4_full_size():
     ref = fp4.contiguous_fp8_fp4(cpu["A"], cpu["A_scale"], cpu["B"], cpu["B_scale"], w.counts, rows)
     P.check_gemm(P.rows_as_float(C, rows), ref, "fp8", what=f"fp4 full size block_m={st.block_m}")
     assert P.untouched_rows_ok(C, w.counts, w.seg_align)
+    # the paneled weights the benchmark streams: every element, bit for bit
+    inp = wl.materialize(w, "cuda")
+    C1, _ = run_contiguous_fp4(w, inp, 0, mg.B_NK_PANEL)
+    assert torch.equal(C.view(torch.int16), C1.view(torch.int16))
 
 
 # ----------------------------------------------------------------- exemplar selection
@@ -986,9 +1020,9 @@ def test_swiglu_e4m3_h_and_fp8_down_projection(block_m):
     P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain_e4m3", what=f"mlp fp8 H block_m={block_m} y")
 
 
-def run_mlp_fp4(counts, K, I, N2, block_m, seed):
+def run_mlp_fp4(counts, K, I, N2, block_m, seed, w1_layout=mg.B_NK):
     """L1 with fp4 gate/up weights (fp8 activations, E8M0 scales) and the e4m3 H
-    epilogue, then the fp8 L2 on H."""
+    epilogue, then the fp8 L2 on H.  w1_layout B_NK_PANEL: W1 in 256-row panels."""
     G, R = len(counts), sum(counts)
     inp = wl.materialize_mlp(counts, K=K, I=I, N2=N2, dtype="fp8", seed=seed, device="cuda", l2="fp8",
                              w1_format="e2m1")
@@ -997,8 +1031,9 @@ def run_mlp_fp4(counts, K, I, N2, block_m, seed):
     H = torch.empty((R, I), dtype=torch.float8_e4m3fn, device="cuda")
     Hs = torch.full((R, I // 128), float("nan"), device="cuda")
     Y = P.sentinel_like((R, N2))
-    mg.grouped_gemm_swiglu_scheduled(inp["A"], inp["W1"], H, G, ws, inp["A_scale_e8m0"], inp["W1_scale_e8m0"],
-                                     block_m=block_m, H_scale=Hs)
+    W1 = inp["W1"] if w1_layout == mg.B_NK else mg.pack_panels(inp["W1"], mg.B_NK_PANEL, mg.PANEL_CONTIGUOUS)
+    mg.grouped_gemm_swiglu_scheduled(inp["A"], W1, H, G, ws, inp["A_scale_e8m0"], inp["W1_scale_e8m0"],
+                                     block_m=block_m, H_scale=Hs, b_layout=w1_layout)
     mg.grouped_gemm_contiguous_scheduled(H, inp["W2"], Y, G, ws, Hs, inp["W2_scale"], block_m=block_m,
                                          b_layout=mg.B_NK)
     torch.cuda.synchronize()
@@ -1021,6 +1056,18 @@ def test_swiglu_fp4_weights(block_m):
     y = og.contiguous(qa, cpu["W2"].transpose(1, 2).contiguous(), counts, rows,
                       A_scale=torch.from_numpy(s).float().contiguous(), B_scale=cpu["W2_scale"])
     P.check_gemm(P.rows_as_float(Y, rows), y, "fp8", bound="chain_e4m3", what=f"mlp fp4 L1 block_m={block_m} y")
+
+
+@pytest.mark.parametrize("block_m", [0, mg.BLOCK_M_PER_EXPERT])
+def test_swiglu_fp4_panels_bit_exact(block_m):
+    """fp4 gate/up weights in 256-row panels: H, its scales and y bit for bit
+    as with [G, 2I, K/2]."""
+    counts = [70, 0, 300, 6, 129, 3]
+    announce("expert MLP fp4 L1 panels", counts, "block_m", block_m)
+    outs = [run_mlp_fp4(counts, 256, 256, 512, block_m, seed=31, w1_layout=lay)[1:]
+            for lay in (mg.B_NK, mg.B_NK_PANEL)]
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
 def test_expert_mlp_fp4_full_size():
