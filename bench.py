@@ -105,7 +105,7 @@ def algorithmic_bytes(w: wl.Workload) -> int:
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "device.hpp"):
+    for f in ("gemm.hip", "device.hpp", "tile_order.hpp", "mlp_order.hpp"):
         with open(os.path.join(ROOT, "moe_grouped_gemm_sizes_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

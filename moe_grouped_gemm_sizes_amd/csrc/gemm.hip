@@ -43,6 +43,7 @@
 #include "launch.hpp"
 #include "workspace.hpp"
 #include "mlp_order.hpp"
+#include "tile_order.hpp"
 
 namespace moegg {
 
@@ -918,7 +919,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void grouped_gemm_kernel(Contig
     const int item = block_to_item(blockIdx.x);
     if (item >= n_rt * n_ct) return;
     int rt, ct;
-    item_to_tiles(item, n_rt, n_ct, rt, ct);
+    item_to_list_tiles(item, n_rt, n_ct, (const moegg_tile_t*)(p.ws + L.tiles), false, rt, ct);
     const moegg_tile_t t = ((const moegg_tile_t*)(p.ws + L.tiles))[rt];
     if (t.tile == 0 && t.rows_valid < C::BM) {
         // the expert's only tile: this column's weight panel has no other reader, so it streams
@@ -998,7 +999,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_auto_kernel(ContigArgs p)
     const int item = block_to_item(blockIdx.x);
     if (item >= n_rt * n_ct) return;
     int rt, ct;
-    item_to_tiles(item, n_rt, n_ct, rt, ct);
+    item_to_list_tiles(item, n_rt, n_ct, tiles, bm == MOEGG_BLOCK_M_PER_EXPERT, rt, ct);
     const moegg_tile_t t = tiles[rt];
     // A weight panel that one tile alone reads streams (non-temporal loads): the per-expert list's tails
     // (1..128 rows, run after all full tiles) and, at any height, an expert's only tile.
