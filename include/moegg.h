@@ -379,12 +379,13 @@ moegg_status_t moegg_grouped_gemm_contiguous_scheduled(
  *            with MOEGG_FP8_E4M3_SCALE_KM), or (MOEGG_FP8_E4M3_FP4_E2M1) e4m3
  *            with E8M0 scale bytes [K/128, rows_total].  MOEGG_FP8_E4M3_E8M0
  *            is not supported here.
- *   W1       [G, 2I, K] (K-contiguous; b_layout must be MOEGG_B_NK): for
- *            q = 0 .. I/16 - 1 and w = 0 .. 15, row 32q + w is gate column
- *            16q + w and row 32q + 16 + w is up column 16q + w.  W1_scale
- *            (fp8): fp32 [G, K/128, 2I/128] over those interleaved rows.
- *            MOEGG_FP8_E4M3_FP4_E2M1: packed E2M1 [G, 2I, K/2], same row
- *            order, E8M0 W1_scale bytes [G, K/128, 2I/128].
+ *   W1       [G, 2I, K] (K-contiguous: b_layout MOEGG_B_NK, or its
+ *            256-row panels with MOEGG_B_NK_PANEL): for q = 0 .. I/16 - 1
+ *            and w = 0 .. 15, row 32q + w is gate column 16q + w and row
+ *            32q + 16 + w is up column 16q + w.  W1_scale (fp8): fp32
+ *            [G, K/128, 2I/128] over those interleaved rows.
+ *            MOEGG_FP8_E4M3_FP4_E2M1: packed E2M1 [G, 2I, K/2] (or its
+ *            panels), same row order, E8M0 W1_scale bytes [G, K/128, 2I/128].
  *   H        [rows_total, I].  For each valid row R of expert e:
  *                g = sum_k A[R,k] Wgate_e[k,c],  u = sum_k A[R,k] Wup_e[k,c],
  *                h[R, c] = silu(g) * u,  silu(g) = g / (1 + e^-g)
