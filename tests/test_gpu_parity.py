@@ -548,6 +548,46 @@ def test_masked_graph_replay():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_masked_graph_replay_across_heights(dtype):
+    """The masked kernel picks its row-tile height from masked_m on the device:
+    one captured graph replayed with counts that move every expert across the 64-
+    and 128-row heights and the multi-tile walk (and to empty and to cap), stats
+    included, each replay against the oracle."""
+    cap, K, N = 300, 256, 256
+    seqs = ([3, 0, 64, 65, 130], [128, 129, 0, 300, 1], [0, 0, 0, 0, 0], [257, 64, 65, 1, 200],
+            [300, 300, 300, 300, 300], [3, 0, 64, 65, 130])
+    announce("masked graph replay across heights", dtype)
+    w, inp = masked_case(seqs[0], cap, K, N, dtype, seed=33)
+    C = P.sentinel_like((w.G, cap, N))
+    ws = mg.workspace(w.G, w.G * cap)
+    mm = inp["counts"]
+    call = lambda: mg.grouped_gemm_masked(inp["A"], inp["B"], C, mm, ws, inp.get("A_scale"), inp.get("B_scale"),
+                                          mg.B_KN)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                                   # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for counts in seqs:
+        fresh = wl.materialize(wl.Workload("m", "masked", dtype, counts, K=K, N=N, cap=cap, seed=33), "cuda")
+        for k in ("A", "A_scale"):
+            if fresh.get(k) is not None:
+                inp[k].copy_(fresh[k])
+        mm.copy_(torch.tensor(counts, dtype=torch.int32))
+        C.view(torch.int16).fill_(P.SENTINEL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        P.check_stats(mg.stats_read(ws), counts, 128)
+        w.counts = counts
+        check_masked(w, inp, C, counts)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_contiguous_graph_replay(dtype):
     """Scheduler and contiguous GEMM captured together in one graph (block_m = 0:
     the device picks the height, every candidate kernel is in the graph).  The
