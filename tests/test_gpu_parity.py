@@ -212,6 +212,61 @@ def test_contiguous_maximum_expert_count():
     P.check_gemm(P.rows_as_float(C, rows), ref, "bf16", what="G=4096")
 
 
+def _rows_against_oracle(A, B, picks):
+    """Rows A[r] @ B[e] for picks [(r, e)], expert by expert: the oracle runs on
+    the picked rows gathered into a small contiguous problem (the full operand
+    is several GiB), which gives exactly those rows."""
+    picks = sorted(picks, key=lambda p: p[1])
+    G = B.shape[0]
+    counts = [sum(1 for _, e in picks if e == g) for g in range(G)]
+    idx = torch.tensor([r for r, _ in picks], device=A.device)
+    A_sub = A.reshape(-1, A.shape[-1])[idx].cpu()
+    ref = og.contiguous(A_sub, B.cpu(), counts, list(range(len(picks))))
+    return picks, ref
+
+
+def test_contiguous_activations_past_4gib():
+    """Activations of 4.4 GB (bf16 [271000, 8192]): the second expert's rows and
+    rows around the 2 GiB and 4 GiB byte offsets of the first, against the
+    oracle; every tile's buffer starts at a 64-bit offset."""
+    counts, K, N = [263000, 8000], 8192, 256
+    announce("contiguous activations past 4 GiB", counts, K, N)
+    w = wl.Workload("big", "contiguous", "bf16", counts, K=K, N=N, values="normal", seed=43)
+    inp = wl.materialize(w, "cuda")
+    assert inp["A"].numel() * 2 > 1 << 32
+    C, ws = P.run_contiguous(w, inp, block_m=0)
+    P.check_stats(mg.stats_read(ws), counts)
+    row_2g, row_4g = (1 << 31) // (K * 2), (1 << 32) // (K * 2)
+    first = [0, 1] + list(range(row_2g - 20, row_2g + 20)) + list(range(row_4g - 300, counts[0]))
+    second = sorted({counts[0] + b + random.Random(b).randrange(16) for b in range(0, counts[1] - 15, 16)}
+                    | {counts[0], sum(counts) - 1})
+    picks, ref = _rows_against_oracle(inp["A"], inp["B"], [(r, 0) for r in first] + [(r, 1) for r in second])
+    P.check_gemm(P.rows_as_float(C, [r for r, _ in picks]), ref, "bf16", what="activations past 4 GiB")
+
+
+def test_masked_capacity_buffer_past_4gib():
+    """A masked capacity buffer of 4.4 GB (bf16 [32, 8448, 8192]) with the valid
+    rows in experts around the 2 GiB and 4 GiB offsets and in the last one."""
+    G, cap, K, N = 32, 8448, 8192, 256
+    counts = [0] * G
+    for e, m in ((0, 5), (15, 300), (16, 130), (30, 64), (31, 1000)):
+        counts[e] = m
+    announce("masked capacity buffer past 4 GiB", counts)
+    w = wl.Workload("bigm", "masked", "bf16", counts, K=K, N=N, cap=cap, values="normal", seed=44)
+    inp = wl.materialize(w, "cuda")
+    assert inp["A"].numel() * 2 > 1 << 32
+    C = P.sentinel_like((G, cap, N))
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"])
+    torch.cuda.synchronize()
+    pairs = [(e, r) for e in range(G) for r in range(counts[e])]
+    picks, ref = _rows_against_oracle(inp["A"], inp["B"], [(e * cap + r, e) for e, r in pairs])
+    got = C.reshape(G * cap, N)[torch.tensor([r for r, _ in picks], device="cuda")].float().cpu().double().numpy()
+    P.check_gemm(got, ref, "bf16", what="masked past 4 GiB")
+    inval = C.reshape(G * cap, N)[torch.tensor([e * cap + r for e in (15, 16, 31) for r in (counts[e], cap - 1)],
+                                               device="cuda")]
+    assert bool((inval.view(torch.int16) == P.SENTINEL_BITS).all())
+
+
 def test_contiguous_e8m0_widest_output():
     """E8M0 scales at their widest supported output, N = 32768 (N / 128 = 256
     scale bytes per row), on a small ragged histogram; sampled rows."""
