@@ -409,7 +409,7 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
 
 /*
  * Expert MLP in one launch: the SwiGLU projection and the down projection of
- * every expert in one persistent kernel (the DeepGEMM record's "Arithmetic
+ * every expert in one kernel launch (the DeepGEMM record's "Arithmetic
  * intensity" section: Mega MoE fuses linear 1, SwiGLU and linear 2 so the
  * activations between them need not round-trip HBM; the dispatch and combine
  * it also fuses are inter-GPU and not part of this call).  It computes
@@ -434,9 +434,11 @@ moegg_status_t moegg_grouped_gemm_swiglu_scheduled(
  *            list is always 256 rows tall).
  *   dtype    MOEGG_FP8_E4M3 or MOEGG_FP8_E4M3_SCALE_KM (else UNSUPPORTED).
  *   ws       moegg_workspace_bytes(G, rows_total), 256-byte aligned; also
- *            holds the row tiles' completion counters and work queues.
+ *            holds the row tiles' completion counters, which the call's
+ *            scheduler launch clears.
  * Constraints: K % 128 == 0, I % 128 == 0, N2 % 256 == 0, every pointer
- * 16-byte aligned (scales 4).  One workgroup per compute unit; a row tile's
+ * 16-byte aligned (scales 4).  One workgroup per tile, every SwiGLU tile
+ * ahead of every down-projection tile in the grid; a row tile's
  * down-projection tiles wait (bounded) for all of its SwiGLU tiles.  A wait
  * that exceeds its bound sets MOEGG_FLAG_SYNC_TIMEOUT in the stats (the
  * affected Y rows are then unspecified); moegg_stats_read shows it.  Calls that

@@ -463,7 +463,7 @@ def grouped_gemm_swiglu_scheduled(A, W1, H, G: int, ws, A_scale=None, W1_scale=N
 
 def expert_mlp_fused(A, W1, W2, H, Y, m_sizes, ws, A_scale, W1_scale, W2_scale, H_scale, seg_align: int = 1,
                      b_layout: int = B_NK, scale_km: bool = False, stream=None):
-    """Y = SwiGLU(A W1) W2 per expert in one persistent launch (see moegg.h): e4m3 A [rows, K], W1
+    """Y = SwiGLU(A W1) W2 per expert in one launch (see moegg.h): e4m3 A [rows, K], W1
     [G, 2I, K] (gate/up interleaved), W2 [G, N2, I], fp32 scales; H e4m3 [rows, I] with H_scale the
     caller's intermediate, written and read back by the kernel; Y bf16 [rows, N2].  b_layout B_NK or
     B_NK_PANEL (P = PANEL_CONTIGUOUS) for both weights; scale_km: A_scale [K/128, rows] in and

@@ -11,6 +11,7 @@
 
 #include "../../include/moegg.h"
 #include "launch.hpp"
+#include "tile_order.hpp"
 #include "workspace.hpp"
 
 
@@ -342,17 +343,16 @@ moegg_status_t moegg_expert_mlp_fused(const void* A, const float* A_scale, const
     if (!ws || !aligned(ws, 256)) return MOEGG_ERR_WORKSPACE;
     const WsLayout L = ws_layout(G, rows_total);
     if (ws_bytes < L.total) return MOEGG_ERR_WORKSPACE;
-    if (((rows_total + 255) / 256 + G) * (int64_t)(2 * I / 256 + N2 / 256) > INT32_MAX) return MOEGG_ERR_UNSUPPORTED;
+    // at most ceil(rows_total / 256) + G row tiles at the 256-row height
+    const int64_t max_rt = (rows_total + 255) / 256 + G;
+    const int64_t blocks = mlp_blocks(max_rt, 2 * I / 256, N2 / 256);
+    if (blocks > INT32_MAX) return MOEGG_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_status(e, "device query");
-    e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, 256, 2 * I / 256, 0, ws, L.max_tiles, s);
-    if (e != hipSuccess) return hip_status(e, "scheduler launch");
+    // the scheduler also clears the completion counters (no memset node under graph capture)
     uint32_t* sync = (uint32_t*)((unsigned char*)ws + L.sync);
-    e = launch_zero(sync, L.max_tiles + kSyncExtra, s);
-    if (e != hipSuccess) return hip_status(e, "sync clear launch");
+    hipError_t e = launch_sched(m_sizes, G, rows_total, seg_align, 0, 0, 256, 2 * I / 256, 0, ws, L.max_tiles, s,
+                                sync, L.max_tiles);
+    if (e != hipSuccess) return hip_status(e, "scheduler launch");
     MlpArgs a{};
     a.l1 = ContigArgs{A, A_scale, W1, W1_scale, H, nullptr, (const unsigned char*)ws, G, K, 2 * I, 0,
                       (int)rows_total, H_scale};
@@ -360,14 +360,11 @@ moegg_status_t moegg_expert_mlp_fused(const void* A, const float* A_scale, const
     a.l1.a_scale_km = a.l2.a_scale_km = dtype == MOEGG_FP8_E4M3_SCALE_KM;
     a.l1.b_panel = a.l2.b_panel = layout_panel(b_layout);
     a.sync = sync;
-    a.max_tiles = (int)L.max_tiles;
-    a.n_queues = std::min(std::max(cus / 32, 1), kSyncExtra);
-    // one workgroup per work item: at most ceil(rows_total / 256) + G row tiles, each with 2I/256 + N2/256 items
-    const int64_t items = ((rows_total + 255) / 256 + G) * (int64_t)(2 * I / 256 + N2 / 256);
-    e = launch_mlp_fused(a, (int)std::min<int64_t>(items, INT32_MAX), s);
+    a.l1_blocks = (int)mlp_l1_blocks(max_rt, 2 * I / 256);
+    e = launch_mlp_fused(a, (int)blocks, s);
     if (debug_on())
-        fprintf(stderr, "moegg: expert MLP fused G=%d rows=%lld K=%d I=%d N2=%d dtype=%d b_layout=%d CUs=%d\n", G,
-                (long long)rows_total, K, I, N2, (int)dtype, (int)b_layout, cus);
+        fprintf(stderr, "moegg: expert MLP fused G=%d rows=%lld K=%d I=%d N2=%d dtype=%d b_layout=%d blocks=%lld\n", G,
+                (long long)rows_total, K, I, N2, (int)dtype, (int)b_layout, (long long)blocks);
     return hip_status(e, "fused expert MLP launch");
 }
 

@@ -42,7 +42,6 @@
 #include "device.hpp"
 #include "launch.hpp"
 #include "workspace.hpp"
-#include "mlp_order.hpp"
 #include "tile_order.hpp"
 
 namespace moegg {
@@ -225,8 +224,9 @@ __device__ __forceinline__ v4i frag_mn_bf16(const char* tile, int n0, int kk) {
 
 // ---------------------------------------------------------------- work items
 
-// Work item -> (row tile, column tile).  Items come in groups of up to 4
-// row tiles; within a group the column tile varies slowest.
+// K-grouped work item of one expert -> (i tile, j tile) of its dW.  Items come
+// in groups of up to 4 i tiles; within a group the j tile varies slowest.  (The
+// contiguous GEMM and the expert MLP use item_to_list_tiles.)
 __device__ __forceinline__ void item_to_tiles(int item, int n_rt, int n_ct, int& rt, int& ct) {
     const int GM = 4;
     int per_group = GM * n_ct;
@@ -234,11 +234,6 @@ __device__ __forceinline__ void item_to_tiles(int item, int n_rt, int n_ct, int&
     int gm = min(GM, n_rt - g * GM);
     ct = r / gm;
     rt = g * GM + (r - ct * gm);
-}
-
-// Block -> work item: XCD x (= b % 8) takes items in runs of 32.
-__device__ __forceinline__ int block_to_item(int b) {
-    return (b >> 8) * 256 + (b & 7) * 32 + ((b & 255) >> 3);
 }
 
 // ---------------------------------------------------------------- contiguous / masked
@@ -1036,29 +1031,17 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_auto_kernel(ContigArgs p)
 
 // ---------------------------------------------------------------- expert MLP, one launch
 
-// XCD this wave runs on (hardware register XCC_ID, bits 3:0).
-__device__ __forceinline__ unsigned xcc_id() {
-    unsigned x;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-    return x & 0xFu;
-}
-
 constexpr int kMlpSpinLimit = 1 << 15;      // polls (with a short sleep each) before a wait gives up
 
 // The expert MLP (the compute half of the DeepGEMM record's Mega MoE: both
 // expert GEMMs and SwiGLU in one kernel, "Arithmetic intensity") in one
 // launch, so the down projection of a row tile starts as soon as its H is
 // complete and the two GEMMs share one tail instead of two.  (H still goes
-// through its buffer: each release writes the XCD's L2 back.)  Each workgroup runs one
-// work item taken from a queue: the row tiles are cut into n_queues
-// consecutive ranges, one queue per XCD, so an expert's row tiles mostly share
-// one XCD's L2.  A workgroup takes a ticket from the queue of the XCD it runs
-// on (hardware XCC_ID), or, once that queue is used up, from the others in
-// turn.  Exactly as many workgroups take part as there are items (the rest exit
-// at once), and each takes one, so every item is taken; which workgroup runs
-// which item does not depend on dispatch order.  (A persistent form that loops
-// over items ran its tiles about 10 % slower: values hoisted out of the item
-// loop stayed live across it and cost the main loop its LDS read-ahead.)
+// through its buffer: each release writes the XCD's L2 back.)  One workgroup
+// per work item, statically: the grid holds all L1 items first, then all L2
+// items, each phase in the contiguous GEMM's order (runs of 32 items per XCD,
+// row tiles of one expert in groups of four), so each phase shares operands
+// across XCDs as the two launches of the chain do.
 //   L1 item (rt, c): the SwiGLU tile writing H rows of rt, columns [128c,
 //   128c + 128), and their scales; every wave waits for its stores, then one
 //   thread releases (agent scope) an increment of rt's completion counter.
@@ -1067,53 +1050,29 @@ constexpr int kMlpSpinLimit = 1 << 15;      // polls (with a short sleep each) b
 //   then the tile of Y = H W2 runs.  The wait is bounded: past the poll limit
 //   it sets MOEGG_FLAG_SYNC_TIMEOUT, which also ends every later wait at once,
 //   and goes on (those output rows are then unspecified).
-// Deadlock-free: an L2 item waits only on L1 items that its queue handed out
-// under earlier tickets, to workgroups that are running them and wait on
-// nothing.
+// Deadlock-free: an L2 workgroup waits only on L1 workgroups, which wait on
+// nothing and all have lower indices.  Workgroups are dispatched in index
+// order, so when an L2 workgroup runs every L1 workgroup has been dispatched
+// and finishes.  The lone tile of an expert (its only row tile, not full)
+// streams its weight panel, as in the contiguous GEMM.
 __global__ __launch_bounds__(512, 1) void expert_mlp_fused_kernel(MlpArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];
-    __shared__ int pick_s[2];
     using C = Contig256<true>;
     const WsLayout L = ws_layout(p.l1.G, 0);
     const Control* ctl = (const Control*)(p.l1.ws + L.control);
     if (ctl->block_m != 256) return;         // needs the 256-row schedule
-    const int n_rt = ctl->n_tiles;
+    const moegg_tile_t* tiles = (const moegg_tile_t*)(p.l1.ws + L.tiles);
     const int C1 = p.l1.N / 256, C2 = p.l2.N / 256;
-    if ((int64_t)blockIdx.x >= (int64_t)n_rt * (C1 + C2)) return;
-    const int nq = p.n_queues;
-    uint32_t* qheads = p.sync + p.max_tiles;
-    if (threadIdx.x == 0) {
-        const int x0 = (int)(xcc_id() % (unsigned)nq);
-        int q = -1, k = 0;
-        for (int i = 0; i < nq; ++i) {
-            const int x = x0 + i < nq ? x0 + i : x0 + i - nq;
-            int r0, R;
-            mlp_queue_rows(n_rt, x, nq, r0, R);
-            const uint32_t len = (uint32_t)(R * (C1 + C2));
-            if (len == 0) continue;
-            if (i > 0 && __hip_atomic_load(&qheads[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len)
-                continue;                     // used up: no ticket needed
-            const uint32_t t = atomicAdd(&qheads[x], 1u);
-            if (t < len) {
-                q = x;
-                k = (int)t;
-                break;
-            }
-        }
-        pick_s[0] = q;
-        pick_s[1] = k;
-    }
-    __syncthreads();
-    const int q = pick_s[0];
-    if (q < 0) return;                        // not reached: every taking part workgroup finds an item
-    int r0, R, phase, j, c;
-    mlp_queue_rows(n_rt, q, nq, r0, R);
-    if (!mlp_item(pick_s[1], R, C1, C2, phase, j, c)) return;
-    const int rt = r0 + j;
-    const moegg_tile_t t = ((const moegg_tile_t*)(p.l1.ws + L.tiles))[rt];
+    int phase, rt, c;
+    if (!mlp_block_item((int)blockIdx.x, p.l1_blocks, ctl->n_tiles, C1, C2, tiles, phase, rt, c)) return;
+    const moegg_tile_t t = tiles[rt];
+    const bool alone = t.tile == 0 && t.rows_valid < C::BM;
     uint32_t* done = p.sync + rt;
     if (phase == 1) {
-        contig_tile<C, false, 2>(p.l1, lds, t.expert, t.row_start, t.rows_valid, c);
+        if (alone)
+            contig_tile<C, false, 2, true>(p.l1, lds, t.expert, t.row_start, t.rows_valid, c);
+        else
+            contig_tile<C, false, 2>(p.l1, lds, t.expert, t.row_start, t.rows_valid, c);
         wait_vmcnt<0>();                      // this wave's H stores are done
         __syncthreads();
         if (threadIdx.x == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -1134,13 +1093,11 @@ __global__ __launch_bounds__(512, 1) void expert_mlp_fused_kernel(MlpArgs p) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
-        contig_tile<C, false, 0>(p.l2, lds, t.expert, t.row_start, t.rows_valid, c);
+        if (alone)
+            contig_tile<C, false, 0, true>(p.l2, lds, t.expert, t.row_start, t.rows_valid, c);
+        else
+            contig_tile<C, false, 0>(p.l2, lds, t.expert, t.row_start, t.rows_valid, c);
     }
-}
-
-__global__ void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
 }
 
 // ---------------------------------------------------------------- K-grouped
@@ -1469,13 +1426,6 @@ static hipError_t launch_k_grouped_t(const KGroupedArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     const int64_t items = (int64_t)a.G * (a.Mw / C::BM) * (a.Nw / C::BN);
     hipLaunchKernelGGL(k, dim3(round256(items)), dim3(C::THREADS), C::LDS_BYTES, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero(uint32_t* p, int64_t n_words, hipStream_t s) {
-    if (n_words <= 0) return hipSuccess;
-    const int blocks = (int)std::min<int64_t>((n_words + 255) / 256, 1024);
-    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, p, n_words);
     return hipGetLastError();
 }
 

@@ -28,9 +28,8 @@ struct ContigArgs {
 // C_scale = H_scale, N = 2I), l2 the down projection on H (A = H, K = I, N = N2).
 struct MlpArgs {
     ContigArgs l1, l2;
-    uint32_t* sync;               // per-row-tile completion counters [max_tiles], then the queue heads
-    int max_tiles;
-    int n_queues;                 // one work queue per XCD
+    uint32_t* sync;               // per-row-tile completion counters [max_tiles], zero at launch
+    int l1_blocks;                // blocks [0, l1_blocks) run L1 items, the rest L2 items
 };
 
 struct KGroupedArgs {
@@ -47,7 +46,7 @@ struct KGroupedArgs {
 // mode 0: contiguous (tile list); mode 1: masked (stats only).
 hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int seg_align, int cap, int mode,
                         int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
-                        hipStream_t stream);
+                        hipStream_t stream, uint32_t* clear = nullptr, int64_t n_clear = 0);
 // exemplar-matching tile height (moegg_schedule_exemplar); exemplars: device
 // array of n_ex entries
 hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_total, int seg_align, int n_col_tiles,
@@ -68,7 +67,6 @@ hipError_t launch_contiguous_swiglu(const ContigArgs& a, bool fp8, bool w4, int6
 hipError_t launch_masked(const ContigArgs& a, bool fp8, bool e8m0, bool w4, bool b_kn, hipStream_t s);
 hipError_t launch_k_grouped(const KGroupedArgs& a, bool fp8, bool e8m0, hipStream_t s);
 // n_words 32-bit zeros at p (a fill kernel: graph-capturable, no memset node)
-hipError_t launch_zero(uint32_t* p, int64_t n_words, hipStream_t s);
 // the fused expert MLP on fp8 operands (e4m3 A, W1, H, W2 with fp32 scales); one workgroup per
 // work item, n_workgroups at least the items the schedule can produce
 hipError_t launch_mlp_fused(const MlpArgs& a, int n_workgroups, hipStream_t s);

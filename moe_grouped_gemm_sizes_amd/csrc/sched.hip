@@ -205,11 +205,15 @@ __device__ int select_exemplar(const int32_t* m_s, int32_t* srt_s, int64_t (*lor
 // Thread t owns a contiguous run of ceil(G / 256) experts, so block scans run
 // in expert order and, up to 256 experts, every per-expert loop runs once.
 // Those loops stay rolled (values go through LDS) to keep the kernel's code
-// small: it runs cold before every GEMM.
+// small: it runs cold before every GEMM.  It also zeroes n_clear words at
+// clear (the expert MLP's completion counters), so a captured call needs no
+// memset node.
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(
     const int32_t* __restrict__ counts, int G, int64_t rows_total, int seg_align, int cap,
     int mode, int block_m_req, int n_col_tiles, int exec_block_m, unsigned char* __restrict__ ws,
-    int64_t max_tiles, const moegg_exemplar_t* __restrict__ exemplars, int n_ex, int hysteresis) {
+    int64_t max_tiles, const moegg_exemplar_t* __restrict__ exemplars, int n_ex, int hysteresis,
+    uint32_t* __restrict__ clear, int64_t n_clear) {
+    for (int64_t i = threadIdx.x; i < n_clear; i += kSchedThreads) clear[i] = 0u;   // a caller's counters
     constexpr int NV = 3 + MOEGG_NUM_Q + kNumCand + 2;       // U, active, sum_sq, P(q) x6, tiles(q) x3, tails x2
     __shared__ int64_t wave_buf[kWaves];
     __shared__ int64_t sums_buf[kWaves][NV];
@@ -495,10 +499,10 @@ namespace moegg {
 
 hipError_t launch_sched(const int32_t* counts, int G, int64_t rows_total, int seg_align, int cap, int mode,
                         int block_m_req, int n_col_tiles, int exec_block_m, void* ws, int64_t max_tiles,
-                        hipStream_t stream) {
+                        hipStream_t stream, uint32_t* clear, int64_t n_clear) {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, counts, G, rows_total, seg_align,
                        cap, mode, block_m_req, n_col_tiles, exec_block_m, (unsigned char*)ws, max_tiles,
-                       (const moegg_exemplar_t*)nullptr, 0, 0);
+                       (const moegg_exemplar_t*)nullptr, 0, 0, clear, n_clear);
     return hipGetLastError();
 }
 
@@ -506,7 +510,8 @@ hipError_t launch_sched_exemplar(const int32_t* counts, int G, int64_t rows_tota
                                  const moegg_exemplar_t* exemplars, int n_ex, int hysteresis, void* ws,
                                  int64_t max_tiles, hipStream_t stream) {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, counts, G, rows_total, seg_align, 0,
-                       0, 0, n_col_tiles, 0, (unsigned char*)ws, max_tiles, exemplars, n_ex, hysteresis);
+                       0, 0, n_col_tiles, 0, (unsigned char*)ws, max_tiles, exemplars, n_ex, hysteresis,
+                       (uint32_t*)nullptr, (int64_t)0);
     return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
-// Order of the contiguous GEMM's work items over the scheduler's tile list.
-// Host and device code: a host test checks on the CPU that every (row tile,
-// column tile) pair is handed out exactly once.
+// Order of the contiguous GEMM's and the one-launch expert MLP's work items
+// over the scheduler's tile list.  Host and device code: a host test checks on
+// the CPU that every (row tile, column tile) pair is handed out exactly once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +32,37 @@ __host__ __device__ inline void item_to_list_tiles(int item, int n_rt, int n_ct,
     const int r = item - first * n_ct;
     ct = r / gm;
     rt = first + (r - ct * gm);
+}
+
+// Block -> work item: XCD x (= b % 8, the dispatcher's round robin over the
+// eight XCDs) takes items in runs of 32, so each run of 256 blocks is one
+// permutation of 256 items.
+__host__ __device__ inline int block_to_item(int b) {
+    return (b >> 8) * 256 + (b & 7) * 32 + ((b & 255) >> 3);
+}
+
+// Grid of the one-launch expert MLP over a 256-row tile list of at most
+// max_rt row tiles: first the SwiGLU-projection (L1) items, max_rt * c1 of
+// them rounded up to whole runs of 256 blocks, then the down-projection (L2)
+// items, max_rt * c2 rounded likewise.  Every L1 block has a lower index than
+// every L2 block.
+__host__ __device__ inline int64_t mlp_l1_blocks(int64_t max_rt, int c1) { return (max_rt * c1 + 255) / 256 * 256; }
+__host__ __device__ inline int64_t mlp_blocks(int64_t max_rt, int c1, int c2) {
+    return mlp_l1_blocks(max_rt, c1) + (max_rt * c2 + 255) / 256 * 256;
+}
+
+// Block b of that grid -> phase (1 = L1, 2 = L2), row tile rt and column
+// tile ct of an n_rt-tile list, each phase in the contiguous GEMM's order;
+// false for a block with no item.
+__host__ __device__ inline bool mlp_block_item(int b, int l1_blocks, int n_rt, int c1, int c2,
+                                               const moegg_tile_t* tiles, int& phase, int& rt, int& ct) {
+    const bool l1 = b < l1_blocks;
+    const int nc = l1 ? c1 : c2;
+    const int item = block_to_item(l1 ? b : b - l1_blocks);
+    if (item >= n_rt * nc) return false;
+    phase = l1 ? 1 : 2;
+    item_to_list_tiles(item, n_rt, nc, tiles, false, rt, ct);
+    return true;
 }
 
 }  // namespace moegg

@@ -22,7 +22,6 @@ constexpr int kMaxExperts = 4096;
 constexpr int kMinBlockM = 64;     // smallest schedulable tile height
 constexpr int kExecRows = 16;      // MFMA row block: rows are executed in 16s
 constexpr int kNumCand = 3;        // candidate tile heights 64, 128, 256
-constexpr int kSyncExtra = 16;     // sync words past the per-tile counters: queue heads
 
 // Tag of a valid exemplar-selector state in the control block.
 constexpr uint64_t kSelectorTag = 0x4D4F454753454C31ull;
@@ -62,7 +61,7 @@ __host__ __device__ inline WsLayout ws_layout(int G, int64_t max_rows) {
     L.tiles = L.groups + align256(sizeof(int64_t) * (size_t)(G + 1));
     L.max_tiles = (max_rows + kMinBlockM - 1) / kMinBlockM + G;
     L.sync = L.tiles + align256(sizeof(moegg_tile_t) * (size_t)L.max_tiles);
-    L.total = L.sync + align256(sizeof(uint32_t) * (size_t)(L.max_tiles + kSyncExtra));
+    L.total = L.sync + align256(sizeof(uint32_t) * (size_t)L.max_tiles);
     return L;
 }
 

@@ -1,4 +1,4 @@
-"""GPU parity of the expert MLP in one persistent launch (moegg_expert_mlp_fused).
+"""GPU parity of the expert MLP in one launch (moegg_expert_mlp_fused).
 
 The fused kernel runs the same tile code as the two-launch chain (scheduler at
 block_m = 256, the SwiGLU call with the e4m3 H epilogue, the fp8 contiguous

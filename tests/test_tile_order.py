@@ -4,7 +4,9 @@ launched) and maps every work item of the oracle's tile lists (every height and
 per-expert heights, 200 random histograms plus the workloads, several
 column-tile counts) to its (row tile, column tile): each pair once, all in
 range.  The groups of row tiles the order forms are also checked to stay within
-one expert."""
+one expert.  The one-launch expert MLP's grid (L1 blocks, then L2 blocks) is
+checked over the same lists: each (phase, row tile, column tile) once, every L1
+block ahead of every L2 block."""
 import os
 import random
 import subprocess
