@@ -172,6 +172,33 @@ def test_contiguous_small_full_compare(case, block_m, b_layout):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("height", [64, 128])
+def test_contiguous_one_launch_long_list(dtype, height):
+    """The one-launch kernel (block_m = 0) on a list the scheduler cut at 64
+    or 128 rows: a 66000-row expert and a few small ones, one column tile, so
+    1037 work items at 64 rows and 520 at 128 run through the launch that
+    reads the height from the control block.  Every valid row is written (no
+    sentinel left) and every 7th row, plus all rows of the small experts, is
+    checked against the oracle."""
+    counts, K, N = [66000, 3, 130, 0, 64], 128, 256
+    announce("one launch long list", dtype, height, counts)
+    w, inp = small_contig(counts, K, N, dtype, seed=21)
+    ws = mg.workspace(w.G, w.rows_total)
+    mg.schedule(inp["counts"], w.rows_total, ws, seg_align=1, block_m=height, N=N)
+    C = P.sentinel_like((w.rows_total, N))
+    mg.grouped_gemm_contiguous_scheduled(inp["A"], inp["B"], C, w.G, ws, inp.get("A_scale"), inp.get("B_scale"),
+                                         block_m=0, b_layout=mg.B_KN)
+    torch.cuda.synchronize()
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, height)
+    assert not bool((C[:sum(counts)].view(torch.int16) == P.SENTINEL_BITS).any())
+    rows = sorted(set(range(0, 66000, 7)) | set(range(65990, sum(counts))))
+    inp_cpu = {k: P.cpu(v) for k, v in inp.items()}
+    ref = P.oracle_contiguous_rows(w, inp_cpu, rows)
+    P.check_gemm(P.rows_as_float(C, rows), ref, dtype, what=f"one launch long list {dtype} {height}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_contiguous_integer_exact(dtype):
     """Inputs in {-1, 0, 1}, K <= 256, unit scales: every result is an integer
     of magnitude <= 256, exact in bf16, so GPU == oracle bit for bit."""
