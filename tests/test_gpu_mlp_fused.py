@@ -136,8 +136,9 @@ def test_fused_mlp_small(b_layout, scale_km):
 
 @pytest.mark.parametrize("seed", [0, 1])
 def test_fused_mlp_many_row_tiles(seed):
-    """Enough 256-row tiles that every XCD queue holds more rows than the L1/L2 lag,
-    with ragged tails in each expert: bit for bit against the chain."""
+    """Enough 256-row tiles that each phase of the grid spans several runs of
+    256 workgroups, with ragged tails in each expert: bit for bit against the
+    chain."""
     rng = random.Random(900 + seed)
     counts = [rng.choice([0, 1, 77, 255, 256, 257, 600, 1500]) for _ in range(24)]
     K, I, N2 = 512, 512, 768
@@ -155,13 +156,25 @@ def test_fused_mlp_tiny_and_single_expert():
 
 
 def test_fused_mlp_one_column_tile_each():
-    """I = 128 and N2 = 256: one SwiGLU item and one down-projection item per row tile,
-    so every queue alternates single items of the two phases."""
+    """I = 128 and N2 = 256: one SwiGLU item and one down-projection item per
+    row tile, so the two phases of the grid hold the same number of items."""
     counts = [300, 5, 0, 700, 1]
     K, I, N2 = 128, 128, 256
     announce("fused expert MLP one column tile each", counts)
     inp = operands(counts, K, I, N2, 47, mg.B_NK, False)
     check_against_chain(inp, counts, I, N2, mg.B_NK, False)
+
+
+def test_fused_mlp_many_small_experts():
+    """300 experts of 0..300 rows: most row tiles are an expert's only tile
+    (their weight panels stream in both phases), and the grid's L1 part alone
+    spans several runs of 256 workgroups: bit for bit against the chain."""
+    rng = random.Random(951)
+    counts = [rng.choice([0, 1, 40, 129, 255, 256, 300]) for _ in range(300)]
+    K, I, N2 = 128, 256, 512
+    announce("fused expert MLP many small experts", "rows", sum(counts))
+    inp = operands(counts, K, I, N2, 48, mg.B_NK_PANEL, False)
+    check_against_chain(inp, counts, I, N2, mg.B_NK_PANEL, False)
 
 
 def test_fused_mlp_all_experts_empty():
