@@ -6,8 +6,7 @@
 //   [...]       int32 order[G]        (K-grouped: experts, longest first)
 //   [...]       int64 groups[G + 1]   (K-grouped fp8: first 128-row scale group of each expert)
 //   [...]       moegg_tile_t tiles[max_tiles]
-//   [...]       uint32 sync[max_tiles + 16]   (fused expert MLP: per-row-tile completion counters, then
-//                                              one queue head per XCD)
+//   [...]       uint32 sync[max_tiles]        (fused expert MLP: per-row-tile completion counters)
 // Every region starts on a 256-byte boundary.  The regions up to `tiles` depend
 // on G alone; `sync` follows the tile list, so its offset also depends on max_rows.
 #pragma once

@@ -200,8 +200,9 @@ def test_fused_mlp_all_experts_empty():
 
 
 def test_fused_mlp_graph_replay():
-    """Captured in a HIP graph and replayed: the completion counters and queues are
-    cleared by a fill kernel inside the call, so every replay equals the eager run."""
+    """Captured in a HIP graph and replayed: the completion counters are cleared
+    by the call's scheduler kernel (no memset node), so every replay equals the
+    eager run."""
     counts = [300, 0, 513, 40]
     K, I, N2 = 256, 256, 512
     G, R = len(counts), sum(counts)
