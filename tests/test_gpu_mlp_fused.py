@@ -177,6 +177,55 @@ def test_fused_mlp_many_small_experts():
     check_against_chain(inp, counts, I, N2, mg.B_NK_PANEL, False)
 
 
+def test_fused_mlp_aligned_segments():
+    """seg_align = 128: each expert's segment starts on a multiple of 128 rows,
+    with unused rows (holding junk codes) between segments.  One launch against
+    the chain scheduled with the same alignment, bit for bit on H, its scales
+    and Y; the rows between segments keep the sentinel in Y; H and Y on every
+    valid row against the oracle."""
+    counts = [70, 0, 300, 6, 129, 1]
+    K, I, N2, align = 256, 256, 512, 128
+    announce("fused expert MLP aligned segments", counts, "seg_align", align)
+    inp = operands(counts, K, I, N2, 49, mg.B_NK, False)
+    packed, offs = acc.segment_offsets(counts, 1), acc.segment_offsets(counts, align)
+    R, G = offs[-1], len(counts)
+    A = torch.full((R, K), 0x3C, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    As = torch.full((R, K // 128), 3.0, device="cuda")
+    for e, m in enumerate(counts):
+        A[offs[e]:offs[e] + m] = inp["A"][packed[e]:packed[e] + m]
+        As[offs[e]:offs[e] + m] = inp["A_scale_op"][packed[e]:packed[e] + m]
+    outs = []
+    for fused in (True, False):
+        ws = mg.workspace(G, R)
+        H, Hs = h_buffers(R, I, False)
+        Y = P.sentinel_like((R, N2))
+        if fused:
+            mg.expert_mlp_fused(A, inp["W1_op"], inp["W2_op"], H, Y, inp["counts"], ws, As, inp["W1_scale"],
+                                inp["W2_scale"], Hs, seg_align=align)
+        else:
+            mg.schedule(inp["counts"], R, ws, seg_align=align, block_m=256, N=2 * I)
+            mg.grouped_gemm_swiglu_scheduled(A, inp["W1_op"], H, G, ws, As, inp["W1_scale"], block_m=256,
+                                             H_scale=Hs, b_layout=mg.B_NK)
+            mg.grouped_gemm_contiguous_scheduled(H, inp["W2_op"], Y, G, ws, Hs, inp["W2_scale"], block_m=256,
+                                                 b_layout=mg.B_NK)
+        torch.cuda.synchronize()
+        st = mg.stats_read(ws)
+        assert st.error_flags == 0
+        outs.append((H, Hs, Y))
+    valid = torch.tensor([r for e, m in enumerate(counts) for r in range(offs[e], offs[e] + m)], device="cuda")
+    for name, a, b in zip(("H", "H_scale", "Y"), outs[0], outs[1]):
+        same_bits(a[valid], b[valid], name)
+    assert P.untouched_rows_ok(outs[0][2], counts, align)
+    # and against the oracle, on the packed operands the aligned ones were copied from
+    H, Hs, Y = (t[valid] for t in outs[0])
+    rows = list(range(sum(counts)))
+    cpu = {k: P.cpu(v) for k, v in inp.items()}
+    h = omlp.swiglu_rows(cpu["A"], cpu["W1"], counts, rows, A_scale=cpu["A_scale"], W1_scale=cpu["W1_scale"])
+    q, s = check_fp8_h(H, Hs, h, rows)
+    P.check_gemm(Y.float().cpu().double().numpy(), oracle_y(cpu, q, s, counts, rows, N2), "fp8",
+                 bound="chain_e4m3", what="fused mlp aligned y")
+
+
 def test_fused_mlp_all_experts_empty():
     """Every count 0 on a 4-row buffer: no tile, nothing written, no wait."""
     K, I, N2, G, R = 128, 128, 256, 3, 4
