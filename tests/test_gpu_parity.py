@@ -580,6 +580,28 @@ def test_masked_counts_out_of_range_are_clamped():
     assert torch.equal(C2.view(torch.int16), C.view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("cap", [1, 3, 17])
+def test_masked_tiny_capacity(dtype, cap):
+    """Capacity buffers smaller than one MFMA row block: a tile's rows past
+    masked_m read zeros from the expert's bounded buffer range, not the next
+    expert's rows.  Counts at, over and under the capacity: flags, clamped
+    stats, every valid row against the oracle, the rest keep the sentinel."""
+    counts = [cap, 0, cap + 5, -2, 1, cap, min(2, cap)]
+    clamped = [min(max(c, 0), cap) for c in counts]
+    announce("masked tiny capacity", dtype, cap, counts)
+    w, inp = masked_case(counts, cap, 256, 256, dtype, seed=61)
+    C = P.sentinel_like((w.G, w.cap, w.N))
+    ws = mg.workspace(w.G, w.G * w.cap)
+    mg.grouped_gemm_masked(inp["A"], inp["B"], C, inp["counts"], ws, inp.get("A_scale"), inp.get("B_scale"))
+    torch.cuda.synchronize()
+    st = mg.stats_read(ws)
+    assert st.error_flags == mg.FLAG_NEGATIVE_COUNT | mg.FLAG_COUNT_OVER_CAP, hex(st.error_flags)
+    ref = acc.summary(clamped)
+    assert (st.U, st.active, st.sum_sq, st.P_at) == (ref["U"], ref["active"], ref["sum_sq"], ref["P"])
+    check_masked(w, inp, C, counts)
+
+
 @pytest.mark.parametrize("scale_km", [False, True])
 def test_masked_fp8_fp32_scales_full_size(scale_km):
     """The masked decode workload's shape (32 experts, cap 256, K 2048, N 7168,
