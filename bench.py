@@ -624,7 +624,8 @@ def main():
     # (one launch that runs whatever height the scheduler chose) unless --block-m fixes a height
     bm_req = {"auto": 0, "exemplar": 0, "per-expert": mg.BLOCK_M_PER_EXPERT}[args.block_m] \
         if not args.block_m.isdigit() else int(args.block_m)
-    exemplars = mg.exemplar_table() if args.block_m == "exemplar" and w.layout == "contiguous" else None
+    exemplars = mg.exemplar_table(dtype=w.dtype) if args.block_m == "exemplar" and w.layout == "contiguous" \
+        else None
     # the kernels take E8M0 bytes; the oracle (cpu_baseline) keeps the same scales as fp32 (the K-grouped
     # step picks its byte arrays itself)
     inp_gpu = dict(inp, A_scale=inp["A_scale_e8m0"], B_scale=inp["B_scale_e8m0"]) \
@@ -697,7 +698,7 @@ def main():
                               "fp32, activation scales [K/128, rows]" if scale_km else "fp32")
                    if w.dtype == "fp8" else None,
                    "cache": "cold (512 MiB written between steps)" if args.cold else "warm",
-                   "tile_choice": "exemplar table (MI355X)" if exemplars is not None else
+                   "tile_choice": f"exemplar table (MI355X, {w.dtype})" if exemplars is not None else
                    ("cost rule" if args.block_m == "auto" else "fixed")},
         "pct_mfma_peak": round(100.0 * eff / peak, 2),
     }

@@ -327,14 +327,18 @@ def schedule(m_sizes: torch.Tensor, rows_total: int, ws: torch.Tensor, seg_align
 
 
 EXEMPLAR_FIELDS = 10            # moegg_exemplar_t: size_class, lorenz[8], block_m (int32 each)
-EXEMPLAR_TABLE_PATH = os.path.join(_HERE, "exemplars_mi355x.json")
+EXEMPLAR_TABLE_PATH = os.path.join(_HERE, "exemplars_mi355x.json")           # fp8 e4m3, fp32 block scales
+EXEMPLAR_TABLE_PATHS = {"fp8": EXEMPLAR_TABLE_PATH, "bf16": os.path.join(_HERE, "exemplars_mi355x_bf16.json")}
 
 
-def exemplar_table(device="cuda", path: Optional[str] = None) -> torch.Tensor:
+def exemplar_table(device="cuda", path: Optional[str] = None, dtype: str = "fp8") -> torch.Tensor:
     """The exemplar table as an int32 [n, 10] device tensor (moegg_exemplar_t rows).
-    Default: the table measured on MI355X that ships with the package."""
+    Default: the table measured on MI355X for the operand type that ships with the
+    package (dtype "fp8": e4m3 with fp32 block scales; "bf16")."""
     import json
-    with open(path or EXEMPLAR_TABLE_PATH) as f:
+    if path is None and dtype not in EXEMPLAR_TABLE_PATHS:
+        raise ValueError(f"dtype: one of {sorted(EXEMPLAR_TABLE_PATHS)} expected, got {dtype!r}")
+    with open(path or EXEMPLAR_TABLE_PATHS[dtype]) as f:
         rows = json.load(f)["exemplars"]
     t = torch.tensor([[r["size_class"], *r["lorenz"], r["block_m"]] for r in rows], dtype=torch.int32)
     return t.to(device)

@@ -12,10 +12,11 @@ benchmarking:
     two) routed rows, Zipf exponents 0 (uniform), 0.8, 1.2 and 2.0 over the
     experts, a fifth of the experts empty (the seeded generator of the
     workloads module);
-  - for each, the contiguous fp8 GEMM (K = 7168, N = 4096, e4m3 with fp32
-    block scales, [G, N, K] weights, 512 MiB written between calls so the
-    operands come from HBM) at every tile configuration: 64, 128 and 256 rows
-    and per-expert heights; the median of 8 timed calls;
+  - for each, the contiguous GEMM (K = 7168, N = 4096; --dtype fp8: e4m3 with
+    fp32 block scales, the default; --dtype bf16: bf16 operands; [G, N, K]
+    weights, 512 MiB written between calls so the operands come from HBM) at
+    every tile configuration: 64, 128 and 256 rows and per-expert heights; the
+    median of 8 timed calls;
   - each entry keeps the histogram, its descriptor as the device computes it
     (moegg_selection_read), the times, and the fastest configuration.
 
@@ -24,8 +25,9 @@ between the table's grid points, other seeds) at every configuration and
 reports, for the exemplar choice and for the cost rule of the contiguous call
 (block_m = 0), the time of the chosen configuration over the fastest one.
 
-Usage, on the GPU:  python -m moe_grouped_gemm_sizes_amd.tune_exemplars [--out PATH]
-                    python -m moe_grouped_gemm_sizes_amd.tune_exemplars --evaluate [--out PATH]
+Usage, on the GPU:  python -m moe_grouped_gemm_sizes_amd.tune_exemplars [--dtype bf16] [--out PATH]
+                    python -m moe_grouped_gemm_sizes_amd.tune_exemplars --evaluate [--dtype bf16] [--out PATH]
+Each dtype has its own table (mg.EXEMPLAR_TABLE_PATHS).
 """
 from __future__ import annotations
 
@@ -51,14 +53,19 @@ EVAL_SKEWS = (0.4, 1.0, 1.6)
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--out", default=mg.EXEMPLAR_TABLE_PATH)
+    ap.add_argument("--out", default=None, help="default: the package's table for --dtype")
+    ap.add_argument("--dtype", choices=sorted(mg.EXEMPLAR_TABLE_PATHS), default="fp8")
     ap.add_argument("--iters", type=int, default=8)
     ap.add_argument("--evaluate", action="store_true")
     ap.add_argument("--hysteresis", type=int, default=0)
     args = ap.parse_args()
+    out_path = args.out or mg.EXEMPLAR_TABLE_PATHS[args.dtype]
     w = wl.workload(3)                        # shapes of the fp8 Zipf workload: 64 experts, K 7168, N 4096
+    if args.dtype == "bf16":
+        w = wl.Workload("exemplar tuning, bf16", "contiguous", "bf16", w.counts, K=w.K, N=w.N, values="normal",
+                        seed=w.seed)
     inp = wl.materialize(w, "cuda", nan_padding=False)
-    A, As, Bs = inp["A"], inp["A_scale"], inp["B_scale"]
+    A, As, Bs = inp["A"], inp.get("A_scale"), inp.get("B_scale")
     B = inp["B"].transpose(1, 2).contiguous()
     del inp
     G, R, N = w.G, w.rows_total, w.N
@@ -69,7 +76,7 @@ def main():
     probe[0, -1] = 256
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     entries = []
-    table = mg.exemplar_table() if args.evaluate else None
+    table = mg.exemplar_table(dtype=args.dtype) if args.evaluate else None
     grid = [(U, s) for U in (EVAL_SIZES if args.evaluate else SIZES) for s in (EVAL_SKEWS if args.evaluate else SKEWS)]
     for U, s in grid:
         seed = (5000 if args.evaluate else 1000) + U + int(10 * s)
@@ -115,20 +122,21 @@ def main():
         gr = math.exp(sum(math.log(e["rule_over_best"]) for e in entries) / len(entries))
         print(f"geomean time over the fastest: exemplar {gx:.4f}, cost rule {gr:.4f}", flush=True)
         out = {"device": torch.cuda.get_device_name(0),
-               "command": "python -m moe_grouped_gemm_sizes_amd.tune_exemplars --evaluate",
+               "command": "python -m moe_grouped_gemm_sizes_amd.tune_exemplars --evaluate --dtype " + args.dtype,
                "geomean_exemplar_over_best": round(gx, 4), "geomean_rule_over_best": round(gr, 4),
                "held_out": entries}
-        with open(args.out, "w") as f:
+        with open(out_path, "w") as f:
             json.dump(out, f, indent=1)
         return
     out = {"device": torch.cuda.get_device_name(0),
-           "workload": "64 experts, K 7168, N 4096, fp8 e4m3 with fp32 block scales, [G,N,K] weights, contiguous, "
-                       "cold caches; median of %d calls per configuration" % args.iters,
-           "command": "python -m moe_grouped_gemm_sizes_amd.tune_exemplars",
+           "workload": "64 experts, K 7168, N 4096, %s, [G,N,K] weights, contiguous, cold caches; median of %d "
+                       "calls per configuration" % ("fp8 e4m3 with fp32 block scales" if args.dtype == "fp8" else
+                                                    "bf16", args.iters),
+           "command": "python -m moe_grouped_gemm_sizes_amd.tune_exemplars --dtype " + args.dtype,
            "exemplars": entries}
-    with open(args.out, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
-    print(f"wrote {len(entries)} exemplars to {args.out}", flush=True)
+    print(f"wrote {len(entries)} exemplars to {out_path}", flush=True)
 
 
 if __name__ == "__main__":

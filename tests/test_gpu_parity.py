@@ -939,13 +939,14 @@ def check_selection(counts, table_rows, got, st, expect_idx, expect_d):
     P.check_stats(st, counts)
 
 
+@pytest.mark.parametrize("dtype", sorted(mg.EXEMPLAR_TABLE_PATHS))
 @pytest.mark.parametrize("name", sorted(SELECT_HISTS))
-def test_exemplar_selection_matches_oracle(name):
+def test_exemplar_selection_matches_oracle(name, dtype):
     """Descriptor, nearest exemplar, distance and the resulting tile list,
-    bit-exact against the oracle, with the shipped MI355X table."""
+    bit-exact against the oracle, with each shipped MI355X table."""
     counts = SELECT_HISTS[name]
-    announce("exemplar selection", name, len(counts))
-    table = mg.exemplar_table()
+    announce("exemplar selection", name, len(counts), dtype)
+    table = mg.exemplar_table(dtype=dtype)
     rows = table.cpu().tolist()
     rows_total = max(1, sum(counts))
     ws = torch.zeros(mg.workspace_bytes(len(counts), rows_total), dtype=torch.uint8, device="cuda")

@@ -89,8 +89,9 @@ def test_planted_mistake_in_the_oracle_fails_a_pin():
     assert wrong != sel.lorenz(c)
 
 
-def test_shipped_exemplar_table_is_well_formed():
-    with open(mg.EXEMPLAR_TABLE_PATH) as f:
+@pytest.mark.parametrize("dtype", sorted(mg.EXEMPLAR_TABLE_PATHS))
+def test_shipped_exemplar_table_is_well_formed(dtype):
+    with open(mg.EXEMPLAR_TABLE_PATHS[dtype]) as f:
         t = json.load(f)
     rows = t["exemplars"]
     assert 1 <= len(rows) <= 256
@@ -101,3 +102,13 @@ def test_shipped_exemplar_table_is_well_formed():
         # the stored descriptor is the one of the stored histogram
         assert (r["size_class"], r["lorenz"]) == (sel.size_class(sum(r["counts"])), sel.lorenz(r["counts"]))
         assert r["block_m"] == int(min(r["times_ms"], key=r["times_ms"].get))
+
+
+def test_exemplar_table_per_dtype():
+    """One table per operand type; the device tensor has one moegg_exemplar_t row per entry."""
+    for dtype, path in mg.EXEMPLAR_TABLE_PATHS.items():
+        with open(path) as f:
+            n = len(json.load(f)["exemplars"])
+        assert tuple(mg.exemplar_table(device="cpu", dtype=dtype).shape) == (n, mg.EXEMPLAR_FIELDS)
+    with pytest.raises(ValueError):
+        mg.exemplar_table(device="cpu", dtype="fp16")
