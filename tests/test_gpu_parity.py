@@ -199,6 +199,26 @@ def test_contiguous_one_launch_long_list(dtype, height):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("seg_align", [3, 7, 100])
+@pytest.mark.parametrize("block_m", [0, 64, 256, mg.BLOCK_M_PER_EXPERT])
+def test_contiguous_odd_segment_alignment(dtype, seg_align, block_m):
+    """Segment starts on multiples of 3, 7 or 100 rows, so tiles start at rows
+    that no power of two divides: every valid row against the oracle, the
+    rows between segments keep the sentinel, the stats exact."""
+    counts = [70, 0, 300, 6, 129, 1, 257]
+    announce("odd alignment", dtype, seg_align, block_m)
+    w, inp = small_contig(counts, 256, 512, dtype, seg_align, seed=71)
+    C, ws = P.run_contiguous(w, inp, block_m=block_m, b_layout=mg.B_NK)
+    st = mg.stats_read(ws)
+    P.check_stats(st, counts, block_m if block_m else None)
+    offs = acc.segment_offsets(counts, seg_align)
+    rows = [r for e, m in enumerate(counts) for r in range(offs[e], offs[e] + m)]
+    ref = P.oracle_contiguous_rows(w, {k: P.cpu(v) for k, v in inp.items()}, rows)
+    P.check_gemm(P.rows_as_float(C, rows), ref, dtype, what=f"odd alignment {seg_align} {block_m}")
+    assert P.untouched_rows_ok(C, counts, seg_align)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_contiguous_integer_exact(dtype):
     """Inputs in {-1, 0, 1}, K <= 256, unit scales: every result is an integer
     of magnitude <= 256, exact in bf16, so GPU == oracle bit for bit."""
