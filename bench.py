@@ -169,6 +169,20 @@ def cpu_baseline(w: wl.Workload, inp, target_s: float = 15.0):
             "sample": f"{len(sample)} output rows x {w.N} columns of this workload (fp64 oracle, {dt:.1f} s)"}
 
 
+def settle(fn, ms: float = 100.0):
+    """Call fn() back to back until about `ms` of GPU time has passed: in a fresh process, or after the GPU
+    has idled, the first tens of milliseconds of work run below the steady state."""
+    t = 0.0
+    while t < ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        t += a.elapsed_time(b)
+
+
 def time_candidates(w: wl.Workload, inp, b_layout: int, scale_km: bool, args):
     """Every candidate tile height of the contiguous GEMM timed on its own (the padding page,
     "Build a routing-shaped benchmark": P, padding fraction, tiles, latency, effective and physical
@@ -177,9 +191,7 @@ def time_candidates(w: wl.Workload, inp, b_layout: int, scale_km: bool, args):
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
     for bm in (64, 128, 256, mg.BLOCK_M_PER_EXPERT):
         sched, gemm, ws = build_step(w, inp, bm, b_layout, bm, None, 0, scale_km=scale_km)
-        for _ in range(3):
-            sched(); gemm()
-        torch.cuda.synchronize()
+        settle(lambda: (sched(), gemm()), 20.0)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
         for i, (a, b) in enumerate(ev):
             if scratch is not None:
@@ -449,11 +461,11 @@ def run_decode_buckets(args):
         inp["B"] = inp["B"].transpose(1, 2).contiguous()
         a_s = inp["A_scale"]
         inp = dict(inp, A_scale=a_s.t().contiguous())
-        cands = time_candidates(w, inp, mg.B_NK, True, args)
         sched, gemm, ws = build_step(w, inp, 0, mg.B_NK, 0, None, 0, scale_km=True)
+        settle(lambda: (sched(), gemm()))
+        cands = time_candidates(w, inp, mg.B_NK, True, args)
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        for _ in range(3):
-            sched(); gemm()
+        settle(lambda: (sched(), gemm()), 20.0)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for i, (a, b) in enumerate(ev):
             scratch.fill_(i & 255)
@@ -483,8 +495,7 @@ def run_decode_buckets(args):
         inp["B"] = mg.pack_panels(inp["B"], mg.B_KN_PANEL, mg.PANEL_MASKED)
         _, gemm, _ = build_step(w, inp, 0, mg.B_KN_PANEL)
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        for _ in range(3):
-            gemm()
+        settle(gemm)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for i, (a, b) in enumerate(ev):
             scratch.fill_(i & 255)
